@@ -1,0 +1,143 @@
+"""Seeded synthetic attention inputs.
+
+The SageAttention2 pages measure end-to-end quality on language, image and
+video generation models (arXiv 2411.10958 abstract page).  Those models are not
+available here, so attention inputs are synthesised with the shapes and value
+structure of such layers: LLM prefill, DiT image generation, video generation
+with a long token sequence, and a long-context sweep.
+
+This module holds no step of the attention method.  It draws random numbers
+(numpy PCG64 via ``default_rng(seed)``), adds per-channel offsets and outlier
+channels, and rounds to the 16-bit input dtype with round-to-nearest-even.  The
+same bits feed the GPU path and the CPU oracle.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str            # "f16" or "bf16"
+    causal: bool
+    seed: int
+    k_offset_std: float = 0.0       # shared per-(b,h) channel offset added to every K token
+    v_offset_std: float = 0.0       # same for V
+    outlier_channels: int = 0       # channels scaled by outlier_scale
+    outlier_scale: float = 1.0
+    outliers_in_k: bool = False     # same channel indices in K as in Q
+    t_noise_scale: float = 0.0      # Student-t(3) noise added to Q and K
+    sm_scale: float | None = None   # default 1/sqrt(D)
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale is not None else 1.0 / math.sqrt(self.D)
+
+    @property
+    def ops(self) -> float:
+        """Attention operations 4*B*H*N^2*D, halved when causal."""
+        o = 4.0 * self.B * self.H * self.N * self.N * self.D
+        return o / 2 if self.causal else o
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+# The five workload families (sizes and distributions of the method's target
+# layers).  The long-context family has three lengths, causal and not.
+TINY = Workload("tiny_b1h2n256d64_f16", 1, 2, 256, 64, F16, False, seed=1, k_offset_std=3.0,
+                note="tiny non-causal; fp16; K channel offset ~N(0,3)")
+LLM = Workload("llm_prefill_b4h32n4096d128_causal", 4, 32, 4096, 128, BF16, True, seed=2, k_offset_std=4.0,
+               outlier_channels=4, outlier_scale=20.0,
+               note="LLM prefill; causal; K offset ~N(0,4); 4 Q outlier channels x20")
+DIT = Workload("dit_b1h24n4608d128", 1, 24, 4608, 128, BF16, False, seed=3, k_offset_std=4.0, v_offset_std=1.0,
+               note="DiT image generation; K offset ~N(0,4); V offset ~N(0,1)")
+VIDEO = Workload("video_b2h48n17776d64", 2, 48, 17776, 64, BF16, False, seed=4, k_offset_std=5.0,
+                 outlier_channels=8, outlier_scale=15.0, outliers_in_k=True,
+                 note="video generation; 8 outlier channels x15 in Q and K; K offset ~N(0,5)")
+
+
+def long_context(N: int, causal: bool) -> Workload:
+    return Workload(f"long_b1h16n{N}d128{'_causal' if causal else ''}", 1, 16, N, 128, BF16, causal, seed=5,
+                    k_offset_std=4.0, t_noise_scale=0.5,
+                    note="long context; N(0,1)+0.5*t(3) on Q,K; K offset ~N(0,4)")
+
+
+LONG = [long_context(n, c) for n in (8192, 16384, 32768) for c in (False, True)]
+ALL = [TINY, LLM, DIT, VIDEO] + LONG
+BY_NAME = {w.name: w for w in ALL}
+# The configuration the headline throughput is quoted on: N = 16k, D = 128.
+HEADLINE = long_context(16384, False)
+
+
+def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp32 values to the 16-bit dtype (RNE) and return the raw bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F16:
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        u = x.view(np.uint32).astype(np.uint64)
+        r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        return r.astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F16:
+        return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def generate(w: Workload, heads: slice | None = None):
+    """Return (q_bits, k_bits, v_bits) as uint16 arrays of shape [B,H,N,D].
+
+    ``heads`` optionally restricts the output to a slice of the flattened B*H
+    head index (the draw for every head is still the same as in the full
+    tensor, because each head has its own sub-stream)."""
+    B, H, N, D = w.B, w.H, w.N, w.D
+    root = np.random.default_rng(w.seed)
+    # shared outlier channel indices (same for every head)
+    out_idx = root.choice(D, w.outlier_channels, replace=False) if w.outlier_channels else np.zeros(0, np.int64)
+    hsel = range(B * H) if heads is None else range(B * H)[heads]
+    seeds = root.integers(0, 2**63 - 1, size=B * H)
+    qs, ks, vs = [], [], []
+    for bh in hsel:
+        rng = np.random.default_rng(int(seeds[bh]))
+        q = rng.standard_normal((N, D), dtype=np.float32)
+        k = rng.standard_normal((N, D), dtype=np.float32)
+        v = rng.standard_normal((N, D), dtype=np.float32)
+        if w.t_noise_scale:
+            q += (w.t_noise_scale * rng.standard_t(3, (N, D))).astype(np.float32)
+            k += (w.t_noise_scale * rng.standard_t(3, (N, D))).astype(np.float32)
+        if w.outlier_channels:
+            q[:, out_idx] *= np.float32(w.outlier_scale)
+            if w.outliers_in_k:
+                k[:, out_idx] *= np.float32(w.outlier_scale)
+        if w.k_offset_std:
+            k += (w.k_offset_std * rng.standard_normal(D)).astype(np.float32)[None, :]
+        if w.v_offset_std:
+            v += (w.v_offset_std * rng.standard_normal(D)).astype(np.float32)[None, :]
+        qs.append(round_to_bits(q, w.dtype))
+        ks.append(round_to_bits(k, w.dtype))
+        vs.append(round_to_bits(v, w.dtype))
+    nh = len(qs)
+    shape = (B, H, N, D) if heads is None else (nh, 1, N, D)
+    return (np.stack(qs).reshape(shape), np.stack(ks).reshape(shape), np.stack(vs).reshape(shape))
+
+
+def custom(B, H, N, D, dtype=BF16, causal=False, seed=0, **kw) -> Workload:
+    return Workload(f"custom_b{B}h{H}n{N}d{D}", B, H, N, D, dtype, causal, seed, **kw)

@@ -1,0 +1,209 @@
+"""CPU oracle for the SageAttention2 forward pass -- test infrastructure only.
+
+This package is the reference that the GPU path is checked against.  It may be
+imported only by ``tests/``, by ``__graft_entry__.smoke()`` and by the CPU
+baseline leg of ``bench.py``.  The product package never imports it.
+
+The arithmetic lives in ``sage_oracle.cpp`` (plain C++17, scalar loops, built
+with ``-O2 -ffp-contract=off``); this module only builds it and marshals numpy
+arrays through ctypes.  Which passage of the SageAttention2 pages each step
+follows, and the readings taken where the pages are silent, are listed in the
+header of ``sage_oracle.cpp``.
+
+Pins (the tests under ``tests/test_oracle_*.py`` tie each function to
+something other than itself):
+  * e4m3 codec            -- exhaustive comparison with torch.float8_e4m3fn.
+  * quant_smooth          -- hand-derived example (tests/golden), closed-form
+                             means, quantizer properties, power-of-two scaling.
+  * qk_int32              -- numpy int64 matrix product; closed forms.
+  * attn_exact            -- direct fp64 brute force (numpy); the three
+                             invariants (K mean shift, Q compensation, rows of
+                             P sum to one).
+  * attn_mirror           -- equals attn_exact over the same quantized operands
+                             when P~ is not quantized (online softmax identity);
+                             special cases Q = 0, causal row 0, one dominant key.
+Parity unpinned: the cosine similarity against FP32 attention is a property of
+the method on the synthetic inputs; the pages print no accuracy figure for it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sage_oracle.cpp")
+_LIB = os.path.join(_HERE, "libsage_oracle.so")
+
+BQ_MEAN = 128
+BK = 128
+
+MIRROR_QUANT_P = 1
+EXACT_SMOOTH_K = 1
+EXACT_SMOOTH_Q = 2
+EXACT_QUANT_QK = 4
+EXACT_QUANT_V = 8
+
+DT_F16 = 0
+DT_BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library in-tree with g++."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-Wall", "-shared", "-fPIC",
+               "-pthread", "-o", _LIB + ".tmp", _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+        L.oracle_contract_version.restype = i32
+        L.oracle_e4m3_encode.argtypes = [P, P, i64]
+        L.oracle_e4m3_decode.argtypes = [P, P, i64]
+        L.oracle_decode_input.argtypes = [P, i32, P, i64]
+        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32] + [P] * 9 + [i32]
+        L.oracle_quant_smooth.restype = i32
+        L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
+        L.oracle_qk_int32.restype = i32
+        L.oracle_attn_mirror.argtypes = [P] * 7 + [i32, i32, i32, i32, i32, f32, i32, P, i64, f32, P, P, P, i32]
+        L.oracle_attn_mirror.restype = i32
+        L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 7 + [i32, i32, i32, i32, i32, f64, i32, P, i64, P, P, i32]
+        L.oracle_attn_exact.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _threads(n):
+    return n if n else (os.cpu_count() or 1)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def e4m3_decode(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib().oracle_e4m3_decode(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def decode_input(bits: np.ndarray, dtype: int) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float32)
+    lib().oracle_decode_input(_ptr(bits), dtype, _ptr(out), bits.size)
+    return out
+
+
+@dataclass
+class Quant:
+    """Canonical (unpacked, unpadded) prepass outputs."""
+    q_codes: np.ndarray   # int8  [B,H,N,D]
+    q_scale: np.ndarray   # fp32  [B,H,N]
+    k_codes: np.ndarray   # int8  [B,H,N,D]
+    k_scale: np.ndarray   # fp32  [B,H,2*ceil(N/32)]
+    q_mean: np.ndarray    # fp32  [B,H,ceil(N/128),D]
+    k_mean: np.ndarray    # fp32  [B,H,D]
+    v_codes: np.ndarray   # uint8 [B,H,N,D]
+    v_scale: np.ndarray   # fp32  [B,H,D]
+    delta_s: np.ndarray   # fp32  [B,H,ceil(N/128),N]
+
+
+def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0) -> Quant:
+    B, H, N, D = q_bits.shape
+    nqb = (N + BQ_MEAN - 1) // BQ_MEAN
+    G = 2 * ((N + 31) // 32)
+    qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
+    out = Quant(
+        q_codes=np.empty((B, H, N, D), np.int8), q_scale=np.empty((B, H, N), np.float32),
+        k_codes=np.empty((B, H, N, D), np.int8), k_scale=np.empty((B, H, G), np.float32),
+        q_mean=np.empty((B, H, nqb, D), np.float32), k_mean=np.empty((B, H, D), np.float32),
+        v_codes=np.empty((B, H, N, D), np.uint8), v_scale=np.empty((B, H, D), np.float32),
+        delta_s=np.empty((B, H, nqb, N), np.float32))
+    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D,
+                                   _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
+                                   _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),
+                                   _ptr(out.delta_s), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_quant_smooth rejected its arguments")
+    return out
+
+
+def qk_int32(q_codes_head, k_codes_head, q0, k0, nq, nk) -> np.ndarray:
+    qc = np.ascontiguousarray(q_codes_head, dtype=np.int8)
+    kc = np.ascontiguousarray(k_codes_head, dtype=np.int8)
+    D = qc.shape[-1]
+    out = np.empty((nq, nk), np.int32)
+    rc = lib().oracle_qk_int32(_ptr(qc), _ptr(kc), D, q0, k0, nq, nk, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_qk_int32 rejected its arguments")
+    return out
+
+
+def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bool = True,
+                eps: float = 0.0, nthreads: int = 0):
+    """Returns (O [nrows, D] fp32, slack [nrows] fp32, lse [nrows, 2] fp32)."""
+    B, H, N, D = qz.q_codes.shape
+    if rows is None:
+        nrows = B * H * N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    O = np.empty((nrows, D), np.float32)
+    slack = np.empty(nrows, np.float32)
+    lse = np.empty((nrows, 2), np.float32)
+    rc = lib().oracle_attn_mirror(_ptr(qz.q_codes), _ptr(qz.q_scale), _ptr(qz.k_codes), _ptr(qz.k_scale),
+                                  _ptr(qz.v_codes), _ptr(qz.v_scale), _ptr(qz.delta_s),
+                                  B, H, N, D, int(causal), float(sm_scale),
+                                  MIRROR_QUANT_P if quant_p else 0, _ptr(rows_arr), nrows, float(eps),
+                                  _ptr(O), _ptr(slack), _ptr(lse), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_mirror rejected its arguments")
+    return O, slack, lse
+
+
+def attn_exact(q_bits, k_bits, v_bits, dtype: int, causal: bool, sm_scale: float, flags: int,
+               qz: Quant | None = None, rows=None, nthreads: int = 0):
+    """Returns (O [nrows, D] fp64, row sums of P [nrows] fp64)."""
+    B, H, N, D = q_bits.shape
+    qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
+    if rows is None:
+        nrows = B * H * N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.size
+    O = np.empty((nrows, D), np.float64)
+    psum = np.empty(nrows, np.float64)
+    z = qz if qz is not None else Quant(*([None] * 9))
+    rc = lib().oracle_attn_exact(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype,
+                                 _ptr(z.q_codes), _ptr(z.q_scale), _ptr(z.k_codes), _ptr(z.k_scale),
+                                 _ptr(z.v_codes), _ptr(z.v_scale), _ptr(z.delta_s),
+                                 B, H, N, D, int(causal), float(sm_scale), flags, _ptr(rows_arr), nrows,
+                                 _ptr(O), _ptr(psum), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_exact rejected its arguments")
+    return O, psum

@@ -1,0 +1,465 @@
+// SageAttention2 forward -- CPU oracle (test infrastructure only).
+//
+// This file is the plain, slow, obviously-correct reference that the GPU path is
+// checked against. Only the tests, the smoke check and the benchmark's CPU
+// baseline may load it; the product library never links or calls it, and the
+// two share no source, header, table or constant generator.
+//
+// What the method computes comes from the SageAttention2 pages:
+//   * "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
+//     Per-thread INT4 Quantization" (arXiv 2411.10958 abstract page):
+//     Q,K -> INT4 at a hardware-friendly thread-level granularity; P~,V -> FP8;
+//     smoothing of Q to make INT4 QK^T accurate; a two-level accumulation for the
+//     FP8 P~V product.  The title's "thorough outlier smoothing" is read as
+//     smoothing K as well (per-channel mean over tokens).
+//   * "SageAttention2 Technical Report" summary page, Key Contributions 1-2
+//     (INT4 Q,K; FP8 P~,V; smoothing).
+// Everything the pages leave open is a documented reading, applied identically
+// here and in the GPU kernels:
+//   - BQ_MEAN = 128 tokens per Q-smoothing block (the tail block averages its
+//     valid tokens only); K is smoothed with one mean per channel over all N.
+//   - Means: fp32, sequential sums over 128-token chunks in token order, then a
+//     sequential sum of the chunk partials, then one IEEE division by the count.
+//   - INT4: symmetric, delta = amax/7, code = clamp(rint(x/delta), -7, 7) with
+//     true division and round-half-to-even; amax == 0 gives delta = 0, code 0.
+//   - Q: one scale per token.  K: one scale per 16-key group; inside every
+//     32-key tile, group h (0 or 1) holds the keys whose offset o satisfies
+//     (o / 4) % 2 == h.  These are the keys that one half of a 64-lane wave holds
+//     in a 32x32 matrix-core accumulator when the score tile is built as K*Q^T.
+//   - Compensation term DeltaS[qb][j] = sum_c qmean[qb][c] * (K[j][c]-kmean[c]),
+//     accumulated in fp64 and rounded once to fp32.
+//   - V: FP8 OCP e4m3fn (max 448), one scale per channel = amax/448, RNE.
+//   - Scores in the log2 domain:  ks = sm_scale * log2(e) (fp32),
+//     s2 = fma((float)acc, (dq*dk)*ks, DeltaS*ks).
+//   - Online softmax over BK = 128-key blocks in ascending order.
+//     mm = m_t - log2(448);  p' = exp2(s2 - mm) in [0, 448];  P8 = e4m3(p');
+//     l' = alpha*l' + sum(p')  (p' before FP8 rounding).
+//   - Two-level P~V: R_t = sum_j dec(P8_j)*dec(V8_j) in a fresh fp32 buffer per
+//     block; O_t = fma(alpha_t, O_{t-1}, R_t).
+//   - Epilogue: O = (O_T * vscale) / l'_T.
+//
+// Build: g++ -std=c++17 -O2 -ffp-contract=off -shared -fPIC -pthread
+// (no fast-math, no FMA contraction; std::fma only where a step names fma).
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+#include <algorithm>
+#include <limits>
+#include <functional>
+
+namespace {
+
+constexpr int ORACLE_CONTRACT = 1;
+constexpr int BQ_MEAN = 128;   // tokens per Q-smoothing block and per mean chunk
+constexpr int BK = 128;        // keys per online-softmax / two-level block
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float LOG2_448 = 8.80735492205760410744f;
+
+// ---------------------------------------------------------------- decoding ---
+float f16_to_f32(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  float v;
+  if (e == 0) v = std::ldexp((float)m, -24);
+  else if (e == 31) v = m ? std::numeric_limits<float>::quiet_NaN() : std::numeric_limits<float>::infinity();
+  else v = std::ldexp((float)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+float in_to_f32(const uint16_t* p, int64_t idx, int dtype) {
+  return dtype == 0 ? f16_to_f32(p[idx]) : bf16_to_f32(p[idx]);
+}
+
+// ------------------------------------------------------------ e4m3fn codec ---
+// OCP FP8 E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no
+// infinities; 0x7F / 0xFF are NaN; largest finite 448; subnormal step 2^-9.
+// Encode: round to nearest, ties to even; magnitudes beyond 448 saturate.
+uint8_t e4m3_encode(float x) {
+  if (std::isnan(x)) return 0x7F;
+  uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
+  float a = std::fabs(x);
+  if (a >= 464.0f) return sign | 0x7E;            // beyond the 448 / 480 midpoint
+  if (a < 0.015625f) {                             // below 2^-6: subnormal range
+    float m = std::rint(a * 512.0f);               // exact scaling by 2^9, RNE
+    return sign | (uint8_t)m;                      // m == 8 is the smallest normal
+  }
+  int e;
+  std::frexp(a, &e);                               // a = f * 2^e, f in [0.5, 1)
+  int ex = e - 1;                                  // a in [2^ex, 2^(ex+1))
+  float r = std::rint(std::ldexp(a, 3 - ex));      // in [8, 16], RNE
+  if (r == 16.0f) { r = 8.0f; ex += 1; }
+  int code = ((ex + 7) << 3) | ((int)r - 8);
+  if (code > 0x7E) code = 0x7E;
+  return sign | (uint8_t)code;
+}
+float e4m3_decode(uint8_t b) {
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  if (e == 15 && m == 7) return std::numeric_limits<float>::quiet_NaN();
+  float v = (e == 0) ? std::ldexp((float)m, -9) : std::ldexp((float)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+// ------------------------------------------------------------ quantization ---
+int8_t int4_code(float x, float delta) {
+  if (delta == 0.0f) return 0;
+  float r = std::rint(x / delta);
+  if (r > 7.0f) r = 7.0f;
+  if (r < -7.0f) r = -7.0f;
+  return (int8_t)r;
+}
+
+// Group of key j: two 16-key groups per 32-key tile (see header comment).
+int64_t k_group(int64_t j) { return 2 * (j / 32) + ((j % 32) / 4) % 2; }
+
+void parallel_for(int64_t n, int nthreads, const std::function<void(int64_t)>& fn) {
+  if (nthreads <= 1 || n <= 1) {
+    for (int64_t i = 0; i < n; i++) fn(i);
+    return;
+  }
+  int nt = (int)std::min<int64_t>(nthreads, n);
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; t++)
+    th.emplace_back([&, t] {
+      for (int64_t i = t; i < n; i += nt) fn(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_contract_version(void) { return ORACLE_CONTRACT; }
+int oracle_bq_mean(void) { return BQ_MEAN; }
+int oracle_bk(void) { return BK; }
+
+void oracle_e4m3_encode(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = e4m3_encode(x[i]);
+}
+void oracle_e4m3_decode(const uint8_t* in, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = e4m3_decode(in[i]);
+}
+void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = in_to_f32(in, i, dtype);
+}
+
+// Prepass: smoothing statistics, INT4 codes and scales for Q and K, FP8 V with
+// per-channel scales, and the rank-1 compensation term.  All arrays are in the
+// canonical (unpacked, unpadded) layout:
+//   q_codes, k_codes : int8  [B,H,N,D]     values in [-7, 7]
+//   q_scale          : fp32  [B,H,N]
+//   k_scale          : fp32  [B,H,2*ceil(N/32)]
+//   q_mean           : fp32  [B,H,ceil(N/128),D]
+//   k_mean           : fp32  [B,H,D]
+//   v_codes          : uint8 [B,H,N,D]     e4m3fn bit patterns
+//   v_scale          : fp32  [B,H,D]
+//   delta_s          : fp32  [B,H,ceil(N/128),N]
+// Returns 0, or -1 for invalid arguments.
+int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                        int B, int H, int N, int D,
+                        int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
+                        float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale,
+                        float* delta_s, int nthreads) {
+  if (!q || !k || !v || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
+  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
+  parallel_for((int64_t)B * H, nthreads, [&](int64_t bh) {
+    const int64_t base = bh * (int64_t)N * D;
+    // decode this head's inputs to fp32 (exact)
+    std::vector<float> Q((size_t)N * D), K((size_t)N * D), V((size_t)N * D);
+    for (int64_t i = 0; i < (int64_t)N * D; i++) {
+      Q[i] = in_to_f32(q, base + i, dtype);
+      K[i] = in_to_f32(k, base + i, dtype);
+      V[i] = in_to_f32(v, base + i, dtype);
+    }
+    // ---- K channel mean over all N tokens: chunk partials, then their sum.
+    std::vector<float> kbar(D);
+    for (int c = 0; c < D; c++) {
+      float total = 0.0f;
+      for (int64_t t0 = 0; t0 < N; t0 += BQ_MEAN) {
+        float part = 0.0f;
+        for (int64_t j = t0; j < std::min<int64_t>(N, t0 + BQ_MEAN); j++) part = part + K[j * D + c];
+        total = total + part;
+      }
+      kbar[c] = total / (float)N;
+      if (k_mean) k_mean[bh * D + c] = kbar[c];
+    }
+    // ---- Q block means (128-token blocks, partial tail block).
+    std::vector<float> qbar((size_t)NQB * D);
+    for (int64_t qb = 0; qb < NQB; qb++) {
+      int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(N, i0 + BQ_MEAN);
+      for (int c = 0; c < D; c++) {
+        float s = 0.0f;
+        for (int64_t i = i0; i < i1; i++) s = s + Q[i * D + c];
+        qbar[qb * D + c] = s / (float)(i1 - i0);
+        if (q_mean) q_mean[(bh * NQB + qb) * D + c] = qbar[qb * D + c];
+      }
+    }
+    // ---- smoothed values
+    std::vector<float> gQ((size_t)N * D), gK((size_t)N * D);
+    for (int64_t i = 0; i < N; i++)
+      for (int c = 0; c < D; c++) {
+        gQ[i * D + c] = Q[i * D + c] - qbar[(i / BQ_MEAN) * D + c];
+        gK[i * D + c] = K[i * D + c] - kbar[c];
+      }
+    // ---- Q: one INT4 scale per token
+    for (int64_t i = 0; i < N; i++) {
+      float amax = 0.0f;
+      for (int c = 0; c < D; c++) amax = std::max(amax, std::fabs(gQ[i * D + c]));
+      float dq = amax / 7.0f;
+      if (q_scale) q_scale[bh * N + i] = dq;
+      if (q_codes)
+        for (int c = 0; c < D; c++) q_codes[base + i * D + c] = int4_code(gQ[i * D + c], dq);
+    }
+    // ---- K: one INT4 scale per 16-key fragment group
+    std::vector<float> gamax(G, 0.0f);
+    for (int64_t j = 0; j < N; j++) {
+      int64_t g = k_group(j);
+      for (int c = 0; c < D; c++) gamax[g] = std::max(gamax[g], std::fabs(gK[j * D + c]));
+    }
+    std::vector<float> dk(G);
+    for (int64_t g = 0; g < G; g++) {
+      dk[g] = gamax[g] / 7.0f;
+      if (k_scale) k_scale[bh * G + g] = dk[g];
+    }
+    if (k_codes)
+      for (int64_t j = 0; j < N; j++)
+        for (int c = 0; c < D; c++) k_codes[base + j * D + c] = int4_code(gK[j * D + c], dk[k_group(j)]);
+    // ---- V: FP8 e4m3fn with one scale per channel
+    for (int c = 0; c < D; c++) {
+      float amax = 0.0f;
+      for (int64_t j = 0; j < N; j++) amax = std::max(amax, std::fabs(V[j * D + c]));
+      float dv = amax / 448.0f;
+      if (v_scale) v_scale[bh * D + c] = dv;
+      if (v_codes)
+        for (int64_t j = 0; j < N; j++)
+          v_codes[base + j * D + c] = (dv == 0.0f) ? (uint8_t)0 : e4m3_encode(V[j * D + c] / dv);
+    }
+    // ---- rank-1 compensation: DeltaS[qb][j] = qbar[qb] . gK[j]
+    if (delta_s)
+      for (int64_t qb = 0; qb < NQB; qb++)
+        for (int64_t j = 0; j < N; j++) {
+          double acc = 0.0;
+          for (int c = 0; c < D; c++) acc += (double)qbar[qb * D + c] * (double)gK[j * D + c];
+          delta_s[(bh * NQB + qb) * N + j] = (float)acc;
+        }
+  });
+  return 0;
+}
+
+// Exact integer dot products of INT4 codes for one head:
+// out[a][b] = sum_c qc[(q0+a)*D + c] * kc[(k0+b)*D + c].
+int oracle_qk_int32(const int8_t* qc, const int8_t* kc, int D, int q0, int k0, int nq, int nk, int32_t* out) {
+  if (!qc || !kc || !out || D < 1 || nq < 0 || nk < 0) return -1;
+  for (int a = 0; a < nq; a++)
+    for (int b = 0; b < nk; b++) {
+      int64_t acc = 0;
+      for (int c = 0; c < D; c++) acc += (int64_t)qc[(int64_t)(q0 + a) * D + c] * kc[(int64_t)(k0 + b) * D + c];
+      out[(int64_t)a * nk + b] = (int32_t)acc;
+    }
+  return 0;
+}
+
+// Flags for the mirror mode.
+//   1: quantize P~ to FP8 (the method).  Without it, p' itself (fp32) is used.
+enum { MIRROR_QUANT_P = 1 };
+
+// Mirror mode: the method step by step, in the same fp32 operations the GPU
+// path performs, for a list of query rows.  rows[r] = (b*H + h)*N + i.
+// Inputs are the canonical prepass arrays.  Outputs: O[r][c] (fp32) and, per
+// row, slack[r]: an upper bound on how far O may move if any P~ element whose
+// value p' lies within relative distance eps of an FP8 rounding midpoint were
+// rounded the other way (used to tolerate exp2 implementation differences).
+// Optional lse[r] = (final running max m, final l') for diagnostics.
+int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                       const uint8_t* v_codes, const float* v_scale, const float* delta_s,
+                       int B, int H, int N, int D, int causal, float sm_scale, int flags,
+                       const int64_t* rows, int64_t nrows, float eps,
+                       float* O, float* slack, float* lse, int nthreads) {
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !delta_s || !O) return -1;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !(sm_scale > 0.0f)) return -1;
+  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
+  const float ks = sm_scale * LOG2E;
+  const int64_t total = rows ? nrows : (int64_t)B * H * N;
+  parallel_for(total, nthreads, [&](int64_t r) {
+    const int64_t flat = rows ? rows[r] : r;
+    const int64_t bh = flat / N, i = flat % N;
+    const int8_t* qi = q_codes + flat * D;
+    const int8_t* kh = k_codes + bh * (int64_t)N * D;
+    const uint8_t* vh = v_codes + bh * (int64_t)N * D;
+    const float* ds = delta_s + (bh * NQB + i / BQ_MEAN) * N;
+    const float* dvec = v_scale + bh * D;
+    const float dq = q_scale[flat];
+    std::vector<float> Orun(D, 0.0f), R(D), s2(BK), p(BK);
+    float m = -std::numeric_limits<float>::infinity();
+    float l = 0.0f, slk = 0.0f;
+    const int64_t jend = causal ? i + 1 : N;  // keys j < jend are allowed
+    for (int64_t t0 = 0; t0 < jend; t0 += BK) {
+      const int64_t t1 = std::min<int64_t>(t0 + BK, N);
+      // scores in the log2 domain
+      float bmax = -std::numeric_limits<float>::infinity();
+      for (int64_t j = t0; j < t1; j++) {
+        float& s = s2[j - t0];
+        if (j >= jend) { s = -std::numeric_limits<float>::infinity(); continue; }
+        int32_t acc = 0;
+        for (int c = 0; c < D; c++) acc += (int32_t)qi[c] * (int32_t)kh[j * D + c];
+        float cfac = (dq * k_scale[bh * G + k_group(j)]) * ks;
+        float d = ds[j] * ks;
+        s = std::fma((float)acc, cfac, d);
+        bmax = std::max(bmax, s);
+      }
+      const float mnew = std::max(m, bmax);
+      const float alpha = std::exp2(m - mnew);
+      const float mm = mnew - LOG2_448;
+      float rowsum = 0.0f;
+      for (int64_t j = t0; j < t1; j++) {
+        float pj = (j < jend) ? std::exp2(s2[j - t0] - mm) : 0.0f;
+        p[j - t0] = pj;
+        rowsum = rowsum + pj;
+      }
+      // P~ -> FP8 and the level-1 partial R_t in a fresh fp32 buffer
+      std::fill(R.begin(), R.end(), 0.0f);
+      float blk_slack = 0.0f;
+      for (int64_t j = t0; j < t1; j++) {
+        float pj = p[j - t0];
+        float pq = (flags & MIRROR_QUANT_P) ? e4m3_decode(e4m3_encode(pj)) : pj;
+        if (pq == 0.0f && pj == 0.0f) continue;
+        for (int c = 0; c < D; c++) R[c] = R[c] + pq * e4m3_decode(vh[j * D + c]);
+        if ((flags & MIRROR_QUANT_P) && eps > 0.0f && pj > 0.0f) {
+          // Is a rounding midpoint of the FP8 grid within relative eps of pj?
+          float lo = pj * (1.0f - eps), hi = pj * (1.0f + eps);
+          uint8_t clo = e4m3_encode(lo), chi = e4m3_encode(hi);
+          if (clo != chi) {
+            float step = std::fabs(e4m3_decode(chi) - e4m3_decode(clo));
+            float vm = 0.0f;
+            for (int c = 0; c < D; c++) vm = std::max(vm, std::fabs(e4m3_decode(vh[j * D + c]) * dvec[c]));
+            blk_slack += step * vm;
+          }
+        }
+      }
+      // level 2: fold the block into the fp32 running buffer
+      for (int c = 0; c < D; c++) Orun[c] = std::fma(alpha, Orun[c], R[c]);
+      l = alpha * l + rowsum;
+      slk = alpha * slk + blk_slack;
+      m = mnew;
+    }
+    for (int c = 0; c < D; c++) O[r * D + c] = (Orun[c] * dvec[c]) / l;
+    if (slack) slack[r] = slk / l;
+    if (lse) { lse[2 * r] = m; lse[2 * r + 1] = l; }
+  });
+  return 0;
+}
+
+// Exact mode: softmax(S) V in fp64 with a direct (not online) softmax, for a
+// list of rows.  Flags select which parts of the method are applied:
+enum {
+  EXACT_SMOOTH_K = 1,  // subtract the per-channel K mean (fp64 mean)
+  EXACT_SMOOTH_Q = 2,  // subtract the per-block Q mean and add q_mean . gamma(K)
+  EXACT_QUANT_QK = 4,  // use the prepass INT4 codes/scales and DeltaS (given)
+  EXACT_QUANT_V = 8,   // use the prepass FP8 V and scales (given)
+};
+// Without EXACT_QUANT_QK the scores are built from the raw inputs in fp64:
+//   S_ij = sm_scale * ( gQ_i . gK_j + [SMOOTH_Q] qmean_qb(i) . gK_j )
+// With EXACT_QUANT_QK they are built from the canonical prepass arrays:
+//   S_ij = sm_scale * ( (dq_i * qc_i) . (dk_g(j) * kc_j) + DeltaS[qb(i)][j] )
+// Outputs O[r][c] in fp64; optional P row sums in psum[r].
+int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                      const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
+                      const uint8_t* v_codes, const float* v_scale, const float* delta_s,
+                      int B, int H, int N, int D, int causal, double sm_scale, int flags,
+                      const int64_t* rows, int64_t nrows, double* O, double* psum, int nthreads) {
+  if (!q || !k || !v || !O || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
+  if ((flags & EXACT_QUANT_QK) && (!q_codes || !q_scale || !k_codes || !k_scale || !delta_s)) return -1;
+  if ((flags & EXACT_QUANT_V) && (!v_codes || !v_scale)) return -1;
+  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
+  const int64_t total = rows ? nrows : (int64_t)B * H * N;
+  // per-head fp64 statistics, computed lazily per head
+  const int64_t nheads = (int64_t)B * H;
+  std::vector<std::vector<double>> kbar(nheads), qbar(nheads);
+  std::vector<char> need(nheads, rows ? 0 : 1);
+  if (rows)
+    for (int64_t r = 0; r < nrows; r++) need[rows[r] / N] = 1;
+  parallel_for(nheads, nthreads, [&](int64_t bh) {
+    if (!need[bh]) return;
+    const int64_t base = bh * (int64_t)N * D;
+    kbar[bh].assign(D, 0.0);
+    qbar[bh].assign(NQB * D, 0.0);
+    if (flags & EXACT_SMOOTH_K)
+      for (int c = 0; c < D; c++) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; j++) s += in_to_f32(k, base + j * D + c, dtype);
+        kbar[bh][c] = s / N;
+      }
+    if (flags & EXACT_SMOOTH_Q)
+      for (int64_t qb = 0; qb < NQB; qb++) {
+        int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(N, i0 + BQ_MEAN);
+        for (int c = 0; c < D; c++) {
+          double s = 0.0;
+          for (int64_t i = i0; i < i1; i++) s += in_to_f32(q, base + i * D + c, dtype);
+          qbar[bh][qb * D + c] = s / (double)(i1 - i0);
+        }
+      }
+  });
+  parallel_for(total, nthreads, [&](int64_t r) {
+    const int64_t flat = rows ? rows[r] : r;
+    const int64_t bh = flat / N, i = flat % N, qb = i / BQ_MEAN;
+    const int64_t base = bh * (int64_t)N * D;
+    const int64_t jend = causal ? i + 1 : N;
+    std::vector<double> S(jend);
+    std::vector<double> qrow(D), qm(D);
+    for (int c = 0; c < D; c++) {
+      if (flags & EXACT_QUANT_QK) {
+        qrow[c] = (double)q_scale[flat] * (double)q_codes[flat * D + c];
+      } else {
+        double x = in_to_f32(q, base + i * D + c, dtype);
+        qm[c] = (flags & EXACT_SMOOTH_Q) ? qbar[bh][qb * D + c] : 0.0;
+        qrow[c] = x - qm[c];
+      }
+    }
+    for (int64_t j = 0; j < jend; j++) {
+      double s = 0.0;
+      if (flags & EXACT_QUANT_QK) {
+        double dk = k_scale[bh * G + k_group(j)];
+        for (int c = 0; c < D; c++) s += qrow[c] * (dk * (double)k_codes[base + j * D + c]);
+        s += (double)delta_s[(bh * NQB + qb) * N + j];
+      } else {
+        double comp = 0.0;
+        for (int c = 0; c < D; c++) {
+          double kj = (double)in_to_f32(k, base + j * D + c, dtype) - kbar[bh][c];
+          s += qrow[c] * kj;
+          comp += qm[c] * kj;
+        }
+        s += comp;
+      }
+      S[j] = sm_scale * s;
+    }
+    double mx = -std::numeric_limits<double>::infinity();
+    for (int64_t j = 0; j < jend; j++) mx = std::max(mx, S[j]);
+    double denom = 0.0;
+    for (int64_t j = 0; j < jend; j++) { S[j] = std::exp(S[j] - mx); denom += S[j]; }
+    double ps = 0.0;
+    for (int c = 0; c < D; c++) O[r * D + c] = 0.0;
+    for (int64_t j = 0; j < jend; j++) {
+      double pj = S[j] / denom;
+      ps += pj;
+      for (int c = 0; c < D; c++) {
+        double vj = (flags & EXACT_QUANT_V) ? (double)v_scale[bh * D + c] * (double)e4m3_decode(v_codes[base + j * D + c])
+                                            : (double)in_to_f32(v, base + j * D + c, dtype);
+        O[r * D + c] += pj * vj;
+      }
+    }
+    if (psum) psum[r] = ps;
+  });
+  return 0;
+}
+
+}  // extern "C"

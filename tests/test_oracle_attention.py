@@ -1,0 +1,211 @@
+"""Pins for the oracle's attention: integer QK^T, exact (fp64) mode, mirror mode.
+
+Checks against: numpy's int64 matrix product; a direct fp64 softmax(QK^T)V
+written with numpy; the invariants of the method (shifting every key by the
+same vector leaves softmax unchanged; the Q-smoothing compensation term restores
+the unsmoothed scores; rows of P sum to one); lossless special inputs on which
+quantization is exact, so the mirror must reproduce plain attention; and closed
+forms (Q = 0, causal row 0, one dominant key).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from fp8_attention_transformer_amd import workloads as wl
+
+
+def _bits(x, dtype="bf16"):
+    return wl.round_to_bits(np.asarray(x, np.float32), dtype)
+
+
+def _brute_force(Q, K, V, causal, scale):
+    """Plain fp64 attention, one head at a time."""
+    B, H, N, D = Q.shape
+    out = np.empty((B, H, N, D))
+    for b in range(B):
+        for h in range(H):
+            S = (Q[b, h].astype(np.float64) @ K[b, h].astype(np.float64).T) * scale
+            if causal:
+                S = np.where(np.tril(np.ones((N, N), bool)), S, -np.inf)
+            S = S - S.max(1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(1, keepdims=True)
+            out[b, h] = P @ V[b, h].astype(np.float64)
+    return out
+
+
+def test_qk_int32_matches_int64_matmul_and_closed_forms(oracle_lib):
+    rng = np.random.default_rng(1)
+    for D in (64, 128):
+        qc = rng.integers(-7, 8, (70, D)).astype(np.int8)
+        kc = rng.integers(-7, 8, (90, D)).astype(np.int8)
+        got = oracle_lib.qk_int32(qc, kc, 3, 5, 60, 80)
+        ref = qc[3:63].astype(np.int64) @ kc[5:85].astype(np.int64).T
+        assert np.array_equal(got, ref)
+        sev = np.full((4, D), 7, np.int8)
+        assert np.all(oracle_lib.qk_int32(sev, sev, 0, 0, 4, 4) == 49 * D)
+        alt = np.tile(np.array([7, -7], np.int8), (4, D // 2))
+        assert np.all(oracle_lib.qk_int32(sev, alt, 0, 0, 4, 4) == 0)
+        assert np.all(oracle_lib.qk_int32(-sev, sev, 0, 0, 4, 4) == -49 * D)
+
+
+SHAPES = [(1, 64), (17, 64), (33, 128), (129, 64), (256, 128)]
+
+
+@pytest.mark.parametrize("N,D", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_mode_is_plain_attention(oracle_lib, N, D, causal):
+    w = wl.custom(1, 2, N, D, seed=N * 7 + D, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    O, psum = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, 0)
+    Q, K, V = (oracle_lib.decode_input(a, 1) for a in (q, k, v))
+    ref = _brute_force(Q, K, V, causal, w.scale).reshape(-1, D)
+    assert np.allclose(O, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(psum, 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,D", [(17, 64), (200, 128), (300, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_invariants(oracle_lib, N, D, causal):
+    w = wl.custom(1, 2, N, D, seed=N + 3, k_offset_std=4.0, outlier_channels=3, outlier_scale=8.0)
+    q, k, v = wl.generate(w)
+    O0, p0 = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, 0)
+    # K mean-subtraction leaves softmax unchanged
+    Ok, pk = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, oracle_lib.EXACT_SMOOTH_K)
+    # Q smoothing plus the compensation term restores the unsmoothed scores
+    Okq, pkq = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale,
+                                     oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q)
+    Oq, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, oracle_lib.EXACT_SMOOTH_Q)
+    scale = np.abs(O0).max()
+    for O in (Ok, Okq, Oq):
+        assert np.abs(O - O0).max() <= 1e-12 * scale
+    for p in (p0, pk, pkq):
+        assert np.abs(p - 1).max() <= 1e-12
+
+
+def _lossless_inputs(N, D, seed):
+    """Integer Q, K whose INT4 quantization is exact (every token / key group
+    holds a +-7, every block mean is zero) and V exactly representable in FP8
+    after its per-channel scale (amax 3.5 -> scale 1/128)."""
+    assert N % 2 == 0 and N <= 128
+    rng = np.random.default_rng(seed)
+    half = N // 2
+    Qh = rng.integers(-6, 7, (half, D)).astype(np.float32)
+    Qh[np.arange(half), rng.integers(0, D, half)] = 7 * rng.choice([-1, 1], half)
+    Kh = rng.integers(-6, 7, (half, D)).astype(np.float32)
+    Kh[:, 0] = 7 * rng.choice([-1, 1], half)
+    Q = np.concatenate([Qh, -Qh])
+    K = np.concatenate([Kh, -Kh])
+    grid = np.array([0, 0.5, 1, 1.5, 2, 2.5, 3, 3.5], np.float32)
+    V = grid[rng.integers(0, 8, (N, D))] * rng.choice([-1, 1], (N, D))
+    V[rng.integers(0, N, D), np.arange(D)] = 3.5
+    perm = rng.permutation(N)
+    return Q[perm][None, None], K[perm][None, None], V[perm][None, None]
+
+
+@pytest.mark.parametrize("N,D", [(2, 64), (18, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mirror_equals_plain_attention_on_lossless_inputs(oracle_lib, N, D, causal):
+    Q, K, V = _lossless_inputs(N, D, seed=N + D)
+    q, k, v = _bits(Q), _bits(K), _bits(V)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    # the quantization really is lossless
+    assert np.all(z.q_scale == 1) and np.all(z.k_scale[z.k_scale != 0] == 1) and not np.any(z.delta_s)
+    assert np.array_equal(z.q_codes.astype(np.float32), Q) and np.array_equal(z.k_codes.astype(np.float32), K)
+    assert np.all(z.v_scale == np.float32(1 / 128))
+    scale = 0.003  # keeps |scores| below ~20 so fp32 score rounding stays near 1e-6
+    ref = _brute_force(Q, K, V, causal, scale).reshape(-1, D)
+    Om, _, _ = oracle_lib.attn_mirror(z, causal, scale, quant_p=False)
+    assert np.abs(Om - ref).max() <= 5e-6 * np.abs(V).max()
+    # with FP8 P~: each weight is off by at most 2^-4 relative (or 2^-10 absolute on the 448 scale)
+    Op, _, lse = oracle_lib.attn_mirror(z, causal, scale, quant_p=True)
+    nkeys = np.minimum(np.arange(N) + 1, N) if causal else np.full(N, N)
+    lprime = lse[:, 1]
+    bound = (2.0 ** -4 + nkeys * 2.0 ** -10 / lprime) * np.abs(V).max() * 1.01
+    assert np.all(np.abs(Op - ref).max(1) <= bound)
+
+
+@pytest.mark.parametrize("N,D", [(50, 64), (200, 128), (333, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mirror_online_softmax_equals_direct_softmax(oracle_lib, N, D, causal):
+    """Same quantized operands, P~ unquantized: the online softmax over 128-key
+    blocks with the two-level accumulation equals the direct softmax."""
+    w = wl.custom(1, 2, N, D, seed=N * 3 + D, k_offset_std=4.0, outlier_channels=2, outlier_scale=10.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    flags = (oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_QUANT_QK
+             | oracle_lib.EXACT_QUANT_V)
+    Oe, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, flags, qz=z)
+    Om, _, _ = oracle_lib.attn_mirror(z, causal, w.scale, quant_p=False)
+    vmax = (oracle_lib.e4m3_decode(z.v_codes) * z.v_scale[:, :, None, :]).__abs__().max()
+    assert np.abs(Om - Oe).max() <= 1e-5 * vmax
+
+
+def test_q_zero_gives_mean_of_dequantized_v(oracle_lib):
+    N, D = 300, 64
+    w = wl.custom(1, 1, N, D, seed=9, k_offset_std=2.0)
+    _, k, v = wl.generate(w)
+    q = np.zeros_like(k)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    vhat = (oracle_lib.e4m3_decode(z.v_codes) * z.v_scale[:, :, None, :])[0, 0].astype(np.float64)
+    for causal in (False, True):
+        O, _, _ = oracle_lib.attn_mirror(z, causal, 0.125)
+        if causal:
+            ref = np.cumsum(vhat, 0) / np.arange(1, N + 1)[:, None]
+        else:
+            ref = np.broadcast_to(vhat.mean(0), (N, D))
+        assert np.abs(O - ref).max() <= 1e-5 * np.abs(vhat).max()
+        # causal row 0 sees only key 0
+        if causal:
+            assert np.allclose(O[0], vhat[0], rtol=1e-6, atol=0)
+
+
+def test_one_dominant_key(oracle_lib):
+    """All queries equal (so smoothed Q is zero and the scores come entirely
+    from the compensation term); one key aligned with them dominates."""
+    N, D = 160, 128
+    rng = np.random.default_rng(4)
+    Q = np.zeros((1, 1, N, D), np.float32)
+    Q[..., 0] = 4.0
+    K = rng.standard_normal((1, 1, N, D)).astype(np.float32)
+    jstar = 77
+    K[0, 0, :, 0] = -2.0
+    K[0, 0, jstar, 0] = 30.0
+    V = rng.standard_normal((1, 1, N, D)).astype(np.float32)
+    z = oracle_lib.quant_smooth(_bits(Q), _bits(K), _bits(V), oracle_lib.DT_BF16)
+    assert not np.any(z.q_codes)
+    vhat = (oracle_lib.e4m3_decode(z.v_codes) * z.v_scale[:, :, None, :])[0, 0]
+    O, _, _ = oracle_lib.attn_mirror(z, False, 1.0)
+    # score gap is 4*32 = 128 nats: every other weight underflows the FP8 grid
+    assert np.allclose(O, np.broadcast_to(vhat[jstar], (N, D)), rtol=1e-4, atol=0)
+    # a negative gap instead makes key jstar vanish
+    z2 = oracle_lib.quant_smooth(_bits(-Q), _bits(K), _bits(V), oracle_lib.DT_BF16)
+    O2, _, _ = oracle_lib.attn_mirror(z2, False, 1.0)
+    others = np.delete(np.arange(N), jstar)
+    assert np.allclose(O2, np.broadcast_to(vhat[others].astype(np.float64).mean(0), (N, D)), rtol=0,
+                       atol=1e-5 * np.abs(vhat).max())
+
+
+def test_scale_metamorphic(oracle_lib):
+    """Doubling Q (exact in bf16) while halving sm_scale leaves O unchanged."""
+    N, D = 150, 128
+    w = wl.custom(1, 2, N, D, seed=21, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    q2 = q + np.uint16(1 << 7) * (q & 0x7FFF != 0)
+    za = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    zb = oracle_lib.quant_smooth(q2, k, v, oracle_lib.DT_BF16)
+    for causal in (False, True):
+        Oa, _, _ = oracle_lib.attn_mirror(za, causal, w.scale)
+        Ob, _, _ = oracle_lib.attn_mirror(zb, causal, w.scale / 2)
+        assert np.array_equal(Oa, Ob)
+
+
+def test_rows_subset_matches_full(oracle_lib):
+    w = wl.custom(2, 2, 140, 64, seed=5, causal=True, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    Ofull, sfull, _ = oracle_lib.attn_mirror(z, True, w.scale, eps=2.0 ** -16)
+    rows = np.array([0, 1, 139, 140, 300, 559])
+    Osub, ssub, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=2.0 ** -16)
+    assert np.array_equal(Osub, Ofull[rows]) and np.array_equal(ssub, sfull[rows])
