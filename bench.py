@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the SageAttention2 forward (libsage, MI355X / gfx950).
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: the prepass (sage_quant_smooth: smoothing, INT4 Q/K, FP8 V,
+compensation term) followed by the fused attention kernel
+(sage_attn_quantized) -- together exactly what sage_attn_fwd runs.  HIP events
+on the launch stream bracket each kernel group inside the timed region, which
+gives the fused kernel's per-launch duration for the roofline line.
+
+Prints ONE JSON line (the headline workload: B=1, H=16, N=16384, D=128,
+non-causal, bf16 in and out).  ``--workload all`` prints one line per workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TOPS (4·B·H·N²·D/t) at D=128, N=4k–32k; cos-sim vs FP32 attention"
+PEAK_TOPS = 5000.0   # MI355X dense INT8 / OCP FP8 matrix-core peak (OPS), 2:1 sparsity not counted
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
+KERNEL_SOURCES = ["fp8_attention_transformer_amd/csrc/attn_fwd.hip", "fp8_attention_transformer_amd/csrc/sage_device.h",
+                  "fp8_attention_transformer_amd/csrc/sage_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    counter summary, if it was taken on this workload and this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline_leg(w, out_gpu, target_s: float):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: the prepass of head 0 and the mirror-mode attention of a set of
+    its rows, with the host's threads (at most 16).  Also reports, from the
+    same oracle runs, the GPU output's agreement with it on those rows and the
+    cosine similarity against unquantized FP32 attention."""
+    import numpy as np
+
+    import oracle
+    from fp8_attention_transformer_amd import workloads as wl
+
+    nth = host_threads()
+    dt = 0 if w.dtype == wl.F16 else 1
+    q, k, v = wl.generate(w, heads=slice(0, 1))
+    t0 = time.perf_counter()
+    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth)
+    t_pre = time.perf_counter() - t0
+    N, D = w.N, w.D
+    rng = np.random.default_rng(0)
+    # calibrate the number of rows, then time the sample
+    probe = np.sort(rng.choice(N, min(N, 4 * nth), replace=False))
+    t0 = time.perf_counter()
+    oracle.attn_mirror(z, w.causal, w.scale, rows=probe, nthreads=nth)
+    per_row = (time.perf_counter() - t0) / probe.size
+    nrows = int(min(N, max(probe.size, target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(N, nrows, replace=False))
+    t0 = time.perf_counter()
+    O_m, _, _ = oracle.attn_mirror(z, w.causal, w.scale, rows=rows, nthreads=nth)
+    t_rows = time.perf_counter() - t0
+    keys = (rows + 1) if w.causal else np.full(rows.size, N)
+    ops = float(4.0 * D * keys.sum())
+    t_total = t_rows + t_pre * rows.size / N   # the prepass share of the sampled rows
+    gpu_rows = out_gpu[rows].astype(np.float64)
+    sub = rows[:: max(1, rows.size // 96)]
+    O_fp, _ = oracle.attn_exact(q, k, v, dt, w.causal, w.scale, 0, rows=sub, nthreads=nth)
+    cos = float((gpu_rows[:: max(1, rows.size // 96)] * O_fp).sum()
+                / (np.linalg.norm(gpu_rows[:: max(1, rows.size // 96)]) * np.linalg.norm(O_fp)))
+    cos_oracle = float((O_m[:: max(1, rows.size // 96)] * O_fp).sum()
+                       / (np.linalg.norm(O_m[:: max(1, rows.size // 96)]) * np.linalg.norm(O_fp)))
+    base = {
+        "value": ops / t_total / 1e12,
+        "unit": "TOPS",
+        "cores": nth,
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.B * w.H}: oracle prepass ({t_pre:.2f}s, counted pro rata) + mirror attention of "
+                   f"{rows.size} random query rows ({t_rows:.2f}s); ops = 4*D*keys per row"),
+    }
+    acc = {
+        "rows": int(rows.size),
+        "max_abs_vs_oracle_bf16_out": float(np.abs(gpu_rows - O_m).max()),
+        "cos_sim_vs_fp32_sampled": cos,
+        "cos_sim_oracle_vs_fp32_sampled": cos_oracle,
+    }
+    return base, acc
+
+
+def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
+    import numpy as np
+    import torch
+
+    from fp8_attention_transformer_amd import sage
+    from fp8_attention_transformer_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    tdt = torch.float16 if w.dtype == wl.F16 else torch.bfloat16
+    q, k, v = (torch.from_numpy(a.view(np.int16)).view(tdt).cuda() for a in wl.generate(w))
+    B, H, N, D = w.B, w.H, w.N, w.D
+    ws = sage.alloc_workspace(B, H, N, D)
+    bufs = ws.bufs()
+    out = torch.empty((B, H, N, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    in_code = sage.F16 if tdt == torch.float16 else sage.BF16
+
+    def step():
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh)
+        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh)
+        ev[i][1].record(stream)
+        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    ms_per_step = total_ms / steps
+    ops = w.ops
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = ops / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
+                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tops, 1),
+            "peak": PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tops / PEAK_TOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": "attn_kernel",
+            "kernel_us": round(attn_ms * 1e3, 2),
+        },
+        "breakdown": {"prepass_us": round(pre_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                      "e2e_frac_of_peak": round(value / PEAK_TOPS, 4)},
+        "context": "pages: ~3x FlashAttention2 and ~4.5x xformers OPS on RTX4090; ~FlashAttention3(fp8) speed on Hopper",
+    }
+    if cpu:
+        o_host = out.float().cpu().numpy().reshape(B * H, N, D)[0]
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name, or 'all' (default: the N=16k D=128 headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the attention heads of a batch are independent, so a multi-GPU "
+              "deployment shards heads with no exchange; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from fp8_attention_transformer_amd import workloads as wl
+    if args.workload == "all":
+        todo = wl.ALL
+    else:
+        todo = [wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE]
+    for w in todo:
+        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

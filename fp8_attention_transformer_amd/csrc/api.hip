@@ -1,0 +1,242 @@
+// C ABI of libsage (declarations and documentation in include/sage.h).
+#include "sage.h"
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "sage_internal.h"
+
+namespace {
+
+using sage::Bufs;
+using sage::Dims;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool shape_ok(int B, int H, int N, int D) {
+  if (B < 1 || H < 1 || N < 1) return false;
+  if (D != 64 && D != 128) return false;
+  // keep every index computed in 32-bit arithmetic inside the kernels in range
+  const long long NP = ((long long)N + 127) / 128 * 128;
+  if (NP > (1LL << 24)) return false;
+  if ((long long)B * H > 65535) return false;   // grid y dimension of the prepass
+  if ((long long)B * H * (NP / 128) > (1LL << 30)) return false;
+  return true;
+}
+
+Dims make_dims(int B, int H, int N, int D) {
+  Dims d;
+  d.B = B;
+  d.H = H;
+  d.N = N;
+  d.D = D;
+  d.NP = (N + 127) / 128 * 128;
+  d.NQB = d.NP / 128;
+  return d;
+}
+
+// Sizes of the workspace arrays, in the order of sage_quant_bufs.
+bool layout(const Dims& d, size_t sizes[11]) {
+  const size_t bh = (size_t)d.B * d.H, np = (size_t)d.NP, nqb = (size_t)d.NQB, D = (size_t)d.D;
+  size_t rows, t;
+  if (!mul_ok(bh, np, &rows)) return false;
+  if (!mul_ok(rows, D / 2, &sizes[0])) return false;        // q_codes
+  sizes[1] = sizes[0];                                       // k_codes
+  if (!mul_ok(rows, 4, &sizes[2])) return false;            // q_scale
+  sizes[3] = rows / 16 * 4;                                  // k_scale
+  if (!mul_ok(bh * nqb, D * 4, &sizes[4])) return false;    // q_mean
+  sizes[5] = bh * D * 4;                                     // k_mean
+  if (!mul_ok(rows, D, &sizes[6])) return false;            // v_codes
+  sizes[7] = bh * D * 4;                                     // v_scale
+  if (!mul_ok(bh * nqb, np, &t) || !mul_ok(t, 4, &sizes[8])) return false;  // delta_s
+  sizes[9] = sizes[4];                                       // k_part
+  sizes[10] = sizes[4];                                      // v_part
+  return true;
+}
+
+size_t total_bytes(const Dims& d) {
+  size_t s[11];
+  if (!layout(d, s)) return 0;
+  size_t tot = 0;
+  for (int i = 0; i < 11; i++) {
+    const size_t a = align_up(s[i]);
+    if (a < s[i] || tot + a < tot) return 0;
+    tot += a;
+  }
+  return tot;
+}
+
+void carve(void* ws, const Dims& d, sage_quant_bufs* out) {
+  size_t s[11];
+  layout(d, s);
+  char* p = (char*)ws;
+  void** slots[11] = {(void**)&out->q_codes, (void**)&out->k_codes, (void**)&out->q_scale, (void**)&out->k_scale,
+                      (void**)&out->q_mean,  (void**)&out->k_mean,  (void**)&out->v_codes, (void**)&out->v_scale,
+                      (void**)&out->delta_s, (void**)&out->k_part,  (void**)&out->v_part};
+  for (int i = 0; i < 11; i++) {
+    *slots[i] = p;
+    p += align_up(s[i]);
+  }
+}
+
+Bufs to_internal(const sage_quant_bufs& q) {
+  Bufs b;
+  b.q_codes = q.q_codes;
+  b.k_codes = q.k_codes;
+  b.q_scale = q.q_scale;
+  b.k_scale = q.k_scale;
+  b.q_mean = q.q_mean;
+  b.k_mean = q.k_mean;
+  b.v_codes = q.v_codes;
+  b.v_scale = q.v_scale;
+  b.delta_s = q.delta_s;
+  b.k_part = q.k_part;
+  b.v_part = q.v_part;
+  return b;
+}
+
+bool bufs_ok(const sage_quant_bufs* q) {
+  return q && q->q_codes && q->k_codes && q->q_scale && q->k_scale && q->q_mean && q->k_mean && q->v_codes &&
+         q->v_scale && q->delta_s && q->k_part && q->v_part;
+}
+
+// gfx950 check, cached once per device.
+std::once_flag g_once[kMaxDevices];
+int g_is_gfx950[kMaxDevices];
+
+sage_status device_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+  std::call_once(g_once[dev], [dev] {
+    hipDeviceProp_t p;
+    g_is_gfx950[dev] = (hipGetDeviceProperties(&p, dev) == hipSuccess && std::strncmp(p.gcnArchName, "gfx950", 6) == 0)
+                           ? 1
+                           : 0;
+  });
+  return g_is_gfx950[dev] ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_contract_version(void) { return sage::kContractVersion; }
+
+const char* sage_status_string(sage_status st) {
+  switch (st) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID: return "SAGE_ERR_INVALID: invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: device is not gfx950";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace too small";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown sage_status";
+}
+
+size_t sage_workspace_bytes(int B, int H, int N, int D) {
+  if (!shape_ok(B, H, N, D)) return 0;
+  return total_bytes(make_dims(B, H, N, D));
+}
+
+sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H, int N, int D, sage_quant_bufs* out) {
+  if (!ws || !out || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, H, N, D);
+  const size_t need = total_bytes(d);
+  if (need == 0) return SAGE_ERR_INVALID;
+  if (bytes < need) return SAGE_ERR_WORKSPACE;
+  carve(ws, d, out);
+  return SAGE_OK;
+}
+
+sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H, int N,
+                              int D, const sage_quant_bufs* out, hipStream_t stream) {
+  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, H, N, D);
+  if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), 1.0f, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
+                          int causal, float sm_scale, sage_dtype in_dtype, sage_dtype out_dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, H, N, D);
+  const size_t need = total_bytes(d);
+  if (need == 0) return SAGE_ERR_INVALID;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  size_t elems, obytes, ibytes;
+  if (!mul_ok((size_t)B * H * N, (size_t)D, &elems)) return SAGE_ERR_INVALID;
+  if (!mul_ok(elems, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(elems, 2, &ibytes)) return SAGE_ERR_INVALID;
+  if (ranges_overlap(o, obytes, q, ibytes) || ranges_overlap(o, obytes, k, ibytes) ||
+      ranges_overlap(o, obytes, v, ibytes) || ranges_overlap(o, obytes, workspace, need))
+    return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  sage_quant_bufs qb;
+  carve(workspace, d, &qb);
+  const Bufs b = to_internal(qb);
+  const float ks = sm_scale * 1.44269504088896340736f;
+  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, 1.0f, stream);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_attn(b, d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
+                                float sm_scale, sage_dtype out_dtype, hipStream_t stream) {
+  if (!bufs_ok(qb) || !o || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, H, N, D);
+  if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const float ks = sm_scale * 1.44269504088896340736f;
+  const hipError_t e = sage::launch_attn(to_internal(*qb), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int bh, int q0, int k0, int nq,
+                                int nk, int32_t* out, hipStream_t stream) {
+  if (!bufs_ok(qb) || !out || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+  if (bh < 0 || bh >= B * H || q0 < 0 || k0 < 0 || nq < 1 || nk < 1) return SAGE_ERR_INVALID;
+  if ((long long)q0 + nq > N || (long long)k0 + nk > N) return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, N, D), bh, q0, k0, nq, nk, out, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_fp8_encode_debug(const float* in, uint8_t* out, size_t n, hipStream_t stream) {
+  if (!in || !out || n == 0 || n > ((size_t)1 << 40)) return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const hipError_t e = sage::launch_fp8_encode(in, out, n, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+}  // extern "C"

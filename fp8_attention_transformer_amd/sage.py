@@ -1,0 +1,188 @@
+"""ctypes binding of libsage (include/sage.h): argument marshalling only.
+
+Every step of the attention runs in the HIP kernels of libsage.so; torch is
+used here only to allocate device memory and to name the current stream.  The
+functions carry the C names without the ``sage_`` prefix.  There is no CPU
+fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsage.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+F16, BF16, F32 = 0, 1, 2
+
+EXPORTED = [
+    "sage_contract_version", "sage_status_string", "sage_workspace_bytes", "sage_quant_bufs_from_workspace",
+    "sage_quant_smooth", "sage_attn_fwd", "sage_attn_quantized", "sage_qk_int32_debug", "sage_fp8_encode_debug",
+]
+
+
+class QuantBufs(ctypes.Structure):
+    """Mirror of sage_quant_bufs (device pointers)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "q_codes", "k_codes", "q_scale", "k_scale", "q_mean", "k_mean", "v_codes", "v_scale", "delta_s",
+        "k_part", "v_part")]
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                               "python fp8_attention_transformer_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+        L.sage_contract_version.restype = i32
+        L.sage_status_string.argtypes = [i32]
+        L.sage_status_string.restype = ctypes.c_char_p
+        L.sage_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.sage_workspace_bytes.restype = sz
+        L.sage_quant_bufs_from_workspace.argtypes = [P, sz, i32, i32, i32, i32, ctypes.POINTER(QuantBufs)]
+        L.sage_quant_bufs_from_workspace.restype = i32
+        L.sage_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth.restype = i32
+        L.sage_attn_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, P]
+        L.sage_attn_fwd.restype = i32
+        L.sage_attn_quantized.argtypes = [ctypes.POINTER(QuantBufs), P, i32, i32, i32, i32, i32, f32, i32, P]
+        L.sage_attn_quantized.restype = i32
+        L.sage_qk_int32_debug.argtypes = [ctypes.POINTER(QuantBufs), i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          P, P]
+        L.sage_qk_int32_debug.restype = i32
+        L.sage_fp8_encode_debug.argtypes = [P, P, sz, P]
+        L.sage_fp8_encode_debug.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise SageError(status, where)
+
+
+def status_string(status: int) -> str:
+    return lib().sage_status_string(status).decode()
+
+
+def contract_version() -> int:
+    return lib().sage_contract_version()
+
+
+def workspace_bytes(B: int, H: int, N: int, D: int) -> int:
+    return lib().sage_workspace_bytes(B, H, N, D)
+
+
+def quant_bufs_from_workspace(ws_ptr: int, nbytes: int, B: int, H: int, N: int, D: int) -> QuantBufs:
+    qb = QuantBufs()
+    _check(lib().sage_quant_bufs_from_workspace(ws_ptr, nbytes, B, H, N, D, ctypes.byref(qb)),
+           "sage_quant_bufs_from_workspace")
+    return qb
+
+
+def quant_smooth(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, H: int, N: int, D: int,
+                 bufs: QuantBufs, stream: int = 0) -> None:
+    _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, ctypes.byref(bufs), stream),
+           "sage_quant_smooth")
+
+
+def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool,
+             sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(lib().sage_attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale),
+                               in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd")
+
+
+def attn_quantized(bufs: QuantBufs, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool, sm_scale: float,
+                   out_dtype: int, stream: int = 0) -> None:
+    _check(lib().sage_attn_quantized(ctypes.byref(bufs), o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale),
+                                     out_dtype, stream), "sage_attn_quantized")
+
+
+def qk_int32_debug(bufs: QuantBufs, B: int, H: int, N: int, D: int, bh: int, q0: int, k0: int, nq: int, nk: int,
+                   out_ptr: int, stream: int = 0) -> None:
+    _check(lib().sage_qk_int32_debug(ctypes.byref(bufs), B, H, N, D, bh, q0, k0, nq, nk, out_ptr, stream),
+           "sage_qk_int32_debug")
+
+
+def fp8_encode_debug(in_ptr: int, out_ptr: int, n: int, stream: int = 0) -> None:
+    _check(lib().sage_fp8_encode_debug(in_ptr, out_ptr, n, stream), "sage_fp8_encode_debug")
+
+
+# ---------------------------------------------------------------- torch glue --
+# Device memory and the stream handle come from torch; nothing is computed here.
+
+def _torch_dtype_code(t) -> int:
+    import torch
+    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}[t]
+
+
+@dataclass
+class Workspace:
+    tensor: object      # torch.uint8 device tensor
+    B: int
+    H: int
+    N: int
+    D: int
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+    @property
+    def nbytes(self) -> int:
+        return self.tensor.numel()
+
+    def bufs(self) -> QuantBufs:
+        return quant_bufs_from_workspace(self.ptr, self.nbytes, self.B, self.H, self.N, self.D)
+
+
+def alloc_workspace(B: int, H: int, N: int, D: int, device="cuda") -> Workspace:
+    import torch
+    n = workspace_bytes(B, H, N, D)
+    if n == 0:
+        raise SageError(ERR_INVALID, "sage_workspace_bytes")
+    return Workspace(torch.empty(n, dtype=torch.uint8, device=device), B, H, N, D)
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype=None, workspace: Workspace = None,
+         out=None):
+    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors."""
+    import torch
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, D] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, N, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, H, N, D, q.device)
+    attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, causal, sm_scale,
+             _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr, workspace.nbytes,
+             _stream_handle(q.device))
+    return out

@@ -1,0 +1,171 @@
+/*
+ * sage.h -- C ABI of libsage: the SageAttention2 quantized attention forward
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "SageAttention2: Efficient Attention with Thorough
+ * Outlier Smoothing and Per-thread INT4 Quantization" (arXiv 2411.10958,
+ * abstract page): Q and K are smoothed and quantized to INT4 with fine-grained
+ * scales, S = QK^T is computed in integer arithmetic and dequantized, an online
+ * softmax produces P~, and P~ and V are quantized to FP8 with a two-level
+ * accumulation of P~V.  The "SageAttention2 Technical Report" summary page
+ * (Key Contributions 1-2) describes the same INT4 QK / FP8 P~V split.
+ *
+ * Conventions for every entry point
+ *  - Tensors are contiguous, row-major [B, H, N, D] device buffers (self
+ *    attention: queries and keys share N).  D must be 64 or 128; B, H, N >= 1.
+ *  - Every buffer is owned by the caller.  The library allocates no device
+ *    memory, keeps no pointer after returning and holds no mutable state
+ *    (the gfx950 check is cached once per device).
+ *  - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *    returns without synchronising; results are valid after the stream is.
+ *  - Arguments are validated before anything is launched; on error nothing is
+ *    written.  Launch failures return SAGE_ERR_HIP; faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Contract constants (they fix the method's rounding; any change bumps
+ *    sage_contract_version): Q-smoothing block and mean chunk = 128 tokens;
+ *    online-softmax block = 128 keys (also the level-1 block of the two-level
+ *    P~V accumulation); K scale groups of 16 keys (two per 32-key tile).
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID = -1,      /* null pointer, bad size, bad dtype, bad sm_scale, overflow */
+  SAGE_ERR_UNSUPPORTED = -2,  /* current device is not gfx950                               */
+  SAGE_ERR_WORKSPACE = -3,    /* workspace smaller than sage_workspace_bytes()              */
+  SAGE_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed                 */
+} sage_status;
+
+typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
+
+/*
+ * Device buffers written by sage_quant_smooth (and by the prepass inside
+ * sage_attn_fwd).  NP = N rounded up to a multiple of 128, NQB = NP / 128.
+ * Rows or keys at index >= N are padding: codes 0, scales 0, V bytes 0.
+ *
+ *  q_codes, k_codes  uint8 [B,H,NP,D/2]  INT4 codes in [-7,7], two per byte:
+ *                    byte b of a row holds channel 2b (c_even) and 2b+1
+ *                    (c_odd) as the signed value 16*c_odd + c_even + 8, so
+ *                    c_even = (byte & 15) - 8 and c_odd = (int8)byte >> 4.
+ *  q_scale           fp32  [B,H,NP]      one scale per token (delta = amax/7)
+ *  k_scale           fp32  [B,H,NP/16]   one scale per 16-key group; in a
+ *                    32-key tile starting at key 32u, group 2u+h holds the keys
+ *                    32u + o with (o/4) % 2 == h
+ *  q_mean            fp32  [B,H,NQB,D]   per-block Q channel means (tail block
+ *                    averages its valid tokens only)
+ *  k_mean            fp32  [B,H,D]       K channel means over all N tokens
+ *  v_codes           uint8 [B,H,NQB,D,128] OCP e4m3fn codes of V/v_scale,
+ *                    channel-major per 128-key block; position p of a block
+ *                    holds key 64(p/64) + 32(s/16) + 8((s%16)/4) + 4((p%64)/32)
+ *                    + s%4 with s = p%32
+ *  v_scale           fp32  [B,H,D]       per-channel scale (amax/448)
+ *  delta_s           fp32  [B,H,NQB,NP]  compensation term
+ *                    DeltaS[qb][j] = q_mean[qb] . (K[j] - k_mean), fp32
+ *                    accumulation (not scaled by sm_scale)
+ *  k_part, v_part    fp32  [B,H,NQB,D]   scratch: per-chunk K sums, V absmax
+ */
+typedef struct {
+  uint8_t* q_codes;
+  uint8_t* k_codes;
+  float* q_scale;
+  float* k_scale;
+  float* q_mean;
+  float* k_mean;
+  uint8_t* v_codes;
+  float* v_scale;
+  float* delta_s;
+  float* k_part;
+  float* v_part;
+} sage_quant_bufs;
+
+/* Version of the contract constants above (1 = 128/128/16). */
+int sage_contract_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* sage_status_string(sage_status st);
+
+/*
+ * Bytes of device workspace sage_attn_fwd needs for this shape (all
+ * sage_quant_bufs arrays, each 256-byte aligned).  Returns 0 for an invalid
+ * shape or on size_t overflow.
+ */
+size_t sage_workspace_bytes(int B, int H, int N, int D);
+
+/*
+ * Host-only pointer carving: fill *out with the sage_quant_bufs layout inside
+ * a workspace of `bytes` bytes at device address `ws`.  Touches no device.
+ * Errors: SAGE_ERR_INVALID (null pointers, bad shape), SAGE_ERR_WORKSPACE.
+ */
+sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H, int N, int D,
+                                           sage_quant_bufs* out);
+
+/*
+ * Prepass (smoothing, INT4 Q/K quantization and packing, FP8 V with
+ * per-channel scales, compensation term): the smoothing of the method and
+ * the quantization of Q, K to INT4 and V to FP8 (SageAttention2 abstract).
+ * q, k, v: device [B,H,N,D] of in_dtype (SAGE_F16 or SAGE_BF16).  All arrays
+ * of *out must be device buffers of the sizes listed above (for example carved
+ * by sage_quant_bufs_from_workspace).
+ */
+sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H,
+                              int N, int D, const sage_quant_bufs* out, hipStream_t stream);
+
+/*
+ * Attention forward: O = SageAttention2(Q, K, V), i.e. the prepass above
+ * followed by the fused kernel (INT4 QK^T on the INT8 matrix core,
+ * dequantization with the compensation term, online softmax over 128-key
+ * blocks, FP8 P~ and V on the FP8 matrix core with two-level accumulation).
+ *  q, k, v   device [B,H,N,D] of in_dtype (SAGE_F16 / SAGE_BF16)
+ *  o         device [B,H,N,D] of out_dtype (SAGE_F16 / SAGE_BF16 / SAGE_F32);
+ *            must not alias q, k, v or the workspace
+ *  causal    nonzero: query i attends to keys j <= i
+ *  sm_scale  softmax scale (> 0, finite), usually 1/sqrt(D)
+ *  workspace device buffer of at least sage_workspace_bytes(B,H,N,D) bytes;
+ *            afterwards it holds the sage_quant_bufs of this call
+ * Equivalent to sage_quant_smooth followed by sage_attn_quantized.
+ */
+sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
+                          int causal, float sm_scale, sage_dtype in_dtype, sage_dtype out_dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The fused attention kernel alone, over prepass buffers already written by
+ * sage_quant_smooth (or by an earlier sage_attn_fwd): INT4 QK^T,
+ * dequantization with the compensation term, online softmax, FP8 P~V with
+ * two-level accumulation (SageAttention2 abstract).  Arguments as for
+ * sage_attn_fwd; qb must describe buffers of this B, H, N, D.
+ */
+sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
+                                float sm_scale, sage_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Debug: the exact integer dot products of the INT4 codes, computed by the
+ * same matrix-core tile routine as the fused kernel.  For head bh = b*H + h:
+ *   out[a][c] = sum_ch qcode[q0+a][ch] * kcode[k0+c][ch],  a < nq, c < nk
+ * out: device int32 [nq, nk].  Requires 0 <= q0, q0+nq <= N, 0 <= k0,
+ * k0+nk <= N, nq, nk >= 1.
+ */
+sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int bh, int q0, int k0,
+                                int nq, int nk, int32_t* out, hipStream_t stream);
+
+/*
+ * Debug: fp32 -> OCP e4m3fn with the device conversion the kernels use for P~
+ * and V (round to nearest even).  in: device fp32 [n]; out: device uint8 [n].
+ */
+sage_status sage_fp8_encode_debug(const float* in, uint8_t* out, size_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H_ */

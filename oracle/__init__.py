@@ -131,7 +131,9 @@ class Quant:
     delta_s: np.ndarray   # fp32  [B,H,ceil(N/128),N]
 
 
-def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0) -> Quant:
+def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True) -> Quant:
+    """Run the prepass; with_delta_s=False skips the (quadratic) compensation
+    term and leaves ``delta_s`` as None."""
     B, H, N, D = q_bits.shape
     nqb = (N + BQ_MEAN - 1) // BQ_MEAN
     G = 2 * ((N + 31) // 32)
@@ -141,7 +143,7 @@ def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0) -> Quant
         k_codes=np.empty((B, H, N, D), np.int8), k_scale=np.empty((B, H, G), np.float32),
         q_mean=np.empty((B, H, nqb, D), np.float32), k_mean=np.empty((B, H, D), np.float32),
         v_codes=np.empty((B, H, N, D), np.uint8), v_scale=np.empty((B, H, D), np.float32),
-        delta_s=np.empty((B, H, nqb, N), np.float32))
+        delta_s=np.empty((B, H, nqb, N), np.float32) if with_delta_s else None)
     rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D,
                                    _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
                                    _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),

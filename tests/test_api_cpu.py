@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sage.h, and validates arguments synchronously (every error
+path below returns before anything touches a device)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from fp8_attention_transformer_amd import sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000000  # never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "sage.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 8
+    L = sage.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(sage.EXPORTED) == names
+
+
+def test_contract_and_status_strings():
+    assert sage.contract_version() == 1
+    for st in (sage.OK, sage.ERR_INVALID, sage.ERR_UNSUPPORTED, sage.ERR_WORKSPACE, sage.ERR_HIP):
+        assert sage.status_string(st).startswith("SAGE_")
+
+
+@pytest.mark.parametrize("shape", [(0, 1, 10, 64), (1, 0, 10, 64), (1, 1, 0, 64), (1, 1, 10, 96), (1, 1, 10, 32),
+                                   (1, 1, 1 << 25, 64)])
+def test_workspace_bytes_invalid(shape):
+    assert sage.workspace_bytes(*shape) == 0
+
+
+def _sizes(B, H, N, D):
+    NP = (N + 127) // 128 * 128
+    NQB = NP // 128
+    BH = B * H
+    return [BH * NP * D // 2, BH * NP * D // 2, BH * NP * 4, BH * NP // 16 * 4, BH * NQB * D * 4, BH * D * 4,
+            BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * D * 4, BH * NQB * D * 4]
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 256, 64), (4, 32, 4096, 128), (2, 48, 17776, 64), (1, 1, 1, 128)])
+def test_workspace_carving(shape):
+    nbytes = sage.workspace_bytes(*shape)
+    sizes = _sizes(*shape)
+    assert nbytes >= sum(sizes)
+    base = 1 << 40
+    qb = sage.quant_bufs_from_workspace(base, nbytes, *shape)
+    ptrs = [getattr(qb, f) for f, _ in sage.QuantBufs._fields_]
+    for p, s in zip(ptrs, sizes):
+        assert p % 256 == 0 and base <= p and p + s <= base + nbytes
+    spans = sorted(zip(ptrs, sizes))
+    for (p0, s0), (p1, _) in zip(spans, spans[1:]):
+        assert p0 + s0 <= p1
+    with pytest.raises(sage.SageError) as e:
+        sage.quant_bufs_from_workspace(base, nbytes - 1, *shape)
+    assert e.value.status == sage.ERR_WORKSPACE
+    with pytest.raises(sage.SageError) as e:
+        sage.quant_bufs_from_workspace(0, nbytes, *shape)
+    assert e.value.status == sage.ERR_INVALID
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), B=1, H=2, N=256, D=64, causal=0,
+             sm_scale=0.125, in_dtype=sage.F16, out_dtype=sage.F32, ws=FAKE + (4 << 30), ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = sage.workspace_bytes(a["B"], a["H"], a["N"], a["D"])
+    return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["D"], a["causal"],
+                                    a["sm_scale"], a["in_dtype"], a["out_dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), sage.ERR_INVALID), (dict(k=None), sage.ERR_INVALID), (dict(v=None), sage.ERR_INVALID),
+    (dict(o=None), sage.ERR_INVALID), (dict(ws=None), sage.ERR_INVALID), (dict(D=96), sage.ERR_INVALID),
+    (dict(N=0), sage.ERR_INVALID), (dict(B=-1), sage.ERR_INVALID), (dict(sm_scale=0.0), sage.ERR_INVALID),
+    (dict(sm_scale=-1.0), sage.ERR_INVALID), (dict(sm_scale=math.nan), sage.ERR_INVALID),
+    (dict(sm_scale=math.inf), sage.ERR_INVALID), (dict(in_dtype=sage.F32), sage.ERR_INVALID),
+    (dict(in_dtype=7), sage.ERR_INVALID), (dict(out_dtype=5), sage.ERR_INVALID),
+    (dict(ws_bytes=100), sage.ERR_WORKSPACE), (dict(o=FAKE + 64), sage.ERR_INVALID),
+    (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID),
+])
+def test_attn_fwd_validation(kw, expect):
+    assert _attn(**kw) == expect
+
+
+def test_quant_smooth_and_debug_validation():
+    L = sage.lib()
+    qb = sage.QuantBufs(*([FAKE] * 11))
+    assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, ctypes.byref(qb), None) == sage.ERR_INVALID
+    bad = sage.QuantBufs(*([FAKE] * 10 + [0]))
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, ctypes.byref(bad), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, None, None) == sage.ERR_INVALID
+    dbg = L.sage_qk_int32_debug
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 101, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 1, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 99, 0, 2, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, -1, 2, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 0, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 4, 4, None, None) == sage.ERR_INVALID
+    assert L.sage_fp8_encode_debug(None, FAKE, 10, None) == sage.ERR_INVALID
+    assert L.sage_fp8_encode_debug(FAKE, FAKE, 0, None) == sage.ERR_INVALID
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "fp8_attention_transformer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "sage_oracle" not in src, f

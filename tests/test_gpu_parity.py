@@ -1,0 +1,240 @@
+"""GPU parity: libsage (HIP, gfx950) against the CPU oracle, through the C ABI.
+
+Bit-exact: INT4 codes, all scales, means, FP8 V codes, int32 QK^T.
+Toleranced: the compensation term (fp32 vs the oracle's fp64 accumulation,
+bound derived from the fp32 chain) and O (max-abs 2e-3 plus a per-row slack for
+P~ elements that sit within rounding distance of an FP8 midpoint; the slack is
+reported so it cannot hide a bug).  Small cases cover every row; the full-size
+workloads run in the same launch configuration as the benchmark and are
+compared on sampled heads and rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from fp8_attention_transformer_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+EPS_TIE = 2.0 ** -14   # relative window around FP8 midpoints (exp2 and compensation rounding)
+
+SMALL = [
+    wl.TINY,
+    wl.custom(1, 1, 1, 64, seed=101),
+    wl.custom(1, 2, 17, 64, causal=True, seed=102, k_offset_std=3.0),
+    wl.custom(1, 1, 100, 128, causal=True, seed=103, k_offset_std=4.0, outlier_channels=4, outlier_scale=20.0),
+    wl.custom(2, 1, 129, 64, dtype=wl.F16, seed=104, k_offset_std=2.0),
+    wl.custom(1, 2, 300, 128, seed=105, k_offset_std=4.0, v_offset_std=1.0),
+    wl.custom(1, 1, 640, 128, causal=True, seed=106, t_noise_scale=0.5, k_offset_std=4.0),
+    wl.custom(1, 3, 1000, 64, causal=True, seed=107, outlier_channels=8, outlier_scale=15.0, outliers_in_k=True,
+              k_offset_std=5.0),
+]
+FULL = [wl.LLM, wl.DIT, wl.VIDEO] + wl.LONG
+
+
+def _sdt(w):
+    return 0 if w.dtype == wl.F16 else 1
+
+
+def _check_prepass(rb, z):
+    """rb: GPU readback; z: oracle Quant for the same heads."""
+    B, H, N, D = z.q_codes.shape
+    zq = lambda a: a.reshape((B * H,) + a.shape[2:])
+    assert np.array_equal(rb.q_codes, zq(z.q_codes)), "q codes"
+    assert np.array_equal(rb.k_codes, zq(z.k_codes)), "k codes"
+    assert np.array_equal(rb.q_scale, zq(z.q_scale)), "q scales"
+    assert np.array_equal(rb.k_scale, zq(z.k_scale)), "k scales"
+    assert np.array_equal(rb.q_mean, zq(z.q_mean)), "q means"
+    assert np.array_equal(rb.k_mean, zq(z.k_mean)), "k means"
+    assert np.array_equal(rb.v_scale, zq(z.v_scale)), "v scales"
+    assert np.array_equal(rb.v_codes, zq(z.v_codes)), "v codes"
+    # padding rows: zero codes (byte 8) and zero scales
+    assert np.all(rb.q_scale_p[:, N:] == 0) and np.all(rb.q_codes_packed[:, N:] == 8)
+    assert np.all(rb.k_codes_packed[:, N:] == 8)
+
+
+def _ds_bound(oracle_lib, z, k_bits, dtype_code):
+    """(D+2) * 2^-24 * sum_c |qmean_c * gamma(K)_jc|: the error bound of an fp32
+    fma chain over D channels, per compensation-term entry."""
+    B, H, N, D = z.q_codes.shape
+    K = oracle_lib.decode_input(k_bits, dtype_code).reshape(B * H, N, D)
+    gK = np.abs((K - z.k_mean.reshape(B * H, 1, D)).astype(np.float32)).astype(np.float64)
+    qm = np.abs(z.q_mean.reshape(B * H, -1, D)).astype(np.float64)
+    return (D + 2) * 2.0 ** -24 * np.einsum("bqc,bjc->bqj", qm, gK)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
+def test_prepass_bitexact_small(oracle_lib, w):
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w))
+    rb = gh.Readback(gh.run_quant_smooth(q, k, v, w.dtype))
+    _check_prepass(rb, z)
+    # compensation term within the fp32-chain bound
+    err = np.abs(rb.delta_s.astype(np.float64) - z.delta_s.reshape(w.B * w.H, -1, w.N))
+    assert np.all(err <= _ds_bound(oracle_lib, z, k, _sdt(w)) + 1e-30)
+    # padded key columns are zero
+    assert np.all(rb.delta_s_p[:, :, w.N:] == 0)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
+def test_qk_int32_bitexact_small(oracle_lib, w):
+    import torch
+    from fp8_attention_transformer_amd import sage
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False)
+    ws = gh.run_quant_smooth(q, k, v, w.dtype)
+    N = w.N
+    for bh in range(w.B * w.H):
+        out = torch.empty((N, N), dtype=torch.int32, device="cuda")
+        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, bh, 0, 0, N, N, out.data_ptr())
+        qc = z.q_codes.reshape(-1, N, w.D)[bh]
+        kc = z.k_codes.reshape(-1, N, w.D)[bh]
+        ref = oracle_lib.qk_int32(qc, kc, 0, 0, N, N)
+        assert np.array_equal(out.cpu().numpy(), ref)
+    # an interior window with ragged edges
+    if N >= 40:
+        out = torch.empty((N - 7 - 3, N - 11 - 2), dtype=torch.int32, device="cuda")
+        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, 0, 7, 11, N - 10, N - 13, out.data_ptr())
+        ref = oracle_lib.qk_int32(z.q_codes.reshape(-1, N, w.D)[0], z.k_codes.reshape(-1, N, w.D)[0], 7, 11,
+                                  N - 10, N - 13)
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def _compare_o(O_gpu, O_ref, slack, label):
+    err = np.abs(O_gpu.astype(np.float64) - O_ref.astype(np.float64)).max(1)
+    allowed = O_TOL + slack
+    bad = np.nonzero(err > allowed)[0]
+    used = int(np.sum(err > O_TOL))
+    print(f"[{label}] rows={err.size} maxerr={err.max():.3e} rows_using_slack={used} max_slack={slack.max():.3e}")
+    assert bad.size == 0, (label, bad[:5], err[bad[:5]], slack[bad[:5]])
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
+def test_attention_parity_small(oracle_lib, w):
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w))
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, eps=EPS_TIE)
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    O_gpu = out.cpu().numpy().reshape(-1, w.D)
+    _compare_o(O_gpu, O_ref, slack, w.name)
+    # the workspace of the attention call holds the same prepass
+    rb = gh.Readback(ws)
+    _check_prepass(rb, z)
+    # cos-sim against FP32 attention equals the method's own (oracle) value
+    O_fp, _ = oracle_lib.attn_exact(q, k, v, _sdt(w), w.causal, w.scale, 0)
+    c_gpu, c_orc = gh.cos_sim(O_gpu, O_fp), gh.cos_sim(O_ref, O_fp)
+    print(f"[{w.name}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+    assert abs(c_gpu - c_orc) < 1e-4
+
+
+@pytest.mark.parametrize("w", SMALL[:4], ids=lambda w: w.name + ("_c" if w.causal else ""))
+def test_low_precision_outputs(oracle_lib, w):
+    import torch
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w))
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, eps=EPS_TIE)
+    for dt, ulp in ((torch.bfloat16, 2.0 ** -8), (torch.float16, 2.0 ** -11)):
+        out, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, out_dtype=dt)
+        O_gpu = out.float().cpu().numpy().reshape(-1, w.D)
+        # one output rounding (half an ulp of |O|) on top of the fp32 bar
+        extra = ulp * np.abs(O_ref).max(1)
+        _compare_o(O_gpu, O_ref, slack + extra, f"{w.name}-{dt}")
+
+
+def test_determinism(oracle_lib):
+    import gpu_helpers as gh
+    w = SMALL[6]
+    q, k, v = wl.generate(w)
+    a, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    b, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+def test_fp8_conversion_matches_oracle(oracle_lib):
+    """The device e4m3 conversion used for V and P~ equals the oracle codec on a
+    dense sweep of [0, 464] (every 3rd fp32 bit pattern plus neighbourhoods of
+    every midpoint) and on negatives."""
+    import torch
+    from fp8_attention_transformer_amd import sage
+    hi = int(np.array([464.0], np.float32).view(np.uint32)[0])
+    mids = []
+    grid = oracle_lib.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    for a, b in zip(grid[:-1], grid[1:]):
+        m = np.float32((np.float64(a) + np.float64(b)) / 2)
+        mb = int(np.array([m], np.float32).view(np.uint32)[0])
+        mids.append(np.arange(mb - 64, mb + 65, dtype=np.uint32))
+    parts = [np.concatenate(mids)]
+    chunk = 1 << 25
+    for start in range(0, hi + 1, chunk * 3):
+        parts_bits = np.arange(start, min(start + chunk * 3, hi + 1), 3, dtype=np.uint32)
+        x = parts_bits.view(np.float32)
+        for sgn in (1.0, -1.0) if start == 0 else (1.0,):
+            xs = (x * np.float32(sgn)).astype(np.float32)
+            dev_in = torch.from_numpy(xs).cuda()
+            dev_out = torch.empty(xs.size, dtype=torch.uint8, device="cuda")
+            sage.fp8_encode_debug(dev_in.data_ptr(), dev_out.data_ptr(), xs.size)
+            got = dev_out.cpu().numpy()
+            ref = oracle_lib.e4m3_encode(xs)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, (xs[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    x = parts[0].view(np.float32)
+    dev_in = torch.from_numpy(x).cuda()
+    dev_out = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    sage.fp8_encode_debug(dev_in.data_ptr(), dev_out.data_ptr(), x.size)
+    assert np.array_equal(dev_out.cpu().numpy(), oracle_lib.e4m3_encode(x))
+
+
+def _sample_rows(w, heads, rng, per_head=96):
+    N = w.N
+    rows = []
+    for hh in range(heads):
+        pick = set([0, 1, 127, 128, N // 2, N - 1, N - 2, max(0, N - 129)])
+        pick.update(rng.integers(0, N, per_head).tolist())
+        rows.extend(hh * N + np.array(sorted(i for i in pick if 0 <= i < N)))
+    return np.array(rows, np.int64)
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size_parity(oracle_lib, w):
+    """The benchmark's workload and launch: all heads on the GPU; codes and
+    scales of every head bit-exact; compensation term, int32 tiles and O
+    compared on two heads (first and last) and sampled rows."""
+    import torch
+    from fp8_attention_transformer_amd import sage
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    BH = w.B * w.H
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    rb = gh.Readback(ws)
+    z_all = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False)
+    _check_prepass(rb, z_all)
+    del z_all
+    O_gpu_all = out.cpu().numpy().reshape(BH, w.N, w.D)
+    del out
+    rng = np.random.default_rng(w.seed)
+    for bh in (0, BH - 1):
+        qs, kk, vs = (a.reshape(BH, 1, w.N, w.D)[bh:bh + 1] for a in (q, k, v))
+        z = oracle_lib.quant_smooth(qs, kk, vs, _sdt(w))
+        # compensation term within the fp32-chain bound
+        err = np.abs(rb.delta_s[bh].astype(np.float64) - z.delta_s[0, 0])
+        assert np.all(err <= _ds_bound(oracle_lib, z, kk, _sdt(w))[0] + 1e-30)
+        # int32 tiles: first, last, tail and random windows
+        wins = [(0, 0), (w.N - 64, w.N - 64), (0, w.N - 64)] + [tuple(rng.integers(0, w.N - 64, 2)) for _ in range(4)]
+        for q0, k0 in wins:
+            o32 = torch.empty((64, 64), dtype=torch.int32, device="cuda")
+            sage.qk_int32_debug(ws.bufs(), w.B, w.H, w.N, w.D, bh, int(q0), int(k0), 64, 64, o32.data_ptr())
+            ref = oracle_lib.qk_int32(z.q_codes[0, 0], z.k_codes[0, 0], int(q0), int(k0), 64, 64)
+            assert np.array_equal(o32.cpu().numpy(), ref)
+        rows = _sample_rows(w, 1, rng)
+        O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, rows=rows, eps=EPS_TIE)
+        _compare_o(O_gpu_all[bh][rows], O_ref, slack, f"{w.name}/bh{bh}")
+        O_fp, _ = oracle_lib.attn_exact(qs, kk, vs, _sdt(w), w.causal, w.scale, 0, rows=rows)
+        c_gpu, c_orc = gh.cos_sim(O_gpu_all[bh][rows], O_fp), gh.cos_sim(O_ref, O_fp)
+        print(f"[{w.name}/bh{bh}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+        assert abs(c_gpu - c_orc) < 1e-3
