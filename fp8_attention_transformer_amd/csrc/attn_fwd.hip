@@ -43,9 +43,9 @@ struct QOperand {
 
 // Build the query operands for lane (query row `qrow` in padded coordinates,
 // half h) from the packed codes.  Both lanes of a query end with the same
-// correction block.
+// correction block, offset by `start` (added to every accumulator).
 template <int D>
-__device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_codes_head, int qrow, int h,
+__device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_codes_head, int qrow, int h, int start,
                                                QOperand<D>& op) {
   constexpr int KROW = D / 2;
   int corr = 0;
@@ -70,8 +70,15 @@ __device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_cod
   }
   corr += __shfl_xor(corr, 32);
 #pragma unroll
-  for (int r = 0; r < 16; r++) op.cinit[r] = -128 * corr;
+  for (int r = 0; r < 16; r++) op.cinit[r] = start - 128 * corr;
 }
+
+// Accumulators start at the bit pattern of 1.5 * 2^23.  The integer sum
+// 16*acc stays below 2^22 in magnitude, so the int32 result read as fp32 is
+// exactly 1.5 * 2^23 + 16*acc, and one exact subtraction yields float(16*acc)
+// (cheaper than an int->float conversion).
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kMagic = 12582912.0f;
 
 // One 32-key tile of S^T (times 16): `a[pr]` holds this lane's 16 packed K
 // bytes (key row lane%32, half h) for channel pair-block pr.
@@ -110,18 +117,149 @@ __device__ __forceinline__ int xcd_logical_id(int pid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// LDS layouts are XOR-swizzled in 16-byte chunks so that the 16 lanes served
+// together by one ds_read_b128 hit distinct banks.
+//   K tile: 128 rows (keys) x KROW bytes; chunk c of row r at c ^ kswz(r).
+//   V tile: D rows (channels) x 128 bytes; chunk c of row r at c ^ ((r>>1)&7).
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r >> 2) & 3 : (r >> 3) & 1;
+}
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct HBM/L2 -> LDS copy of one 128-key block: K codes and FP8 V.  Lane l
+// of a wave writes LDS chunk (wave base + l); it fetches the global chunk whose
+// swizzled position that is.
+template <int D>
+__device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, const uint8_t* kblk, const uint8_t* vblk,
+                                               int t, int wave, int lane) {
+  constexpr int KROW = D / 2, KCPR = KROW / 16;
+  constexpr int KCH = kBK * KROW / 16 / 256, VCH = D * kBK / 16 / 256;
+  const uint8_t* gk = kblk + (size_t)t * kBK * KROW;
+  const uint8_t* gv = vblk + (size_t)t * D * kBK;
+#pragma unroll
+  for (int i = 0; i < KCH; i++) {
+    const int wbase = 256 * i + 64 * wave;
+    const int e = wbase + lane, r = e / KCPR, c = (e % KCPR) ^ kswz<D>(r);
+    __builtin_amdgcn_global_load_lds((const void*)(gk + r * KROW + 16 * c), (lds_ptr_t)(sK + 16 * wbase), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < VCH; i++) {
+    const int wbase = 256 * i + 64 * wave;
+    const int e = wbase + lane, r = e / 8, c = (e % 8) ^ vswz(r);
+    __builtin_amdgcn_global_load_lds((const void*)(gv + r * kBK + 16 * c), (lds_ptr_t)(sV + 16 * wbase), 16, 0, 0);
+  }
+}
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
+struct AttnState {
+  static constexpr int NDT = D / 32;
+  v16f O[NDT];
+  float m, l;
+};
+
+// One 128-key block for this wave: S^T tiles, dequantization, online softmax,
+// FP8 P~, two-level P~V.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D>& qop, const uint8_t* cK,
+                                           const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
+                                           int t, int qb, int qrow, int n, int h, const Dims& d) {
   constexpr int KROW = D / 2;
   constexpr int NPAIR = D / 64;
   constexpr int NDT = D / 32;
-  __shared__ __align__(16) uint8_t sK[kBK * KROW];
-  __shared__ __align__(16) uint8_t sV[D * kBK];
-  __shared__ float sDS[kBK];
-  __shared__ float sKS[kBK / kKGroup];
+  // ---- S^T for 4 tiles of 32 keys (values 1.5*2^23 + 16*acc as fp32 bits)
+  v16i S[4];
+#pragma unroll
+  for (int T = 0; T < 4; T++) {
+    const int row = 32 * T + n;
+    v4i a[NPAIR];
+#pragma unroll
+    for (int pr = 0; pr < NPAIR; pr++) a[pr] = *(const v4i*)(cK + row * KROW + 16 * ((2 * pr + h) ^ kswz<D>(row)));
+    S[T] = qk_tile<D>(a, qop);
+  }
+  // ---- dequantize into the log2 domain, mask, block max
+  float s2[4][16];
+  float bmax = -__builtin_inff();
+  const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
+#pragma unroll
+  for (int T = 0; T < 4; T++) {
+    const float c = ((dq * cKS[2 * T + h]) * ks) * 0.0625f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+      const float f16acc = __int_as_float(S[T][r]) - kMagic;
+      s2[T][r] = __builtin_fmaf(f16acc, c, cDS[key]);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int key = t * kBK + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool bad = (key >= d.N) || (CAUSAL && key > qrow);
+        if (bad) s2[T][r] = -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) bmax = fmaxf(bmax, s2[T][r]);
+  }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+  const float mnew = fmaxf(as.m, bmax);
+  const float alpha = __builtin_amdgcn_exp2f(as.m - mnew);
+  const float mm = mnew - kLog2_448;
+  // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
+  float rowsum = 0.0f;
+  v8i P8[2];
+#pragma unroll
+  for (int T = 0; T < 4; T++) {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
+      rowsum += p[r];
+    }
+#pragma unroll
+    for (int w = 0; w < 4; w++) P8[T >> 1][4 * (T & 1) + w] = (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
+  }
+  rowsum += __shfl_xor(rowsum, 32);
+  as.l = alpha * as.l + rowsum;
+  as.m = mnew;
+  // ---- two-level P~V: fresh FP32 partial R per d-tile, then O = alpha*O + R
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++) {
+    const int row = 32 * dt + n;
+    v16f R;
+#pragma unroll
+    for (int r = 0; r < 16; r++) R[r] = 0.0f;
+#pragma unroll
+    for (int kh = 0; kh < 2; kh++) {
+      const int c0 = 4 * kh + 2 * h;
+      const v4i lo = *(const v4i*)(cV + row * kBK + 16 * (c0 ^ vswz(row)));
+      const v4i hi = *(const v4i*)(cV + row * kBK + 16 * ((c0 + 1) ^ vswz(row)));
+      const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      R = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], R, 0, 0, 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) as.O[dt][r] = __builtin_fmaf(alpha, as.O[dt][r], R[r]);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
+  constexpr int KROW = D / 2;
+  constexpr int NDT = D / 32;
+  // Two LDS buffers as separate arrays, so the compiler can tell the block
+  // being read from the block being filled by the asynchronous copy.
+  __shared__ __align__(16) uint8_t sK0[kBK * KROW];
+  __shared__ __align__(16) uint8_t sK1[kBK * KROW];
+  __shared__ __align__(16) uint8_t sV0[D * kBK];
+  __shared__ __align__(16) uint8_t sV1[D * kBK];
+  __shared__ float sDS0[kBK], sDS1[kBK];
+  __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -131,108 +269,52 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const int qrow = qb * kBQ + wave * 32 + n;     // padded query index of this lane
   const size_t hrowp = (size_t)bh * d.NP;
 
-  QOperand<D> qop;
-  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, qop);
-  const float dq = b.q_scale[hrowp + qrow];
   const float* dsrow = b.delta_s + ((size_t)bh * d.NQB + qb) * d.NP;
   const uint8_t* kblk = b.k_codes + hrowp * KROW;
   const uint8_t* vblk = b.v_codes + (size_t)bh * d.NQB * D * kBK;
   const float* kscl = b.k_scale + hrowp / kKGroup;
+  const int tend = CAUSAL ? qb + 1 : d.NQB;
 
-  v16f O[NDT];
+  // block 0 -> buffer 0
+  stage_kv_async<D>(sK0, sV0, kblk, vblk, 0, wave, lane);
+  float ds_next = tid < kBK ? dsrow[tid] : 0.0f;
+  float ks_next = tid < kBK / kKGroup ? kscl[tid] : 0.0f;
+
+  QOperand<D> qop;
+  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, kMagicBits, qop);
+  const float dq = b.q_scale[hrowp + qrow];
+
+  AttnState<D, CAUSAL> as;
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) O[dt][r] = 0.0f;
-  float m = -__builtin_inff(), l = 0.0f;
+    for (int r = 0; r < 16; r++) as.O[dt][r] = 0.0f;
+  as.m = -__builtin_inff();
+  as.l = 0.0f;
 
-  const int tend = CAUSAL ? qb + 1 : d.NQB;
+  if (tid < kBK) sDS0[tid] = ds_next * ks;
+  if (tid < kBK / kKGroup) sKS0[tid] = ks_next;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   for (int t = 0; t < tend; t++) {
+    const bool odd = t & 1;
+    const bool more = t + 1 < tend;
+    uint8_t* nK = odd ? sK0 : sK1;
+    uint8_t* nV = odd ? sV0 : sV1;
+    if (more) {
+      stage_kv_async<D>(nK, nV, kblk, vblk, t + 1, wave, lane);
+      ds_next = tid < kBK ? dsrow[(t + 1) * kBK + tid] : 0.0f;
+      ks_next = tid < kBK / kKGroup ? kscl[(t + 1) * (kBK / kKGroup) + tid] : 0.0f;
+    }
+    attn_block<D, CAUSAL>(as, qop, odd ? sK1 : sK0, odd ? sV1 : sV0, odd ? sDS1 : sDS0, odd ? sKS1 : sKS0, dq, ks, t,
+                          qb, qrow, n, h, d);
+    if (more) {
+      if (tid < kBK) (odd ? sDS0 : sDS1)[tid] = ds_next * ks;
+      if (tid < kBK / kKGroup) (odd ? sKS0 : sKS1)[tid] = ks_next;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    {  // stage this key block: K codes, FP8 V, compensation row (times ks), K scales
-      const v4i* gk = (const v4i*)(kblk + (size_t)t * kBK * KROW);
-      v4i* lk = (v4i*)sK;
-#pragma unroll
-      for (int e = tid; e < kBK * KROW / 16; e += 256) lk[e] = gk[e];
-      const v4i* gv = (const v4i*)(vblk + (size_t)t * D * kBK);
-      v4i* lv = (v4i*)sV;
-#pragma unroll
-      for (int e = tid; e < D * kBK / 16; e += 256) lv[e] = gv[e];
-      if (tid < kBK) sDS[tid] = dsrow[t * kBK + tid] * ks;
-      if (tid < kBK / kKGroup) sKS[tid] = kscl[t * (kBK / kKGroup) + tid];
-    }
-    __syncthreads();
-
-    // ---- S^T for 4 tiles of 32 keys
-    v16i S[4];
-#pragma unroll
-    for (int T = 0; T < 4; T++) {
-      v4i a[NPAIR];
-#pragma unroll
-      for (int pr = 0; pr < NPAIR; pr++) a[pr] = *(const v4i*)(sK + (32 * T + n) * KROW + pr * 32 + h * 16);
-      S[T] = qk_tile<D>(a, qop);
-    }
-
-    // ---- dequantize into the log2 domain, mask, block max
-    float s2[4][16];
-    float bmax = -__builtin_inff();
-    const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
-#pragma unroll
-    for (int T = 0; T < 4; T++) {
-      const float c = ((dq * sKS[2 * T + h]) * ks) * 0.0625f;
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-        s2[T][r] = __builtin_fmaf((float)S[T][r], c, sDS[key]);
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int key = t * kBK + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool bad = (key >= d.N) || (CAUSAL && key > qrow);
-          if (bad) s2[T][r] = -__builtin_inff();
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; r++) bmax = fmaxf(bmax, s2[T][r]);
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float mnew = fmaxf(m, bmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    const float mm = mnew - kLog2_448;
-
-    // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
-    float rowsum = 0.0f;
-    v8i P8[2];
-#pragma unroll
-    for (int T = 0; T < 4; T++) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
-        rowsum += p[r];
-      }
-#pragma unroll
-      for (int w = 0; w < 4; w++) P8[T >> 1][4 * (T & 1) + w] = (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
-    }
-    rowsum += __shfl_xor(rowsum, 32);
-    l = alpha * l + rowsum;
-    m = mnew;
-
-    // ---- two-level P~V: fresh FP32 partial R per d-tile, then O = alpha*O + R
-#pragma unroll
-    for (int dt = 0; dt < NDT; dt++) {
-      v16f R;
-#pragma unroll
-      for (int r = 0; r < 16; r++) R[r] = 0.0f;
-#pragma unroll
-      for (int kh = 0; kh < 2; kh++) {
-        const v8i av = *(const v8i*)(sV + (32 * dt + n) * kBK + kh * 64 + h * 32);
-        R = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], R, 0, 0, 0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; r++) O[dt][r] = __builtin_fmaf(alpha, O[dt][r], R[r]);
-    }
   }
 
   // ---- epilogue: O = (O_run * vscale) / l'
@@ -245,7 +327,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int ch = 32 * dt + 8 * (r >> 2) + 4 * h + (r & 3);
-        store_out(o, orow + ch, (O[dt][r] * vs[ch]) / l, out_dtype);
+        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) / as.l, out_dtype);
       }
   }
 }
@@ -262,7 +344,7 @@ __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, in
   const int kbase = blockIdx.y * 32;
   const int qrow = min(q0 + qloc, d.NP - 1);
   QOperand<D> qop;
-  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, qop);
+  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, 0, qop);
   const int krow = min(k0 + kbase + n, d.NP - 1);
   v4i a[D / 64];
 #pragma unroll
