@@ -203,12 +203,22 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name, or 'all' (default: the N=16k D=128 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention heads of a batch are independent, so a multi-GPU "
               "deployment shards heads with no exchange; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     from fp8_attention_transformer_amd import workloads as wl
+    if args.copy_calibration_mb:
+        import torch
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "all":
         todo = wl.ALL
     else:

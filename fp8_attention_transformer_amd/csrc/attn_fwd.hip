@@ -28,10 +28,32 @@
 #include "sage_internal.h"
 #include "sage_device.h"
 
+// Pipeline depth of the K/V staging (LDS buffers in flight) and whether the
+// matrix-core issue phases run at raised wave priority.
+#ifndef SAGE_STAGES
+#define SAGE_STAGES 2
+#endif
+#ifndef SAGE_SETPRIO
+#define SAGE_SETPRIO 0
+#endif
+
 namespace sage {
 namespace {
 
 constexpr float kLog2_448 = 8.80735492205760410744f;
+
+// Values of lane l and lane l^32 (the two half-waves hold the same query):
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so with both operands equal to v the two results
+// hold, in every lane, v of the lane itself and of its partner.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
 struct QOperand {
@@ -171,6 +193,7 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   constexpr int NDT = D / 32;
   // ---- S^T for 4 tiles of 32 keys (values 1.5*2^23 + 16*acc as fp32 bits)
   v16i S[4];
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     const int row = 32 * T + n;
@@ -179,9 +202,11 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
     for (int pr = 0; pr < NPAIR; pr++) a[pr] = *(const v4i*)(cK + row * KROW + 16 * ((2 * pr + h) ^ kswz<D>(row)));
     S[T] = qk_tile<D>(a, qop);
   }
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   // ---- dequantize into the log2 domain, mask, block max
   float s2[4][16];
-  float bmax = -__builtin_inff();
+  float tmax[4];
+  float bmax;
   const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
@@ -200,15 +225,19 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
         if (bad) s2[T][r] = -__builtin_inff();
       }
     }
+    // four independent max chains per tile (a short tree, not one long chain)
+    float m4[4];
 #pragma unroll
-    for (int r = 0; r < 16; r++) bmax = fmaxf(bmax, s2[T][r]);
+    for (int q4 = 0; q4 < 4; q4++)
+      m4[q4] = fmaxf(fmaxf(s2[T][4 * q4], s2[T][4 * q4 + 1]), fmaxf(s2[T][4 * q4 + 2], s2[T][4 * q4 + 3]));
+    tmax[T] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
   }
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+  bmax = pair_max(fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3])));
   const float mnew = fmaxf(as.m, bmax);
   const float alpha = __builtin_amdgcn_exp2f(as.m - mnew);
   const float mm = mnew - kLog2_448;
   // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
-  float rowsum = 0.0f;
+  float part[4][4];   // independent partial row sums (tile, register quad)
   v8i P8[2];
 #pragma unroll
   for (int T = 0; T < 4; T++) {
@@ -216,15 +245,20 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
-      rowsum += p[r];
     }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) part[T][q4] = (p[4 * q4] + p[4 * q4 + 1]) + (p[4 * q4 + 2] + p[4 * q4 + 3]);
 #pragma unroll
     for (int w = 0; w < 4; w++) P8[T >> 1][4 * (T & 1) + w] = (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
   }
-  rowsum += __shfl_xor(rowsum, 32);
+  float tsum[4];
+#pragma unroll
+  for (int T = 0; T < 4; T++) tsum[T] = (part[T][0] + part[T][1]) + (part[T][2] + part[T][3]);
+  const float rowsum = pair_sum((tsum[0] + tsum[1]) + (tsum[2] + tsum[3]));
   as.l = alpha * as.l + rowsum;
   as.m = mnew;
   // ---- two-level P~V: fresh FP32 partial R per d-tile, then O = alpha*O + R
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) {
     const int row = 32 * dt + n;
@@ -242,20 +276,36 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
 #pragma unroll
     for (int r = 0; r < 16; r++) as.O[dt][r] = __builtin_fmaf(alpha, as.O[dt][r], R[r]);
   }
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+}
+
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
   constexpr int KROW = D / 2;
   constexpr int NDT = D / 32;
-  // Two LDS buffers as separate arrays, so the compiler can tell the block
-  // being read from the block being filled by the asynchronous copy.
-  __shared__ __align__(16) uint8_t sK0[kBK * KROW];
-  __shared__ __align__(16) uint8_t sK1[kBK * KROW];
-  __shared__ __align__(16) uint8_t sV0[D * kBK];
-  __shared__ __align__(16) uint8_t sV1[D * kBK];
-  __shared__ float sDS0[kBK], sDS1[kBK];
-  __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup];
+  constexpr int S = SAGE_STAGES;
+  // vector-memory ops one block's staging issues per wave: K and V chunks via
+  // direct-to-LDS copies, plus the compensation and K-scale loads
+  constexpr int VM_PER_BLOCK = kBK * KROW / 16 / 256 + D * kBK / 16 / 256 + 2;
+  // LDS buffers as separate arrays, so the compiler can tell the block being
+  // read from the blocks being filled by the asynchronous copies.
+  __shared__ __align__(16) uint8_t sK0[kBK * KROW], sK1[kBK * KROW], sK2[S > 2 ? kBK * KROW : 16];
+  __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK], sV2[S > 2 ? D * kBK : 16];
+  __shared__ float sDS0[kBK], sDS1[kBK], sDS2[S > 2 ? kBK : 1];
+  __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup], sKS2[S > 2 ? kBK / kKGroup : 1];
+  auto bK = [&](int i) { return i == 0 ? sK0 : (i == 1 ? sK1 : sK2); };
+  auto bV = [&](int i) { return i == 0 ? sV0 : (i == 1 ? sV1 : sV2); };
+  auto bDS = [&](int i) { return i == 0 ? sDS0 : (i == 1 ? sDS1 : sDS2); };
+  auto bKS = [&](int i) { return i == 0 ? sKS0 : (i == 1 ? sKS1 : sKS2); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,10 +325,22 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const float* kscl = b.k_scale + hrowp / kKGroup;
   const int tend = CAUSAL ? qb + 1 : d.NQB;
 
-  // block 0 -> buffer 0
-  stage_kv_async<D>(sK0, sV0, kblk, vblk, 0, wave, lane);
-  float ds_next = tid < kBK ? dsrow[tid] : 0.0f;
-  float ks_next = tid < kBK / kKGroup ? kscl[tid] : 0.0f;
+  // Every wave issues the same number of memory ops per block (the small
+  // loads are unconditional, with in-range indices), so a vmcnt limit of
+  // VM_PER_BLOCK * k waits exactly for all but the newest k blocks.
+  float ds_reg[S - 1], ks_reg[S - 1];
+  auto issue = [&](int t, int slot) {
+    stage_kv_async<D>(bK(slot), bV(slot), kblk, vblk, t, wave, lane);
+    ds_reg[t % (S - 1)] = dsrow[t * kBK + (tid & (kBK - 1))];
+    ks_reg[t % (S - 1)] = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
+  };
+  auto publish = [&](int t, int slot) {   // compensation row and K scales of block t -> LDS
+    if (tid < kBK) bDS(slot)[tid] = ds_reg[t % (S - 1)] * ks;
+    if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg[t % (S - 1)];
+  };
+
+  issue(0, 0);
+  if (S > 2 && tend > 1) issue(1, 1);
 
   QOperand<D> qop;
   load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, kMagicBits, qop);
@@ -292,28 +354,22 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   as.m = -__builtin_inff();
   as.l = 0.0f;
 
-  if (tid < kBK) sDS0[tid] = ds_next * ks;
-  if (tid < kBK / kKGroup) sKS0[tid] = ks_next;
-  __builtin_amdgcn_s_waitcnt(0);
+  if (S > 2 && tend > 1) wait_vmcnt<VM_PER_BLOCK>();
+  else wait_vmcnt<0>();
+  publish(0, 0);
   __syncthreads();
 
   for (int t = 0; t < tend; t++) {
-    const bool odd = t & 1;
-    const bool more = t + 1 < tend;
-    uint8_t* nK = odd ? sK0 : sK1;
-    uint8_t* nV = odd ? sV0 : sV1;
-    if (more) {
-      stage_kv_async<D>(nK, nV, kblk, vblk, t + 1, wave, lane);
-      ds_next = tid < kBK ? dsrow[(t + 1) * kBK + tid] : 0.0f;
-      ks_next = tid < kBK / kKGroup ? kscl[(t + 1) * (kBK / kKGroup) + tid] : 0.0f;
+    const int slot = t % S;
+    const bool ahead = t + S - 1 < tend;          // block t+S-1 exists: stage it now
+    if (ahead) issue(t + S - 1, (t + S - 1) % S);
+    attn_block<D, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, d);
+    if (t + 1 < tend) {
+      // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
+      if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
+      else wait_vmcnt<0>();
+      publish(t + 1, (t + 1) % S);
     }
-    attn_block<D, CAUSAL>(as, qop, odd ? sK1 : sK0, odd ? sV1 : sV0, odd ? sDS1 : sDS0, odd ? sKS1 : sKS0, dq, ks, t,
-                          qb, qrow, n, h, d);
-    if (more) {
-      if (tid < kBK) (odd ? sDS0 : sDS1)[tid] = ds_next * ks;
-      if (tid < kBK / kKGroup) (odd ? sKS0 : sKS1)[tid] = ks_next;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

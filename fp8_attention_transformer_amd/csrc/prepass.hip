@@ -17,52 +17,81 @@ namespace sage {
 namespace {
 
 // ---------------------------------------------------------------------------
-// stats: grid (NQB, B*H), D threads.  Thread c walks the 128 tokens of its
-// chunk in order: Q block sum -> Q block mean, K chunk sum, V chunk absmax.
+// stats: 256 threads, one channel pair per thread, 256/(D/2) chunks of 128
+// tokens per workgroup.  Each thread walks its chunk in token order (the sums
+// are sequential per channel); loads are issued 32 tokens ahead.
 template <int IN, int D>
-__global__ void __launch_bounds__(D) stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                  const uint16_t* __restrict__ v, Dims d, Bufs b) {
-  const int qb = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+__global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, Dims d, Bufs b) {
+  constexpr int LPC = D / 2;          // lanes per chunk
+  constexpr int CPW = 256 / LPC;      // chunks per workgroup
+  constexpr int U = 32;               // tokens in flight
+  const int tid = threadIdx.x, cp = tid % LPC;
+  const int chunk = blockIdx.x * CPW + tid / LPC;
+  if (chunk >= d.BH() * d.NQB) return;
+  const int bh = chunk / d.NQB, qb = chunk % d.NQB;
   const int i0 = qb * kBQ, i1 = min(d.N, i0 + kBQ);
-  const size_t base = ((size_t)bh * d.N) * D + c;
-  float qs = 0.0f, ks = 0.0f, vm = 0.0f;
-  int i = i0;
-  for (; i + 8 <= i1; i += 8) {
-    uint16_t qv[8], kv[8], vv[8];
+  const size_t base = ((size_t)bh * d.N) * D + 2 * cp;
+  float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vm0 = 0.0f, vm1 = 0.0f;
+  auto add = [&](uint32_t qv, uint32_t kv, uint32_t vv) {
+    qs0 = qs0 + in_to_f32<IN>((uint16_t)(qv & 0xFFFF));
+    qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
+    ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
+    ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
+    vm0 = fmaxf(vm0, fabsf(in_to_f32<IN>((uint16_t)(vv & 0xFFFF))));
+    vm1 = fmaxf(vm1, fabsf(in_to_f32<IN>((uint16_t)(vv >> 16))));
+  };
+  if (i1 - i0 == kBQ) {
+    // full chunk: branch-free, U tokens of loads in flight
+    for (int i = i0; i < i1; i += U) {
+      uint32_t qv[U], kv[U], vv[U];
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      qv[u] = q[base + (size_t)(i + u) * D];
-      kv[u] = k[base + (size_t)(i + u) * D];
-      vv[u] = v[base + (size_t)(i + u) * D];
+      for (int u = 0; u < U; u++) {
+        const size_t o = base + (size_t)(i + u) * D;
+        qv[u] = *(const uint32_t*)(q + o);
+        kv[u] = *(const uint32_t*)(k + o);
+        vv[u] = *(const uint32_t*)(v + o);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) add(qv[u], kv[u], vv[u]);
     }
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      qs = qs + in_to_f32<IN>(qv[u]);
-      ks = ks + in_to_f32<IN>(kv[u]);
-      vm = fmaxf(vm, fabsf(in_to_f32<IN>(vv[u])));
+  } else {
+    for (int i = i0; i < i1; i++) {
+      const size_t o = base + (size_t)i * D;
+      add(*(const uint32_t*)(q + o), *(const uint32_t*)(k + o), *(const uint32_t*)(v + o));
     }
   }
-  for (; i < i1; i++) {
-    qs = qs + in_to_f32<IN>(q[base + (size_t)i * D]);
-    ks = ks + in_to_f32<IN>(k[base + (size_t)i * D]);
-    vm = fmaxf(vm, fabsf(in_to_f32<IN>(v[base + (size_t)i * D])));
-  }
-  const size_t o = ((size_t)bh * d.NQB + qb) * D + c;
-  b.q_mean[o] = qs / (float)(i1 - i0);
-  b.k_part[o] = ks;
-  b.v_part[o] = vm;
+  const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
+  const float cnt = (float)(i1 - i0);
+  b.q_mean[o] = qs0 / cnt;
+  b.q_mean[o + 1] = qs1 / cnt;
+  b.k_part[o] = ks0;
+  b.k_part[o + 1] = ks1;
+  b.v_part[o] = vm0;
+  b.v_part[o + 1] = vm1;
 }
 
 // ---------------------------------------------------------------------------
 // finalize: grid (B*H), D threads.  K mean = (sum of chunk sums, in chunk
 // order) / N; V scale = (max of chunk absmax) / 448.
 __global__ void finalize_kernel(Dims d, Bufs b) {
+  constexpr int U = 16;
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
+  const size_t base = (size_t)bh * d.NQB * D + c;
   float tot = 0.0f, vm = 0.0f;
-  for (int t = 0; t < d.NQB; t++) {
-    const size_t o = ((size_t)bh * d.NQB + t) * D + c;
-    tot = tot + b.k_part[o];
-    vm = fmaxf(vm, b.v_part[o]);
+  for (int t = 0; t < d.NQB; t += U) {
+    float kp[U], vp[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const bool ok = t + u < d.NQB;
+      kp[u] = ok ? b.k_part[base + (size_t)(t + u) * D] : 0.0f;
+      vp[u] = ok ? b.v_part[base + (size_t)(t + u) * D] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (t + u < d.NQB) tot = tot + kp[u];
+      vm = fmaxf(vm, vp[u]);
+    }
   }
   b.k_mean[(size_t)bh * D + c] = tot / (float)d.N;
   b.v_scale[(size_t)bh * D + c] = vm / 448.0f;
@@ -77,139 +106,325 @@ __device__ __forceinline__ int vperm_key(int p) {
   return 64 * (p >> 6) + 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * ((p & 63) >> 5) + (s & 3);
 }
 
+// 16 consecutive 16-bit inputs (32 bytes) -> fp32
+template <int IN>
+__device__ __forceinline__ void load16(const uint16_t* p, float* x) {
+  const v4i a = *(const v4i*)p;
+  const v4i c = *(const v4i*)(p + 8);
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    x[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)a[w] & 0xFFFF));
+    x[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)a[w] >> 16));
+    x[8 + 2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)c[w] & 0xFFFF));
+    x[8 + 2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)c[w] >> 16));
+  }
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ void split3(float x, uint32_t& a, uint32_t& bb, uint32_t& c) {
+  a = bf16_rne_bits(x);
+  const float r1 = x - __uint_as_float(a << 16);
+  bb = bf16_rne_bits(r1);
+  const float r2 = r1 - __uint_as_float(bb << 16);
+  c = bf16_rne_bits(r2);
+}
+// 8 fp32 values -> three v8bf operands
+__device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf& p3) {
+  v4i w1, w2, w3;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    uint32_t a0, b0, c0, a1, b1, c1;
+    split3(x[2 * e], a0, b0, c0);
+    split3(x[2 * e + 1], a1, b1, c1);
+    w1[e] = (int)(a0 | (a1 << 16));
+    w2[e] = (int)(b0 | (b1 << 16));
+    w3[e] = (int)(c0 | (c1 << 16));
+  }
+  p1 = __builtin_bit_cast(v8bf, w1);
+  p2 = __builtin_bit_cast(v8bf, w2);
+  p3 = __builtin_bit_cast(v8bf, w3);
+}
+
+// INT4 codes rint(x/delta) of NV values sharing one scale, bit-identical to a
+// true IEEE division per element: multiply by the correctly rounded
+// reciprocal (relative error below 2^-22), and if any lane of the wave lands
+// within 2^-19 of a rounding midpoint (half-integer), redo the whole wave
+// with true divisions.  |x| <= 7*delta makes the [-7, 7] clamp unnecessary.
+template <int NV>
+__device__ __forceinline__ void int4_codes(const float* x, float delta, int* code) {
+  const float r = delta == 0.0f ? 0.0f : 1.0f / delta;
+  bool amb = false;
+  float c[NV];
+#pragma unroll
+  for (int e = 0; e < NV; e++) {
+    const float q = x[e] * r;
+    c[e] = rintf(q);
+    amb |= fabsf(fabsf(q - c[e]) - 0.5f) < 0x1p-19f;
+  }
+  if (__any(amb)) {
+#pragma unroll
+    for (int e = 0; e < NV; e++) c[e] = delta == 0.0f ? 0.0f : rintf(x[e] / delta);
+  }
+#pragma unroll
+  for (int e = 0; e < NV; e++) code[e] = (int)c[e];
+}
+
+// x / dv for FP8 V codes: reciprocal multiply unless, in some lane of the wave,
+// the quotient lies within 2^-21 (relative) of an e4m3 rounding midpoint or
+// below the e4m3 normal range -- then true division for the whole wave.
+template <int NV>
+__device__ __forceinline__ void fp8_quotients(float* x, float dv) {
+  const float r = dv == 0.0f ? 0.0f : 1.0f / dv;
+  bool amb = false;
+  float y[NV];
+#pragma unroll
+  for (int e = 0; e < NV; e++) {
+    y[e] = x[e] * r;
+    const float a = fabsf(y[e]);
+    const int low = (int)(__float_as_uint(a) & 0xFFFFFu) - 0x80000;
+    amb |= (a != 0.0f) && (a < 0.015625f || (low <= 8 && low >= -8));
+  }
+  if (__any(amb)) {
+#pragma unroll
+    for (int e = 0; e < NV; e++) y[e] = dv == 0.0f ? 0.0f : x[e] / dv;
+  }
+#pragma unroll
+  for (int e = 0; e < NV; e++) x[e] = y[e];
+}
+
 // ---------------------------------------------------------------------------
 // quant: grid (NQB, B*H), 256 threads.  One 128-token block of one head:
-//  Q: one scale per token; K: one scale per 16-key fragment group; V: FP8.
+//  Q: one scale per token (D/16 lanes per token, 16 channels each);
+//  K: one scale per 16-key fragment group (one group = 16 keys x D/32 lanes);
+//  V: FP8 with the per-channel scale, written in the permuted channel-major
+//     layout through an LDS copy of the block.
 template <int IN, int D>
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
-  constexpr int LPR = D / 2;          // lanes per row: one lane per channel pair
-  constexpr int ROWS = 256 / LPR;     // rows handled in parallel
-  __shared__ float sV[kBK][D + 1];
+  __shared__ __align__(16) uint16_t sV[kBK * D];
   const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int lb = tid % LPR, slot = tid / LPR;
+  const int lane = tid & 63, wave = tid >> 6;
   const int i0 = qb * kBQ;
   const size_t hrow = (size_t)bh * d.N;      // first input row of this head
   const size_t hrowp = (size_t)bh * d.NP;    // first padded row of this head
 
-  // ---- Q: per token
-  {
-    const float m0 = b.q_mean[((size_t)bh * d.NQB + qb) * D + 2 * lb];
-    const float m1 = b.q_mean[((size_t)bh * d.NQB + qb) * D + 2 * lb + 1];
-    for (int r = slot; r < kBQ; r += ROWS) {
-      const int i = i0 + r;
-      float g0 = 0.0f, g1 = 0.0f;
-      if (i < d.N) {
-        const uint32_t pr = *(const uint32_t*)(q + (hrow + i) * D + 2 * lb);
-        g0 = in_to_f32<IN>((uint16_t)(pr & 0xFFFF)) - m0;
-        g1 = in_to_f32<IN>((uint16_t)(pr >> 16)) - m1;
-      }
-      const float amax = group_max<LPR>(fmaxf(fabsf(g0), fabsf(g1)));
-      const float dq = amax / 7.0f;
-      b.q_codes[(hrowp + i) * (D / 2) + lb] = (uint8_t)pack_pair(int4_code(g0, dq), int4_code(g1, dq));
-      if (lb == 0) b.q_scale[hrowp + i] = dq;
-    }
+  // ---- V block -> LDS (rows >= N are zero)
+  for (int e = tid; e < kBK * D / 8; e += 256) {
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    v4i val = {0, 0, 0, 0};
+    if (i0 + r < d.N) val = *(const v4i*)(v + (hrow + i0 + r) * D + 8 * c8);
+    *(v4i*)(sV + r * D + 8 * c8) = val;
   }
-  // ---- K: per 16-key group.  Group (T, hh) of the block holds keys
-  //      32*T + 8*u + 4*hh + w, u, w in 0..3.
+
+  // ---- Q: LPT lanes per token, 16 channels per lane
   {
-    const float m0 = b.k_mean[(size_t)bh * D + 2 * lb];
-    const float m1 = b.k_mean[(size_t)bh * D + 2 * lb + 1];
-    for (int grp = slot; grp < kBK / kKGroup; grp += ROWS) {
-      const int T = grp >> 1, hh = grp & 1;
-      float g[16][2];
+    constexpr int LPT = D / 16, TPP = 256 / LPT;
+    const int sub = tid % LPT, c0 = 16 * sub;
+    float qm[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) qm[e] = b.q_mean[((size_t)bh * d.NQB + qb) * D + c0 + e];
+    // three bf16 pieces of this block's channel means for the compensation
+    // kernel: pieces 1 and 2 in k_part, piece 3 in v_part (both are free once
+    // the K means and V scales are final)
+    if (tid < LPT) {
+      uint16_t* p12 = (uint16_t*)b.k_part + ((size_t)bh * d.NQB + qb) * 2 * D;
+      uint16_t* p3s = (uint16_t*)b.v_part + ((size_t)bh * d.NQB + qb) * D;
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        uint32_t p1, p2, p3;
+        split3(qm[e], p1, p2, p3);
+        p12[c0 + e] = (uint16_t)p1;
+        p12[D + c0 + e] = (uint16_t)p2;
+        p3s[c0 + e] = (uint16_t)p3;
+      }
+    }
+    for (int r = tid / LPT; r < kBQ; r += TPP) {
+      const int i = i0 + r;
+      float g[16];
+      if (i < d.N) {
+        load16<IN>(q + (hrow + i) * D + c0, g);
+#pragma unroll
+        for (int e = 0; e < 16; e++) g[e] = g[e] - qm[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) g[e] = 0.0f;
+      }
       float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const int j = i0 + 32 * T + 8 * (e >> 2) + 4 * hh + (e & 3);
-        g[e][0] = 0.0f;
-        g[e][1] = 0.0f;
-        if (j < d.N) {
-          const uint32_t pr = *(const uint32_t*)(k + (hrow + j) * D + 2 * lb);
-          g[e][0] = in_to_f32<IN>((uint16_t)(pr & 0xFFFF)) - m0;
-          g[e][1] = in_to_f32<IN>((uint16_t)(pr >> 16)) - m1;
-        }
-        amax = fmaxf(amax, fmaxf(fabsf(g[e][0]), fabsf(g[e][1])));
-      }
-      amax = group_max<LPR>(amax);
-      const float dk = amax / 7.0f;
+      for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(g[e]));
+      amax = group_max<LPT>(amax);
+      const float dq = amax / 7.0f;
+      int cq[16];
+      int4_codes<16>(g, dq, cq);
+      uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-      for (int e = 0; e < 16; e++) {
-        const int j = i0 + 32 * T + 8 * (e >> 2) + 4 * hh + (e & 3);
-        b.k_codes[(hrowp + j) * (D / 2) + lb] = (uint8_t)pack_pair(int4_code(g[e][0], dk), int4_code(g[e][1], dk));
+      for (int e = 0; e < 4; e++) {
+        w0 |= pack_pair(cq[2 * e], cq[2 * e + 1]) << (8 * e);
+        w1 |= pack_pair(cq[8 + 2 * e], cq[8 + 2 * e + 1]) << (8 * e);
       }
-      if (lb == 0) b.k_scale[hrowp / kKGroup + (i0 / kKGroup) + grp] = dk;
+      uint2 pk;
+      pk.x = w0;
+      pk.y = w1;
+      *(uint2*)(b.q_codes + (hrowp + i) * (D / 2) + 8 * sub) = pk;
+      if (sub == 0) b.q_scale[hrowp + i] = dq;
     }
   }
-  // ---- V: stage the block in LDS as fp32, then write FP8 in the permuted,
-  //      channel-major layout [D][128].
-  for (int e = tid; e < kBK * D / 2; e += 256) {
-    const int r = e / (D / 2), cp = e % (D / 2);
-    const int j = i0 + r;
-    float a = 0.0f, c2 = 0.0f;
-    if (j < d.N) {
-      const uint32_t pr = *(const uint32_t*)(v + (hrow + j) * D + 2 * cp);
-      a = in_to_f32<IN>((uint16_t)(pr & 0xFFFF));
-      c2 = in_to_f32<IN>((uint16_t)(pr >> 16));
+  // ---- K: a group (T, hh) holds keys 32T + 8u + 4hh + w (u, w in 0..3);
+  //      LPK lanes per key, 32 channels per lane.
+  {
+    constexpr int LPK = D / 32, LPG = 16 * LPK;          // lanes per key / per group
+    constexpr int GPW = 64 / LPG;                          // groups per wave
+    const int sub = lane % LPK, c0 = 32 * sub;
+    const int ki = (lane % LPG) / LPK;
+    float km[32];
+#pragma unroll
+    for (int e = 0; e < 32; e++) km[e] = b.k_mean[(size_t)bh * D + c0 + e];
+    for (int grp = wave * GPW + lane / LPG; grp < kBK / kKGroup; grp += 4 * GPW) {
+      const int T = grp >> 1, hh = grp & 1;
+      const int j = i0 + 32 * T + 8 * (ki >> 2) + 4 * hh + (ki & 3);
+      float g[32];
+      if (j < d.N) {
+        load16<IN>(k + (hrow + j) * D + c0, g);
+        load16<IN>(k + (hrow + j) * D + c0 + 16, g + 16);
+#pragma unroll
+        for (int e = 0; e < 32; e++) g[e] = g[e] - km[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; e++) g[e] = 0.0f;
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; e++) amax = fmaxf(amax, fabsf(g[e]));
+      amax = group_max<LPG>(amax);
+      const float dk = amax / 7.0f;
+      int ck[32];
+      int4_codes<32>(g, dk, ck);
+      v4i pk;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) word |= pack_pair(ck[8 * w + 2 * e], ck[8 * w + 2 * e + 1]) << (8 * e);
+        pk[w] = (int)word;
+      }
+      *(v4i*)(b.k_codes + (hrowp + j) * (D / 2) + 16 * sub) = pk;
+      if ((lane % LPG) == 0) b.k_scale[hrowp / kKGroup + (i0 / kKGroup) + grp] = dk;
     }
-    sV[r][2 * cp] = a;
-    sV[r][2 * cp + 1] = c2;
   }
   __syncthreads();
-  uint32_t* vout = (uint32_t*)(b.v_codes + ((size_t)bh * d.NQB + qb) * D * kBK);
-  for (int w = tid; w < D * kBK / 4; w += 256) {
-    const int ch = w % D, p4 = w / D;
-    const float dv = b.v_scale[(size_t)bh * D + ch];
-    float x[4];
+  // ---- V: 16-key chunks of one channel -> 16 FP8 bytes
+  {
+    uint8_t* vout = b.v_codes + ((size_t)bh * d.NQB + qb) * D * kBK;
+    for (int e = tid; e < D * 8; e += 256) {
+      const int ch = e % D, c = e / D;
+      const float dv = b.v_scale[(size_t)bh * D + ch];
+      float x[16];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int key = vperm_key(4 * p4 + u);
-      x[u] = (dv == 0.0f || i0 + key >= d.N) ? 0.0f : sV[key][ch] / dv;
+      for (int u = 0; u < 16; u++) x[u] = in_to_f32<IN>(sV[vperm_key(16 * c + u) * D + ch]);
+      fp8_quotients<16>(x, dv);
+      v4i pk;
+#pragma unroll
+      for (int w = 0; w < 4; w++) pk[w] = (int)fp8x4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
+      *(v4i*)(vout + ch * kBK + 16 * c) = pk;
     }
-    vout[(ch * kBK) / 4 + p4] = fp8x4(x[0], x[1], x[2], x[3]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// delta_s: grid (NQB key blocks, B*H), 256 threads.  For the 128 keys of the
-// block and every Q block qb: sum_c qmean[qb][c] * (K[j][c] - kmean[c]), an
-// fp32 fma chain in channel order, times ds_scale.
+// delta_s: grid (NQB key blocks, B*H), 256 threads; wave w owns keys
+// j0 + 32w .. +31 and all Q blocks.  DeltaS = qmean . gamma(K) on the bf16
+// matrix core: every fp32 operand is split into three bf16 pieces
+// (x = x1 + x2 + x3 up to 2^-24 |x|) and the six products x_a*y_b with
+// a + b <= 4 are accumulated in fp32, which reproduces an fp32 dot product to
+// within a few units in the last place.
 template <int IN, int D>
-__global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b, float ds_scale) {
-  constexpr int QC = 16;  // Q blocks per pass
-  __shared__ float sG[D][kBK];
-  __shared__ float sQ[QC][D];
+__global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
+  constexpr int NK = D / 16;   // k-steps of the 32x32x16 bf16 MFMA
   const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int j0 = kb * kBK;
-  const size_t hrow = (size_t)bh * d.N;
-  for (int e = tid; e < kBK * D; e += 256) {
-    const int r = e / D, c = e % D;
-    const int j = j0 + r;
-    float g = 0.0f;
-    if (j < d.N) g = in_to_f32<IN>(k[(hrow + j) * D + c]) - b.k_mean[(size_t)bh * D + c];
-    sG[c][r] = g;
+  const int lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
+  const int j = kb * kBK + 32 * wave + n;        // this lane's key (B operand column)
+  const float* km = b.k_mean + (size_t)bh * D;
+  // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
+  v8bf B1[NK], B2[NK], B3[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; kk++) {
+    const int c0 = 16 * kk + 8 * h;
+    const float4 m0 = *(const float4*)(km + c0);
+    const float4 m1 = *(const float4*)(km + c0 + 4);
+    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float g[8];
+    if (j < d.N) {
+      const v4i raw = *(const v4i*)(k + ((size_t)bh * d.N + j) * D + c0);
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF)) - mv[2 * w];
+        g[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] >> 16)) - mv[2 * w + 1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[e] = 0.0f;
+    }
+    split8(g, B1[kk], B2[kk], B3[kk]);
   }
-  const int jl = tid % kBK, half = tid / kBK;   // 2 groups of 128 threads
-  for (int qc0 = 0; qc0 < d.NQB; qc0 += QC) {
+  // A operands: the three bf16 pieces of the Q-block means (pieces 1, 2:
+  // [NQB][2][D] in k_part; piece 3: [NQB][D] in v_part), staged per 32-block
+  // Q tile into LDS by direct copies, double-buffered.  LDS tile layout
+  // [piece][row][D] with 16-byte chunks XOR-swizzled by row.
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr int TILE = 3 * 32 * D;                 // bf16 elements per staged tile
+  constexpr int NCH = TILE / 8 / 256;              // chunks per thread
+  __shared__ __align__(16) uint16_t sA0[TILE], sA1[TILE];
+  const uint16_t* p12 = (const uint16_t*)b.k_part + (size_t)bh * d.NQB * 2 * D;
+  const uint16_t* p3s = (const uint16_t*)b.v_part + (size_t)bh * d.NQB * D;
+  auto stage = [&](int qt, uint16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < NCH; i++) {
+      const int wbase = 256 * i + 64 * wave;
+      const int e = wbase + lane;
+      const int piece = e / (32 * CPR), rem = e % (32 * CPR), r = rem / CPR, c = (rem % CPR) ^ (r & (CPR - 1));
+      const int qrow = min(qt + r, d.NQB - 1);
+      const uint16_t* src = piece < 2 ? p12 + ((size_t)qrow * 2 + piece) * D + 8 * c : p3s + (size_t)qrow * D + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + 8 * wbase), 16,
+                                       0, 0);
+    }
+  };
+  float* out = b.delta_s + (size_t)bh * d.NQB * d.NP + j;
+  stage(0, sA0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qt = 0, it = 0; qt < d.NQB; qt += 32, it++) {
+    const bool more = qt + 32 < d.NQB;
+    if (more) stage(qt + 32, (it & 1) ? sA0 : sA1);
+    const uint16_t* A = (it & 1) ? sA1 : sA0;
+    v16f acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NK; kk++) {
+      const int c = (2 * kk + h) ^ (n & (CPR - 1));
+      const v8bf A1 = __builtin_bit_cast(v8bf, *(const v4i*)(A + (0 * 32 + n) * D + 8 * c));
+      const v8bf A2 = __builtin_bit_cast(v8bf, *(const v4i*)(A + (1 * 32 + n) * D + 8 * c));
+      const v8bf A3 = __builtin_bit_cast(v8bf, *(const v4i*)(A + (2 * 32 + n) * D + 8 * c));
+      // smallest products first
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A3, B1[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B3[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B1[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B2[kk], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1[kk], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int q2 = qt + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (q2 < d.NQB) out[(size_t)q2 * d.NP] = acc[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int e = tid; e < QC * D; e += 256) {
-      const int qq = e / D, c = e % D;
-      sQ[qq][c] = (qc0 + qq < d.NQB) ? b.q_mean[((size_t)bh * d.NQB + qc0 + qq) * D + c] : 0.0f;
-    }
-    __syncthreads();
-    float acc[QC / 2];
-#pragma unroll
-    for (int u = 0; u < QC / 2; u++) acc[u] = 0.0f;
-    for (int c = 0; c < D; c++) {
-      const float g = sG[c][jl];
-#pragma unroll
-      for (int u = 0; u < QC / 2; u++) acc[u] = __builtin_fmaf(sQ[half + 2 * u][c], g, acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < QC / 2; u++) {
-      const int qb = qc0 + half + 2 * u;
-      if (qb < d.NQB) b.delta_s[((size_t)bh * d.NQB + qb) * d.NP + j0 + jl] = acc[u] * ds_scale;
-    }
   }
 }
 
@@ -225,14 +440,17 @@ __global__ void fp8_encode_kernel(const float* __restrict__ in, uint8_t* __restr
 template <int IN, int D>
 hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims& d, const Bufs& b, float ds_scale,
                         hipStream_t s) {
+  (void)ds_scale;
   const dim3 grid(d.NQB, d.BH());
   const uint16_t* q16 = (const uint16_t*)q;
   const uint16_t* k16 = (const uint16_t*)k;
   const uint16_t* v16 = (const uint16_t*)v;
-  hipLaunchKernelGGL((stats_kernel<IN, D>), grid, dim3(D), 0, s, q16, k16, v16, d, b);
+  constexpr int CPW = 256 / (D / 2);
+  const unsigned nstat = (unsigned)((d.BH() * d.NQB + CPW - 1) / CPW);
+  hipLaunchKernelGGL((stats_kernel<IN, D>), dim3(nstat), dim3(256), 0, s, q16, k16, v16, d, b);
   hipLaunchKernelGGL(finalize_kernel, dim3(d.BH()), dim3(D), 0, s, d, b);
   hipLaunchKernelGGL((quant_kernel<IN, D>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
-  hipLaunchKernelGGL((delta_s_kernel<IN, D>), grid, dim3(256), 0, s, k16, d, b, ds_scale);
+  hipLaunchKernelGGL((delta_s_kernel<IN, D>), grid, dim3(256), 0, s, k16, d, b);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ struct Dims {
   int B, H, N, D;
   int NP;    // N rounded up to a multiple of 128
   int NQB;   // NP / 128
-  int BH() const { return B * H; }
+  __host__ __device__ int BH() const { return B * H; }
 };
 
 // Device buffers written by the prepass and read by the attention kernel.
@@ -36,8 +36,8 @@ struct Bufs {
   uint8_t* v_codes;   // [B,H,NQB,D,128] e4m3fn, keys permuted inside each 128-key block
   float* v_scale;     // [B,H,D]
   float* delta_s;     // [B,H,NQB,NP]   compensation term times ds_scale
-  float* k_part;      // [B,H,NQB,D]    per-chunk K channel sums
-  float* v_part;      // [B,H,NQB,D]    per-chunk V channel absmax
+  float* k_part;      // [B,H,NQB,D]    per-chunk K channel sums; then bf16 q_mean pieces 1-2
+  float* v_part;      // [B,H,NQB,D]    per-chunk V channel absmax; then bf16 q_mean piece 3
 };
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d,

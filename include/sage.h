@@ -72,7 +72,8 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
  *  delta_s           fp32  [B,H,NQB,NP]  compensation term
  *                    DeltaS[qb][j] = q_mean[qb] . (K[j] - k_mean), fp32
  *                    accumulation (not scaled by sm_scale)
- *  k_part, v_part    fp32  [B,H,NQB,D]   scratch: per-chunk K sums, V absmax
+ *  k_part, v_part    fp32  [B,H,NQB,D]   scratch: per-chunk K sums and V
+ *                    absmax, later reused for bf16 pieces of q_mean
  */
 typedef struct {
   uint8_t* q_codes;

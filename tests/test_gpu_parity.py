@@ -56,13 +56,17 @@ def _check_prepass(rb, z):
 
 
 def _ds_bound(oracle_lib, z, k_bits, dtype_code):
-    """(D+2) * 2^-24 * sum_c |qmean_c * gamma(K)_jc|: the error bound of an fp32
-    fma chain over D channels, per compensation-term entry."""
+    """Error bound of the GPU compensation term, per entry:
+    (6*D + 8) * 2^-24 * sum_c |qmean_c * gamma(K)_jc|.
+    The GPU splits each fp32 operand into three bf16 pieces (residual at most
+    2^-24 relative) and accumulates the six products x_a*y_b with a+b <= 4 in
+    fp32: the dropped products and residuals cost at most ~5 * 2^-24 per term,
+    and fp32 accumulation of 6*D products in any order at most 6*D * 2^-24."""
     B, H, N, D = z.q_codes.shape
     K = oracle_lib.decode_input(k_bits, dtype_code).reshape(B * H, N, D)
     gK = np.abs((K - z.k_mean.reshape(B * H, 1, D)).astype(np.float32)).astype(np.float64)
     qm = np.abs(z.q_mean.reshape(B * H, -1, D)).astype(np.float64)
-    return (D + 2) * 2.0 ** -24 * np.einsum("bqc,bjc->bqj", qm, gK)
+    return (6 * D + 8) * 2.0 ** -24 * np.einsum("bqc,bjc->bqj", qm, gK)
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
