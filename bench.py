@@ -212,13 +212,19 @@ def main():
         sys.exit(2)
     from fp8_attention_transformer_amd import workloads as wl
     if args.copy_calibration_mb:
+        # One plain device-to-device copy of a known size, with its source
+        # evicted from L2 and the 256 MB Infinity Cache first: the reference
+        # that scales the FETCH_SIZE / WRITE_SIZE counters to HBM bytes.
         import torch
         n = args.copy_calibration_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        evict.fill_(1)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, evict
     if args.workload == "all":
         todo = wl.ALL
     else:
