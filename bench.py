@@ -2,7 +2,7 @@
 """Benchmark of the SageAttention2 forward (libsage, MI355X / gfx950).
 
 One step = the whole hot path on one batch of synthetic input already resident
-in HBM: the prepass (sage_quant_smooth: smoothing, INT4 Q/K, FP8 V,
+in HBM: the prepass (sage_quant_smooth: smoothing, INT4 (or INT8) Q/K, FP8 V,
 compensation term) followed by the fused attention kernel
 (sage_attn_quantized) -- together exactly what sage_attn_fwd runs.  HIP events
 on the launch stream bracket each kernel group inside the timed region, which
@@ -60,7 +60,7 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline_leg(w, out_gpu, target_s: float):
+def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the prepass of head 0 and the mirror-mode attention of a set of
     its rows, with the host's threads (at most 16).  Also reports, from the
@@ -75,7 +75,7 @@ def cpu_baseline_leg(w, out_gpu, target_s: float):
     dt = 0 if w.dtype == wl.F16 else 1
     q, k, v = wl.generate(w, heads=slice(0, 1))
     t0 = time.perf_counter()
-    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth)
+    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth, qk_bits=qk_bits)
     t_pre = time.perf_counter() - t0
     N, D = w.N, w.D
     rng = np.random.default_rng(0)
@@ -116,7 +116,7 @@ def cpu_baseline_leg(w, out_gpu, target_s: float):
     return base, acc
 
 
-def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
+def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4):
     import numpy as np
     import torch
 
@@ -135,8 +135,8 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
     in_code = sage.F16 if tdt == torch.float16 else sage.BF16
 
     def step():
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh)
-        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh)
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits)
+        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
 
     for _ in range(warmup):
         step()
@@ -147,9 +147,9 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
     start.record(stream)
     for i in range(steps):
         ev[i][0].record(stream)
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh)
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits)
         ev[i][1].record(stream)
-        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh)
+        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
         ev[i][2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -171,10 +171,10 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp8",
+        "dtype": f"int{qk_bits}+fp8",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
-                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale},
+                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale, "qk_bits": qk_bits},
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tops, 1),
@@ -191,7 +191,7 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float):
     }
     if cpu:
         o_host = out.float().cpu().numpy().reshape(B * H, N, D)[0]
-        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds)
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds, qk_bits)
     return rec
 
 
@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name, or 'all' (default: the N=16k D=128 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--qk-bits", type=int, default=4, choices=(4, 8),
+                    help="width of the Q/K codes: 4 (INT4, the method's default) or 8 (INT8)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -230,7 +232,7 @@ def main():
     else:
         todo = [wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE]
     for w in todo:
-        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds)
+        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits)
         print(json.dumps(rec), flush=True)
 
 

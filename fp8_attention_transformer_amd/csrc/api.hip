@@ -34,7 +34,9 @@ bool shape_ok(int B, int H, int N, int D) {
   return true;
 }
 
-Dims make_dims(int B, int H, int N, int D) {
+bool bits_ok(int qk_bits) { return qk_bits == 4 || qk_bits == 8; }
+
+Dims make_dims(int B, int H, int N, int D, int qk_bits = 8) {
   Dims d;
   d.B = B;
   d.H = H;
@@ -42,15 +44,17 @@ Dims make_dims(int B, int H, int N, int D) {
   d.D = D;
   d.NP = (N + 127) / 128 * 128;
   d.NQB = d.NP / 128;
+  d.QB = qk_bits;
   return d;
 }
 
-// Sizes of the workspace arrays, in the order of sage_quant_bufs.
+// Sizes of the workspace arrays, in the order of sage_quant_bufs.  The code
+// arrays are sized for 8-bit codes so that one layout serves both code widths.
 bool layout(const Dims& d, size_t sizes[11]) {
   const size_t bh = (size_t)d.B * d.H, np = (size_t)d.NP, nqb = (size_t)d.NQB, D = (size_t)d.D;
   size_t rows, t;
   if (!mul_ok(bh, np, &rows)) return false;
-  if (!mul_ok(rows, D / 2, &sizes[0])) return false;        // q_codes
+  if (!mul_ok(rows, D, &sizes[0])) return false;            // q_codes
   sizes[1] = sizes[0];                                       // k_codes
   if (!mul_ok(rows, 4, &sizes[2])) return false;            // q_scale
   sizes[3] = rows / 16 * 4;                                  // k_scale
@@ -166,10 +170,10 @@ sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H,
 }
 
 sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H, int N,
-                              int D, const sage_quant_bufs* out, hipStream_t stream) {
-  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+                              int D, int qk_bits, const sage_quant_bufs* out, hipStream_t stream) {
+  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D);
+  const Dims d = make_dims(B, H, N, D, qk_bits);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
@@ -178,13 +182,13 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
 }
 
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
-                          int causal, float sm_scale, sage_dtype in_dtype, sage_dtype out_dtype, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+                          int causal, float sm_scale, int qk_bits, sage_dtype in_dtype, sage_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D);
+  const Dims d = make_dims(B, H, N, D, qk_bits);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
@@ -207,11 +211,11 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
 }
 
 sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
-                                float sm_scale, sage_dtype out_dtype, hipStream_t stream) {
-  if (!bufs_ok(qb) || !o || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+                                float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream) {
+  if (!bufs_ok(qb) || !o || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D);
+  const Dims d = make_dims(B, H, N, D, qk_bits);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
@@ -220,14 +224,14 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int bh, int q0, int k0, int nq,
-                                int nk, int32_t* out, hipStream_t stream) {
-  if (!bufs_ok(qb) || !out || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
+sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int qk_bits, int bh, int q0,
+                                int k0, int nq, int nk, int32_t* out, hipStream_t stream) {
+  if (!bufs_ok(qb) || !out || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
   if (bh < 0 || bh >= B * H || q0 < 0 || k0 < 0 || nq < 1 || nk < 1) return SAGE_ERR_INVALID;
   if ((long long)q0 + nq > N || (long long)k0 + nk > N) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, N, D), bh, q0, k0, nq, nk, out, stream);
+  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, N, D, qk_bits), bh, q0, k0, nq, nk, out, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

@@ -55,63 +55,82 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// Code layout per query/key row: INT4 (BITS 4) packs channel pairs into bytes
+// (see the pair format above), INT8 (BITS 8) stores one int8 code per
+// channel.  Either way a lane feeds the matrix core 16-byte chunks: chunk
+// 2m + h of the row for matrix step m and half-wave h.
+template <int D, int BITS>
+struct QKCfg {
+  static constexpr int KROW = D * BITS / 8;   // code bytes per row
+  static constexpr int NCH = KROW / 32;       // 16-byte chunks per lane per 32-key tile
+  static constexpr int CPR = KROW / 16;       // 16-byte chunks per row
+};
+
+template <int D, int BITS>
 struct QOperand {
-  static constexpr int NPAIR = D / 64;
-  v4i x[NPAIR];
-  v4i y[NPAIR];
+  static constexpr int NCH = QKCfg<D, BITS>::NCH;
+  v4i x[NCH];
+  v4i y[BITS == 4 ? NCH : 1];
   v16i cinit;
 };
 
 // Build the query operands for lane (query row `qrow` in padded coordinates,
-// half h) from the packed codes.  Both lanes of a query end with the same
-// correction block, offset by `start` (added to every accumulator).
-template <int D>
+// half h) from its codes.  INT4: x/y operands of the pair identity and the
+// correction -128*sum(q_even) (both lanes of a query end with the same one);
+// INT8: the raw codes.  `start` is added to every accumulator.
+template <int D, int BITS>
 __device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_codes_head, int qrow, int h, int start,
-                                               QOperand<D>& op) {
-  constexpr int KROW = D / 2;
+                                               QOperand<D, BITS>& op) {
+  constexpr int KROW = QKCfg<D, BITS>::KROW;
   int corr = 0;
 #pragma unroll
-  for (int pr = 0; pr < QOperand<D>::NPAIR; pr++) {
-    const v4i raw = *(const v4i*)(q_codes_head + (size_t)qrow * KROW + pr * 32 + h * 16);
+  for (int m = 0; m < QOperand<D, BITS>::NCH; m++) {
+    const v4i raw = *(const v4i*)(q_codes_head + (size_t)qrow * KROW + m * 32 + h * 16);
+    if constexpr (BITS == 8) {
+      op.x[m] = raw;
+    } else {
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
-      uint32_t xw = 0, yw = 0;
+      for (int w = 0; w < 4; w++) {
+        uint32_t xw = 0, yw = 0;
 #pragma unroll
-      for (int bb = 0; bb < 4; bb++) {
-        const int v = (int)(int8_t)((uint32_t)raw[w] >> (8 * bb));
-        const int ce = (v & 15) - 8;
-        const int co = v >> 4;
-        corr += ce;
-        xw |= ((uint32_t)(16 * ce) & 0xFFu) << (8 * bb);
-        yw |= ((uint32_t)(co - 16 * ce) & 0xFFu) << (8 * bb);
+        for (int bb = 0; bb < 4; bb++) {
+          const int v = (int)(int8_t)((uint32_t)raw[w] >> (8 * bb));
+          const int ce = (v & 15) - 8;
+          const int co = v >> 4;
+          corr += ce;
+          xw |= ((uint32_t)(16 * ce) & 0xFFu) << (8 * bb);
+          yw |= ((uint32_t)(co - 16 * ce) & 0xFFu) << (8 * bb);
+        }
+        op.x[m][w] = (int)xw;
+        op.y[m][w] = (int)yw;
       }
-      op.x[pr][w] = (int)xw;
-      op.y[pr][w] = (int)yw;
     }
   }
-  corr += __shfl_xor(corr, 32);
+  if constexpr (BITS == 4) corr += __shfl_xor(corr, 32);
 #pragma unroll
   for (int r = 0; r < 16; r++) op.cinit[r] = start - 128 * corr;
 }
 
 // Accumulators start at the bit pattern of 1.5 * 2^23.  The integer sum
-// 16*acc stays below 2^22 in magnitude, so the int32 result read as fp32 is
-// exactly 1.5 * 2^23 + 16*acc, and one exact subtraction yields float(16*acc)
-// (cheaper than an int->float conversion).
+// (16*acc for INT4, acc for INT8) stays below 2^22 in magnitude, so the int32
+// result read as fp32 is exactly 1.5 * 2^23 + that sum, and one exact
+// subtraction yields it as a float (cheaper than an int->float conversion).
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
-// One 32-key tile of S^T (times 16): `a[pr]` holds this lane's 16 packed K
-// bytes (key row lane%32, half h) for channel pair-block pr.
-template <int D>
-__device__ __forceinline__ v16i qk_tile(const v4i* a, const QOperand<D>& op) {
+// One 32-key tile of S^T: `a[m]` holds this lane's 16 K-code bytes (key row
+// lane%32, half h) for chunk m.  Returns 16*dot (INT4) or dot (INT8) plus the
+// start value.
+template <int D, int BITS>
+__device__ __forceinline__ v16i qk_tile(const v4i* a, const QOperand<D, BITS>& op) {
   v16i s = op.cinit;
 #pragma unroll
-  for (int pr = 0; pr < QOperand<D>::NPAIR; pr++) {
-    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[pr], op.x[pr], s, 0, 0, 0);
-    const v4i hi = a[pr] & (int)0xF0F0F0F0;
-    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, op.y[pr], s, 0, 0, 0);
+  for (int m = 0; m < QOperand<D, BITS>::NCH; m++) {
+    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[m], op.x[m], s, 0, 0, 0);
+    if constexpr (BITS == 4) {
+      const v4i hi = a[m] & (int)0xF0F0F0F0;
+      s = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, op.y[m], s, 0, 0, 0);
+    }
   }
   return s;
 }
@@ -143,9 +162,10 @@ __device__ __forceinline__ int xcd_logical_id(int pid, int nwg) {
 // together by one ds_read_b128 hit distinct banks.
 //   K tile: 128 rows (keys) x KROW bytes; chunk c of row r at c ^ kswz(r).
 //   V tile: D rows (channels) x 128 bytes; chunk c of row r at c ^ ((r>>1)&7).
-template <int D>
+template <int CPR>
 __device__ __forceinline__ int kswz(int r) {
-  return D == 128 ? (r >> 2) & 3 : (r >> 3) & 1;
+  static_assert(CPR == 2 || CPR == 4 || CPR == 8, "chunks per row");
+  return CPR == 8 ? (r >> 1) & 7 : (CPR == 4 ? (r >> 2) & 3 : (r >> 3) & 1);
 }
 __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 
@@ -154,17 +174,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Direct HBM/L2 -> LDS copy of one 128-key block: K codes and FP8 V.  Lane l
 // of a wave writes LDS chunk (wave base + l); it fetches the global chunk whose
 // swizzled position that is.
-template <int D>
+template <int D, int BITS>
 __device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, const uint8_t* kblk, const uint8_t* vblk,
                                                int t, int wave, int lane) {
-  constexpr int KROW = D / 2, KCPR = KROW / 16;
+  constexpr int KROW = QKCfg<D, BITS>::KROW, KCPR = KROW / 16;
   constexpr int KCH = kBK * KROW / 16 / 256, VCH = D * kBK / 16 / 256;
   const uint8_t* gk = kblk + (size_t)t * kBK * KROW;
   const uint8_t* gv = vblk + (size_t)t * D * kBK;
 #pragma unroll
   for (int i = 0; i < KCH; i++) {
     const int wbase = 256 * i + 64 * wave;
-    const int e = wbase + lane, r = e / KCPR, c = (e % KCPR) ^ kswz<D>(r);
+    const int e = wbase + lane, r = e / KCPR, c = (e % KCPR) ^ kswz<KCPR>(r);
     __builtin_amdgcn_global_load_lds((const void*)(gk + r * KROW + 16 * c), (lds_ptr_t)(sK + 16 * wbase), 16, 0, 0);
   }
 #pragma unroll
@@ -184,23 +204,23 @@ struct AttnState {
 
 // One 128-key block for this wave: S^T tiles, dequantization, online softmax,
 // FP8 P~, two-level P~V.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D>& qop, const uint8_t* cK,
+template <int D, int BITS, bool CAUSAL>
+__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
                                            int t, int qb, int qrow, int n, int h, const Dims& d) {
-  constexpr int KROW = D / 2;
-  constexpr int NPAIR = D / 64;
+  constexpr int KROW = QKCfg<D, BITS>::KROW, NCH = QKCfg<D, BITS>::NCH, CPR = QKCfg<D, BITS>::CPR;
   constexpr int NDT = D / 32;
-  // ---- S^T for 4 tiles of 32 keys (values 1.5*2^23 + 16*acc as fp32 bits)
+  constexpr float kAccScale = BITS == 4 ? 0.0625f : 1.0f;   // INT4 accumulators hold 16*dot
+  // ---- S^T for 4 tiles of 32 keys (values 1.5*2^23 + (16*)acc as fp32 bits)
   v16i S[4];
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     const int row = 32 * T + n;
-    v4i a[NPAIR];
+    v4i a[NCH];
 #pragma unroll
-    for (int pr = 0; pr < NPAIR; pr++) a[pr] = *(const v4i*)(cK + row * KROW + 16 * ((2 * pr + h) ^ kswz<D>(row)));
-    S[T] = qk_tile<D>(a, qop);
+    for (int m = 0; m < NCH; m++) a[m] = *(const v4i*)(cK + row * KROW + 16 * ((2 * m + h) ^ kswz<CPR>(row)));
+    S[T] = qk_tile<D, BITS>(a, qop);
   }
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   // ---- dequantize into the log2 domain, mask, block max
@@ -210,7 +230,7 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
-    const float c = ((dq * cKS[2 * T + h]) * ks) * 0.0625f;
+    const float c = ((dq * cKS[2 * T + h]) * ks) * kAccScale;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -288,9 +308,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, bool CAUSAL>
+template <int D, int BITS, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
-  constexpr int KROW = D / 2;
+  constexpr int KROW = QKCfg<D, BITS>::KROW;
   constexpr int NDT = D / 32;
   constexpr int S = SAGE_STAGES;
   // vector-memory ops one block's staging issues per wave: K and V chunks via
@@ -330,7 +350,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // VM_PER_BLOCK * k waits exactly for all but the newest k blocks.
   float ds_reg[S - 1], ks_reg[S - 1];
   auto issue = [&](int t, int slot) {
-    stage_kv_async<D>(bK(slot), bV(slot), kblk, vblk, t, wave, lane);
+    stage_kv_async<D, BITS>(bK(slot), bV(slot), kblk, vblk, t, wave, lane);
     ds_reg[t % (S - 1)] = dsrow[t * kBK + (tid & (kBK - 1))];
     ks_reg[t % (S - 1)] = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
   };
@@ -342,8 +362,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   issue(0, 0);
   if (S > 2 && tend > 1) issue(1, 1);
 
-  QOperand<D> qop;
-  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, kMagicBits, qop);
+  QOperand<D, BITS> qop;
+  load_q_operand<D, BITS>(b.q_codes + hrowp * KROW, qrow, h, kMagicBits, qop);
   const float dq = b.q_scale[hrowp + qrow];
 
   AttnState<D, CAUSAL> as;
@@ -363,7 +383,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     const int slot = t % S;
     const bool ahead = t + S - 1 < tend;          // block t+S-1 exists: stage it now
     if (ahead) issue(t + S - 1, (t + S - 1) % S);
-    attn_block<D, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, d);
+    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, d);
     if (t + 1 < tend) {
       // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
       if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
@@ -390,48 +410,52 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 
 // Debug: exact int32 QK^T for a (nq x nk) window of one head, through the same
 // tile function as the fused kernel.  Grid (ceil(nq/32), ceil(nk/32)), 64 threads.
-template <int D>
+template <int D, int BITS>
 __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, int q0, int k0, int nq, int nk,
                                                       int32_t* __restrict__ out) {
-  constexpr int KROW = D / 2;
+  constexpr int KROW = QKCfg<D, BITS>::KROW, NCH = QKCfg<D, BITS>::NCH;
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
   const size_t hrowp = (size_t)bh * d.NP;
   const int qloc = blockIdx.x * 32 + n;
   const int kbase = blockIdx.y * 32;
   const int qrow = min(q0 + qloc, d.NP - 1);
-  QOperand<D> qop;
-  load_q_operand<D>(b.q_codes + hrowp * KROW, qrow, h, 0, qop);
+  QOperand<D, BITS> qop;
+  load_q_operand<D, BITS>(b.q_codes + hrowp * KROW, qrow, h, 0, qop);
   const int krow = min(k0 + kbase + n, d.NP - 1);
-  v4i a[D / 64];
+  v4i a[NCH];
 #pragma unroll
-  for (int pr = 0; pr < D / 64; pr++) a[pr] = *(const v4i*)(b.k_codes + (hrowp + krow) * KROW + pr * 32 + h * 16);
-  const v16i s = qk_tile<D>(a, qop);
+  for (int m = 0; m < NCH; m++) a[m] = *(const v4i*)(b.k_codes + (hrowp + krow) * KROW + m * 32 + h * 16);
+  const v16i s = qk_tile<D, BITS>(a, qop);
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int kloc = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (qloc < nq && kloc < nk) out[(size_t)qloc * nk + kloc] = s[r] >> 4;
+    if (qloc < nq && kloc < nk) out[(size_t)qloc * nk + kloc] = BITS == 4 ? s[r] >> 4 : s[r];
   }
 }
 
-template <int D>
+template <int D, int BITS>
 hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype, hipStream_t s) {
   const dim3 grid(d.NQB * d.BH());
-  if (causal) hipLaunchKernelGGL((attn_kernel<D, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
-  else hipLaunchKernelGGL((attn_kernel<D, false>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
+  if (causal) hipLaunchKernelGGL((attn_kernel<D, BITS, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
+  else hipLaunchKernelGGL((attn_kernel<D, BITS, false>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype, hipStream_t s) {
-  return d.D == 64 ? attn_impl<64>(b, d, causal, ks, o, out_dtype, s) : attn_impl<128>(b, d, causal, ks, o, out_dtype, s);
+  if (d.QB == 8)
+    return d.D == 64 ? attn_impl<64, 8>(b, d, causal, ks, o, out_dtype, s) : attn_impl<128, 8>(b, d, causal, ks, o, out_dtype, s);
+  return d.D == 64 ? attn_impl<64, 4>(b, d, causal, ks, o, out_dtype, s) : attn_impl<128, 4>(b, d, causal, ks, o, out_dtype, s);
 }
 
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk, int32_t* out,
                            hipStream_t s) {
   const dim3 grid((nq + 31) / 32, (nk + 31) / 32);
-  if (d.D == 64) hipLaunchKernelGGL(qk_debug_kernel<64>, grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
-  else hipLaunchKernelGGL(qk_debug_kernel<128>, grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
+  if (d.D == 64 && d.QB == 4) hipLaunchKernelGGL((qk_debug_kernel<64, 4>), grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
+  else if (d.D == 64) hipLaunchKernelGGL((qk_debug_kernel<64, 8>), grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
+  else if (d.QB == 4) hipLaunchKernelGGL((qk_debug_kernel<128, 4>), grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
+  else hipLaunchKernelGGL((qk_debug_kernel<128, 8>), grid, dim3(64), 0, s, b, d, bh, q0, k0, nq, nk, out);
   return hipGetLastError();
 }
 

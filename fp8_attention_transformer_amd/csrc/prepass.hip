@@ -150,13 +150,15 @@ __device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf&
   p3 = __builtin_bit_cast(v8bf, w3);
 }
 
-// INT4 codes rint(x/delta) of NV values sharing one scale, bit-identical to a
-// true IEEE division per element: multiply by the correctly rounded
-// reciprocal (relative error below 2^-22), and if any lane of the wave lands
-// within 2^-19 of a rounding midpoint (half-integer), redo the whole wave
-// with true divisions.  |x| <= 7*delta makes the [-7, 7] clamp unnecessary.
-template <int NV>
-__device__ __forceinline__ void int4_codes(const float* x, float delta, int* code) {
+// Integer codes rint(x/delta) of NV values sharing one scale (INT4: |code|
+// <= 7, INT8: <= 127), bit-identical to a true IEEE division per element:
+// multiply by the correctly rounded reciprocal (absolute error below 2^-19
+// for INT4 and 2^-15 for INT8 quotients), and if any lane of the wave lands
+// within twice that of a rounding midpoint (half-integer), redo the whole
+// wave with true divisions.  |x| <= qmax*delta makes the clamp unnecessary.
+template <int NV, int BITS>
+__device__ __forceinline__ void int_codes(const float* x, float delta, int* code) {
+  constexpr float kWindow = BITS == 4 ? 0x1p-19f : 0x1p-14f;
   const float r = delta == 0.0f ? 0.0f : 1.0f / delta;
   bool amb = false;
   float c[NV];
@@ -164,7 +166,7 @@ __device__ __forceinline__ void int4_codes(const float* x, float delta, int* cod
   for (int e = 0; e < NV; e++) {
     const float q = x[e] * r;
     c[e] = rintf(q);
-    amb |= fabsf(fabsf(q - c[e]) - 0.5f) < 0x1p-19f;
+    amb |= fabsf(fabsf(q - c[e]) - 0.5f) < kWindow;
   }
   if (__any(amb)) {
 #pragma unroll
@@ -203,9 +205,11 @@ __device__ __forceinline__ void fp8_quotients(float* x, float dv) {
 //  K: one scale per 16-key fragment group (one group = 16 keys x D/32 lanes);
 //  V: FP8 with the per-channel scale, written in the permuted channel-major
 //     layout through an LDS copy of the block.
-template <int IN, int D>
+template <int IN, int D, int BITS>
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
+  constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
+  constexpr int KROW = D * BITS / 8;     // code bytes per row
   __shared__ __align__(16) uint16_t sV[kBK * D];
   const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -258,19 +262,31 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPT>(amax);
-      const float dq = amax / 7.0f;
+      const float dq = amax / kQmax;
       int cq[16];
-      int4_codes<16>(g, dq, cq);
-      uint32_t w0 = 0, w1 = 0;
+      int_codes<16, BITS>(g, dq, cq);
+      if constexpr (BITS == 4) {
+        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        w0 |= pack_pair(cq[2 * e], cq[2 * e + 1]) << (8 * e);
-        w1 |= pack_pair(cq[8 + 2 * e], cq[8 + 2 * e + 1]) << (8 * e);
+        for (int e = 0; e < 4; e++) {
+          w0 |= pack_pair(cq[2 * e], cq[2 * e + 1]) << (8 * e);
+          w1 |= pack_pair(cq[8 + 2 * e], cq[8 + 2 * e + 1]) << (8 * e);
+        }
+        uint2 pk;
+        pk.x = w0;
+        pk.y = w1;
+        *(uint2*)(b.q_codes + (hrowp + i) * KROW + 8 * sub) = pk;
+      } else {
+        v4i pk;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; e++) word |= ((uint32_t)cq[4 * w + e] & 0xFFu) << (8 * e);
+          pk[w] = (int)word;
+        }
+        *(v4i*)(b.q_codes + (hrowp + i) * KROW + 16 * sub) = pk;
       }
-      uint2 pk;
-      pk.x = w0;
-      pk.y = w1;
-      *(uint2*)(b.q_codes + (hrowp + i) * (D / 2) + 8 * sub) = pk;
       if (sub == 0) b.q_scale[hrowp + i] = dq;
     }
   }
@@ -301,18 +317,33 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 32; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPG>(amax);
-      const float dk = amax / 7.0f;
+      const float dk = amax / kQmax;
       int ck[32];
-      int4_codes<32>(g, dk, ck);
-      v4i pk;
+      int_codes<32, BITS>(g, dk, ck);
+      if constexpr (BITS == 4) {
+        v4i pk;
 #pragma unroll
-      for (int w = 0; w < 4; w++) {
-        uint32_t word = 0;
+        for (int w = 0; w < 4; w++) {
+          uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 4; e++) word |= pack_pair(ck[8 * w + 2 * e], ck[8 * w + 2 * e + 1]) << (8 * e);
-        pk[w] = (int)word;
+          for (int e = 0; e < 4; e++) word |= pack_pair(ck[8 * w + 2 * e], ck[8 * w + 2 * e + 1]) << (8 * e);
+          pk[w] = (int)word;
+        }
+        *(v4i*)(b.k_codes + (hrowp + j) * KROW + 16 * sub) = pk;
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+          v4i pk;
+#pragma unroll
+          for (int w = 0; w < 4; w++) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) word |= ((uint32_t)ck[16 * half + 4 * w + e] & 0xFFu) << (8 * e);
+            pk[w] = (int)word;
+          }
+          *(v4i*)(b.k_codes + (hrowp + j) * KROW + 32 * sub + 16 * half) = pk;
+        }
       }
-      *(v4i*)(b.k_codes + (hrowp + j) * (D / 2) + 16 * sub) = pk;
       if ((lane % LPG) == 0) b.k_scale[hrowp / kKGroup + (i0 / kKGroup) + grp] = dk;
     }
   }
@@ -449,7 +480,8 @@ hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims&
   const unsigned nstat = (unsigned)((d.BH() * d.NQB + CPW - 1) / CPW);
   hipLaunchKernelGGL((stats_kernel<IN, D>), dim3(nstat), dim3(256), 0, s, q16, k16, v16, d, b);
   hipLaunchKernelGGL(finalize_kernel, dim3(d.BH()), dim3(D), 0, s, d, b);
-  hipLaunchKernelGGL((quant_kernel<IN, D>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
+  if (d.QB == 8) hipLaunchKernelGGL((quant_kernel<IN, D, 8>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
+  else hipLaunchKernelGGL((quant_kernel<IN, D, 4>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
   hipLaunchKernelGGL((delta_s_kernel<IN, D>), grid, dim3(256), 0, s, k16, d, b);
   return hipGetLastError();
 }

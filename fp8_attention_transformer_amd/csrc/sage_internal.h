@@ -22,13 +22,14 @@ struct Dims {
   int B, H, N, D;
   int NP;    // N rounded up to a multiple of 128
   int NQB;   // NP / 128
+  int QB;    // bits per Q/K code: 4 (INT4, packed pairs) or 8 (INT8)
   __host__ __device__ int BH() const { return B * H; }
 };
 
 // Device buffers written by the prepass and read by the attention kernel.
 struct Bufs {
-  uint8_t* q_codes;   // [B,H,NP,D/2] packed INT4 pairs
-  uint8_t* k_codes;   // [B,H,NP,D/2]
+  uint8_t* q_codes;   // [B,H,NP,D*QB/8]: packed INT4 pairs or INT8 codes
+  uint8_t* k_codes;   // [B,H,NP,D*QB/8]
   float* q_scale;     // [B,H,NP]
   float* k_scale;     // [B,H,NP/16]
   float* q_mean;      // [B,H,NQB,D]

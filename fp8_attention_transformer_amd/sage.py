@@ -55,14 +55,14 @@ def lib() -> ctypes.CDLL:
         L.sage_workspace_bytes.restype = sz
         L.sage_quant_bufs_from_workspace.argtypes = [P, sz, i32, i32, i32, i32, ctypes.POINTER(QuantBufs)]
         L.sage_quant_bufs_from_workspace.restype = i32
-        L.sage_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(QuantBufs), P]
         L.sage_quant_smooth.restype = i32
-        L.sage_attn_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, P]
+        L.sage_attn_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32, P, sz, P]
         L.sage_attn_fwd.restype = i32
-        L.sage_attn_quantized.argtypes = [ctypes.POINTER(QuantBufs), P, i32, i32, i32, i32, i32, f32, i32, P]
+        L.sage_attn_quantized.argtypes = [ctypes.POINTER(QuantBufs), P, i32, i32, i32, i32, i32, f32, i32, i32, P]
         L.sage_attn_quantized.restype = i32
         L.sage_qk_int32_debug.argtypes = [ctypes.POINTER(QuantBufs), i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          P, P]
+                                          i32, P, P]
         L.sage_qk_int32_debug.restype = i32
         L.sage_fp8_encode_debug.argtypes = [P, P, sz, P]
         L.sage_fp8_encode_debug.restype = i32
@@ -95,26 +95,27 @@ def quant_bufs_from_workspace(ws_ptr: int, nbytes: int, B: int, H: int, N: int, 
 
 
 def quant_smooth(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, H: int, N: int, D: int,
-                 bufs: QuantBufs, stream: int = 0) -> None:
-    _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, ctypes.byref(bufs), stream),
+                 bufs: QuantBufs, stream: int = 0, qk_bits: int = 4) -> None:
+    _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, qk_bits, ctypes.byref(bufs), stream),
            "sage_quant_smooth")
 
 
 def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool,
-             sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0) -> None:
-    _check(lib().sage_attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale),
+             sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0,
+             qk_bits: int = 4) -> None:
+    _check(lib().sage_attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale), qk_bits,
                                in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd")
 
 
 def attn_quantized(bufs: QuantBufs, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool, sm_scale: float,
-                   out_dtype: int, stream: int = 0) -> None:
+                   out_dtype: int, stream: int = 0, qk_bits: int = 4) -> None:
     _check(lib().sage_attn_quantized(ctypes.byref(bufs), o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale),
-                                     out_dtype, stream), "sage_attn_quantized")
+                                     qk_bits, out_dtype, stream), "sage_attn_quantized")
 
 
 def qk_int32_debug(bufs: QuantBufs, B: int, H: int, N: int, D: int, bh: int, q0: int, k0: int, nq: int, nk: int,
-                   out_ptr: int, stream: int = 0) -> None:
-    _check(lib().sage_qk_int32_debug(ctypes.byref(bufs), B, H, N, D, bh, q0, k0, nq, nk, out_ptr, stream),
+                   out_ptr: int, stream: int = 0, qk_bits: int = 4) -> None:
+    _check(lib().sage_qk_int32_debug(ctypes.byref(bufs), B, H, N, D, qk_bits, bh, q0, k0, nq, nk, out_ptr, stream),
            "sage_qk_int32_debug")
 
 
@@ -164,8 +165,8 @@ def _stream_handle(device) -> int:
 
 
 def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype=None, workspace: Workspace = None,
-         out=None):
-    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors."""
+         out=None, qk_bits: int = 4):
+    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors (qk_bits 4: INT4 Q/K codes, 8: INT8)."""
     import torch
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
         raise ValueError("q, k, v must share one [B, H, N, D] shape")
@@ -184,5 +185,5 @@ def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype
         workspace = alloc_workspace(B, H, N, D, q.device)
     attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, causal, sm_scale,
              _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr, workspace.nbytes,
-             _stream_handle(q.device))
+             _stream_handle(q.device), qk_bits)
     return out

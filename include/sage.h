@@ -26,6 +26,12 @@
  *    sage_contract_version): Q-smoothing block and mean chunk = 128 tokens;
  *    online-softmax block = 128 keys (also the level-1 block of the two-level
  *    P~V accumulation); K scale groups of 16 keys (two per 32-key tile).
+ *  - qk_bits selects the width of the Q and K codes: 4 (INT4 in [-7, 7], the
+ *    method's default) or 8 (INT8 in [-127, 127], the more accurate choice
+ *    the adaptive quantization of SageAttention2 (summary page, Key
+ *    Contribution 3) falls back to where INT4 loses accuracy; same
+ *    granularity, scale = amax/qmax).  Any other value is SAGE_ERR_INVALID.
+ *    Buffers written with one qk_bits must be read with the same value.
  */
 #ifndef SAGE_H_
 #define SAGE_H_
@@ -53,11 +59,15 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
  * sage_attn_fwd).  NP = N rounded up to a multiple of 128, NQB = NP / 128.
  * Rows or keys at index >= N are padding: codes 0, scales 0, V bytes 0.
  *
- *  q_codes, k_codes  uint8 [B,H,NP,D/2]  INT4 codes in [-7,7], two per byte:
- *                    byte b of a row holds channel 2b (c_even) and 2b+1
- *                    (c_odd) as the signed value 16*c_odd + c_even + 8, so
+ *  q_codes, k_codes  uint8 [B,H,NP,D]    (space for 8-bit codes; row r starts
+ *                    at byte r*D*qk_bits/8, i.e. rows are packed densely)
+ *                    qk_bits 4: INT4 codes in [-7,7], two per byte: byte b
+ *                    of a row holds channel 2b (c_even) and 2b+1 (c_odd) as
+ *                    the signed value 16*c_odd + c_even + 8, so
  *                    c_even = (byte & 15) - 8 and c_odd = (int8)byte >> 4.
- *  q_scale           fp32  [B,H,NP]      one scale per token (delta = amax/7)
+ *                    qk_bits 8: one int8 code in [-127,127] per channel.
+ *  q_scale           fp32  [B,H,NP]      one scale per token (amax/7 or
+ *                    amax/127)
  *  k_scale           fp32  [B,H,NP/16]   one scale per 16-key group; in a
  *                    32-key tile starting at key 32u, group 2u+h holds the keys
  *                    32u + o with (o/4) % 2 == h
@@ -111,15 +121,15 @@ sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H,
                                            sage_quant_bufs* out);
 
 /*
- * Prepass (smoothing, INT4 Q/K quantization and packing, FP8 V with
+ * Prepass (smoothing, INT4/INT8 Q/K quantization and packing, FP8 V with
  * per-channel scales, compensation term): the smoothing of the method and
  * the quantization of Q, K to INT4 and V to FP8 (SageAttention2 abstract).
- * q, k, v: device [B,H,N,D] of in_dtype (SAGE_F16 or SAGE_BF16).  All arrays
- * of *out must be device buffers of the sizes listed above (for example carved
- * by sage_quant_bufs_from_workspace).
+ * q, k, v: device [B,H,N,D] of in_dtype (SAGE_F16 or SAGE_BF16); qk_bits 4 or
+ * 8.  All arrays of *out must be device buffers of the sizes listed above
+ * (for example carved by sage_quant_bufs_from_workspace).
  */
 sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H,
-                              int N, int D, const sage_quant_bufs* out, hipStream_t stream);
+                              int N, int D, int qk_bits, const sage_quant_bufs* out, hipStream_t stream);
 
 /*
  * Attention forward: O = SageAttention2(Q, K, V), i.e. the prepass above
@@ -131,33 +141,36 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
  *            must not alias q, k, v or the workspace
  *  causal    nonzero: query i attends to keys j <= i
  *  sm_scale  softmax scale (> 0, finite), usually 1/sqrt(D)
+ *  qk_bits   4 (INT4 Q/K codes) or 8 (INT8)
  *  workspace device buffer of at least sage_workspace_bytes(B,H,N,D) bytes;
  *            afterwards it holds the sage_quant_bufs of this call
  * Equivalent to sage_quant_smooth followed by sage_attn_quantized.
  */
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
-                          int causal, float sm_scale, sage_dtype in_dtype, sage_dtype out_dtype, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream);
+                          int causal, float sm_scale, int qk_bits, sage_dtype in_dtype, sage_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The fused attention kernel alone, over prepass buffers already written by
  * sage_quant_smooth (or by an earlier sage_attn_fwd): INT4 QK^T,
  * dequantization with the compensation term, online softmax, FP8 P~V with
  * two-level accumulation (SageAttention2 abstract).  Arguments as for
- * sage_attn_fwd; qb must describe buffers of this B, H, N, D.
+ * sage_attn_fwd; qb must describe buffers of this B, H, N, D written with
+ * this qk_bits.
  */
 sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
-                                float sm_scale, sage_dtype out_dtype, hipStream_t stream);
+                                float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream);
 
 /*
- * Debug: the exact integer dot products of the INT4 codes, computed by the
- * same matrix-core tile routine as the fused kernel.  For head bh = b*H + h:
+ * Debug: the exact integer dot products of the Q/K codes (qk_bits as written
+ * by the prepass), computed by the same matrix-core tile routine as the fused
+ * kernel.  For head bh = b*H + h:
  *   out[a][c] = sum_ch qcode[q0+a][ch] * kcode[k0+c][ch],  a < nq, c < nk
  * out: device int32 [nq, nk].  Requires 0 <= q0, q0+nq <= N, 0 <= k0,
  * k0+nk <= N, nq, nk >= 1.
  */
-sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int bh, int q0, int k0,
-                                int nq, int nk, int32_t* out, hipStream_t stream);
+sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int qk_bits, int bh,
+                                int q0, int k0, int nq, int nk, int32_t* out, hipStream_t stream);
 
 /*
  * Debug: fp32 -> OCP e4m3fn with the device conversion the kernels use for P~

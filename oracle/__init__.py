@@ -76,7 +76,7 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [P, P, i64]
         L.oracle_e4m3_decode.argtypes = [P, P, i64]
         L.oracle_decode_input.argtypes = [P, i32, P, i64]
-        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32] + [P] * 9 + [i32]
+        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32] + [P] * 9 + [i32]
         L.oracle_quant_smooth.restype = i32
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
         L.oracle_qk_int32.restype = i32
@@ -131,9 +131,11 @@ class Quant:
     delta_s: np.ndarray   # fp32  [B,H,ceil(N/128),N]
 
 
-def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True) -> Quant:
+def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True,
+                 qk_bits: int = 4) -> Quant:
     """Run the prepass; with_delta_s=False skips the (quadratic) compensation
-    term and leaves ``delta_s`` as None."""
+    term and leaves ``delta_s`` as None.  qk_bits selects INT4 (4) or INT8 (8)
+    codes for Q and K."""
     B, H, N, D = q_bits.shape
     nqb = (N + BQ_MEAN - 1) // BQ_MEAN
     G = 2 * ((N + 31) // 32)
@@ -144,7 +146,7 @@ def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_del
         q_mean=np.empty((B, H, nqb, D), np.float32), k_mean=np.empty((B, H, D), np.float32),
         v_codes=np.empty((B, H, N, D), np.uint8), v_scale=np.empty((B, H, D), np.float32),
         delta_s=np.empty((B, H, nqb, N), np.float32) if with_delta_s else None)
-    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D,
+    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D, qk_bits,
                                    _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
                                    _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),
                                    _ptr(out.delta_s), _threads(nthreads))

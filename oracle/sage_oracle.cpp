@@ -22,6 +22,9 @@
 //     sequential sum of the chunk partials, then one IEEE division by the count.
 //   - INT4: symmetric, delta = amax/7, code = clamp(rint(x/delta), -7, 7) with
 //     true division and round-half-to-even; amax == 0 gives delta = 0, code 0.
+//     The adaptive alternative for Q and K ("adaptive quantization method",
+//     technical-report summary, Key Contribution 3; 8-bit codes as in the
+//     SageAttention v1 page) uses the same rule with 127 in place of 7.
 //   - Q: one scale per token.  K: one scale per 16-key group; inside every
 //     32-key tile, group h (0 or 1) holds the keys whose offset o satisfies
 //     (o / 4) % 2 == h.  These are the keys that one half of a 64-lane wave holds
@@ -107,11 +110,12 @@ float e4m3_decode(uint8_t b) {
 }
 
 // ------------------------------------------------------------ quantization ---
-int8_t int4_code(float x, float delta) {
+// Symmetric integer code with maximum magnitude qmax (7 for INT4, 127 for INT8).
+int8_t int_code(float x, float delta, float qmax) {
   if (delta == 0.0f) return 0;
   float r = std::rint(x / delta);
-  if (r > 7.0f) r = 7.0f;
-  if (r < -7.0f) r = -7.0f;
+  if (r > qmax) r = qmax;
+  if (r < -qmax) r = -qmax;
   return (int8_t)r;
 }
 
@@ -153,7 +157,7 @@ void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
 // Prepass: smoothing statistics, INT4 codes and scales for Q and K, FP8 V with
 // per-channel scales, and the rank-1 compensation term.  All arrays are in the
 // canonical (unpacked, unpadded) layout:
-//   q_codes, k_codes : int8  [B,H,N,D]     values in [-7, 7]
+//   q_codes, k_codes : int8  [B,H,N,D]     values in [-7, 7] (qk_bits 4) or [-127, 127] (8)
 //   q_scale          : fp32  [B,H,N]
 //   k_scale          : fp32  [B,H,2*ceil(N/32)]
 //   q_mean           : fp32  [B,H,ceil(N/128),D]
@@ -163,11 +167,13 @@ void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
 //   delta_s          : fp32  [B,H,ceil(N/128),N]
 // Returns 0, or -1 for invalid arguments.
 int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
-                        int B, int H, int N, int D,
+                        int B, int H, int N, int D, int qk_bits,
                         int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
                         float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale,
                         float* delta_s, int nthreads) {
   if (!q || !k || !v || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
+  if (qk_bits != 4 && qk_bits != 8) return -1;
+  const float qmax = qk_bits == 4 ? 7.0f : 127.0f;
   const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
   const int64_t G = 2 * ((int64_t)(N + 31) / 32);
   parallel_for((int64_t)B * H, nthreads, [&](int64_t bh) {
@@ -213,10 +219,10 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     for (int64_t i = 0; i < N; i++) {
       float amax = 0.0f;
       for (int c = 0; c < D; c++) amax = std::max(amax, std::fabs(gQ[i * D + c]));
-      float dq = amax / 7.0f;
+      float dq = amax / qmax;
       if (q_scale) q_scale[bh * N + i] = dq;
       if (q_codes)
-        for (int c = 0; c < D; c++) q_codes[base + i * D + c] = int4_code(gQ[i * D + c], dq);
+        for (int c = 0; c < D; c++) q_codes[base + i * D + c] = int_code(gQ[i * D + c], dq, qmax);
     }
     // ---- K: one INT4 scale per 16-key fragment group
     std::vector<float> gamax(G, 0.0f);
@@ -226,12 +232,12 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     }
     std::vector<float> dk(G);
     for (int64_t g = 0; g < G; g++) {
-      dk[g] = gamax[g] / 7.0f;
+      dk[g] = gamax[g] / qmax;
       if (k_scale) k_scale[bh * G + g] = dk[g];
     }
     if (k_codes)
       for (int64_t j = 0; j < N; j++)
-        for (int c = 0; c < D; c++) k_codes[base + j * D + c] = int4_code(gK[j * D + c], dk[k_group(j)]);
+        for (int c = 0; c < D; c++) k_codes[base + j * D + c] = int_code(gK[j * D + c], dk[k_group(j)], qmax);
     // ---- V: FP8 e4m3fn with one scale per channel
     for (int c = 0; c < D; c++) {
       float amax = 0.0f;

@@ -35,8 +35,10 @@ def vperm_keys() -> np.ndarray:
     return 64 * (p // 64) + 32 * (s // 16) + 8 * ((s % 16) // 4) + 4 * ((p % 64) // 32) + s % 4
 
 
-def unpack_codes(packed: np.ndarray, N: int) -> np.ndarray:
-    """[BH, NP, D/2] packed pairs -> int8 codes [BH, N, D]."""
+def unpack_codes(packed: np.ndarray, N: int, qk_bits: int = 4) -> np.ndarray:
+    """[BH, NP, D*qk_bits/8] code rows -> int8 codes [BH, N, D] (INT4: packed pairs; INT8: one byte each)."""
+    if qk_bits == 8:
+        return packed.view(np.int8)[:, :N].copy()
     v = packed.view(np.int8).astype(np.int16)[:, :N]
     even = (v & 15) - 8
     odd = v >> 4
@@ -58,7 +60,7 @@ def unpermute_v(vcodes: np.ndarray, BH: int, NQB: int, D: int, N: int) -> np.nda
 class Readback:
     """The prepass arrays of a workspace, copied to host in canonical form."""
 
-    def __init__(self, ws: sage.Workspace):
+    def __init__(self, ws: sage.Workspace, qk_bits: int = 4):
         torch = torch_mod()
         B, H, N, D = ws.B, ws.H, ws.N, ws.D
         BH = B * H
@@ -73,10 +75,13 @@ class Readback:
             return host[off:off + nbytes].view(dtype).reshape(shape)
 
         self.N, self.NP, self.NQB, self.D, self.BH = N, NP, NQB, D, BH
-        self.q_codes_packed = arr(qb.q_codes, BH * NP * D // 2, np.uint8, (BH, NP, D // 2))
-        self.k_codes_packed = arr(qb.k_codes, BH * NP * D // 2, np.uint8, (BH, NP, D // 2))
-        self.q_codes = unpack_codes(self.q_codes_packed, N)
-        self.k_codes = unpack_codes(self.k_codes_packed, N)
+        self.qk_bits = qk_bits
+        krow = D * qk_bits // 8
+        self.q_codes_packed = arr(qb.q_codes, BH * NP * krow, np.uint8, (BH, NP, krow))
+        self.k_codes_packed = arr(qb.k_codes, BH * NP * krow, np.uint8, (BH, NP, krow))
+        self.zero_code_byte = 8 if qk_bits == 4 else 0
+        self.q_codes = unpack_codes(self.q_codes_packed, N, qk_bits)
+        self.k_codes = unpack_codes(self.k_codes_packed, N, qk_bits)
         self.q_scale_p = arr(qb.q_scale, BH * NP * 4, np.float32, (BH, NP))
         self.k_scale_p = arr(qb.k_scale, BH * NP // 16 * 4, np.float32, (BH, NP // 16))
         self.q_mean = arr(qb.q_mean, BH * NQB * D * 4, np.float32, (BH, NQB, D))
@@ -92,24 +97,25 @@ class Readback:
         torch.cuda.synchronize()
 
 
-def run_quant_smooth(q_bits, k_bits, v_bits, dtype: str):
+def run_quant_smooth(q_bits, k_bits, v_bits, dtype: str, qk_bits: int = 4):
     torch = torch_mod()
     B, H, N, D = q_bits.shape
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
     ws = sage.alloc_workspace(B, H, N, D)
     ws.tensor.fill_(0xA5)  # poison: every array element the prepass owns must be written
     sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code(dtype), B, H, N, D, ws.bufs(),
-                      torch.cuda.current_stream().cuda_stream)
+                      torch.cuda.current_stream().cuda_stream, qk_bits=qk_bits)
     torch.cuda.synchronize()
     return ws
 
 
-def run_attn(q_bits, k_bits, v_bits, dtype: str, causal: bool, sm_scale: float, out_dtype=None):
+def run_attn(q_bits, k_bits, v_bits, dtype: str, causal: bool, sm_scale: float, out_dtype=None, qk_bits: int = 4):
     torch = torch_mod()
     B, H, N, D = q_bits.shape
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
     ws = sage.alloc_workspace(B, H, N, D)
-    out = sage.attn(q, k, v, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or torch.float32, workspace=ws)
+    out = sage.attn(q, k, v, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or torch.float32, workspace=ws,
+                    qk_bits=qk_bits)
     torch.cuda.synchronize()
     return out, ws
 

@@ -45,7 +45,7 @@ def _sizes(B, H, N, D):
     NP = (N + 127) // 128 * 128
     NQB = NP // 128
     BH = B * H
-    return [BH * NP * D // 2, BH * NP * D // 2, BH * NP * 4, BH * NP // 16 * 4, BH * NQB * D * 4, BH * D * 4,
+    return [BH * NP * D, BH * NP * D, BH * NP * 4, BH * NP // 16 * 4, BH * NQB * D * 4, BH * D * 4,
             BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * D * 4, BH * NQB * D * 4]
 
 
@@ -72,12 +72,13 @@ def test_workspace_carving(shape):
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), B=1, H=2, N=256, D=64, causal=0,
-             sm_scale=0.125, in_dtype=sage.F16, out_dtype=sage.F32, ws=FAKE + (4 << 30), ws_bytes=None)
+             sm_scale=0.125, qk_bits=4, in_dtype=sage.F16, out_dtype=sage.F32, ws=FAKE + (4 << 30), ws_bytes=None)
     a.update(kw)
     if a["ws_bytes"] is None:
         a["ws_bytes"] = sage.workspace_bytes(a["B"], a["H"], a["N"], a["D"])
     return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["D"], a["causal"],
-                                    a["sm_scale"], a["in_dtype"], a["out_dtype"], a["ws"], a["ws_bytes"], None)
+                                    a["sm_scale"], a["qk_bits"], a["in_dtype"], a["out_dtype"], a["ws"], a["ws_bytes"],
+                                    None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -88,7 +89,8 @@ def _attn(**kw):
     (dict(sm_scale=math.inf), sage.ERR_INVALID), (dict(in_dtype=sage.F32), sage.ERR_INVALID),
     (dict(in_dtype=7), sage.ERR_INVALID), (dict(out_dtype=5), sage.ERR_INVALID),
     (dict(ws_bytes=100), sage.ERR_WORKSPACE), (dict(o=FAKE + 64), sage.ERR_INVALID),
-    (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID),
+    (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID), (dict(qk_bits=0), sage.ERR_INVALID),
+    (dict(qk_bits=2), sage.ERR_INVALID), (dict(qk_bits=6), sage.ERR_INVALID), (dict(qk_bits=16), sage.ERR_INVALID),
 ])
 def test_attn_fwd_validation(kw, expect):
     assert _attn(**kw) == expect
@@ -97,18 +99,22 @@ def test_attn_fwd_validation(kw, expect):
 def test_quant_smooth_and_debug_validation():
     L = sage.lib()
     qb = sage.QuantBufs(*([FAKE] * 11))
-    assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, ctypes.byref(qb), None) == sage.ERR_INVALID
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, 4, ctypes.byref(qb), None) == sage.ERR_INVALID
     bad = sage.QuantBufs(*([FAKE] * 10 + [0]))
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, ctypes.byref(bad), None) == sage.ERR_INVALID
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, None, None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, ctypes.byref(bad), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, None, None) == sage.ERR_INVALID
     dbg = L.sage_qk_int32_debug
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 101, 4, FAKE, None) == sage.ERR_INVALID
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 1, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 99, 0, 2, 4, FAKE, None) == sage.ERR_INVALID
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, -1, 2, 4, FAKE, None) == sage.ERR_INVALID
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 0, 4, FAKE, None) == sage.ERR_INVALID
-    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 0, 0, 0, 4, 4, None, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 101, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 1, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 99, 0, 2, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, -1, 2, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 0, 4, FAKE, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 4, 4, None, None) == sage.ERR_INVALID
+    assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 7, 0, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 3, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_attn_quantized(ctypes.byref(qb), FAKE, 1, 1, 10, 64, 0, 0.125, 5, sage.F32, None) == sage.ERR_INVALID
+    assert L.sage_attn_quantized(ctypes.byref(qb), FAKE, 1, 1, 10, 64, 0, 0.0, 8, sage.F32, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(None, FAKE, 10, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(FAKE, FAKE, 0, None) == sage.ERR_INVALID
 

@@ -1,6 +1,7 @@
 """GPU parity: libsage (HIP, gfx950) against the CPU oracle, through the C ABI.
 
-Bit-exact: INT4 codes, all scales, means, FP8 V codes, int32 QK^T.
+Both code widths of Q and K (qk_bits 4: INT4, 8: INT8) are covered.
+Bit-exact: Q/K codes, all scales, means, FP8 V codes, int32 QK^T.
 Toleranced: the compensation term (fp32 vs the oracle's fp64 accumulation,
 bound derived from the fp32 chain) and O (max-abs 2e-3 plus a per-row slack for
 P~ elements that sit within rounding distance of an FP8 midpoint; the slack is
@@ -32,6 +33,12 @@ SMALL = [
               k_offset_std=5.0),
 ]
 FULL = [wl.LLM, wl.DIT, wl.VIDEO] + wl.LONG
+FULL_CASES = [(w, 4) for w in FULL] + [(w, 8) for w in (wl.LLM, wl.VIDEO, wl.HEADLINE)]
+BITS = [4, 8]
+
+
+def _id(w):
+    return w.name + ("_c" if w.causal else "")
 
 
 def _sdt(w):
@@ -50,9 +57,9 @@ def _check_prepass(rb, z):
     assert np.array_equal(rb.k_mean, zq(z.k_mean)), "k means"
     assert np.array_equal(rb.v_scale, zq(z.v_scale)), "v scales"
     assert np.array_equal(rb.v_codes, zq(z.v_codes)), "v codes"
-    # padding rows: zero codes (byte 8) and zero scales
-    assert np.all(rb.q_scale_p[:, N:] == 0) and np.all(rb.q_codes_packed[:, N:] == 8)
-    assert np.all(rb.k_codes_packed[:, N:] == 8)
+    # padding rows: zero codes (byte 8 for INT4 pairs, 0 for INT8) and zero scales
+    assert np.all(rb.q_scale_p[:, N:] == 0) and np.all(rb.q_codes_packed[:, N:] == rb.zero_code_byte)
+    assert np.all(rb.k_codes_packed[:, N:] == rb.zero_code_byte)
 
 
 def _ds_bound(oracle_lib, z, k_bits, dtype_code):
@@ -69,12 +76,13 @@ def _ds_bound(oracle_lib, z, k_bits, dtype_code):
     return (6 * D + 8) * 2.0 ** -24 * np.einsum("bqc,bjc->bqj", qm, gK)
 
 
-@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
-def test_prepass_bitexact_small(oracle_lib, w):
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("w", SMALL, ids=_id)
+def test_prepass_bitexact_small(oracle_lib, w, bits):
     import gpu_helpers as gh
     q, k, v = wl.generate(w)
-    z = oracle_lib.quant_smooth(q, k, v, _sdt(w))
-    rb = gh.Readback(gh.run_quant_smooth(q, k, v, w.dtype))
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), qk_bits=bits)
+    rb = gh.Readback(gh.run_quant_smooth(q, k, v, w.dtype, qk_bits=bits), qk_bits=bits)
     _check_prepass(rb, z)
     # compensation term within the fp32-chain bound
     err = np.abs(rb.delta_s.astype(np.float64) - z.delta_s.reshape(w.B * w.H, -1, w.N))
@@ -83,18 +91,19 @@ def test_prepass_bitexact_small(oracle_lib, w):
     assert np.all(rb.delta_s_p[:, :, w.N:] == 0)
 
 
-@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
-def test_qk_int32_bitexact_small(oracle_lib, w):
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("w", SMALL, ids=_id)
+def test_qk_int32_bitexact_small(oracle_lib, w, bits):
     import torch
     from fp8_attention_transformer_amd import sage
     import gpu_helpers as gh
     q, k, v = wl.generate(w)
-    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False)
-    ws = gh.run_quant_smooth(q, k, v, w.dtype)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False, qk_bits=bits)
+    ws = gh.run_quant_smooth(q, k, v, w.dtype, qk_bits=bits)
     N = w.N
     for bh in range(w.B * w.H):
         out = torch.empty((N, N), dtype=torch.int32, device="cuda")
-        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, bh, 0, 0, N, N, out.data_ptr())
+        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, bh, 0, 0, N, N, out.data_ptr(), qk_bits=bits)
         qc = z.q_codes.reshape(-1, N, w.D)[bh]
         kc = z.k_codes.reshape(-1, N, w.D)[bh]
         ref = oracle_lib.qk_int32(qc, kc, 0, 0, N, N)
@@ -102,7 +111,7 @@ def test_qk_int32_bitexact_small(oracle_lib, w):
     # an interior window with ragged edges
     if N >= 40:
         out = torch.empty((N - 7 - 3, N - 11 - 2), dtype=torch.int32, device="cuda")
-        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, 0, 7, 11, N - 10, N - 13, out.data_ptr())
+        sage.qk_int32_debug(ws.bufs(), w.B, w.H, N, w.D, 0, 7, 11, N - 10, N - 13, out.data_ptr(), qk_bits=bits)
         ref = oracle_lib.qk_int32(z.q_codes.reshape(-1, N, w.D)[0], z.k_codes.reshape(-1, N, w.D)[0], 7, 11,
                                   N - 10, N - 13)
         assert np.array_equal(out.cpu().numpy(), ref)
@@ -117,26 +126,27 @@ def _compare_o(O_gpu, O_ref, slack, label):
     assert bad.size == 0, (label, bad[:5], err[bad[:5]], slack[bad[:5]])
 
 
-@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name + ("_c" if w.causal else ""))
-def test_attention_parity_small(oracle_lib, w):
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("w", SMALL, ids=_id)
+def test_attention_parity_small(oracle_lib, w, bits):
     import gpu_helpers as gh
     q, k, v = wl.generate(w)
-    z = oracle_lib.quant_smooth(q, k, v, _sdt(w))
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), qk_bits=bits)
     O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, eps=EPS_TIE)
-    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits)
     O_gpu = out.cpu().numpy().reshape(-1, w.D)
-    _compare_o(O_gpu, O_ref, slack, w.name)
+    _compare_o(O_gpu, O_ref, slack, f"{w.name}/int{bits}")
     # the workspace of the attention call holds the same prepass
-    rb = gh.Readback(ws)
+    rb = gh.Readback(ws, qk_bits=bits)
     _check_prepass(rb, z)
     # cos-sim against FP32 attention equals the method's own (oracle) value
     O_fp, _ = oracle_lib.attn_exact(q, k, v, _sdt(w), w.causal, w.scale, 0)
     c_gpu, c_orc = gh.cos_sim(O_gpu, O_fp), gh.cos_sim(O_ref, O_fp)
-    print(f"[{w.name}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+    print(f"[{w.name}/int{bits}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
     assert abs(c_gpu - c_orc) < 1e-4
 
 
-@pytest.mark.parametrize("w", SMALL[:4], ids=lambda w: w.name + ("_c" if w.causal else ""))
+@pytest.mark.parametrize("w", SMALL[:4], ids=_id)
 def test_low_precision_outputs(oracle_lib, w):
     import torch
     import gpu_helpers as gh
@@ -151,12 +161,13 @@ def test_low_precision_outputs(oracle_lib, w):
         _compare_o(O_gpu, O_ref, slack + extra, f"{w.name}-{dt}")
 
 
-def test_determinism(oracle_lib):
+@pytest.mark.parametrize("bits", BITS)
+def test_determinism(oracle_lib, bits):
     import gpu_helpers as gh
     w = SMALL[6]
     q, k, v = wl.generate(w)
-    a, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
-    b, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
+    a, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits)
+    b, _ = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits)
     assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
@@ -204,8 +215,8 @@ def _sample_rows(w, heads, rng, per_head=96):
     return np.array(rows, np.int64)
 
 
-@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
-def test_full_size_parity(oracle_lib, w):
+@pytest.mark.parametrize("w,bits", FULL_CASES, ids=lambda c: c.name if hasattr(c, "name") else f"int{c}")
+def test_full_size_parity(oracle_lib, w, bits):
     """The benchmark's workload and launch: all heads on the GPU; codes and
     scales of every head bit-exact; compensation term, int32 tiles and O
     compared on two heads (first and last) and sampled rows."""
@@ -214,9 +225,9 @@ def test_full_size_parity(oracle_lib, w):
     import gpu_helpers as gh
     q, k, v = wl.generate(w)
     BH = w.B * w.H
-    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale)
-    rb = gh.Readback(ws)
-    z_all = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False)
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits)
+    rb = gh.Readback(ws, qk_bits=bits)
+    z_all = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False, qk_bits=bits)
     _check_prepass(rb, z_all)
     del z_all
     O_gpu_all = out.cpu().numpy().reshape(BH, w.N, w.D)
@@ -224,7 +235,7 @@ def test_full_size_parity(oracle_lib, w):
     rng = np.random.default_rng(w.seed)
     for bh in (0, BH - 1):
         qs, kk, vs = (a.reshape(BH, 1, w.N, w.D)[bh:bh + 1] for a in (q, k, v))
-        z = oracle_lib.quant_smooth(qs, kk, vs, _sdt(w))
+        z = oracle_lib.quant_smooth(qs, kk, vs, _sdt(w), qk_bits=bits)
         # compensation term within the fp32-chain bound
         err = np.abs(rb.delta_s[bh].astype(np.float64) - z.delta_s[0, 0])
         assert np.all(err <= _ds_bound(oracle_lib, z, kk, _sdt(w))[0] + 1e-30)
@@ -232,13 +243,14 @@ def test_full_size_parity(oracle_lib, w):
         wins = [(0, 0), (w.N - 64, w.N - 64), (0, w.N - 64)] + [tuple(rng.integers(0, w.N - 64, 2)) for _ in range(4)]
         for q0, k0 in wins:
             o32 = torch.empty((64, 64), dtype=torch.int32, device="cuda")
-            sage.qk_int32_debug(ws.bufs(), w.B, w.H, w.N, w.D, bh, int(q0), int(k0), 64, 64, o32.data_ptr())
+            sage.qk_int32_debug(ws.bufs(), w.B, w.H, w.N, w.D, bh, int(q0), int(k0), 64, 64, o32.data_ptr(),
+                                qk_bits=bits)
             ref = oracle_lib.qk_int32(z.q_codes[0, 0], z.k_codes[0, 0], int(q0), int(k0), 64, 64)
             assert np.array_equal(o32.cpu().numpy(), ref)
         rows = _sample_rows(w, 1, rng)
         O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, rows=rows, eps=EPS_TIE)
-        _compare_o(O_gpu_all[bh][rows], O_ref, slack, f"{w.name}/bh{bh}")
+        _compare_o(O_gpu_all[bh][rows], O_ref, slack, f"{w.name}/int{bits}/bh{bh}")
         O_fp, _ = oracle_lib.attn_exact(qs, kk, vs, _sdt(w), w.causal, w.scale, 0, rows=rows)
         c_gpu, c_orc = gh.cos_sim(O_gpu_all[bh][rows], O_fp), gh.cos_sim(O_ref, O_fp)
-        print(f"[{w.name}/bh{bh}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+        print(f"[{w.name}/int{bits}/bh{bh}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
         assert abs(c_gpu - c_orc) < 1e-3

@@ -84,17 +84,18 @@ def test_invariants(oracle_lib, N, D, causal):
         assert np.abs(p - 1).max() <= 1e-12
 
 
-def _lossless_inputs(N, D, seed):
-    """Integer Q, K whose INT4 quantization is exact (every token / key group
-    holds a +-7, every block mean is zero) and V exactly representable in FP8
-    after its per-channel scale (amax 3.5 -> scale 1/128)."""
+def _lossless_inputs(N, D, seed, qmax=7):
+    """Integer Q, K whose INT4 (qmax 7) or INT8 (qmax 127) quantization is
+    exact (every token / key group holds a +-qmax, every block mean is zero)
+    and V exactly representable in FP8 after its per-channel scale (amax 3.5
+    -> scale 1/128).  Integers up to 127 are exact in bf16."""
     assert N % 2 == 0 and N <= 128
     rng = np.random.default_rng(seed)
     half = N // 2
-    Qh = rng.integers(-6, 7, (half, D)).astype(np.float32)
-    Qh[np.arange(half), rng.integers(0, D, half)] = 7 * rng.choice([-1, 1], half)
-    Kh = rng.integers(-6, 7, (half, D)).astype(np.float32)
-    Kh[:, 0] = 7 * rng.choice([-1, 1], half)
+    Qh = rng.integers(-qmax + 1, qmax, (half, D)).astype(np.float32)
+    Qh[np.arange(half), rng.integers(0, D, half)] = qmax * rng.choice([-1, 1], half)
+    Kh = rng.integers(-qmax + 1, qmax, (half, D)).astype(np.float32)
+    Kh[:, 0] = qmax * rng.choice([-1, 1], half)
     Q = np.concatenate([Qh, -Qh])
     K = np.concatenate([Kh, -Kh])
     grid = np.array([0, 0.5, 1, 1.5, 2, 2.5, 3, 3.5], np.float32)
@@ -106,15 +107,17 @@ def _lossless_inputs(N, D, seed):
 
 @pytest.mark.parametrize("N,D", [(2, 64), (18, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_mirror_equals_plain_attention_on_lossless_inputs(oracle_lib, N, D, causal):
-    Q, K, V = _lossless_inputs(N, D, seed=N + D)
+@pytest.mark.parametrize("qk_bits", [4, 8])
+def test_mirror_equals_plain_attention_on_lossless_inputs(oracle_lib, N, D, causal, qk_bits):
+    qmax = 7 if qk_bits == 4 else 127
+    Q, K, V = _lossless_inputs(N, D, seed=N + D, qmax=qmax)
     q, k, v = _bits(Q), _bits(K), _bits(V)
-    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=qk_bits)
     # the quantization really is lossless
     assert np.all(z.q_scale == 1) and np.all(z.k_scale[z.k_scale != 0] == 1) and not np.any(z.delta_s)
     assert np.array_equal(z.q_codes.astype(np.float32), Q) and np.array_equal(z.k_codes.astype(np.float32), K)
     assert np.all(z.v_scale == np.float32(1 / 128))
-    scale = 0.003  # keeps |scores| below ~20 so fp32 score rounding stays near 1e-6
+    scale = 0.003 * (7 / qmax) ** 2  # keeps |scores| below ~20 so fp32 score rounding stays near 1e-6
     ref = _brute_force(Q, K, V, causal, scale).reshape(-1, D)
     Om, _, _ = oracle_lib.attn_mirror(z, causal, scale, quant_p=False)
     assert np.abs(Om - ref).max() <= 5e-6 * np.abs(V).max()

@@ -75,14 +75,16 @@ def _random_inputs(N, D, seed, dtype="bf16", B=1, H=2, **kw):
 
 
 @pytest.mark.parametrize("N,D", [(1, 64), (17, 64), (100, 128), (129, 64), (300, 128)])
-def test_quantizer_properties(oracle_lib, N, D):
+@pytest.mark.parametrize("qk_bits", [4, 8])
+def test_quantizer_properties(oracle_lib, N, D, qk_bits):
+    qmax = 7 if qk_bits == 4 else 127
     q, k, v = _random_inputs(N, D, seed=N + D, k_offset_std=3.0, outlier_channels=2, outlier_scale=10.0)
-    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=qk_bits)
     Q = oracle_lib.decode_input(q, 1)
     K = oracle_lib.decode_input(k, 1)
     V = oracle_lib.decode_input(v, 1)
     for codes in (z.q_codes, z.k_codes):
-        assert codes.min() >= -7 and codes.max() <= 7
+        assert codes.min() >= -qmax and codes.max() <= qmax
     # smoothed values rebuilt from the reported means (fp32 subtraction)
     qb = np.arange(N) // 128
     gQ = Q - z.q_mean[:, :, qb, :]
@@ -90,9 +92,9 @@ def test_quantizer_properties(oracle_lib, N, D):
     # Q: reconstruction error at most half a step, and the largest |value| maps to +-7
     dq = z.q_scale[..., None]
     assert np.all(np.abs(gQ - z.q_codes * dq) <= dq * 0.5 * (1 + 2 ** -20) + 1e-30)
-    tok_has7 = (np.abs(z.q_codes) == 7).any(-1) | (z.q_scale == 0)
-    assert tok_has7.all()
-    assert np.array_equal(z.q_scale, np.abs(gQ).max(-1) / np.float32(7))
+    tok_has_max = (np.abs(z.q_codes) == qmax).any(-1) | (z.q_scale == 0)
+    assert tok_has_max.all()
+    assert np.array_equal(z.q_scale, np.abs(gQ).max(-1) / np.float32(qmax))
     # K: per fragment group
     j = np.arange(N)
     grp = 2 * (j // 32) + ((j % 32) // 4) % 2
