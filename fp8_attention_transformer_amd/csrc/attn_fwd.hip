@@ -6,25 +6,24 @@
 // into an FP32 running buffer).
 //
 // gfx950 mapping.  A workgroup owns one 128-query block of one head (4 waves x
-// 32 queries).  Scores are built transposed, S^T = K * Q^T, with the INT8
-// matrix core (v_mfma_i32_32x32x32_i8): every lane then holds one query and 16
-// keys of each 32-key tile, so the dequantization factor is one scalar per
-// lane and tile (per-token Q scale times the scale of the lane's 16-key K
-// group) and row reductions of the online softmax stay inside a lane plus one
-// exchange with the partner lane 32 away.  P~ stays in registers: converted to
-// e4m3 it is directly the B operand of the FP8 matrix core
-// (v_mfma_f32_32x32x64_f8f6f4) computing O^T += V^T P~^T, with V stored by the
-// prepass in the matching permuted channel-major layout.
+// 32 queries).  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
+// core tiles: every lane then holds one query and 16 keys of each 32-key tile,
+// so the dequantization factor is one scalar per lane and tile (per-token Q
+// scale times the scale of the lane's 16-key K group) and row reductions of
+// the online softmax stay inside a lane plus one exchange with the partner
+// lane 32 away.  P~ stays in registers: converted to e4m3 it is directly the
+// B operand of the FP8 matrix core (v_mfma_f32_32x32x64_f8f6f4) computing
+// O^T += V^T P~^T, with V stored by the prepass in the matching permuted
+// channel-major layout.
 //
-// INT4 on the INT8 matrix core without unpacking.  A packed byte holds the
-// pair (c_even, c_odd) as 16*c_odd + c_even + 8.  Read as int8, byte b is
-// 16*c_odd + u with u = c_even + 8; masked with 0xF0 it is 16*c_odd.  With the
-// query operands x = 16*q_even and y = q_odd - 16*q_even (both within int8),
-//   raw*x + masked*y = 16*(c_odd*q_odd + c_even*q_even) + 128*q_even,
-// so two MFMAs over the raw and masked K bytes give 16 times the integer dot
-// product plus a per-query constant 128*sum(q_even).  That constant is removed
-// by starting the accumulation from a register block holding -128*sum(q_even)
-// (MFMA C operand distinct from D), so each K byte costs a quarter of an AND.
+// INT4 codes on the FP6 matrix core.  gfx950 has no INT4 matrix instruction,
+// but every integer in [-7, 7] is exact in FP6 e2m3, and the f8f6f4
+// instruction with FP6 operands (format 2) runs at twice the FP8 rate and sums
+// the integer products exactly in fp32 (|dot| <= 49*128 < 2^24).  The prepass
+// stores the codes as FP6 in the lane order of the instruction, so a lane's
+// operand is one contiguous chunk and the accumulator is the dot product as a
+// float, with no unpacking and no conversion.  INT8 codes use the INT8 matrix
+// core (v_mfma_i32_32x32x32_i8).
 #include "sage_internal.h"
 #include "sage_device.h"
 
@@ -55,84 +54,89 @@ __device__ __forceinline__ float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Code layout per query/key row: INT4 (BITS 4) packs channel pairs into bytes
-// (see the pair format above), INT8 (BITS 8) stores one int8 code per
-// channel.  Either way a lane feeds the matrix core 16-byte chunks: chunk
-// 2m + h of the row for matrix step m and half-wave h.
+// Code layout and operand shapes.  BITS 4: FP6 tiles of lane chunks (see
+// fp6_chunk_offset), D/64 FP6 instructions per 32x32 tile.  BITS 8: int8 rows
+// of D bytes; a lane feeds 16-byte chunks 2m + h of its row (matrix step m,
+// half-wave h), D/32 INT8 instructions per tile.
 template <int D, int BITS>
-struct QKCfg {
-  static constexpr int KROW = D * BITS / 8;   // code bytes per row
-  static constexpr int NCH = KROW / 32;       // 16-byte chunks per lane per 32-key tile
-  static constexpr int CPR = KROW / 16;       // 16-byte chunks per row
+struct QKCfg;
+template <int D>
+struct QKCfg<D, 4> {
+  static constexpr int LS = fp6_lane_bytes(D);   // bytes per lane chunk
+  static constexpr int ROWB = 2 * LS;            // bytes per row (average)
+  static constexpr int NM = D / 64;              // FP6 instructions per tile
+};
+template <int D>
+struct QKCfg<D, 8> {
+  static constexpr int ROWB = D;
+  static constexpr int NCH = D / 32;   // 16-byte chunks per lane per tile
+  static constexpr int CPR = D / 16;   // 16-byte chunks per row
 };
 
 template <int D, int BITS>
-struct QOperand {
-  static constexpr int NCH = QKCfg<D, BITS>::NCH;
-  v4i x[NCH];
-  v4i y[BITS == 4 ? NCH : 1];
-  v16i cinit;
+struct QOperand;
+template <int D>
+struct QOperand<D, 4> {
+  v8i x[D / 64];   // six dwords of FP6 fields used per instruction
+};
+template <int D>
+struct QOperand<D, 8> {
+  v4i x[D / 32];
 };
 
-// Build the query operands for lane (query row `qrow` in padded coordinates,
-// half h) from its codes.  INT4: x/y operands of the pair identity and the
-// correction -128*sum(q_even) (both lanes of a query end with the same one);
-// INT8: the raw codes.  `start` is added to every accumulator.
-template <int D, int BITS>
-__device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_codes_head, int qrow, int h, int start,
-                                               QOperand<D, BITS>& op) {
-  constexpr int KROW = QKCfg<D, BITS>::KROW;
-  int corr = 0;
-#pragma unroll
-  for (int m = 0; m < QOperand<D, BITS>::NCH; m++) {
-    const v4i raw = *(const v4i*)(q_codes_head + (size_t)qrow * KROW + m * 32 + h * 16);
-    if constexpr (BITS == 8) {
-      op.x[m] = raw;
-    } else {
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        uint32_t xw = 0, yw = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; bb++) {
-          const int v = (int)(int8_t)((uint32_t)raw[w] >> (8 * bb));
-          const int ce = (v & 15) - 8;
-          const int co = v >> 4;
-          corr += ce;
-          xw |= ((uint32_t)(16 * ce) & 0xFFu) << (8 * bb);
-          yw |= ((uint32_t)(co - 16 * ce) & 0xFFu) << (8 * bb);
-        }
-        op.x[m][w] = (int)xw;
-        op.y[m][w] = (int)yw;
-      }
-    }
+// The FP6 operands of one lane chunk (`ci` = its chunk index in the tile).
+template <int D>
+__device__ __forceinline__ void load_fp6_chunk(const uint8_t* chunk, int ci, v8i* a) {
+  if constexpr (D == 128) {
+    const v4i u0 = *(const v4i*)chunk, u1 = *(const v4i*)(chunk + 16), u2 = *(const v4i*)(chunk + 32);
+    a[0] = (v8i){u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], 0, 0};
+    a[1] = (v8i){u1[2], u1[3], u2[0], u2[1], u2[2], u2[3], 0, 0};
+  } else {
+    const v4i lo = *(const v4i*)(chunk + fp6_half_offset(ci, 0));
+    const v4i hi = *(const v4i*)(chunk + fp6_half_offset(ci, 1));
+    a[0] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
   }
-  if constexpr (BITS == 4) corr += __shfl_xor(corr, 32);
-#pragma unroll
-  for (int r = 0; r < 16; r++) op.cinit[r] = start - 128 * corr;
 }
 
-// Accumulators start at the bit pattern of 1.5 * 2^23.  The integer sum
-// (16*acc for INT4, acc for INT8) stays below 2^22 in magnitude, so the int32
-// result read as fp32 is exactly 1.5 * 2^23 + that sum, and one exact
-// subtraction yields it as a float (cheaper than an int->float conversion).
+// Query operands of this lane (query row `qrow` of the head in padded
+// coordinates, half h).
+template <int D, int BITS>
+__device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_codes_head, int qrow, int h,
+                                               QOperand<D, BITS>& op) {
+  if constexpr (BITS == 4) {
+    load_fp6_chunk<D>(q_codes_head + fp6_chunk_offset(D, qrow, h), 32 * h + (qrow & 31), op.x);
+  } else {
+#pragma unroll
+    for (int m = 0; m < D / 32; m++) op.x[m] = *(const v4i*)(q_codes_head + (size_t)qrow * D + m * 32 + h * 16);
+  }
+}
+
+// INT8 accumulators start at the bit pattern of 1.5 * 2^23.  |dot| <= 127^2 *
+// 128 < 2^22, so the int32 result read as fp32 is exactly 1.5 * 2^23 + dot,
+// and one exact subtraction yields it as a float.
 constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
-// One 32-key tile of S^T: `a[m]` holds this lane's 16 K-code bytes (key row
-// lane%32, half h) for chunk m.  Returns 16*dot (INT4) or dot (INT8) plus the
-// start value.
-template <int D, int BITS>
-__device__ __forceinline__ v16i qk_tile(const v4i* a, const QOperand<D, BITS>& op) {
-  v16i s = op.cinit;
+// One 32-key tile of S^T as floats holding the exact integer dot products.
+// FP6: a[m] = this lane's K chunk operands; INT8: a[m] = its 16-byte chunks.
+template <int D>
+__device__ __forceinline__ v16f qk_tile_fp6(const v8i* a, const QOperand<D, 4>& op) {
+  v16f s = {};
 #pragma unroll
-  for (int m = 0; m < QOperand<D, BITS>::NCH; m++) {
-    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[m], op.x[m], s, 0, 0, 0);
-    if constexpr (BITS == 4) {
-      const v4i hi = a[m] & (int)0xF0F0F0F0;
-      s = __builtin_amdgcn_mfma_i32_32x32x32_i8(hi, op.y[m], s, 0, 0, 0);
-    }
-  }
+  for (int m = 0; m < D / 64; m++) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[m], op.x[m], s, 2, 2, 0, 0, 0, 0);
   return s;
+}
+template <int D>
+__device__ __forceinline__ v16f qk_tile_i8(const v4i* a, const QOperand<D, 8>& op) {
+  v16i s;
+#pragma unroll
+  for (int r = 0; r < 16; r++) s[r] = kMagicBits;
+#pragma unroll
+  for (int m = 0; m < D / 32; m++) s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[m], op.x[m], s, 0, 0, 0);
+  v16f f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) f[r] = __int_as_float(s[r]) - kMagic;
+  return f;
 }
 
 __device__ __forceinline__ void store_out(void* o, size_t idx, float val, int out_dtype) {
@@ -160,7 +164,9 @@ __device__ __forceinline__ int xcd_logical_id(int pid, int nwg) {
 
 // LDS layouts are XOR-swizzled in 16-byte chunks so that the 16 lanes served
 // together by one ds_read_b128 hit distinct banks.
-//   K tile: 128 rows (keys) x KROW bytes; chunk c of row r at c ^ kswz(r).
+//   K tile (INT8): 128 rows (keys) x D bytes; chunk c of row r at c ^ kswz(r).
+//   K tile (FP6): copied as stored; lane chunks of 48 bytes (D = 128) or with
+//   swapped halves (D = 64) already spread 16 lanes over all banks.
 //   V tile: D rows (channels) x 128 bytes; chunk c of row r at c ^ ((r>>1)&7).
 template <int CPR>
 __device__ __forceinline__ int kswz(int r) {
@@ -177,15 +183,22 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 template <int D, int BITS>
 __device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, const uint8_t* kblk, const uint8_t* vblk,
                                                int t, int wave, int lane) {
-  constexpr int KROW = QKCfg<D, BITS>::KROW, KCPR = KROW / 16;
-  constexpr int KCH = kBK * KROW / 16 / 256, VCH = D * kBK / 16 / 256;
-  const uint8_t* gk = kblk + (size_t)t * kBK * KROW;
+  constexpr int ROWB = QKCfg<D, BITS>::ROWB;
+  constexpr int KCH = kBK * ROWB / 16 / 256, VCH = D * kBK / 16 / 256;
+  static_assert(KCH * 16 * 256 == kBK * ROWB, "whole copy rounds");
+  const uint8_t* gk = kblk + (size_t)t * kBK * ROWB;
   const uint8_t* gv = vblk + (size_t)t * D * kBK;
 #pragma unroll
   for (int i = 0; i < KCH; i++) {
     const int wbase = 256 * i + 64 * wave;
-    const int e = wbase + lane, r = e / KCPR, c = (e % KCPR) ^ kswz<KCPR>(r);
-    __builtin_amdgcn_global_load_lds((const void*)(gk + r * KROW + 16 * c), (lds_ptr_t)(sK + 16 * wbase), 16, 0, 0);
+    const int e = wbase + lane;
+    int src = 16 * e;
+    if constexpr (BITS == 8) {
+      constexpr int CPR = QKCfg<D, 8>::CPR;
+      const int r = e / CPR, c = (e % CPR) ^ kswz<CPR>(r);
+      src = r * ROWB + 16 * c;
+    }
+    __builtin_amdgcn_global_load_lds((const void*)(gk + src), (lds_ptr_t)(sK + 16 * wbase), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < VCH; i++) {
@@ -208,19 +221,26 @@ template <int D, int BITS, bool CAUSAL>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
                                            int t, int qb, int qrow, int n, int h, const Dims& d) {
-  constexpr int KROW = QKCfg<D, BITS>::KROW, NCH = QKCfg<D, BITS>::NCH, CPR = QKCfg<D, BITS>::CPR;
   constexpr int NDT = D / 32;
-  constexpr float kAccScale = BITS == 4 ? 0.0625f : 1.0f;   // INT4 accumulators hold 16*dot
-  // ---- S^T for 4 tiles of 32 keys (values 1.5*2^23 + (16*)acc as fp32 bits)
-  v16i S[4];
+  // ---- S^T for 4 tiles of 32 keys (exact integer dot products as floats)
+  v16f S[4];
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
-    const int row = 32 * T + n;
-    v4i a[NCH];
+    if constexpr (BITS == 4) {
+      constexpr int LS = QKCfg<D, 4>::LS;
+      const int ci = 32 * h + n;
+      v8i a[D / 64];
+      load_fp6_chunk<D>(cK + (64 * T + ci) * LS, ci, a);
+      S[T] = qk_tile_fp6<D>(a, qop);
+    } else {
+      constexpr int NCH = QKCfg<D, 8>::NCH, CPR = QKCfg<D, 8>::CPR;
+      const int row = 32 * T + n;
+      v4i a[NCH];
 #pragma unroll
-    for (int m = 0; m < NCH; m++) a[m] = *(const v4i*)(cK + row * KROW + 16 * ((2 * m + h) ^ kswz<CPR>(row)));
-    S[T] = qk_tile<D, BITS>(a, qop);
+      for (int m = 0; m < NCH; m++) a[m] = *(const v4i*)(cK + row * D + 16 * ((2 * m + h) ^ kswz<CPR>(row)));
+      S[T] = qk_tile_i8<D>(a, qop);
+    }
   }
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   // ---- dequantize into the log2 domain, mask, block max
@@ -230,12 +250,11 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
-    const float c = ((dq * cKS[2 * T + h]) * ks) * kAccScale;
+    const float c = (dq * cKS[2 * T + h]) * ks;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-      const float f16acc = __int_as_float(S[T][r]) - kMagic;
-      s2[T][r] = __builtin_fmaf(f16acc, c, cDS[key]);
+      s2[T][r] = __builtin_fmaf(S[T][r], c, cDS[key]);
     }
     if (need_mask) {
 #pragma unroll
@@ -310,15 +329,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int D, int BITS, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
-  constexpr int KROW = QKCfg<D, BITS>::KROW;
+  constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int NDT = D / 32;
   constexpr int S = SAGE_STAGES;
   // vector-memory ops one block's staging issues per wave: K and V chunks via
   // direct-to-LDS copies, plus the compensation and K-scale loads
-  constexpr int VM_PER_BLOCK = kBK * KROW / 16 / 256 + D * kBK / 16 / 256 + 2;
+  constexpr int VM_PER_BLOCK = kBK * ROWB / 16 / 256 + D * kBK / 16 / 256 + 2;
   // LDS buffers as separate arrays, so the compiler can tell the block being
   // read from the blocks being filled by the asynchronous copies.
-  __shared__ __align__(16) uint8_t sK0[kBK * KROW], sK1[kBK * KROW], sK2[S > 2 ? kBK * KROW : 16];
+  __shared__ __align__(16) uint8_t sK0[kBK * ROWB], sK1[kBK * ROWB], sK2[S > 2 ? kBK * ROWB : 16];
   __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK], sV2[S > 2 ? D * kBK : 16];
   __shared__ float sDS0[kBK], sDS1[kBK], sDS2[S > 2 ? kBK : 1];
   __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup], sKS2[S > 2 ? kBK / kKGroup : 1];
@@ -340,7 +359,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const size_t hrowp = (size_t)bh * d.NP;
 
   const float* dsrow = b.delta_s + ((size_t)bh * d.NQB + qb) * d.NP;
-  const uint8_t* kblk = b.k_codes + hrowp * KROW;
+  const uint8_t* kblk = b.k_codes + hrowp * ROWB;
   const uint8_t* vblk = b.v_codes + (size_t)bh * d.NQB * D * kBK;
   const float* kscl = b.k_scale + hrowp / kKGroup;
   const int tend = CAUSAL ? qb + 1 : d.NQB;
@@ -363,7 +382,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   if (S > 2 && tend > 1) issue(1, 1);
 
   QOperand<D, BITS> qop;
-  load_q_operand<D, BITS>(b.q_codes + hrowp * KROW, qrow, h, kMagicBits, qop);
+  load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
   const float dq = b.q_scale[hrowp + qrow];
 
   AttnState<D, CAUSAL> as;
@@ -413,23 +432,31 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 template <int D, int BITS>
 __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, int q0, int k0, int nq, int nk,
                                                       int32_t* __restrict__ out) {
-  constexpr int KROW = QKCfg<D, BITS>::KROW, NCH = QKCfg<D, BITS>::NCH;
+  constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
   const size_t hrowp = (size_t)bh * d.NP;
   const int qloc = blockIdx.x * 32 + n;
   const int kbase = blockIdx.y * 32;
   const int qrow = min(q0 + qloc, d.NP - 1);
   QOperand<D, BITS> qop;
-  load_q_operand<D, BITS>(b.q_codes + hrowp * KROW, qrow, h, 0, qop);
+  load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
   const int krow = min(k0 + kbase + n, d.NP - 1);
-  v4i a[NCH];
+  const uint8_t* khead = b.k_codes + hrowp * ROWB;
+  v16f s;
+  if constexpr (BITS == 4) {
+    v8i a[D / 64];
+    load_fp6_chunk<D>(khead + fp6_chunk_offset(D, krow, h), 32 * h + (krow & 31), a);
+    s = qk_tile_fp6<D>(a, qop);
+  } else {
+    v4i a[D / 32];
 #pragma unroll
-  for (int m = 0; m < NCH; m++) a[m] = *(const v4i*)(b.k_codes + (hrowp + krow) * KROW + m * 32 + h * 16);
-  const v16i s = qk_tile<D, BITS>(a, qop);
+    for (int m = 0; m < D / 32; m++) a[m] = *(const v4i*)(khead + (size_t)krow * D + m * 32 + h * 16);
+    s = qk_tile_i8<D>(a, qop);
+  }
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int kloc = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (qloc < nq && kloc < nk) out[(size_t)qloc * nk + kloc] = BITS == 4 ? s[r] >> 4 : s[r];
+    if (qloc < nq && kloc < nk) out[(size_t)qloc * nk + kloc] = (int32_t)s[r];
   }
 }
 

@@ -209,7 +209,6 @@ template <int IN, int D, int BITS>
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
   constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
-  constexpr int KROW = D * BITS / 8;     // code bytes per row
   __shared__ __align__(16) uint16_t sV[kBK * D];
   const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -266,16 +265,25 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       int cq[16];
       int_codes<16, BITS>(g, dq, cq);
       if constexpr (BITS == 4) {
-        uint32_t w0 = 0, w1 = 0;
+        // FP6 tile layout: this lane's 16 channels are fields 16*(sub&1)..+15
+        // of group c0/64 in half (c0/32)&1 of the row's chunk
+        uint32_t w[3];
+        pack_fp6<16>(cq, w);
+        const int hq = (c0 >> 5) & 1, odd = sub & 1;
+        uint32_t* chunk = (uint32_t*)(b.q_codes + fp6_chunk_offset(D, hrowp + i, hq));
+        if constexpr (D == 128) {
+          const int d0 = 6 * (c0 >> 6) + 3 * odd;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          w0 |= pack_pair(cq[2 * e], cq[2 * e + 1]) << (8 * e);
-          w1 |= pack_pair(cq[8 + 2 * e], cq[8 + 2 * e + 1]) << (8 * e);
+          for (int k2 = 0; k2 < 3; k2++) chunk[d0 + k2] = w[k2];
+        } else {
+          const int rot = 4 * (((32 * hq + (i & 31)) >> 3) & 1);   // swapped halves
+#pragma unroll
+          for (int k2 = 0; k2 < 3; k2++) chunk[(3 * odd + k2 + rot) & 7] = w[k2];
+          if (odd) {
+            chunk[(6 + rot) & 7] = 0u;
+            chunk[(7 + rot) & 7] = 0u;
+          }
         }
-        uint2 pk;
-        pk.x = w0;
-        pk.y = w1;
-        *(uint2*)(b.q_codes + (hrowp + i) * KROW + 8 * sub) = pk;
       } else {
         v4i pk;
 #pragma unroll
@@ -285,7 +293,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
           for (int e = 0; e < 4; e++) word |= ((uint32_t)cq[4 * w + e] & 0xFFu) << (8 * e);
           pk[w] = (int)word;
         }
-        *(v4i*)(b.q_codes + (hrowp + i) * KROW + 16 * sub) = pk;
+        *(v4i*)(b.q_codes + (hrowp + i) * D + 16 * sub) = pk;
       }
       if (sub == 0) b.q_scale[hrowp + i] = dq;
     }
@@ -321,15 +329,26 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       int ck[32];
       int_codes<32, BITS>(g, dk, ck);
       if constexpr (BITS == 4) {
-        v4i pk;
+        // FP6 tile layout: this lane's 32 channels are group sub/2 of half sub&1
+        uint32_t w[6];
+        pack_fp6<32>(ck, w);
+        const int hk = sub & 1;
+        uint8_t* chunk = b.k_codes + fp6_chunk_offset(D, hrowp + j, hk);
+        if constexpr (D == 128) {
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int e = 0; e < 4; e++) word |= pack_pair(ck[8 * w + 2 * e], ck[8 * w + 2 * e + 1]) << (8 * e);
-          pk[w] = (int)word;
+          for (int k2 = 0; k2 < 3; k2++) {
+            uint2 u;
+            u.x = w[2 * k2];
+            u.y = w[2 * k2 + 1];
+            *(uint2*)(chunk + 24 * (sub >> 1) + 8 * k2) = u;
+          }
+        } else {
+          const int ci = 32 * hk + (j & 31);
+          const v4i lo = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+          const v4i hi = {(int)w[4], (int)w[5], 0, 0};
+          *(v4i*)(chunk + fp6_half_offset(ci, 0)) = lo;
+          *(v4i*)(chunk + fp6_half_offset(ci, 1)) = hi;
         }
-        *(v4i*)(b.k_codes + (hrowp + j) * KROW + 16 * sub) = pk;
       } else {
 #pragma unroll
         for (int half = 0; half < 2; half++) {
@@ -341,7 +360,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
             for (int e = 0; e < 4; e++) word |= ((uint32_t)ck[16 * half + 4 * w + e] & 0xFFu) << (8 * e);
             pk[w] = (int)word;
           }
-          *(v4i*)(b.k_codes + (hrowp + j) * KROW + 32 * sub + 16 * half) = pk;
+          *(v4i*)(b.k_codes + (hrowp + j) * D + 32 * sub + 16 * half) = pk;
         }
       }
       if ((lane % LPG) == 0) b.k_scale[hrowp / kKGroup + (i0 / kKGroup) + grp] = dk;

@@ -18,6 +18,27 @@ constexpr int kContractVersion = 1;
 enum InDtype { kF16 = 0, kBF16 = 1 };
 enum OutDtype { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
 
+// Q/K code layout for 4-bit codes.  Every integer in [-7, 7] is exact in OCP
+// FP6 e2m3 (sign, 2 exponent bits with bias 1, 3 mantissa bits), so the codes
+// are stored as FP6 values and multiplied on the FP6 matrix core, which forms
+// the integer dot products exactly in fp32 (|sum| <= 49*128 < 2^24).
+// Rows (tokens) are grouped in tiles of 32.  A tile holds 64 lane chunks of
+// fp6_lane_bytes(D) bytes: the chunk of row r and half h is chunk 32h + r%32,
+// the data one lane of the 32x32x64 matrix-core instruction reads.  It holds,
+// for m < D/64, a 24-byte group with channels 64m + 32h + i (i < 32) as 6-bit
+// fields at bit 6i (little endian).  D = 64: a chunk is 24 data bytes and 8
+// zero bytes, and its two 16-byte halves are stored swapped when bit 3 of the
+// chunk index is set (so 16 neighbouring lanes reading their first halves hit
+// distinct LDS banks).  Bytes per row on average: 2 * fp6_lane_bytes(D).
+__host__ __device__ constexpr int fp6_lane_bytes(int D) { return D == 128 ? 48 : 32; }
+__host__ __device__ inline size_t fp6_chunk_offset(int D, size_t row, int h) {
+  return (row >> 5) * 64 * (size_t)fp6_lane_bytes(D) + (size_t)(32 * h + (int)(row & 31)) * fp6_lane_bytes(D);
+}
+// Byte offset inside a D = 64 chunk of its 16-byte half `half` (0: dwords 0-3).
+__host__ __device__ inline int fp6_half_offset(int chunk_index, int half) {
+  return 16 * (half ^ ((chunk_index >> 3) & 1));
+}
+
 struct Dims {
   int B, H, N, D;
   int NP;    // N rounded up to a multiple of 128
@@ -28,8 +49,8 @@ struct Dims {
 
 // Device buffers written by the prepass and read by the attention kernel.
 struct Bufs {
-  uint8_t* q_codes;   // [B,H,NP,D*QB/8]: packed INT4 pairs or INT8 codes
-  uint8_t* k_codes;   // [B,H,NP,D*QB/8]
+  uint8_t* q_codes;   // QB 4: FP6 tiles (above), QB 8: int8 [B,H,NP,D]
+  uint8_t* k_codes;   // same layout as q_codes
   float* q_scale;     // [B,H,NP]
   float* k_scale;     // [B,H,NP/16]
   float* q_mean;      // [B,H,NQB,D]

@@ -59,13 +59,19 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
  * sage_attn_fwd).  NP = N rounded up to a multiple of 128, NQB = NP / 128.
  * Rows or keys at index >= N are padding: codes 0, scales 0, V bytes 0.
  *
- *  q_codes, k_codes  uint8 [B,H,NP,D]    (space for 8-bit codes; row r starts
- *                    at byte r*D*qk_bits/8, i.e. rows are packed densely)
- *                    qk_bits 4: INT4 codes in [-7,7], two per byte: byte b
- *                    of a row holds channel 2b (c_even) and 2b+1 (c_odd) as
- *                    the signed value 16*c_odd + c_even + 8, so
- *                    c_even = (byte & 15) - 8 and c_odd = (int8)byte >> 4.
- *                    qk_bits 8: one int8 code in [-127,127] per channel.
+ *  q_codes, k_codes  uint8, B*H*NP*D bytes reserved (the INT8 size); a head
+ *                    starts at byte (b*H + h) * NP * RB with RB the row bytes
+ *                    qk_bits 8: int8 [NP][D], codes in [-127,127], RB = D.
+ *                    qk_bits 4: INT4 codes in [-7,7] stored as OCP FP6 e2m3
+ *                    bit patterns (magnitudes 0..7 -> 0,8,16,20,24,26,28,30;
+ *                    sign in bit 5), grouped in tiles of 32 rows.  Tile t of
+ *                    a head is 64 chunks of LB bytes (LB = 48 for D = 128, 32
+ *                    for D = 64; RB = 2*LB): chunk 32*h + (r % 32) of tile
+ *                    r / 32 holds, for m < D/64, a 24-byte group with the
+ *                    codes of row r, channels 64m + 32h + i (i < 32), as
+ *                    6-bit fields starting at bit 6i (little endian).  D = 64:
+ *                    bytes 24-31 of a chunk are zero, and the two 16-byte
+ *                    halves of chunk c are stored swapped when (c >> 3) & 1.
  *  q_scale           fp32  [B,H,NP]      one scale per token (amax/7 or
  *                    amax/127)
  *  k_scale           fp32  [B,H,NP/16]   one scale per 16-key group; in a
@@ -133,7 +139,7 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
 
 /*
  * Attention forward: O = SageAttention2(Q, K, V), i.e. the prepass above
- * followed by the fused kernel (INT4 QK^T on the INT8 matrix core,
+ * followed by the fused kernel (INT4 QK^T on the FP6 matrix core, exact,
  * dequantization with the compensation term, online softmax over 128-key
  * blocks, FP8 P~ and V on the FP8 matrix core with two-level accumulation).
  *  q, k, v   device [B,H,N,D] of in_dtype (SAGE_F16 / SAGE_BF16)

@@ -35,17 +35,69 @@ def vperm_keys() -> np.ndarray:
     return 64 * (p // 64) + 32 * (s // 16) + 8 * ((s % 16) // 4) + 4 * ((p % 64) // 32) + s % 4
 
 
-def unpack_codes(packed: np.ndarray, N: int, qk_bits: int = 4) -> np.ndarray:
-    """[BH, NP, D*qk_bits/8] code rows -> int8 codes [BH, N, D] (INT4: packed pairs; INT8: one byte each)."""
+FP6_MAG = np.array([0, 8, 16, 20, 24, 26, 28, 30], np.uint8)   # e2m3 patterns of 0..7
+
+
+def fp6_lane_bytes(D: int) -> int:
+    return 48 if D == 128 else 32
+
+
+def fp6_row_bytes(D: int) -> int:
+    return 2 * fp6_lane_bytes(D)
+
+
+def _fp6_value(v: np.ndarray) -> np.ndarray:
+    """FP6 e2m3 bit patterns -> float values."""
+    v = v.astype(np.int64)
+    e, m = (v >> 3) & 3, v & 7
+    mag = np.where(e == 0, m / 8.0, 2.0 ** (e - 1) * (1.0 + m / 8.0))
+    return np.where(v & 32, -mag, mag)
+
+
+def fp6_tiles_to_codes(raw: np.ndarray, D: int) -> np.ndarray:
+    """[BH, NP * row_bytes] FP6 tile layout (include/sage.h) -> int8 codes [BH, NP, D]."""
+    LS = fp6_lane_bytes(D)
+    BH = raw.shape[0]
+    ch = raw.reshape(BH, -1, 64, LS).copy()          # [BH, tile, chunk, bytes]
+    if D == 64:                                       # undo the swapped halves
+        sw = ((np.arange(64) >> 3) & 1).astype(bool)
+        ch[:, :, sw] = np.concatenate([ch[:, :, sw, 16:], ch[:, :, sw, :16]], axis=-1)
+    groups = ch[..., :24 * (D // 64)].reshape(BH, ch.shape[1], 64, D // 64, 24)
+    bits = np.unpackbits(groups, axis=-1, bitorder="little").reshape(groups.shape[:-1] + (32, 6))
+    fields = (bits.astype(np.int64) << np.arange(6)).sum(-1)          # [BH, tile, chunk, m, i]
+    vals = _fp6_value(fields)
+    assert np.all(vals == np.rint(vals)) and np.all(np.abs(vals) <= 7), "FP6 fields are not INT4 codes"
+    T = ch.shape[1]
+    out = np.empty((BH, T, 32, D), np.int8)
+    for h in range(2):
+        for m in range(D // 64):
+            out[:, :, :, 64 * m + 32 * h: 64 * m + 32 * h + 32] = vals[:, :, 32 * h:32 * h + 32, m, :]
+    return out.reshape(BH, T * 32, D)
+
+
+def codes_to_fp6_tiles(codes: np.ndarray, D: int) -> np.ndarray:
+    """Inverse of fp6_tiles_to_codes: int8 codes [BH, NP, D] -> [BH, NP * row_bytes] bytes."""
+    BH, NP, _ = codes.shape
+    LS = fp6_lane_bytes(D)
+    c = codes.astype(np.int64).reshape(BH, NP // 32, 32, D)
+    pat = FP6_MAG[np.abs(c)].astype(np.int64) | np.where(c < 0, 32, 0)
+    ch = np.zeros((BH, NP // 32, 64, LS), np.uint8)
+    for h in range(2):
+        for m in range(D // 64):
+            f = pat[:, :, :, 64 * m + 32 * h: 64 * m + 32 * h + 32]          # [BH, T, 32 rows, 32 fields]
+            bits = ((f[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(f.shape[:-1] + (192,))
+            ch[:, :, 32 * h:32 * h + 32, 24 * m:24 * m + 24] = np.packbits(bits, axis=-1, bitorder="little")
+    if D == 64:
+        sw = ((np.arange(64) >> 3) & 1).astype(bool)
+        ch[:, :, sw] = np.concatenate([ch[:, :, sw, 16:], ch[:, :, sw, :16]], axis=-1)
+    return ch.reshape(BH, -1)
+
+
+def unpack_codes(packed: np.ndarray, N: int, D: int, qk_bits: int = 4) -> np.ndarray:
+    """Stored code rows -> int8 codes [BH, N, D] (INT4: FP6 tiles; INT8: one byte per channel)."""
     if qk_bits == 8:
-        return packed.view(np.int8)[:, :N].copy()
-    v = packed.view(np.int8).astype(np.int16)[:, :N]
-    even = (v & 15) - 8
-    odd = v >> 4
-    out = np.empty(v.shape[:-1] + (v.shape[-1] * 2,), np.int8)
-    out[..., 0::2] = even
-    out[..., 1::2] = odd
-    return out
+        return packed.reshape(packed.shape[0], -1, D).view(np.int8)[:, :N].copy()
+    return fp6_tiles_to_codes(packed, D)[:, :N]
 
 
 def unpermute_v(vcodes: np.ndarray, BH: int, NQB: int, D: int, N: int) -> np.ndarray:
@@ -76,12 +128,13 @@ class Readback:
 
         self.N, self.NP, self.NQB, self.D, self.BH = N, NP, NQB, D, BH
         self.qk_bits = qk_bits
-        krow = D * qk_bits // 8
-        self.q_codes_packed = arr(qb.q_codes, BH * NP * krow, np.uint8, (BH, NP, krow))
-        self.k_codes_packed = arr(qb.k_codes, BH * NP * krow, np.uint8, (BH, NP, krow))
-        self.zero_code_byte = 8 if qk_bits == 4 else 0
-        self.q_codes = unpack_codes(self.q_codes_packed, N, qk_bits)
-        self.k_codes = unpack_codes(self.k_codes_packed, N, qk_bits)
+        rowb = fp6_row_bytes(D) if qk_bits == 4 else D
+        self.q_codes_raw = arr(qb.q_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
+        self.k_codes_raw = arr(qb.k_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
+        self.q_codes_all = unpack_codes(self.q_codes_raw, NP, D, qk_bits)   # padded rows included
+        self.k_codes_all = unpack_codes(self.k_codes_raw, NP, D, qk_bits)
+        self.q_codes = self.q_codes_all[:, :N]
+        self.k_codes = self.k_codes_all[:, :N]
         self.q_scale_p = arr(qb.q_scale, BH * NP * 4, np.float32, (BH, NP))
         self.k_scale_p = arr(qb.k_scale, BH * NP // 16 * 4, np.float32, (BH, NP // 16))
         self.q_mean = arr(qb.q_mean, BH * NQB * D * 4, np.float32, (BH, NQB, D))

@@ -6,6 +6,8 @@ import math
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from fp8_attention_transformer_amd import sage
@@ -127,3 +129,30 @@ def test_product_package_does_not_import_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
                 assert "sage_oracle" not in src, f
+
+
+def test_fp6_tile_layout_helpers():
+    """The test-side decoder of the FP6 code layout (include/sage.h), pinned by
+    bytes worked out by hand and by a round trip."""
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_helpers as gh
+    # D = 128, row 0: channel 0 = +1 (e2m3 0b001000), channel 1 = -7 (0b111110):
+    # byte 0 = 8 | (62 << 6) & 255 = 136, byte 1 = 62 >> 2 = 15; channel 32
+    # (half 1) = +3 (0b010100) lands in chunk 32 at byte 0; channel 64 (group
+    # 1, half 0) = -1 (0b101000) at byte 24 of chunk 0.
+    codes = np.zeros((1, 32, 128), np.int8)
+    codes[0, 0, 0], codes[0, 0, 1], codes[0, 0, 32], codes[0, 0, 64] = 1, -7, 3, -1
+    raw = gh.codes_to_fp6_tiles(codes, 128)
+    assert raw.shape == (1, 32 * 96)
+    assert raw[0, 0] == 136 and raw[0, 1] == 15 and raw[0, 32 * 48] == 20 and raw[0, 24] == 40
+    assert np.count_nonzero(raw) == 4
+    # D = 64, row 9 (chunk 9, halves swapped): channel 0 = +2 (0b010000) at byte 16
+    codes = np.zeros((1, 32, 64), np.int8)
+    codes[0, 9, 0] = 2
+    raw = gh.codes_to_fp6_tiles(codes, 64)
+    assert raw[0, 9 * 32 + 16] == 16 and np.count_nonzero(raw) == 1
+    rng = np.random.default_rng(3)
+    for D in (64, 128):
+        c = rng.integers(-7, 8, (2, 96, D)).astype(np.int8)
+        assert np.array_equal(gh.fp6_tiles_to_codes(gh.codes_to_fp6_tiles(c, D), D), c)

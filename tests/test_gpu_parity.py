@@ -57,9 +57,14 @@ def _check_prepass(rb, z):
     assert np.array_equal(rb.k_mean, zq(z.k_mean)), "k means"
     assert np.array_equal(rb.v_scale, zq(z.v_scale)), "v scales"
     assert np.array_equal(rb.v_codes, zq(z.v_codes)), "v codes"
-    # padding rows: zero codes (byte 8 for INT4 pairs, 0 for INT8) and zero scales
-    assert np.all(rb.q_scale_p[:, N:] == 0) and np.all(rb.q_codes_packed[:, N:] == rb.zero_code_byte)
-    assert np.all(rb.k_codes_packed[:, N:] == rb.zero_code_byte)
+    # padding rows: zero codes and zero scales
+    assert np.all(rb.q_scale_p[:, N:] == 0)
+    assert np.all(rb.q_codes_all[:, N:] == 0) and np.all(rb.k_codes_all[:, N:] == 0)
+    if rb.qk_bits == 4:
+        # every stored byte is the layout's encoding of the codes (pad bytes zero)
+        import gpu_helpers as gh
+        assert np.array_equal(rb.q_codes_raw, gh.codes_to_fp6_tiles(rb.q_codes_all, D)), "q FP6 layout"
+        assert np.array_equal(rb.k_codes_raw, gh.codes_to_fp6_tiles(rb.k_codes_all, D)), "k FP6 layout"
 
 
 def _ds_bound(oracle_lib, z, k_bits, dtype_code):
