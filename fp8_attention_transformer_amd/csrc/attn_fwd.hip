@@ -288,7 +288,9 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) part[T][q4] = (p[4 * q4] + p[4 * q4 + 1]) + (p[4 * q4 + 2] + p[4 * q4 + 3]);
 #pragma unroll
-    for (int w = 0; w < 4; w++) P8[T >> 1][4 * (T & 1) + w] = (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
+    for (int w = 0; w < 4; w++)
+      P8[T >> 1][4 * (T & 1) + w] =
+          (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3], __float_as_int(s2[T][4 * w]));
   }
   float tsum[4];
 #pragma unroll
@@ -412,17 +414,18 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     __syncthreads();
   }
 
-  // ---- epilogue: O = (O_run * vscale) / l'
+  // ---- epilogue: O = (O_run * vscale) * (1 / l')
   const int qi = qrow;
   if (qi < d.N) {
     const float* vs = b.v_scale + (size_t)bh * D;
     const size_t orow = ((size_t)bh * d.N + qi) * D;
+    const float inv_l = 1.0f / as.l;
 #pragma unroll
     for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int ch = 32 * dt + 8 * (r >> 2) + 4 * h + (r & 3);
-        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) / as.l, out_dtype);
+        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) * inv_l, out_dtype);
       }
   }
 }

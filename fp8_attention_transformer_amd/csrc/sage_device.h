@@ -28,8 +28,11 @@ __device__ __forceinline__ float in_to_f32(uint16_t bits) {
 __device__ __forceinline__ uint32_t fp8x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// `dead` is any register value the caller no longer needs: the conversions
+// write bytes 0-1 and then 2-3 of it, so its prior contents never matter and
+// it needs no zero initialisation.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, int dead = 0) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, dead, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
