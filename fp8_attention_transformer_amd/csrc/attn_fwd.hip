@@ -111,12 +111,6 @@ __device__ __forceinline__ void load_q_operand(const uint8_t* __restrict__ q_cod
   }
 }
 
-// INT8 accumulators start at the bit pattern of 1.5 * 2^23.  |dot| <= 127^2 *
-// 128 < 2^22, so the int32 result read as fp32 is exactly 1.5 * 2^23 + dot,
-// and one exact subtraction yields it as a float.
-constexpr int kMagicBits = 0x4B400000;
-constexpr float kMagic = 12582912.0f;
-
 // One 32-key tile of S^T as floats holding the exact integer dot products.
 // FP6: a[m] = this lane's K chunk operands; INT8: a[m] = its 16-byte chunks.
 template <int D>
@@ -126,16 +120,15 @@ __device__ __forceinline__ v16f qk_tile_fp6(const v8i* a, const QOperand<D, 4>& 
   for (int m = 0; m < D / 64; m++) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[m], op.x[m], s, 2, 2, 0, 0, 0, 0);
   return s;
 }
+// INT8: |dot| <= 127^2 * 128 < 2^24, so the int32 -> fp32 conversion is exact.
 template <int D>
 __device__ __forceinline__ v16f qk_tile_i8(const v4i* a, const QOperand<D, 8>& op) {
-  v16i s;
-#pragma unroll
-  for (int r = 0; r < 16; r++) s[r] = kMagicBits;
+  v16i s = {};
 #pragma unroll
   for (int m = 0; m < D / 32; m++) s = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[m], op.x[m], s, 0, 0, 0);
   v16f f;
 #pragma unroll
-  for (int r = 0; r < 16; r++) f[r] = __int_as_float(s[r]) - kMagic;
+  for (int r = 0; r < 16; r++) f[r] = (float)s[r];
   return f;
 }
 
@@ -179,33 +172,52 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Direct HBM/L2 -> LDS copy of one 128-key block: K codes and FP8 V.  Lane l
 // of a wave writes LDS chunk (wave base + l); it fetches the global chunk whose
-// swizzled position that is.
+// swizzled position that is.  Chunk e = 256*i + 64*wave + lane of either array
+// comes from byte 4096*i + 1024*wave + off, where the lane part `off` does not
+// depend on i (the swizzles repeat every 256 chunks): one 32-bit offset per
+// array, computed once, and a wave-uniform base per copy instruction.
 template <int D, int BITS>
-__device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, const uint8_t* kblk, const uint8_t* vblk,
-                                               int t, int wave, int lane) {
+__device__ __forceinline__ uint32_t k_src_offset(int wave, int lane) {
+  constexpr int ROWB = QKCfg<D, BITS>::ROWB;
+  const int e = 64 * wave + lane;
+  int src = 16 * e;
+  if constexpr (BITS == 8) {
+    constexpr int CPR = QKCfg<D, 8>::CPR;
+    const int r = e / CPR, c = (e % CPR) ^ kswz<CPR>(r);
+    src = r * ROWB + 16 * c;
+  }
+  return (uint32_t)(src - 1024 * wave);
+}
+__device__ __forceinline__ uint32_t v_src_offset(int wave, int lane) {
+  const int e = 64 * wave + lane, r = e / 8, c = (e % 8) ^ vswz(r);
+  return (uint32_t)(r * kBK + 16 * c - 1024 * wave);
+}
+
+// Buffer resource over one head's array: raw addressing, `bytes` records (the
+// hardware returns zeros beyond them), default gfx9 data format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The copies use buffer loads straight to LDS: the per-lane offset is one VGPR
+// and block, round and wave offsets stay scalar.
+template <int D, int BITS>
+__device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, __amdgpu_buffer_rsrc_t rk,
+                                               __amdgpu_buffer_rsrc_t rv, int t, int wave, uint32_t koff,
+                                               uint32_t voff) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int KCH = kBK * ROWB / 16 / 256, VCH = D * kBK / 16 / 256;
   static_assert(KCH * 16 * 256 == kBK * ROWB, "whole copy rounds");
-  const uint8_t* gk = kblk + (size_t)t * kBK * ROWB;
-  const uint8_t* gv = vblk + (size_t)t * D * kBK;
+  const uint32_t kb = (uint32_t)t * (kBK * ROWB) + 1024u * wave;
+  const uint32_t vb = (uint32_t)t * (D * kBK) + 1024u * wave;
 #pragma unroll
-  for (int i = 0; i < KCH; i++) {
-    const int wbase = 256 * i + 64 * wave;
-    const int e = wbase + lane;
-    int src = 16 * e;
-    if constexpr (BITS == 8) {
-      constexpr int CPR = QKCfg<D, 8>::CPR;
-      const int r = e / CPR, c = (e % CPR) ^ kswz<CPR>(r);
-      src = r * ROWB + 16 * c;
-    }
-    __builtin_amdgcn_global_load_lds((const void*)(gk + src), (lds_ptr_t)(sK + 16 * wbase), 16, 0, 0);
-  }
+  for (int i = 0; i < KCH; i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sK + 4096 * i + 1024 * wave), 16, koff, kb + 4096 * i, 0,
+                                             0);
 #pragma unroll
-  for (int i = 0; i < VCH; i++) {
-    const int wbase = 256 * i + 64 * wave;
-    const int e = wbase + lane, r = e / 8, c = (e % 8) ^ vswz(r);
-    __builtin_amdgcn_global_load_lds((const void*)(gv + r * kBK + 16 * c), (lds_ptr_t)(sV + 16 * wbase), 16, 0, 0);
-  }
+  for (int i = 0; i < VCH; i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sV + 4096 * i + 1024 * wave), 16, voff, vb + 4096 * i, 0,
+                                             0);
 }
 
 template <int D, bool CAUSAL>
@@ -215,16 +227,13 @@ struct AttnState {
   float m, l;
 };
 
-// One 128-key block for this wave: S^T tiles, dequantization, online softmax,
-// FP8 P~, two-level P~V.
-template <int D, int BITS, bool CAUSAL>
-__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
-                                           const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
-                                           int t, int qb, int qrow, int n, int h, const Dims& d) {
-  constexpr int NDT = D / 32;
-  // ---- S^T for 4 tiles of 32 keys (exact integer dot products as floats)
-  v16f S[4];
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+// The three parts of one 128-key block for this wave.  qk_part: S^T tiles
+// (exact integer dot products as floats).  softmax_part: dequantization into
+// the log2 domain, masking, online-softmax update, P~ -> e4m3 matrix-core
+// operands.  pv_part: two-level P~V (a fresh FP32 partial R per d-tile, then
+// O = alpha*O + R).
+template <int D, int BITS>
+__device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, const uint8_t* cK, int n, int h) {
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     if constexpr (BITS == 4) {
@@ -242,11 +251,14 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
       S[T] = qk_tile_i8<D>(a, qop);
     }
   }
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  // ---- dequantize into the log2 domain, mask, block max
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
+                                             const float* cKS, float dq, float ks, int t, int qb, int qrow, int h,
+                                             const Dims& d, v8i* P8, float& alpha) {
   float s2[4][16];
   float tmax[4];
-  float bmax;
   const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
@@ -271,20 +283,17 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
       m4[q4] = fmaxf(fmaxf(s2[T][4 * q4], s2[T][4 * q4 + 1]), fmaxf(s2[T][4 * q4 + 2], s2[T][4 * q4 + 3]));
     tmax[T] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
   }
-  bmax = pair_max(fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3])));
+  const float bmax = pair_max(fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3])));
   const float mnew = fmaxf(as.m, bmax);
-  const float alpha = __builtin_amdgcn_exp2f(as.m - mnew);
+  alpha = __builtin_amdgcn_exp2f(as.m - mnew);
   const float mm = mnew - kLog2_448;
   // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
   float part[4][4];   // independent partial row sums (tile, register quad)
-  v8i P8[2];
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
-    }
+    for (int r = 0; r < 16; r++) p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) part[T][q4] = (p[4 * q4] + p[4 * q4 + 1]) + (p[4 * q4 + 2] + p[4 * q4 + 3]);
 #pragma unroll
@@ -298,10 +307,13 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   const float rowsum = pair_sum((tsum[0] + tsum[1]) + (tsum[2] + tsum[3]));
   as.l = alpha * as.l + rowsum;
   as.m = mnew;
-  // ---- two-level P~V: fresh FP32 partial R per d-tile, then O = alpha*O + R
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8, float alpha, const uint8_t* cV, int n,
+                                        int h) {
 #pragma unroll
-  for (int dt = 0; dt < NDT; dt++) {
+  for (int dt = 0; dt < D / 32; dt++) {
     const int row = 32 * dt + n;
     v16f R;
 #pragma unroll
@@ -317,6 +329,22 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
 #pragma unroll
     for (int r = 0; r < 16; r++) as.O[dt][r] = __builtin_fmaf(alpha, as.O[dt][r], R[r]);
   }
+}
+
+// One whole block in sequence (the four-wave kernel).
+template <int D, int BITS, bool CAUSAL>
+__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
+                                           const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
+                                           int t, int qb, int qrow, int n, int h, const Dims& d) {
+  v16f S[4];
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+  qk_part<D, BITS>(S, qop, cK, n, h);
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
+  v8i P8[2];
+  float alpha;
+  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, qb, qrow, h, d, P8, alpha);
+  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
+  pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
 }
 
@@ -370,8 +398,11 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // loads are unconditional, with in-range indices), so a vmcnt limit of
   // VM_PER_BLOCK * k waits exactly for all but the newest k blocks.
   float ds_reg[S - 1], ks_reg[S - 1];
+  const uint32_t koff = k_src_offset<D, BITS>(wave, lane), voff = v_src_offset(wave, lane);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NP * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NP * D);
   auto issue = [&](int t, int slot) {
-    stage_kv_async<D, BITS>(bK(slot), bV(slot), kblk, vblk, t, wave, lane);
+    stage_kv_async<D, BITS>(bK(slot), bV(slot), rk, rv, t, wave, koff, voff);
     ds_reg[t % (S - 1)] = dsrow[t * kBK + (tid & (kBK - 1))];
     ks_reg[t % (S - 1)] = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
   };
