@@ -276,14 +276,17 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
         if (bad) s2[T][r] = -__builtin_inff();
       }
     }
-    // four independent max chains per tile (a short tree, not one long chain)
-    float m4[4];
+    // two chains of three-input maxima per tile (v_max3: two values per op)
+    float c0 = fmaxf(fmaxf(s2[T][0], s2[T][1]), s2[T][2]);
+    float c1 = fmaxf(fmaxf(s2[T][8], s2[T][9]), s2[T][10]);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; q4++)
-      m4[q4] = fmaxf(fmaxf(s2[T][4 * q4], s2[T][4 * q4 + 1]), fmaxf(s2[T][4 * q4 + 2], s2[T][4 * q4 + 3]));
-    tmax[T] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    for (int r = 3; r < 7; r += 2) {
+      c0 = fmaxf(fmaxf(c0, s2[T][r]), s2[T][r + 1]);
+      c1 = fmaxf(fmaxf(c1, s2[T][8 + r]), s2[T][8 + r + 1]);
+    }
+    tmax[T] = fmaxf(fmaxf(c0, s2[T][7]), fmaxf(c1, s2[T][15]));
   }
-  const float bmax = pair_max(fmaxf(fmaxf(tmax[0], tmax[1]), fmaxf(tmax[2], tmax[3])));
+  const float bmax = pair_max(fmaxf(fmaxf(fmaxf(tmax[0], tmax[1]), tmax[2]), tmax[3]));
   const float mnew = fmaxf(as.m, bmax);
   alpha = __builtin_amdgcn_exp2f(as.m - mnew);
   const float mm = mnew - kLog2_448;

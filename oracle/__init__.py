@@ -46,6 +46,7 @@ EXACT_SMOOTH_K = 1
 EXACT_SMOOTH_Q = 2
 EXACT_QUANT_QK = 4
 EXACT_QUANT_V = 8
+EXACT_SMOOTH_V = 16
 
 DT_F16 = 0
 DT_BF16 = 1
@@ -76,13 +77,13 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [P, P, i64]
         L.oracle_e4m3_decode.argtypes = [P, P, i64]
         L.oracle_decode_input.argtypes = [P, i32, P, i64]
-        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32] + [P] * 9 + [i32]
+        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32] + [P] * 10 + [i32]
         L.oracle_quant_smooth.restype = i32
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
         L.oracle_qk_int32.restype = i32
-        L.oracle_attn_mirror.argtypes = [P] * 7 + [i32, i32, i32, i32, i32, f32, i32, P, i64, f32, P, P, P, i32]
+        L.oracle_attn_mirror.argtypes = [P] * 8 + [i32, i32, i32, i32, i32, f32, i32, P, i64, f32, P, P, P, i32]
         L.oracle_attn_mirror.restype = i32
-        L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 7 + [i32, i32, i32, i32, i32, f64, i32, P, i64, P, P, i32]
+        L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 8 + [i32, i32, i32, i32, i32, f64, i32, P, i64, P, P, i32]
         L.oracle_attn_exact.restype = i32
         _lib = L
     return _lib
@@ -129,13 +130,14 @@ class Quant:
     v_codes: np.ndarray   # uint8 [B,H,N,D]
     v_scale: np.ndarray   # fp32  [B,H,D]
     delta_s: np.ndarray   # fp32  [B,H,ceil(N/128),N]
+    v_mean: np.ndarray = None   # fp32 [B,H,D]: V channel means (zeros without V smoothing)
 
 
 def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True,
-                 qk_bits: int = 4) -> Quant:
+                 qk_bits: int = 4, smooth_v: bool = False) -> Quant:
     """Run the prepass; with_delta_s=False skips the (quadratic) compensation
     term and leaves ``delta_s`` as None.  qk_bits selects INT4 (4) or INT8 (8)
-    codes for Q and K."""
+    codes for Q and K; smooth_v subtracts the per-channel V mean before FP8."""
     B, H, N, D = q_bits.shape
     nqb = (N + BQ_MEAN - 1) // BQ_MEAN
     G = 2 * ((N + 31) // 32)
@@ -145,11 +147,12 @@ def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_del
         k_codes=np.empty((B, H, N, D), np.int8), k_scale=np.empty((B, H, G), np.float32),
         q_mean=np.empty((B, H, nqb, D), np.float32), k_mean=np.empty((B, H, D), np.float32),
         v_codes=np.empty((B, H, N, D), np.uint8), v_scale=np.empty((B, H, D), np.float32),
-        delta_s=np.empty((B, H, nqb, N), np.float32) if with_delta_s else None)
-    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D, qk_bits,
+        delta_s=np.empty((B, H, nqb, N), np.float32) if with_delta_s else None,
+        v_mean=np.empty((B, H, D), np.float32))
+    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D, qk_bits, int(bool(smooth_v)),
                                    _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
                                    _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),
-                                   _ptr(out.delta_s), _threads(nthreads))
+                                   _ptr(out.v_mean), _ptr(out.delta_s), _threads(nthreads))
     if rc != 0:
         raise ValueError("oracle_quant_smooth rejected its arguments")
     return out
@@ -180,7 +183,7 @@ def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bo
     slack = np.empty(nrows, np.float32)
     lse = np.empty((nrows, 2), np.float32)
     rc = lib().oracle_attn_mirror(_ptr(qz.q_codes), _ptr(qz.q_scale), _ptr(qz.k_codes), _ptr(qz.k_scale),
-                                  _ptr(qz.v_codes), _ptr(qz.v_scale), _ptr(qz.delta_s),
+                                  _ptr(qz.v_codes), _ptr(qz.v_scale), _ptr(qz.v_mean), _ptr(qz.delta_s),
                                   B, H, N, D, int(causal), float(sm_scale),
                                   MIRROR_QUANT_P if quant_p else 0, _ptr(rows_arr), nrows, float(eps),
                                   _ptr(O), _ptr(slack), _ptr(lse), _threads(nthreads))
@@ -205,7 +208,7 @@ def attn_exact(q_bits, k_bits, v_bits, dtype: int, causal: bool, sm_scale: float
     z = qz if qz is not None else Quant(*([None] * 9))
     rc = lib().oracle_attn_exact(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype,
                                  _ptr(z.q_codes), _ptr(z.q_scale), _ptr(z.k_codes), _ptr(z.k_scale),
-                                 _ptr(z.v_codes), _ptr(z.v_scale), _ptr(z.delta_s),
+                                 _ptr(z.v_codes), _ptr(z.v_scale), _ptr(z.v_mean), _ptr(z.delta_s),
                                  B, H, N, D, int(causal), float(sm_scale), flags, _ptr(rows_arr), nrows,
                                  _ptr(O), _ptr(psum), _threads(nthreads))
     if rc != 0:

@@ -32,6 +32,11 @@
 //   - Compensation term DeltaS[qb][j] = sum_c qmean[qb][c] * (K[j][c]-kmean[c]),
 //     accumulated in fp64 and rounded once to fp32.
 //   - V: FP8 OCP e4m3fn (max 448), one scale per channel = amax/448, RNE.
+//     Optional V smoothing (technical-report summary, Key Contribution 2:
+//     smoothing of Q and V): the per-channel mean of V over all N tokens
+//     (same fp32 chunked order as the K mean) is subtracted before the FP8
+//     quantization and added back to the output, which is exact for the
+//     unquantized method because every row of softmax(S) sums to one.
 //   - Scores in the log2 domain:  ks = sm_scale * log2(e) (fp32),
 //     s2 = fma((float)acc, (dq*dk)*ks, DeltaS*ks).
 //   - Online softmax over BK = 128-key blocks in ascending order.
@@ -39,7 +44,7 @@
 //     l' = alpha*l' + sum(p')  (p' before FP8 rounding).
 //   - Two-level P~V: R_t = sum_j dec(P8_j)*dec(V8_j) in a fresh fp32 buffer per
 //     block; O_t = fma(alpha_t, O_{t-1}, R_t).
-//   - Epilogue: O = (O_T * vscale) / l'_T.
+//   - Epilogue: O = (O_T * vscale) / l'_T (+ vmean with V smoothing).
 //
 // Build: g++ -std=c++17 -O2 -ffp-contract=off -shared -fPIC -pthread
 // (no fast-math, no FMA contraction; std::fma only where a step names fma).
@@ -162,17 +167,19 @@ void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
 //   k_scale          : fp32  [B,H,2*ceil(N/32)]
 //   q_mean           : fp32  [B,H,ceil(N/128),D]
 //   k_mean           : fp32  [B,H,D]
-//   v_codes          : uint8 [B,H,N,D]     e4m3fn bit patterns
+//   v_codes          : uint8 [B,H,N,D]     e4m3fn bit patterns of (V - vmean)/vscale
 //   v_scale          : fp32  [B,H,D]
+//   v_mean           : fp32  [B,H,D]       per-channel V mean (zeros without smoothing)
 //   delta_s          : fp32  [B,H,ceil(N/128),N]
 // Returns 0, or -1 for invalid arguments.
 int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
-                        int B, int H, int N, int D, int qk_bits,
+                        int B, int H, int N, int D, int qk_bits, int smooth_v,
                         int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
-                        float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale,
+                        float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale, float* v_mean,
                         float* delta_s, int nthreads) {
   if (!q || !k || !v || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
   if (qk_bits != 4 && qk_bits != 8) return -1;
+  if (smooth_v != 0 && smooth_v != 1) return -1;
   const float qmax = qk_bits == 4 ? 7.0f : 127.0f;
   const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
   const int64_t G = 2 * ((int64_t)(N + 31) / 32);
@@ -238,8 +245,20 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (k_codes)
       for (int64_t j = 0; j < N; j++)
         for (int c = 0; c < D; c++) k_codes[base + j * D + c] = int_code(gK[j * D + c], dk[k_group(j)], qmax);
-    // ---- V: FP8 e4m3fn with one scale per channel
+    // ---- V: optional smoothing, then FP8 e4m3fn with one scale per channel
     for (int c = 0; c < D; c++) {
+      float vbar = 0.0f;
+      if (smooth_v) {
+        float total = 0.0f;
+        for (int64_t t0 = 0; t0 < N; t0 += BQ_MEAN) {
+          float part = 0.0f;
+          for (int64_t j = t0; j < std::min<int64_t>(N, t0 + BQ_MEAN); j++) part = part + V[j * D + c];
+          total = total + part;
+        }
+        vbar = total / (float)N;
+        for (int64_t j = 0; j < N; j++) V[j * D + c] = V[j * D + c] - vbar;
+      }
+      if (v_mean) v_mean[bh * D + c] = vbar;
       float amax = 0.0f;
       for (int64_t j = 0; j < N; j++) amax = std::max(amax, std::fabs(V[j * D + c]));
       float dv = amax / 448.0f;
@@ -285,7 +304,7 @@ enum { MIRROR_QUANT_P = 1 };
 // rounded the other way (used to tolerate exp2 implementation differences).
 // Optional lse[r] = (final running max m, final l') for diagnostics.
 int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
-                       const uint8_t* v_codes, const float* v_scale, const float* delta_s,
+                       const uint8_t* v_codes, const float* v_scale, const float* v_mean, const float* delta_s,
                        int B, int H, int N, int D, int causal, float sm_scale, int flags,
                        const int64_t* rows, int64_t nrows, float eps,
                        float* O, float* slack, float* lse, int nthreads) {
@@ -357,7 +376,10 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
       slk = alpha * slk + blk_slack;
       m = mnew;
     }
-    for (int c = 0; c < D; c++) O[r * D + c] = (Orun[c] * dvec[c]) / l;
+    for (int c = 0; c < D; c++) {
+      O[r * D + c] = (Orun[c] * dvec[c]) / l;
+      if (v_mean) O[r * D + c] = O[r * D + c] + v_mean[bh * D + c];
+    }
     if (slack) slack[r] = slk / l;
     if (lse) { lse[2 * r] = m; lse[2 * r + 1] = l; }
   });
@@ -370,7 +392,8 @@ enum {
   EXACT_SMOOTH_K = 1,  // subtract the per-channel K mean (fp64 mean)
   EXACT_SMOOTH_Q = 2,  // subtract the per-block Q mean and add q_mean . gamma(K)
   EXACT_QUANT_QK = 4,  // use the prepass INT4 codes/scales and DeltaS (given)
-  EXACT_QUANT_V = 8,   // use the prepass FP8 V and scales (given)
+  EXACT_QUANT_V = 8,   // use the prepass FP8 V and scales (given), plus v_mean if given
+  EXACT_SMOOTH_V = 16, // without QUANT_V: subtract the fp64 per-channel V mean, add it back to O
 };
 // Without EXACT_QUANT_QK the scores are built from the raw inputs in fp64:
 //   S_ij = sm_scale * ( gQ_i . gK_j + [SMOOTH_Q] qmean_qb(i) . gK_j )
@@ -379,7 +402,7 @@ enum {
 // Outputs O[r][c] in fp64; optional P row sums in psum[r].
 int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
                       const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
-                      const uint8_t* v_codes, const float* v_scale, const float* delta_s,
+                      const uint8_t* v_codes, const float* v_scale, const float* v_mean, const float* delta_s,
                       int B, int H, int N, int D, int causal, double sm_scale, int flags,
                       const int64_t* rows, int64_t nrows, double* O, double* psum, int nthreads) {
   if (!q || !k || !v || !O || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
@@ -390,7 +413,7 @@ int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
   const int64_t total = rows ? nrows : (int64_t)B * H * N;
   // per-head fp64 statistics, computed lazily per head
   const int64_t nheads = (int64_t)B * H;
-  std::vector<std::vector<double>> kbar(nheads), qbar(nheads);
+  std::vector<std::vector<double>> kbar(nheads), qbar(nheads), vbar(nheads);
   std::vector<char> need(nheads, rows ? 0 : 1);
   if (rows)
     for (int64_t r = 0; r < nrows; r++) need[rows[r] / N] = 1;
@@ -399,6 +422,13 @@ int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
     const int64_t base = bh * (int64_t)N * D;
     kbar[bh].assign(D, 0.0);
     qbar[bh].assign(NQB * D, 0.0);
+    vbar[bh].assign(D, 0.0);
+    if ((flags & EXACT_SMOOTH_V) && !(flags & EXACT_QUANT_V))
+      for (int c = 0; c < D; c++) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; j++) s += in_to_f32(v, base + j * D + c, dtype);
+        vbar[bh][c] = s / N;
+      }
     if (flags & EXACT_SMOOTH_K)
       for (int c = 0; c < D; c++) {
         double s = 0.0;
@@ -459,9 +489,13 @@ int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
       ps += pj;
       for (int c = 0; c < D; c++) {
         double vj = (flags & EXACT_QUANT_V) ? (double)v_scale[bh * D + c] * (double)e4m3_decode(v_codes[base + j * D + c])
-                                            : (double)in_to_f32(v, base + j * D + c, dtype);
+                                            : (double)in_to_f32(v, base + j * D + c, dtype) - vbar[bh][c];
         O[r * D + c] += pj * vj;
       }
+    }
+    for (int c = 0; c < D; c++) {
+      if (flags & EXACT_QUANT_V) O[r * D + c] += v_mean ? (double)v_mean[bh * D + c] : 0.0;
+      else O[r * D + c] += vbar[bh][c];
     }
     if (psum) psum[r] = ps;
   });

@@ -212,3 +212,53 @@ def test_rows_subset_matches_full(oracle_lib):
     rows = np.array([0, 1, 139, 140, 300, 559])
     Osub, ssub, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=2.0 ** -16)
     assert np.array_equal(Osub, Ofull[rows]) and np.array_equal(ssub, sfull[rows])
+
+
+@pytest.mark.parametrize("N,D", [(17, 64), (200, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_smoothing_invariant(oracle_lib, N, D, causal):
+    """Rows of softmax(S) sum to one, so subtracting a per-channel vector from
+    every V token and adding it to O changes nothing (fp64, no quantization)."""
+    w = wl.custom(1, 2, N, D, seed=N + 11, k_offset_std=3.0, v_offset_std=2.0)
+    q, k, v = wl.generate(w)
+    O0, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, 0)
+    Ov, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, oracle_lib.EXACT_SMOOTH_V)
+    assert np.abs(Ov - O0).max() <= 1e-12 * np.abs(O0).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_smoothing_mirror_online_softmax(oracle_lib, causal):
+    """With V smoothing the mirror (P~ unquantized) still equals the direct
+    softmax over the same quantized operands, mean added back."""
+    N, D = 200, 128
+    w = wl.custom(1, 2, N, D, seed=77, k_offset_std=4.0, v_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, smooth_v=True)
+    assert np.any(z.v_mean)
+    flags = (oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_QUANT_QK
+             | oracle_lib.EXACT_QUANT_V)
+    Oe, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, flags, qz=z)
+    Om, _, _ = oracle_lib.attn_mirror(z, causal, w.scale, quant_p=False)
+    vmax = np.abs(oracle_lib.decode_input(v, 1)).max()
+    assert np.abs(Om - Oe).max() <= 1e-5 * vmax
+
+
+def test_v_smoothing_restores_offset_exactly(oracle_lib):
+    """V = constant offset per channel + values exact in FP8 after scaling:
+    smoothing removes the offset (integer-valued, so the mean is exact), the
+    mirror with unquantized P~ reproduces plain attention, and the offset
+    comes back through the epilogue."""
+    N, D = 128, 64
+    Q, K, V = _lossless_inputs(N, D, seed=5)
+    # _lossless_inputs' V has no zero-mean guarantee; make each channel's sum
+    # zero by pairing tokens, then add an integer offset per channel
+    V = np.concatenate([V[0, 0, :N // 2], -V[0, 0, :N // 2]])[None, None]
+    off = np.arange(D, dtype=np.float32)[None, None, None, :] % 7 - 3
+    Vo = V + off
+    q, k, v = _bits(Q), _bits(K), _bits(Vo)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, smooth_v=True)
+    assert np.array_equal(z.v_mean[0, 0], off[0, 0, 0])
+    scale = 0.003
+    ref = _brute_force(Q, K, Vo, False, scale).reshape(-1, D)
+    Om, _, _ = oracle_lib.attn_mirror(z, False, scale, quant_p=False)
+    assert np.abs(Om - ref).max() <= 5e-6 * np.abs(Vo).max()

@@ -183,3 +183,30 @@ def test_zero_inputs(oracle_lib):
     z = oracle_lib.quant_smooth(z0, z0, z0, oracle_lib.DT_BF16)
     for a in (z.q_codes, z.k_codes, z.v_codes, z.q_scale, z.k_scale, z.v_scale, z.delta_s, z.q_mean, z.k_mean):
         assert not np.any(a)
+
+
+@pytest.mark.parametrize("N", [128, 300])
+def test_v_smoothing_mean_and_codes(oracle_lib, N):
+    """V smoothing (technical-report summary, Key Contribution 2): integer V
+    gives an exact closed-form channel mean; the FP8 codes are those of
+    V - mean with scale amax|V - mean| / 448; without smoothing the mean
+    output is zero and the codes are unchanged from the plain prepass."""
+    rng = np.random.default_rng(N + 1)
+    D = 64
+    Qi = rng.integers(-8, 9, (1, 1, N, D)).astype(np.float32)
+    Vi = rng.integers(-8, 9, (1, 1, N, D)).astype(np.float32) + rng.integers(-20, 21, (1, 1, 1, D))
+    q, v = _bits(Qi), _bits(Vi)
+    z0 = oracle_lib.quant_smooth(q, q, v, oracle_lib.DT_BF16)
+    z1 = oracle_lib.quant_smooth(q, q, v, oracle_lib.DT_BF16, smooth_v=True)
+    assert not np.any(z0.v_mean)
+    vsum = Vi[0, 0].astype(np.int64).sum(0)
+    vbar = vsum.astype(np.float32) / np.float32(N)
+    assert np.array_equal(z1.v_mean[0, 0], vbar)
+    gV = (Vi[0, 0] - vbar).astype(np.float32)
+    dv = (np.abs(gV).max(0) / np.float32(448)).astype(np.float32)
+    assert np.array_equal(z1.v_scale[0, 0], dv)
+    ref = oracle_lib.e4m3_encode((gV / dv).astype(np.float32))
+    assert np.array_equal(z1.v_codes[0, 0], ref)
+    # everything else of the prepass is untouched by V smoothing
+    for f in ("q_codes", "q_scale", "k_codes", "k_scale", "q_mean", "k_mean", "delta_s"):
+        assert np.array_equal(getattr(z0, f), getattr(z1, f)), f
