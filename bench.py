@@ -60,7 +60,7 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int):
+def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool = False):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the prepass of head 0 and the mirror-mode attention of a set of
     its rows, with the host's threads (at most 16).  Also reports, from the
@@ -75,7 +75,7 @@ def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int):
     dt = 0 if w.dtype == wl.F16 else 1
     q, k, v = wl.generate(w, heads=slice(0, 1))
     t0 = time.perf_counter()
-    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth, qk_bits=qk_bits)
+    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth, qk_bits=qk_bits, smooth_v=smooth_v)
     t_pre = time.perf_counter() - t0
     N, D = w.N, w.D
     rng = np.random.default_rng(0)
@@ -116,7 +116,7 @@ def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int):
     return base, acc
 
 
-def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4):
+def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4, smooth_v: bool = False):
     import numpy as np
     import torch
 
@@ -135,7 +135,8 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     in_code = sage.F16 if tdt == torch.float16 else sage.BF16
 
     def step():
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits)
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits,
+                          smooth_v=smooth_v)
         sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
 
     for _ in range(warmup):
@@ -147,7 +148,8 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     start.record(stream)
     for i in range(steps):
         ev[i][0].record(stream)
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits)
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits,
+                          smooth_v=smooth_v)
         ev[i][1].record(stream)
         sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
         ev[i][2].record(stream)
@@ -174,7 +176,8 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
         "dtype": f"int{qk_bits}+fp8",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
-                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale, "qk_bits": qk_bits},
+                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale, "qk_bits": qk_bits,
+                   "smooth_v": smooth_v},
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tops, 1),
@@ -191,7 +194,7 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     }
     if cpu:
         o_host = out.float().cpu().numpy().reshape(B * H, N, D)[0]
-        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds, qk_bits)
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds, qk_bits, smooth_v)
     return rec
 
 
@@ -205,6 +208,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--qk-bits", type=int, default=4, choices=(4, 8),
                     help="width of the Q/K codes: 4 (INT4, the method's default) or 8 (INT8)")
+    ap.add_argument("--smooth-v", action="store_true", help="subtract the V channel means before FP8 (added back to O)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -232,7 +236,7 @@ def main():
     else:
         todo = [wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE]
     for w in todo:
-        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits)
+        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits, args.smooth_v)
         print(json.dumps(rec), flush=True)
 
 

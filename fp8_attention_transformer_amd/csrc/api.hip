@@ -36,7 +36,7 @@ bool shape_ok(int B, int H, int N, int D) {
 
 bool bits_ok(int qk_bits) { return qk_bits == 4 || qk_bits == 8; }
 
-Dims make_dims(int B, int H, int N, int D, int qk_bits = 8) {
+Dims make_dims(int B, int H, int N, int D, int qk_bits = 8, int smooth_v = 0) {
   Dims d;
   d.B = B;
   d.H = H;
@@ -45,12 +45,15 @@ Dims make_dims(int B, int H, int N, int D, int qk_bits = 8) {
   d.NP = (N + 127) / 128 * 128;
   d.NQB = d.NP / 128;
   d.QB = qk_bits;
+  d.SV = smooth_v;
   return d;
 }
 
+constexpr int kNumArrays = 12;
+
 // Sizes of the workspace arrays, in the order of sage_quant_bufs.  The code
 // arrays are sized for 8-bit codes so that one layout serves both code widths.
-bool layout(const Dims& d, size_t sizes[11]) {
+bool layout(const Dims& d, size_t sizes[kNumArrays]) {
   const size_t bh = (size_t)d.B * d.H, np = (size_t)d.NP, nqb = (size_t)d.NQB, D = (size_t)d.D;
   size_t rows, t;
   if (!mul_ok(bh, np, &rows)) return false;
@@ -63,16 +66,17 @@ bool layout(const Dims& d, size_t sizes[11]) {
   if (!mul_ok(rows, D, &sizes[6])) return false;            // v_codes
   sizes[7] = bh * D * 4;                                     // v_scale
   if (!mul_ok(bh * nqb, np, &t) || !mul_ok(t, 4, &sizes[8])) return false;  // delta_s
-  sizes[9] = sizes[4];                                       // k_part
-  sizes[10] = sizes[4];                                      // v_part
+  sizes[9] = 2 * sizes[4];                                   // k_part
+  sizes[10] = 2 * sizes[4];                                  // v_part
+  sizes[11] = bh * D * 4;                                    // v_mean
   return true;
 }
 
 size_t total_bytes(const Dims& d) {
-  size_t s[11];
+  size_t s[kNumArrays];
   if (!layout(d, s)) return 0;
   size_t tot = 0;
-  for (int i = 0; i < 11; i++) {
+  for (int i = 0; i < kNumArrays; i++) {
     const size_t a = align_up(s[i]);
     if (a < s[i] || tot + a < tot) return 0;
     tot += a;
@@ -81,13 +85,14 @@ size_t total_bytes(const Dims& d) {
 }
 
 void carve(void* ws, const Dims& d, sage_quant_bufs* out) {
-  size_t s[11];
+  size_t s[kNumArrays];
   layout(d, s);
   char* p = (char*)ws;
-  void** slots[11] = {(void**)&out->q_codes, (void**)&out->k_codes, (void**)&out->q_scale, (void**)&out->k_scale,
-                      (void**)&out->q_mean,  (void**)&out->k_mean,  (void**)&out->v_codes, (void**)&out->v_scale,
-                      (void**)&out->delta_s, (void**)&out->k_part,  (void**)&out->v_part};
-  for (int i = 0; i < 11; i++) {
+  void** slots[kNumArrays] = {(void**)&out->q_codes, (void**)&out->k_codes, (void**)&out->q_scale,
+                              (void**)&out->k_scale, (void**)&out->q_mean,  (void**)&out->k_mean,
+                              (void**)&out->v_codes, (void**)&out->v_scale, (void**)&out->delta_s,
+                              (void**)&out->k_part,  (void**)&out->v_part,  (void**)&out->v_mean};
+  for (int i = 0; i < kNumArrays; i++) {
     *slots[i] = p;
     p += align_up(s[i]);
   }
@@ -106,12 +111,13 @@ Bufs to_internal(const sage_quant_bufs& q) {
   b.delta_s = q.delta_s;
   b.k_part = q.k_part;
   b.v_part = q.v_part;
+  b.v_mean = q.v_mean;
   return b;
 }
 
 bool bufs_ok(const sage_quant_bufs* q) {
   return q && q->q_codes && q->k_codes && q->q_scale && q->k_scale && q->q_mean && q->k_mean && q->v_codes &&
-         q->v_scale && q->delta_s && q->k_part && q->v_part;
+         q->v_scale && q->delta_s && q->k_part && q->v_part && q->v_mean;
 }
 
 // gfx950 check, cached once per device.
@@ -170,10 +176,11 @@ sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H,
 }
 
 sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H, int N,
-                              int D, int qk_bits, const sage_quant_bufs* out, hipStream_t stream) {
+                              int D, int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream) {
   if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D, qk_bits);
+  const Dims d = make_dims(B, H, N, D, qk_bits, smooth_v);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
@@ -182,13 +189,14 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
 }
 
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
-                          int causal, float sm_scale, int qk_bits, sage_dtype in_dtype, sage_dtype out_dtype,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
+                          sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k || !v || !o || !workspace || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D, qk_bits);
+  const Dims d = make_dims(B, H, N, D, qk_bits, smooth_v);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;

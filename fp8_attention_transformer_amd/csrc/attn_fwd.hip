@@ -448,10 +448,11 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     __syncthreads();
   }
 
-  // ---- epilogue: O = (O_run * vscale) * (1 / l')
+  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
   const int qi = qrow;
   if (qi < d.N) {
     const float* vs = b.v_scale + (size_t)bh * D;
+    const float* vm = b.v_mean + (size_t)bh * D;
     const size_t orow = ((size_t)bh * d.N + qi) * D;
     const float inv_l = 1.0f / as.l;
 #pragma unroll
@@ -459,7 +460,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int ch = 32 * dt + 8 * (r >> 2) + 4 * h + (r & 3);
-        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) * inv_l, out_dtype);
+        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) * inv_l + vm[ch], out_dtype);
       }
   }
 }

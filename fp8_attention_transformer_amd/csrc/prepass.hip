@@ -32,14 +32,20 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   const int bh = chunk / d.NQB, qb = chunk % d.NQB;
   const int i0 = qb * kBQ, i1 = min(d.N, i0 + kBQ);
   const size_t base = ((size_t)bh * d.N) * D + 2 * cp;
-  float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vm0 = 0.0f, vm1 = 0.0f;
+  float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
+  float vx0 = -__builtin_inff(), vx1 = -__builtin_inff(), vn0 = __builtin_inff(), vn1 = __builtin_inff();
   auto add = [&](uint32_t qv, uint32_t kv, uint32_t vv) {
     qs0 = qs0 + in_to_f32<IN>((uint16_t)(qv & 0xFFFF));
     qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
     ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
     ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
-    vm0 = fmaxf(vm0, fabsf(in_to_f32<IN>((uint16_t)(vv & 0xFFFF))));
-    vm1 = fmaxf(vm1, fabsf(in_to_f32<IN>((uint16_t)(vv >> 16))));
+    const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
+    vs0 = vs0 + v0;
+    vs1 = vs1 + v1;
+    vx0 = fmaxf(vx0, v0);
+    vx1 = fmaxf(vx1, v1);
+    vn0 = fminf(vn0, v0);
+    vn1 = fminf(vn1, v1);
   };
   if (i1 - i0 == kBQ) {
     // full chunk: branch-free, U tokens of loads in flight
@@ -62,39 +68,55 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
     }
   }
   const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
+  const size_t o2 = ((size_t)bh * d.NQB + qb) * 2 * D + 2 * cp;
   const float cnt = (float)(i1 - i0);
   b.q_mean[o] = qs0 / cnt;
   b.q_mean[o + 1] = qs1 / cnt;
-  b.k_part[o] = ks0;
-  b.k_part[o + 1] = ks1;
-  b.v_part[o] = vm0;
-  b.v_part[o + 1] = vm1;
+  b.k_part[o2] = ks0;
+  b.k_part[o2 + 1] = ks1;
+  b.k_part[o2 + D] = vs0;
+  b.k_part[o2 + D + 1] = vs1;
+  b.v_part[o2] = vx0;
+  b.v_part[o2 + 1] = vx1;
+  b.v_part[o2 + D] = vn0;
+  b.v_part[o2 + D + 1] = vn1;
 }
 
 // ---------------------------------------------------------------------------
 // finalize: grid (B*H), D threads.  K mean = (sum of chunk sums, in chunk
-// order) / N; V scale = (max of chunk absmax) / 448.
+// order) / N; likewise the V mean when V is smoothed (else 0).  V scale =
+// max|V - vmean| / 448, from the chunk maxima and minima: rounding is
+// monotonic, so max_j |fl(V_j - m)| = max(|fl(max V - m)|, |fl(min V - m)|).
 __global__ void finalize_kernel(Dims d, Bufs b) {
-  constexpr int U = 16;
+  constexpr int U = 8;
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
-  const size_t base = (size_t)bh * d.NQB * D + c;
-  float tot = 0.0f, vm = 0.0f;
+  const size_t base = (size_t)bh * d.NQB * 2 * D + c;
+  float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
   for (int t = 0; t < d.NQB; t += U) {
-    float kp[U], vp[U];
+    float kp[U], vp[U], xp[U], np[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const bool ok = t + u < d.NQB;
-      kp[u] = ok ? b.k_part[base + (size_t)(t + u) * D] : 0.0f;
-      vp[u] = ok ? b.v_part[base + (size_t)(t + u) * D] : 0.0f;
+      const size_t o = base + (size_t)(t + u) * 2 * D;
+      kp[u] = ok ? b.k_part[o] : 0.0f;
+      vp[u] = ok ? b.k_part[o + D] : 0.0f;
+      xp[u] = ok ? b.v_part[o] : -__builtin_inff();
+      np[u] = ok ? b.v_part[o + D] : __builtin_inff();
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      if (t + u < d.NQB) tot = tot + kp[u];
-      vm = fmaxf(vm, vp[u]);
+      if (t + u < d.NQB) {
+        tot = tot + kp[u];
+        vtot = vtot + vp[u];
+      }
+      vx = fmaxf(vx, xp[u]);
+      vn = fminf(vn, np[u]);
     }
   }
   b.k_mean[(size_t)bh * D + c] = tot / (float)d.N;
-  b.v_scale[(size_t)bh * D + c] = vm / 448.0f;
+  const float vbar = d.SV ? vtot / (float)d.N : 0.0f;
+  b.v_mean[(size_t)bh * D + c] = vbar;
+  b.v_scale[(size_t)bh * D + c] = fmaxf(fabsf(vx - vbar), fabsf(vn - vbar)) / 448.0f;
 }
 
 // Position p (0..127) inside a 128-key block of the FP8 V layout holds key
@@ -373,9 +395,14 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
     for (int e = tid; e < D * 8; e += 256) {
       const int ch = e % D, c = e / D;
       const float dv = b.v_scale[(size_t)bh * D + ch];
+      const float vbar = b.v_mean[(size_t)bh * D + ch];   // 0 without V smoothing
       float x[16];
 #pragma unroll
-      for (int u = 0; u < 16; u++) x[u] = in_to_f32<IN>(sV[vperm_key(16 * c + u) * D + ch]);
+      for (int u = 0; u < 16; u++) {
+        // padding keys stay exactly zero (also when V is smoothed)
+        const int key = vperm_key(16 * c + u);
+        x[u] = i0 + key < d.N ? in_to_f32<IN>(sV[key * D + ch]) - vbar : 0.0f;
+      }
       fp8_quotients<16>(x, dv);
       v4i pk;
 #pragma unroll

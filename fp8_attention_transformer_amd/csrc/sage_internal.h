@@ -43,7 +43,8 @@ struct Dims {
   int B, H, N, D;
   int NP;    // N rounded up to a multiple of 128
   int NQB;   // NP / 128
-  int QB;    // bits per Q/K code: 4 (INT4, packed pairs) or 8 (INT8)
+  int QB;    // bits per Q/K code: 4 (INT4, stored as FP6) or 8 (INT8)
+  int SV;    // 1: smooth V (subtract the per-channel V mean before FP8)
   __host__ __device__ int BH() const { return B * H; }
 };
 
@@ -58,8 +59,9 @@ struct Bufs {
   uint8_t* v_codes;   // [B,H,NQB,D,128] e4m3fn, keys permuted inside each 128-key block
   float* v_scale;     // [B,H,D]
   float* delta_s;     // [B,H,NQB,NP]   compensation term times ds_scale
-  float* k_part;      // [B,H,NQB,D]    per-chunk K channel sums; then bf16 q_mean pieces 1-2
-  float* v_part;      // [B,H,NQB,D]    per-chunk V channel absmax; then bf16 q_mean piece 3
+  float* k_part;      // [B,H,NQB,2,D]  per-chunk K and V channel sums; then bf16 q_mean pieces 1-2
+  float* v_part;      // [B,H,NQB,2,D]  per-chunk V channel max and min; then bf16 q_mean piece 3
+  float* v_mean;      // [B,H,D]        V channel means (zeros without V smoothing)
 };
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d,

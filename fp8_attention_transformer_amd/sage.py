@@ -28,7 +28,7 @@ class QuantBufs(ctypes.Structure):
     """Mirror of sage_quant_bufs (device pointers)."""
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "q_codes", "k_codes", "q_scale", "k_scale", "q_mean", "k_mean", "v_codes", "v_scale", "delta_s",
-        "k_part", "v_part")]
+        "k_part", "v_part", "v_mean")]
 
 
 class SageError(RuntimeError):
@@ -55,9 +55,9 @@ def lib() -> ctypes.CDLL:
         L.sage_workspace_bytes.restype = sz
         L.sage_quant_bufs_from_workspace.argtypes = [P, sz, i32, i32, i32, i32, ctypes.POINTER(QuantBufs)]
         L.sage_quant_bufs_from_workspace.restype = i32
-        L.sage_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(QuantBufs), P]
         L.sage_quant_smooth.restype = i32
-        L.sage_attn_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32, P, sz, P]
+        L.sage_attn_fwd.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, P, sz, P]
         L.sage_attn_fwd.restype = i32
         L.sage_attn_quantized.argtypes = [ctypes.POINTER(QuantBufs), P, i32, i32, i32, i32, i32, f32, i32, i32, P]
         L.sage_attn_quantized.restype = i32
@@ -95,16 +95,16 @@ def quant_bufs_from_workspace(ws_ptr: int, nbytes: int, B: int, H: int, N: int, 
 
 
 def quant_smooth(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, H: int, N: int, D: int,
-                 bufs: QuantBufs, stream: int = 0, qk_bits: int = 4) -> None:
-    _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, qk_bits, ctypes.byref(bufs), stream),
-           "sage_quant_smooth")
+                 bufs: QuantBufs, stream: int = 0, qk_bits: int = 4, smooth_v: bool = False) -> None:
+    _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, qk_bits, int(bool(smooth_v)),
+                                   ctypes.byref(bufs), stream), "sage_quant_smooth")
 
 
 def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool,
              sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0,
-             qk_bits: int = 4) -> None:
+             qk_bits: int = 4, smooth_v: bool = False) -> None:
     _check(lib().sage_attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale), qk_bits,
-                               in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd")
+                               int(bool(smooth_v)), in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd")
 
 
 def attn_quantized(bufs: QuantBufs, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool, sm_scale: float,
@@ -165,8 +165,9 @@ def _stream_handle(device) -> int:
 
 
 def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype=None, workspace: Workspace = None,
-         out=None, qk_bits: int = 4):
-    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors (qk_bits 4: INT4 Q/K codes, 8: INT8)."""
+         out=None, qk_bits: int = 4, smooth_v: bool = False):
+    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors (qk_bits 4: INT4 Q/K codes, 8: INT8;
+    smooth_v: subtract the V channel means before FP8)."""
     import torch
     if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
         raise ValueError("q, k, v must share one [B, H, N, D] shape")
@@ -185,5 +186,5 @@ def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype
         workspace = alloc_workspace(B, H, N, D, q.device)
     attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, causal, sm_scale,
              _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr, workspace.nbytes,
-             _stream_handle(q.device), qk_bits)
+             _stream_handle(q.device), qk_bits, smooth_v)
     return out

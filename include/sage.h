@@ -32,6 +32,10 @@
  *    Contribution 3) falls back to where INT4 loses accuracy; same
  *    granularity, scale = amax/qmax).  Any other value is SAGE_ERR_INVALID.
  *    Buffers written with one qk_bits must be read with the same value.
+ *  - smooth_v (0 or 1): smooth V before its FP8 quantization by subtracting
+ *    the per-channel mean over all N tokens, added back to O in the epilogue
+ *    (the smoothing of Q and V of the technical-report summary, Key
+ *    Contribution 2; exact for unquantized softmax, whose rows sum to one).
  */
 #ifndef SAGE_H_
 #define SAGE_H_
@@ -80,16 +84,18 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
  *  q_mean            fp32  [B,H,NQB,D]   per-block Q channel means (tail block
  *                    averages its valid tokens only)
  *  k_mean            fp32  [B,H,D]       K channel means over all N tokens
- *  v_codes           uint8 [B,H,NQB,D,128] OCP e4m3fn codes of V/v_scale,
+ *  v_codes           uint8 [B,H,NQB,D,128] OCP e4m3fn codes of (V - v_mean)/v_scale,
  *                    channel-major per 128-key block; position p of a block
  *                    holds key 64(p/64) + 32(s/16) + 8((s%16)/4) + 4((p%64)/32)
  *                    + s%4 with s = p%32
- *  v_scale           fp32  [B,H,D]       per-channel scale (amax/448)
+ *  v_scale           fp32  [B,H,D]       per-channel scale (max|V - v_mean|/448)
  *  delta_s           fp32  [B,H,NQB,NP]  compensation term
  *                    DeltaS[qb][j] = q_mean[qb] . (K[j] - k_mean), fp32
  *                    accumulation (not scaled by sm_scale)
- *  k_part, v_part    fp32  [B,H,NQB,D]   scratch: per-chunk K sums and V
- *                    absmax, later reused for bf16 pieces of q_mean
+ *  k_part, v_part    fp32  [B,H,NQB,2,D] scratch: per-chunk K and V sums, V
+ *                    maxima and minima, later reused for bf16 pieces of q_mean
+ *  v_mean            fp32  [B,H,D]       V channel means over all N tokens with
+ *                    smooth_v, zeros without; added to O by the fused kernel
  */
 typedef struct {
   uint8_t* q_codes;
@@ -103,6 +109,7 @@ typedef struct {
   float* delta_s;
   float* k_part;
   float* v_part;
+  float* v_mean;
 } sage_quant_bufs;
 
 /* Version of the contract constants above (1 = 128/128/16). */
@@ -131,11 +138,12 @@ sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H,
  * per-channel scales, compensation term): the smoothing of the method and
  * the quantization of Q, K to INT4 and V to FP8 (SageAttention2 abstract).
  * q, k, v: device [B,H,N,D] of in_dtype (SAGE_F16 or SAGE_BF16); qk_bits 4 or
- * 8.  All arrays of *out must be device buffers of the sizes listed above
- * (for example carved by sage_quant_bufs_from_workspace).
+ * 8; smooth_v 0 or 1.  All arrays of *out must be device buffers of the sizes
+ * listed above (for example carved by sage_quant_bufs_from_workspace).
  */
 sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H,
-                              int N, int D, int qk_bits, const sage_quant_bufs* out, hipStream_t stream);
+                              int N, int D, int qk_bits, int smooth_v, const sage_quant_bufs* out,
+                              hipStream_t stream);
 
 /*
  * Attention forward: O = SageAttention2(Q, K, V), i.e. the prepass above
@@ -148,13 +156,14 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
  *  causal    nonzero: query i attends to keys j <= i
  *  sm_scale  softmax scale (> 0, finite), usually 1/sqrt(D)
  *  qk_bits   4 (INT4 Q/K codes) or 8 (INT8)
+ *  smooth_v  1: subtract the V channel means before FP8, add them to O
  *  workspace device buffer of at least sage_workspace_bytes(B,H,N,D) bytes;
  *            afterwards it holds the sage_quant_bufs of this call
  * Equivalent to sage_quant_smooth followed by sage_attn_quantized.
  */
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
-                          int causal, float sm_scale, int qk_bits, sage_dtype in_dtype, sage_dtype out_dtype,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
+                          sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The fused attention kernel alone, over prepass buffers already written by
@@ -162,7 +171,7 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
  * dequantization with the compensation term, online softmax, FP8 P~V with
  * two-level accumulation (SageAttention2 abstract).  Arguments as for
  * sage_attn_fwd; qb must describe buffers of this B, H, N, D written with
- * this qk_bits.
+ * this qk_bits (v_mean, written by the prepass, carries the V smoothing).
  */
 sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
                                 float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream);

@@ -142,6 +142,7 @@ class Readback:
         self.v_codes_raw = arr(qb.v_codes, BH * NP * D, np.uint8, (BH, NQB, D, 128))
         self.v_codes = unpermute_v(self.v_codes_raw, BH, NQB, D, N)
         self.v_scale = arr(qb.v_scale, BH * D * 4, np.float32, (BH, D))
+        self.v_mean = arr(qb.v_mean, BH * D * 4, np.float32, (BH, D))
         self.delta_s_p = arr(qb.delta_s, BH * NQB * NP * 4, np.float32, (BH, NQB, NP))
         G = 2 * ((N + 31) // 32)
         self.q_scale = self.q_scale_p[:, :N]
@@ -150,25 +151,26 @@ class Readback:
         torch.cuda.synchronize()
 
 
-def run_quant_smooth(q_bits, k_bits, v_bits, dtype: str, qk_bits: int = 4):
+def run_quant_smooth(q_bits, k_bits, v_bits, dtype: str, qk_bits: int = 4, smooth_v: bool = False):
     torch = torch_mod()
     B, H, N, D = q_bits.shape
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
     ws = sage.alloc_workspace(B, H, N, D)
     ws.tensor.fill_(0xA5)  # poison: every array element the prepass owns must be written
     sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code(dtype), B, H, N, D, ws.bufs(),
-                      torch.cuda.current_stream().cuda_stream, qk_bits=qk_bits)
+                      torch.cuda.current_stream().cuda_stream, qk_bits=qk_bits, smooth_v=smooth_v)
     torch.cuda.synchronize()
     return ws
 
 
-def run_attn(q_bits, k_bits, v_bits, dtype: str, causal: bool, sm_scale: float, out_dtype=None, qk_bits: int = 4):
+def run_attn(q_bits, k_bits, v_bits, dtype: str, causal: bool, sm_scale: float, out_dtype=None, qk_bits: int = 4,
+             smooth_v: bool = False):
     torch = torch_mod()
     B, H, N, D = q_bits.shape
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
     ws = sage.alloc_workspace(B, H, N, D)
     out = sage.attn(q, k, v, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or torch.float32, workspace=ws,
-                    qk_bits=qk_bits)
+                    qk_bits=qk_bits, smooth_v=smooth_v)
     torch.cuda.synchronize()
     return out, ws
 

@@ -48,7 +48,7 @@ def _sizes(B, H, N, D):
     NQB = NP // 128
     BH = B * H
     return [BH * NP * D, BH * NP * D, BH * NP * 4, BH * NP // 16 * 4, BH * NQB * D * 4, BH * D * 4,
-            BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * D * 4, BH * NQB * D * 4]
+            BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * 2 * D * 4, BH * NQB * 2 * D * 4, BH * D * 4]
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 256, 64), (4, 32, 4096, 128), (2, 48, 17776, 64), (1, 1, 1, 128)])
@@ -74,13 +74,14 @@ def test_workspace_carving(shape):
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), o=FAKE + (3 << 30), B=1, H=2, N=256, D=64, causal=0,
-             sm_scale=0.125, qk_bits=4, in_dtype=sage.F16, out_dtype=sage.F32, ws=FAKE + (4 << 30), ws_bytes=None)
+             sm_scale=0.125, qk_bits=4, smooth_v=0, in_dtype=sage.F16, out_dtype=sage.F32, ws=FAKE + (4 << 30),
+             ws_bytes=None)
     a.update(kw)
     if a["ws_bytes"] is None:
         a["ws_bytes"] = sage.workspace_bytes(a["B"], a["H"], a["N"], a["D"])
     return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["D"], a["causal"],
-                                    a["sm_scale"], a["qk_bits"], a["in_dtype"], a["out_dtype"], a["ws"], a["ws_bytes"],
-                                    None)
+                                    a["sm_scale"], a["qk_bits"], a["smooth_v"], a["in_dtype"], a["out_dtype"], a["ws"],
+                                    a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -93,6 +94,7 @@ def _attn(**kw):
     (dict(ws_bytes=100), sage.ERR_WORKSPACE), (dict(o=FAKE + 64), sage.ERR_INVALID),
     (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID), (dict(qk_bits=0), sage.ERR_INVALID),
     (dict(qk_bits=2), sage.ERR_INVALID), (dict(qk_bits=6), sage.ERR_INVALID), (dict(qk_bits=16), sage.ERR_INVALID),
+    (dict(smooth_v=2), sage.ERR_INVALID), (dict(smooth_v=-1), sage.ERR_INVALID),
 ])
 def test_attn_fwd_validation(kw, expect):
     assert _attn(**kw) == expect
@@ -100,12 +102,12 @@ def test_attn_fwd_validation(kw, expect):
 
 def test_quant_smooth_and_debug_validation():
     L = sage.lib()
-    qb = sage.QuantBufs(*([FAKE] * 11))
-    assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, ctypes.byref(qb), None) == sage.ERR_INVALID
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, 4, ctypes.byref(qb), None) == sage.ERR_INVALID
-    bad = sage.QuantBufs(*([FAKE] * 10 + [0]))
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, ctypes.byref(bad), None) == sage.ERR_INVALID
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, None, None) == sage.ERR_INVALID
+    qb = sage.QuantBufs(*([FAKE] * 12))
+    assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, 4, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
+    bad = sage.QuantBufs(*([FAKE] * 11 + [0]))
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(bad), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, None, None) == sage.ERR_INVALID
     dbg = L.sage_qk_int32_debug
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 101, 4, FAKE, None) == sage.ERR_INVALID
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 1, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
@@ -114,8 +116,9 @@ def test_quant_smooth_and_debug_validation():
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 0, 4, FAKE, None) == sage.ERR_INVALID
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 4, 4, None, None) == sage.ERR_INVALID
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 7, 0, 0, 0, 4, 4, FAKE, None) == sage.ERR_INVALID
-    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 3, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 3, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
     assert L.sage_attn_quantized(ctypes.byref(qb), FAKE, 1, 1, 10, 64, 0, 0.125, 5, sage.F32, None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 2, ctypes.byref(qb), None) == sage.ERR_INVALID
     assert L.sage_attn_quantized(ctypes.byref(qb), FAKE, 1, 1, 10, 64, 0, 0.0, 8, sage.F32, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(None, FAKE, 10, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(FAKE, FAKE, 0, None) == sage.ERR_INVALID

@@ -57,7 +57,12 @@ def _check_prepass(rb, z):
     assert np.array_equal(rb.k_mean, zq(z.k_mean)), "k means"
     assert np.array_equal(rb.v_scale, zq(z.v_scale)), "v scales"
     assert np.array_equal(rb.v_codes, zq(z.v_codes)), "v codes"
-    # padding rows: zero codes and zero scales
+    assert np.array_equal(rb.v_mean, zq(z.v_mean)), "v means"
+    # padding rows: zero codes and zero scales; padding keys of V are zero bytes
+    keys = (np.arange(rb.NQB)[:, None] * 128 + gh_vperm(D)[None, :])            # [NQB, 128] key of each position
+    pad = keys >= N
+    if pad.any():
+        assert np.all(rb.v_codes_raw.transpose(0, 1, 3, 2)[:, pad] == 0), "padding V bytes"
     assert np.all(rb.q_scale_p[:, N:] == 0)
     assert np.all(rb.q_codes_all[:, N:] == 0) and np.all(rb.k_codes_all[:, N:] == 0)
     if rb.qk_bits == 4:
@@ -122,10 +127,15 @@ def test_qk_int32_bitexact_small(oracle_lib, w, bits):
         assert np.array_equal(out.cpu().numpy(), ref)
 
 
+def gh_vperm(D):
+    import gpu_helpers as gh
+    return gh.vperm_keys()
+
+
 def _compare_o(O_gpu, O_ref, slack, label):
     err = np.abs(O_gpu.astype(np.float64) - O_ref.astype(np.float64)).max(1)
     allowed = O_TOL + slack
-    bad = np.nonzero(err > allowed)[0]
+    bad = np.nonzero(~(err <= allowed))[0]   # NaN rows fail too
     used = int(np.sum(err > O_TOL))
     print(f"[{label}] rows={err.size} maxerr={err.max():.3e} rows_using_slack={used} max_slack={slack.max():.3e}")
     assert bad.size == 0, (label, bad[:5], err[bad[:5]], slack[bad[:5]])
@@ -259,3 +269,50 @@ def test_full_size_parity(oracle_lib, w, bits):
         c_gpu, c_orc = gh.cos_sim(O_gpu_all[bh][rows], O_fp), gh.cos_sim(O_ref, O_fp)
         print(f"[{w.name}/int{bits}/bh{bh}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
         assert abs(c_gpu - c_orc) < 1e-3
+
+
+SMOOTH_V_CASES = [SMALL[3], SMALL[4], SMALL[5], SMALL[7],
+                  wl.custom(1, 2, 333, 128, seed=108, k_offset_std=3.0, v_offset_std=4.0)]
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("w", SMOOTH_V_CASES, ids=_id)
+def test_smooth_v_parity_small(oracle_lib, w, bits):
+    """V smoothing: prepass bit-exact (V means, scales of V - mean, FP8 codes)
+    and O within the bar against the oracle's mirror with the mean added back."""
+    import gpu_helpers as gh
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), qk_bits=bits, smooth_v=True)
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, eps=EPS_TIE)
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits, smooth_v=True)
+    rb = gh.Readback(ws, qk_bits=bits)
+    _check_prepass(rb, z)
+    O_gpu = out.cpu().numpy().reshape(-1, w.D)
+    _compare_o(O_gpu, O_ref, slack, f"{w.name}/int{bits}/smooth_v")
+    O_fp, _ = oracle_lib.attn_exact(q, k, v, _sdt(w), w.causal, w.scale, 0)
+    c_gpu, c_orc = gh.cos_sim(O_gpu, O_fp), gh.cos_sim(O_ref, O_fp)
+    print(f"[{w.name}/int{bits}/smooth_v] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+    assert abs(c_gpu - c_orc) < 1e-4
+
+
+def test_smooth_v_full_size_dit(oracle_lib):
+    """The DiT workload (V carries a per-channel offset) with V smoothing, in
+    the benchmark's launch: prepass of every head bit-exact, O on sampled rows
+    of the first and last head."""
+    import gpu_helpers as gh
+    w = wl.DIT
+    q, k, v = wl.generate(w)
+    BH = w.B * w.H
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, smooth_v=True)
+    rb = gh.Readback(ws)
+    z_all = oracle_lib.quant_smooth(q, k, v, _sdt(w), with_delta_s=False, smooth_v=True)
+    _check_prepass(rb, z_all)
+    del z_all
+    O_gpu_all = out.cpu().numpy().reshape(BH, w.N, w.D)
+    rng = np.random.default_rng(w.seed)
+    for bh in (0, BH - 1):
+        qs, kk, vs = (a.reshape(BH, 1, w.N, w.D)[bh:bh + 1] for a in (q, k, v))
+        z = oracle_lib.quant_smooth(qs, kk, vs, _sdt(w), smooth_v=True)
+        rows = _sample_rows(w, 1, rng)
+        O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, rows=rows, eps=EPS_TIE)
+        _compare_o(O_gpu_all[bh][rows], O_ref, slack, f"{w.name}/smooth_v/bh{bh}")
