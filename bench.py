@@ -198,12 +198,80 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     return rec
 
 
+def run_packed(pw, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = False):
+    """A packed variable-length batch through the varlen entry points (prepass,
+    then the fused kernel), timed like the dense workloads."""
+    import numpy as np
+    import torch
+
+    from fp8_attention_transformer_amd import sage
+    from fp8_attention_transformer_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    base = pw.base
+    tdt = torch.float16 if base.dtype == wl.F16 else torch.bfloat16
+    qb, kb, vb, cu = wl.generate_packed(pw)
+    q, k, v = (torch.from_numpy(a.view(np.int16)).view(tdt).cuda() for a in (qb, kb, vb))
+    cu_d = torch.from_numpy(cu).cuda()
+    T, H, D = q.shape
+    nseq, maxlen = len(pw.lengths), max(pw.lengths)
+    ws = sage.alloc_workspace(nseq, H, maxlen, D)
+    bufs = ws.bufs()
+    out = torch.empty((T, H, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    in_code = sage.F16 if tdt == torch.float16 else sage.BF16
+
+    def pre():
+        sage.quant_smooth_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, cu_d.data_ptr(), nseq, maxlen, T,
+                                 H, D, bufs, sh, qk_bits=qk_bits, smooth_v=smooth_v)
+
+    def fused():
+        sage.attn_quantized_varlen(bufs, out.data_ptr(), cu_d.data_ptr(), nseq, maxlen, T, H, D, base.causal,
+                                   base.scale, in_code, sh, qk_bits=qk_bits)
+
+    for _ in range(warmup):
+        pre()
+        fused()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        pre()
+        ev[i][1].record(stream)
+        fused()
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    value = pw.ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = pw.ops / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"int{qk_bits}+fp8", "data": "synthetic",
+        "config": {"workload": pw.name, "nseq": nseq, "lengths": list(pw.lengths), "T": T, "H": H, "D": D,
+                   "causal": base.causal, "in_dtype": base.dtype, "out_dtype": base.dtype, "qk_bits": qk_bits,
+                   "smooth_v": smooth_v, "ops": "sum over sequences of 4*H*N_s^2*D (halved causal)"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": None, "kernel": "attn_kernel",
+                     "kernel_us": round(attn_ms * 1e3, 2)},
+        "breakdown": {"prepass_us": round(pre_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                      "e2e_frac_of_peak": round(value / PEAK_TOPS, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, help="workload name, or 'all' (default: the N=16k D=128 headline)")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (dense or packed), or 'all' (default: the N=16k D=128 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--qk-bits", type=int, default=4, choices=(4, 8),
@@ -231,12 +299,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst, evict
+    packed = {p.name: p for p in wl.PACKED}
     if args.workload == "all":
-        todo = wl.ALL
+        todo = wl.ALL + wl.PACKED
+    elif args.workload in packed:
+        todo = [packed[args.workload]]
     else:
         todo = [wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE]
     for w in todo:
-        rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits, args.smooth_v)
+        if isinstance(w, wl.PackedWorkload):
+            rec = run_packed(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
+        else:
+            rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits,
+                      args.smooth_v)
         print(json.dumps(rec), flush=True)
 
 

@@ -46,6 +46,8 @@ Dims make_dims(int B, int H, int N, int D, int qk_bits = 8, int smooth_v = 0) {
   d.NQB = d.NP / 128;
   d.QB = qk_bits;
   d.SV = smooth_v;
+  d.cu = nullptr;
+  d.T = 0;
   return d;
 }
 
@@ -240,6 +242,83 @@ sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, 
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
   const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, N, D, qk_bits), bh, q0, k0, nq, nk, out, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+// Packed variable-length batches: nseq sequences of at most max_seqlen tokens
+// in token-major [T, H, D] tensors, workspace of the dense shape
+// (nseq, H, max_seqlen, D).
+static bool varlen_ok(const int* cu, int nseq, int max_seqlen, int total, int H, int D) {
+  // the prepass grids put the 128-token blocks in the y dimension (<= 65535)
+  return cu && total >= 1 && shape_ok(nseq, H, max_seqlen, D) && (max_seqlen + 127) / 128 <= 65535;
+}
+
+sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v, sage_dtype in_dtype,
+                                     const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens, int H, int D,
+                                     int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream) {
+  if (!q || !k || !v || !bufs_ok(out) || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
+    return SAGE_ERR_INVALID;
+  if (!bits_ok(qk_bits) || (smooth_v != 0 && smooth_v != 1)) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits, smooth_v);
+  if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
+  d.cu = cu_seqlens;
+  d.T = total_tokens;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), 1.0f, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int* cu_seqlens,
+                                 int nseq, int max_seqlen, int total_tokens, int H, int D, int causal, float sm_scale,
+                                 int qk_bits, int smooth_v, sage_dtype in_dtype, sage_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
+    return SAGE_ERR_INVALID;
+  if (!bits_ok(qk_bits) || (smooth_v != 0 && smooth_v != 1)) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits, smooth_v);
+  const size_t need = total_bytes(d);
+  if (need == 0) return SAGE_ERR_INVALID;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  size_t elems, obytes, ibytes;
+  if (!mul_ok((size_t)total_tokens * H, (size_t)D, &elems)) return SAGE_ERR_INVALID;
+  if (!mul_ok(elems, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(elems, 2, &ibytes)) return SAGE_ERR_INVALID;
+  if (ranges_overlap(o, obytes, q, ibytes) || ranges_overlap(o, obytes, k, ibytes) ||
+      ranges_overlap(o, obytes, v, ibytes) || ranges_overlap(o, obytes, workspace, need))
+    return SAGE_ERR_INVALID;
+  d.cu = cu_seqlens;
+  d.T = total_tokens;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  sage_quant_bufs qb;
+  carve(workspace, d, &qb);
+  const Bufs b = to_internal(qb);
+  const float ks = sm_scale * 1.44269504088896340736f;
+  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, 1.0f, stream);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_attn(b, d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+sage_status sage_attn_quantized_varlen(const sage_quant_bufs* qb, void* o, const int* cu_seqlens, int nseq,
+                                       int max_seqlen, int total_tokens, int H, int D, int causal, float sm_scale,
+                                       int qk_bits, sage_dtype out_dtype, hipStream_t stream) {
+  if (!bufs_ok(qb) || !o || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D) || !bits_ok(qk_bits))
+    return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits);
+  if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
+  d.cu = cu_seqlens;
+  d.T = total_tokens;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const float ks = sm_scale * 1.44269504088896340736f;
+  const hipError_t e = sage::launch_attn(to_internal(*qb), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

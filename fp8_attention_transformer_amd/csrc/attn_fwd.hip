@@ -253,13 +253,14 @@ __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, c
   }
 }
 
+// n: valid keys of the head; nqb: its key blocks.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
                                              const float* cKS, float dq, float ks, int t, int qb, int qrow, int h,
-                                             const Dims& d, v8i* P8, float& alpha) {
+                                             int n, int nqb, v8i* P8, float& alpha) {
   float s2[4][16];
   float tmax[4];
-  const bool need_mask = (CAUSAL && t == qb) || (t == d.NQB - 1 && d.N != d.NP);
+  const bool need_mask = (CAUSAL && t == qb) || (t == nqb - 1 && n != nqb * kBK);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     const float c = (dq * cKS[2 * T + h]) * ks;
@@ -272,7 +273,7 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int key = t * kBK + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool bad = (key >= d.N) || (CAUSAL && key > qrow);
+        const bool bad = (key >= n) || (CAUSAL && key > qrow);
         if (bad) s2[T][r] = -__builtin_inff();
       }
     }
@@ -338,14 +339,14 @@ __device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8,
 template <int D, int BITS, bool CAUSAL>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
-                                           int t, int qb, int qrow, int n, int h, const Dims& d) {
+                                           int t, int qb, int qrow, int n, int h, int nvalid, int nqb) {
   v16f S[4];
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   qk_part<D, BITS>(S, qop, cK, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   v8i P8[2];
   float alpha;
-  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, qb, qrow, h, d, P8, alpha);
+  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, qb, qrow, h, nvalid, nqb, P8, alpha);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -385,9 +386,15 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const int n = lane & 31, h = lane >> 5;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = logical / d.NQB;
-  const int jq = logical % d.NQB;
+  // Dense: head-major (the query blocks of a head share an XCD's L2).
+  // Packed sequences of unequal length: query-block-major, so the heaviest
+  // blocks of every sequence start first and no long sequence trails.
+  const int bh = d.cu ? logical % d.BH() : logical / d.NQB;
+  const int jq = d.cu ? logical / d.BH() : logical % d.NQB;
   const int qb = CAUSAL ? d.NQB - 1 - jq : jq;
+  const HeadIO io = head_io(d, bh);
+  const int nqb = (io.n + kBQ - 1) / kBQ;        // query and key blocks of this head
+  if (qb >= nqb) return;                         // past a shorter packed sequence (whole workgroup)
   const int qrow = qb * kBQ + wave * 32 + n;     // padded query index of this lane
   const size_t hrowp = (size_t)bh * d.NP;
 
@@ -395,7 +402,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const uint8_t* kblk = b.k_codes + hrowp * ROWB;
   const uint8_t* vblk = b.v_codes + (size_t)bh * d.NQB * D * kBK;
   const float* kscl = b.k_scale + hrowp / kKGroup;
-  const int tend = CAUSAL ? qb + 1 : d.NQB;
+  const int tend = CAUSAL ? qb + 1 : nqb;
 
   // Every wave issues the same number of memory ops per block (the small
   // loads are unconditional, with in-range indices), so a vmcnt limit of
@@ -438,7 +445,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     const int slot = t % S;
     const bool ahead = t + S - 1 < tend;          // block t+S-1 exists: stage it now
     if (ahead) issue(t + S - 1, (t + S - 1) % S);
-    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, d);
+    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, io.n,
+                                nqb);
     if (t + 1 < tend) {
       // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
       if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
@@ -450,10 +458,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 
   // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
   const int qi = qrow;
-  if (qi < d.N) {
+  if (qi < io.n) {
     const float* vs = b.v_scale + (size_t)bh * D;
     const float* vm = b.v_mean + (size_t)bh * D;
-    const size_t orow = ((size_t)bh * d.N + qi) * D;
+    const size_t orow = io.base + (size_t)qi * io.stride;
     const float inv_l = 1.0f / as.l;
 #pragma unroll
     for (int dt = 0; dt < NDT; dt++)

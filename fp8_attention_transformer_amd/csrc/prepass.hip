@@ -29,9 +29,12 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   const int tid = threadIdx.x, cp = tid % LPC;
   const int chunk = blockIdx.x * CPW + tid / LPC;
   if (chunk >= d.BH() * d.NQB) return;
-  const int bh = chunk / d.NQB, qb = chunk % d.NQB;
-  const int i0 = qb * kBQ, i1 = min(d.N, i0 + kBQ);
-  const size_t base = ((size_t)bh * d.N) * D + 2 * cp;
+  // dense: the chunks of a head are adjacent; packed [T, H, D]: the heads of a
+  // token block are adjacent, so neighbouring workgroups read whole rows
+  const int bh = d.cu ? chunk % d.BH() : chunk / d.NQB, qb = d.cu ? chunk / d.BH() : chunk % d.NQB;
+  const HeadIO io = head_io(d, bh);
+  const int i0 = qb * kBQ, i1 = min(io.n, i0 + kBQ);   // i1 <= i0: empty chunk (short sequence)
+  const size_t base = io.base + 2 * cp, rs = io.stride;
   float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
   float vx0 = -__builtin_inff(), vx1 = -__builtin_inff(), vn0 = __builtin_inff(), vn1 = __builtin_inff();
   auto add = [&](uint32_t qv, uint32_t kv, uint32_t vv) {
@@ -53,7 +56,7 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
       uint32_t qv[U], kv[U], vv[U];
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        const size_t o = base + (size_t)(i + u) * D;
+        const size_t o = base + (size_t)(i + u) * rs;
         qv[u] = *(const uint32_t*)(q + o);
         kv[u] = *(const uint32_t*)(k + o);
         vv[u] = *(const uint32_t*)(v + o);
@@ -63,15 +66,15 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
     }
   } else {
     for (int i = i0; i < i1; i++) {
-      const size_t o = base + (size_t)i * D;
+      const size_t o = base + (size_t)i * rs;
       add(*(const uint32_t*)(q + o), *(const uint32_t*)(k + o), *(const uint32_t*)(v + o));
     }
   }
   const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
   const size_t o2 = ((size_t)bh * d.NQB + qb) * 2 * D + 2 * cp;
   const float cnt = (float)(i1 - i0);
-  b.q_mean[o] = qs0 / cnt;
-  b.q_mean[o + 1] = qs1 / cnt;
+  b.q_mean[o] = i1 > i0 ? qs0 / cnt : 0.0f;
+  b.q_mean[o + 1] = i1 > i0 ? qs1 / cnt : 0.0f;
   b.k_part[o2] = ks0;
   b.k_part[o2 + 1] = ks1;
   b.k_part[o2 + D] = vs0;
@@ -113,10 +116,11 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
       vn = fminf(vn, np[u]);
     }
   }
-  b.k_mean[(size_t)bh * D + c] = tot / (float)d.N;
-  const float vbar = d.SV ? vtot / (float)d.N : 0.0f;
+  const int n = head_io(d, bh).n;   // 0 only for an empty packed sequence
+  b.k_mean[(size_t)bh * D + c] = n ? tot / (float)n : 0.0f;
+  const float vbar = (d.SV && n) ? vtot / (float)n : 0.0f;
   b.v_mean[(size_t)bh * D + c] = vbar;
-  b.v_scale[(size_t)bh * D + c] = fmaxf(fabsf(vx - vbar), fabsf(vn - vbar)) / 448.0f;
+  b.v_scale[(size_t)bh * D + c] = n ? fmaxf(fabsf(vx - vbar), fabsf(vn - vbar)) / 448.0f : 0.0f;
 }
 
 // Position p (0..127) inside a 128-key block of the FP8 V layout holds key
@@ -232,17 +236,21 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
   constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
   __shared__ __align__(16) uint16_t sV[kBK * D];
-  const int qb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  // grid (NQB, B*H), or (B*H, NQB) for packed [T, H, D] inputs (heads of a
+  // token block adjacent)
+  const int qb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i0 = qb * kBQ;
-  const size_t hrow = (size_t)bh * d.N;      // first input row of this head
+  const HeadIO io = head_io(d, bh);          // input tokens of this head
+  // past the end of a shorter packed sequence: nothing here is ever read
+  if (d.cu && i0 >= io.n) return;
   const size_t hrowp = (size_t)bh * d.NP;    // first padded row of this head
 
   // ---- V block -> LDS (rows >= N are zero)
   for (int e = tid; e < kBK * D / 8; e += 256) {
     const int r = e / (D / 8), c8 = e % (D / 8);
     v4i val = {0, 0, 0, 0};
-    if (i0 + r < d.N) val = *(const v4i*)(v + (hrow + i0 + r) * D + 8 * c8);
+    if (i0 + r < io.n) val = *(const v4i*)(v + io.base + (size_t)(i0 + r) * io.stride + 8 * c8);
     *(v4i*)(sV + r * D + 8 * c8) = val;
   }
 
@@ -271,8 +279,8 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
     for (int r = tid / LPT; r < kBQ; r += TPP) {
       const int i = i0 + r;
       float g[16];
-      if (i < d.N) {
-        load16<IN>(q + (hrow + i) * D + c0, g);
+      if (i < io.n) {
+        load16<IN>(q + io.base + (size_t)i * io.stride + c0, g);
 #pragma unroll
         for (int e = 0; e < 16; e++) g[e] = g[e] - qm[e];
       } else {
@@ -334,9 +342,9 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       const int T = grp >> 1, hh = grp & 1;
       const int j = i0 + 32 * T + 8 * (ki >> 2) + 4 * hh + (ki & 3);
       float g[32];
-      if (j < d.N) {
-        load16<IN>(k + (hrow + j) * D + c0, g);
-        load16<IN>(k + (hrow + j) * D + c0 + 16, g + 16);
+      if (j < io.n) {
+        load16<IN>(k + io.base + (size_t)j * io.stride + c0, g);
+        load16<IN>(k + io.base + (size_t)j * io.stride + c0 + 16, g + 16);
 #pragma unroll
         for (int e = 0; e < 32; e++) g[e] = g[e] - km[e];
       } else {
@@ -401,7 +409,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       for (int u = 0; u < 16; u++) {
         // padding keys stay exactly zero (also when V is smoothed)
         const int key = vperm_key(16 * c + u);
-        x[u] = i0 + key < d.N ? in_to_f32<IN>(sV[key * D + ch]) - vbar : 0.0f;
+        x[u] = i0 + key < io.n ? in_to_f32<IN>(sV[key * D + ch]) - vbar : 0.0f;
       }
       fp8_quotients<16>(x, dv);
       v4i pk;
@@ -422,9 +430,13 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 template <int IN, int D>
 __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
   constexpr int NK = D / 16;   // k-steps of the 32x32x16 bf16 MFMA
-  const int kb = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int kb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
   const int j = kb * kBK + 32 * wave + n;        // this lane's key (B operand column)
+  const HeadIO io = head_io(d, bh);
+  // packed sequences: only key blocks and query blocks inside the sequence
+  const int nqb = d.cu ? (io.n + kBQ - 1) / kBQ : d.NQB;
+  if (kb >= nqb) return;
   const float* km = b.k_mean + (size_t)bh * D;
   // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
   v8bf B1[NK], B2[NK], B3[NK];
@@ -435,8 +447,8 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
     const float4 m1 = *(const float4*)(km + c0 + 4);
     const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     float g[8];
-    if (j < d.N) {
-      const v4i raw = *(const v4i*)(k + ((size_t)bh * d.N + j) * D + c0);
+    if (j < io.n) {
+      const v4i raw = *(const v4i*)(k + io.base + (size_t)j * io.stride + c0);
 #pragma unroll
       for (int w = 0; w < 4; w++) {
         g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF)) - mv[2 * w];
@@ -474,8 +486,8 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
   stage(0, sA0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = 0, it = 0; qt < d.NQB; qt += 32, it++) {
-    const bool more = qt + 32 < d.NQB;
+  for (int qt = 0, it = 0; qt < nqb; qt += 32, it++) {
+    const bool more = qt + 32 < nqb;
     if (more) stage(qt + 32, (it & 1) ? sA0 : sA1);
     const uint16_t* A = (it & 1) ? sA1 : sA0;
     v16f acc;
@@ -518,7 +530,7 @@ template <int IN, int D>
 hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims& d, const Bufs& b, float ds_scale,
                         hipStream_t s) {
   (void)ds_scale;
-  const dim3 grid(d.NQB, d.BH());
+  const dim3 grid = d.cu ? dim3(d.BH(), d.NQB) : dim3(d.NQB, d.BH());
   const uint16_t* q16 = (const uint16_t*)q;
   const uint16_t* k16 = (const uint16_t*)k;
   const uint16_t* v16 = (const uint16_t*)v;

@@ -45,8 +45,39 @@ struct Dims {
   int NQB;   // NP / 128
   int QB;    // bits per Q/K code: 4 (INT4, stored as FP6) or 8 (INT8)
   int SV;    // 1: smooth V (subtract the per-channel V mean before FP8)
+  // Packed variable-length batches: when cu is not null, head b*H + h is
+  // sequence b, tokens cu[b] .. cu[b+1]-1 of a token-major [T, H, D] tensor,
+  // and N is the maximum length (it sets the workspace geometry).
+  const int* cu;
+  int T;
   __host__ __device__ int BH() const { return B * H; }
 };
+
+// Where the tokens of head bh live in q, k, v and o: token i starts at element
+// base + i*stride; n tokens are valid.  For packed batches the sequence length
+// is clamped to [0, N] and to the tensor (offsets outside [0, T] give an
+// empty sequence), so malformed offsets never lead outside the buffers.
+struct HeadIO {
+  int n;
+  size_t base, stride;
+};
+__device__ inline HeadIO head_io(const Dims& d, int bh) {
+  HeadIO io;
+  if (!d.cu) {
+    io.n = d.N;
+    io.base = (size_t)bh * d.N * d.D;
+    io.stride = (size_t)d.D;
+    return io;
+  }
+  const int b = bh / d.H, h = bh % d.H;
+  const int s = d.cu[b], e = d.cu[b + 1];
+  int n = (s < 0 || s > d.T) ? 0 : min(e - s, min(d.N, d.T - s));
+  n = n < 0 ? 0 : n;
+  io.n = n;
+  io.base = (((size_t)(n > 0 ? s : 0)) * d.H + h) * d.D;
+  io.stride = (size_t)d.H * d.D;
+  return io;
+}
 
 // Device buffers written by the prepass and read by the attention kernel.
 struct Bufs {

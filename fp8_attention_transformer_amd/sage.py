@@ -21,6 +21,7 @@ F16, BF16, F32 = 0, 1, 2
 EXPORTED = [
     "sage_contract_version", "sage_status_string", "sage_workspace_bytes", "sage_quant_bufs_from_workspace",
     "sage_quant_smooth", "sage_attn_fwd", "sage_attn_quantized", "sage_qk_int32_debug", "sage_fp8_encode_debug",
+    "sage_quant_smooth_varlen", "sage_attn_fwd_varlen", "sage_attn_quantized_varlen",
 ]
 
 
@@ -66,6 +67,15 @@ def lib() -> ctypes.CDLL:
         L.sage_qk_int32_debug.restype = i32
         L.sage_fp8_encode_debug.argtypes = [P, P, sz, P]
         L.sage_fp8_encode_debug.restype = i32
+        L.sage_quant_smooth_varlen.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
+                                               ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth_varlen.restype = i32
+        L.sage_attn_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, P,
+                                           sz, P]
+        L.sage_attn_fwd_varlen.restype = i32
+        L.sage_attn_quantized_varlen.argtypes = [ctypes.POINTER(QuantBufs), P, P, i32, i32, i32, i32, i32, i32, f32,
+                                                 i32, i32, P]
+        L.sage_attn_quantized_varlen.restype = i32
         _lib = L
     return _lib
 
@@ -121,6 +131,30 @@ def qk_int32_debug(bufs: QuantBufs, B: int, H: int, N: int, D: int, bh: int, q0:
 
 def fp8_encode_debug(in_ptr: int, out_ptr: int, n: int, stream: int = 0) -> None:
     _check(lib().sage_fp8_encode_debug(in_ptr, out_ptr, n, stream), "sage_fp8_encode_debug")
+
+
+def quant_smooth_varlen(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, cu_ptr: int, nseq: int, max_seqlen: int,
+                        total: int, H: int, D: int, bufs: QuantBufs, stream: int = 0, qk_bits: int = 4,
+                        smooth_v: bool = False) -> None:
+    _check(lib().sage_quant_smooth_varlen(q_ptr, k_ptr, v_ptr, in_dtype, cu_ptr, nseq, max_seqlen, total, H, D,
+                                          qk_bits, int(bool(smooth_v)), ctypes.byref(bufs), stream),
+           "sage_quant_smooth_varlen")
+
+
+def attn_quantized_varlen(bufs: QuantBufs, o_ptr: int, cu_ptr: int, nseq: int, max_seqlen: int, total: int, H: int,
+                          D: int, causal: bool, sm_scale: float, out_dtype: int, stream: int = 0,
+                          qk_bits: int = 4) -> None:
+    _check(lib().sage_attn_quantized_varlen(ctypes.byref(bufs), o_ptr, cu_ptr, nseq, max_seqlen, total, H, D,
+                                            int(bool(causal)), float(sm_scale), qk_bits, out_dtype, stream),
+           "sage_attn_quantized_varlen")
+
+
+def attn_fwd_varlen(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int, nseq: int, max_seqlen: int,
+                    total: int, H: int, D: int, causal: bool, sm_scale: float, in_dtype: int, out_dtype: int,
+                    ws_ptr: int, ws_bytes: int, stream: int = 0, qk_bits: int = 4, smooth_v: bool = False) -> None:
+    _check(lib().sage_attn_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, cu_ptr, nseq, max_seqlen, total, H, D,
+                                      int(bool(causal)), float(sm_scale), qk_bits, int(bool(smooth_v)), in_dtype,
+                                      out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd_varlen")
 
 
 # ---------------------------------------------------------------- torch glue --
@@ -187,4 +221,34 @@ def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype
     attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, causal, sm_scale,
              _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr, workspace.nbytes,
              _stream_handle(q.device), qk_bits, smooth_v)
+    return out
+
+
+def attn_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, sm_scale: float | None = None,
+                out_dtype=None, workspace: Workspace = None, out=None, qk_bits: int = 4, smooth_v: bool = False):
+    """Packed variable-length attention: q, k, v token-major [T, H, D] fp16/bf16
+    device tensors, cu_seqlens an int32 device tensor [nseq + 1] of sequence
+    offsets (the form of the varlen entry point named in the code record)."""
+    import torch
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 3:
+        raise ValueError("q, k, v must share one [T, H, D] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for t in (q, k, v, cu_seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v and cu_seqlens must be contiguous device tensors")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [nseq + 1]")
+    T, H, D = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(nseq, H, max_seqlen, D, q.device)
+    attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_seqlens.data_ptr(), nseq, max_seqlen,
+                    T, H, D, causal, sm_scale, _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype),
+                    workspace.ptr, workspace.nbytes, _stream_handle(q.device), qk_bits, smooth_v)
     return out

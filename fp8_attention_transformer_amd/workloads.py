@@ -141,3 +141,42 @@ def generate(w: Workload, heads: slice | None = None):
 
 def custom(B, H, N, D, dtype=BF16, causal=False, seed=0, **kw) -> Workload:
     return Workload(f"custom_b{B}h{H}n{N}d{D}", B, H, N, D, dtype, causal, seed, **kw)
+
+
+@dataclass(frozen=True)
+class PackedWorkload:
+    """A packed variable-length batch: independent sequences of the given
+    lengths in token-major [T, H, D] tensors, each drawn like ``base`` (its
+    H, D, dtype, causal flag and distributions; ``base.N`` is ignored) with
+    seed base.seed + sequence index."""
+    name: str
+    lengths: tuple
+    base: Workload
+
+    @property
+    def ops(self) -> float:
+        o = sum(4.0 * self.base.H * n * n * self.base.D for n in self.lengths)
+        return o / 2 if self.base.causal else o
+
+
+def generate_packed(pw: PackedWorkload):
+    """(q, k, v) token-major [T, H, D] 16-bit patterns and cu_seqlens int32 [nseq + 1]."""
+    H, D = pw.base.H, pw.base.D
+    T = int(sum(pw.lengths))
+    out = [np.zeros((T, H, D), np.uint16) for _ in range(3)]
+    off = 0
+    for s, n in enumerate(pw.lengths):
+        if n:
+            parts = generate(pw.base.with_(B=1, N=int(n), seed=pw.base.seed + s))
+            for dst, src in zip(out, parts):
+                dst[off:off + n] = np.transpose(src[0], (1, 0, 2))
+        off += n
+    cu = np.concatenate([[0], np.cumsum(pw.lengths)]).astype(np.int32)
+    return out[0], out[1], out[2], cu
+
+
+# An LLM-serving-style packed prefill batch: eight prompts of mixed length
+# drawn like the LLM prefill workload (causal, H=32, D=128).
+PACKED_LLM = PackedWorkload("packed_llm_8seq_t17115_h32d128_causal",
+                            (4096, 1024, 3072, 512, 2048, 777, 4096, 1490), LLM)
+PACKED = [PACKED_LLM]

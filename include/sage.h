@@ -177,6 +177,41 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
                                 float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Packed variable-length batches (the varlen form of the drop-in call; the
+ * code record of the SageAttention2 paper names `sageattn_varlen`).  nseq
+ * independent self-attention problems share one launch:
+ *  q, k, v, o   token-major [T, H, D] with T = total_tokens; sequence s owns
+ *               tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of every head
+ *  cu_seqlens   DEVICE int32 [nseq+1], non-decreasing, cu_seqlens[0] = 0,
+ *               cu_seqlens[nseq] <= T, every length <= max_seqlen.  It is read
+ *               only by the kernels: lengths are clamped to [0, max_seqlen]
+ *               and to the tensor, so malformed offsets give wrong results
+ *               but no access outside the buffers.  Empty sequences are
+ *               allowed.
+ *  max_seqlen   >= every sequence length; the workspace and the prepass
+ *               buffers have the dense shape (B = nseq, H, N = max_seqlen, D):
+ *               size them with sage_workspace_bytes(nseq, H, max_seqlen, D).
+ *               Row r of head b*H + h in the buffers is token r of sequence b.
+ * Each sequence is smoothed, quantized and attended on its own (its own K and
+ * V means, 128-token Q blocks from its first token, compensation rows, causal
+ * mask), exactly as a dense call with B = 1, N = its length would do.
+ */
+sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v, sage_dtype in_dtype,
+                                     const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens, int H, int D,
+                                     int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream);
+
+sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, const int* cu_seqlens,
+                                 int nseq, int max_seqlen, int total_tokens, int H, int D, int causal, float sm_scale,
+                                 int qk_bits, int smooth_v, sage_dtype in_dtype, sage_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The fused kernel alone over buffers written by sage_quant_smooth_varlen
+ * with the same cu_seqlens, nseq, max_seqlen, total_tokens, H, D, qk_bits. */
+sage_status sage_attn_quantized_varlen(const sage_quant_bufs* qb, void* o, const int* cu_seqlens, int nseq,
+                                       int max_seqlen, int total_tokens, int H, int D, int causal, float sm_scale,
+                                       int qk_bits, sage_dtype out_dtype, hipStream_t stream);
+
+/*
  * Debug: the exact integer dot products of the Q/K codes (qk_bits as written
  * by the prepass), computed by the same matrix-core tile routine as the fused
  * kernel.  For head bh = b*H + h:

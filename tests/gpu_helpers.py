@@ -54,7 +54,7 @@ def _fp6_value(v: np.ndarray) -> np.ndarray:
     return np.where(v & 32, -mag, mag)
 
 
-def fp6_tiles_to_codes(raw: np.ndarray, D: int) -> np.ndarray:
+def fp6_tiles_to_codes(raw: np.ndarray, D: int, strict: bool = True) -> np.ndarray:
     """[BH, NP * row_bytes] FP6 tile layout (include/sage.h) -> int8 codes [BH, NP, D]."""
     LS = fp6_lane_bytes(D)
     BH = raw.shape[0]
@@ -66,7 +66,9 @@ def fp6_tiles_to_codes(raw: np.ndarray, D: int) -> np.ndarray:
     bits = np.unpackbits(groups, axis=-1, bitorder="little").reshape(groups.shape[:-1] + (32, 6))
     fields = (bits.astype(np.int64) << np.arange(6)).sum(-1)          # [BH, tile, chunk, m, i]
     vals = _fp6_value(fields)
-    assert np.all(vals == np.rint(vals)) and np.all(np.abs(vals) <= 7), "FP6 fields are not INT4 codes"
+    if strict:
+        assert np.all(vals == np.rint(vals)) and np.all(np.abs(vals) <= 7), "FP6 fields are not INT4 codes"
+    vals = np.clip(np.rint(vals), -127, 127)
     T = ch.shape[1]
     out = np.empty((BH, T, 32, D), np.int8)
     for h in range(2):
@@ -93,11 +95,12 @@ def codes_to_fp6_tiles(codes: np.ndarray, D: int) -> np.ndarray:
     return ch.reshape(BH, -1)
 
 
-def unpack_codes(packed: np.ndarray, N: int, D: int, qk_bits: int = 4) -> np.ndarray:
-    """Stored code rows -> int8 codes [BH, N, D] (INT4: FP6 tiles; INT8: one byte per channel)."""
+def unpack_codes(packed: np.ndarray, N: int, D: int, qk_bits: int = 4, strict: bool = True) -> np.ndarray:
+    """Stored code rows -> int8 codes [BH, N, D] (INT4: FP6 tiles; INT8: one byte per channel).
+    strict: every FP6 field must be an INT4 code (off where parts of a workspace are never written)."""
     if qk_bits == 8:
         return packed.reshape(packed.shape[0], -1, D).view(np.int8)[:, :N].copy()
-    return fp6_tiles_to_codes(packed, D)[:, :N]
+    return fp6_tiles_to_codes(packed, D, strict)[:, :N]
 
 
 def unpermute_v(vcodes: np.ndarray, BH: int, NQB: int, D: int, N: int) -> np.ndarray:
@@ -112,7 +115,7 @@ def unpermute_v(vcodes: np.ndarray, BH: int, NQB: int, D: int, N: int) -> np.nda
 class Readback:
     """The prepass arrays of a workspace, copied to host in canonical form."""
 
-    def __init__(self, ws: sage.Workspace, qk_bits: int = 4):
+    def __init__(self, ws: sage.Workspace, qk_bits: int = 4, strict: bool = True):
         torch = torch_mod()
         B, H, N, D = ws.B, ws.H, ws.N, ws.D
         BH = B * H
@@ -131,8 +134,8 @@ class Readback:
         rowb = fp6_row_bytes(D) if qk_bits == 4 else D
         self.q_codes_raw = arr(qb.q_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
         self.k_codes_raw = arr(qb.k_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
-        self.q_codes_all = unpack_codes(self.q_codes_raw, NP, D, qk_bits)   # padded rows included
-        self.k_codes_all = unpack_codes(self.k_codes_raw, NP, D, qk_bits)
+        self.q_codes_all = unpack_codes(self.q_codes_raw, NP, D, qk_bits, strict)   # padded rows included
+        self.k_codes_all = unpack_codes(self.k_codes_raw, NP, D, qk_bits, strict)
         self.q_codes = self.q_codes_all[:, :N]
         self.k_codes = self.k_codes_all[:, :N]
         self.q_scale_p = arr(qb.q_scale, BH * NP * 4, np.float32, (BH, NP))

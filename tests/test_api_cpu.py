@@ -159,3 +159,23 @@ def test_fp6_tile_layout_helpers():
     for D in (64, 128):
         c = rng.integers(-7, 8, (2, 96, D)).astype(np.int8)
         assert np.array_equal(gh.fp6_tiles_to_codes(gh.codes_to_fp6_tiles(c, D), D), c)
+
+
+def test_varlen_validation():
+    L = sage.lib()
+    qb = sage.QuantBufs(*([FAKE] * 12))
+    qs = L.sage_quant_smooth_varlen
+    ok_args = (FAKE, FAKE, FAKE, sage.BF16, FAKE, 3, 256, 500, 2, 64, 4, 0, ctypes.byref(qb), None)
+    for i, bad in [(4, None), (5, 0), (6, 0), (7, 0), (9, 96), (10, 5), (11, 2), (3, sage.F32)]:
+        args = list(ok_args)
+        args[i] = bad
+        assert qs(*args) == sage.ERR_INVALID, (i, bad)
+    fwd = L.sage_attn_fwd_varlen
+    ws_bytes = sage.workspace_bytes(3, 2, 256, 64)
+    base = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE, 3, 256, 500, 2, 64, 0, 0.125, 4, 0,
+            sage.BF16, sage.F32, FAKE + (4 << 30), ws_bytes, None]
+    for i, bad, expect in [(4, None, sage.ERR_INVALID), (11, 0.0, sage.ERR_INVALID), (17, 100, sage.ERR_WORKSPACE),
+                           (3, FAKE + 16, sage.ERR_INVALID), (5, -1, sage.ERR_INVALID), (13, 3, sage.ERR_INVALID)]:
+        args = list(base)
+        args[i] = bad
+        assert fwd(*args) == expect, (i, bad)
