@@ -40,16 +40,31 @@ class Workload:
     t_noise_scale: float = 0.0      # Student-t(3) noise added to Q and K
     sm_scale: float | None = None   # default 1/sqrt(D)
     note: str = ""
+    Hkv: int = 0                    # key/value heads (0: same as H); H must be a multiple
+    Nk: int = 0                     # key/value tokens (0: same as N)
 
     @property
     def scale(self) -> float:
         return self.sm_scale if self.sm_scale is not None else 1.0 / math.sqrt(self.D)
 
     @property
+    def hkv(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def nk(self) -> int:
+        return self.Nk or self.N
+
+    @property
+    def self_attention(self) -> bool:
+        return self.hkv == self.H and self.nk == self.N
+
+    @property
     def ops(self) -> float:
-        """Attention operations 4*B*H*N^2*D, halved when causal."""
-        o = 4.0 * self.B * self.H * self.N * self.N * self.D
-        return o / 2 if self.causal else o
+        """Attention operations 4*B*H*N*Nk*D; causal (aligned at the last key)
+        drops the upper triangle of the N x N corner: 4*B*H*D*(N*Nk - N^2/2)."""
+        pairs = self.N * self.nk - (self.N * self.N / 2 if self.causal else 0)
+        return 4.0 * self.B * self.H * pairs * self.D
 
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
@@ -103,11 +118,16 @@ def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def generate(w: Workload, heads: slice | None = None):
-    """Return (q_bits, k_bits, v_bits) as uint16 arrays of shape [B,H,N,D].
+    """Return (q_bits, k_bits, v_bits) as uint16 arrays of shape [B,H,N,D]
+    (K and V [B,Hkv,Nk,D] for a cross-attention or grouped-query workload).
 
     ``heads`` optionally restricts the output to a slice of the flattened B*H
     head index (the draw for every head is still the same as in the full
     tensor, because each head has its own sub-stream)."""
+    if not w.self_attention:
+        if heads is not None:
+            raise ValueError("head slices are for self-attention workloads")
+        return _generate_cross(w)
     B, H, N, D = w.B, w.H, w.N, w.D
     root = np.random.default_rng(w.seed)
     # shared outlier channel indices (same for every head)
@@ -141,6 +161,41 @@ def generate(w: Workload, heads: slice | None = None):
 
 def custom(B, H, N, D, dtype=BF16, causal=False, seed=0, **kw) -> Workload:
     return Workload(f"custom_b{B}h{H}n{N}d{D}", B, H, N, D, dtype, causal, seed, **kw)
+
+
+def _generate_cross(w: Workload):
+    """Queries and keys/values with their own head counts and lengths: one
+    sub-stream per (batch, query head) for Q, then one per (batch, K/V head)
+    for K and V; distributions as in the self-attention draw."""
+    B, Hq, Hk, Nq, Nk, D = w.B, w.H, w.hkv, w.N, w.nk, w.D
+    root = np.random.default_rng(w.seed)
+    out_idx = root.choice(D, w.outlier_channels, replace=False) if w.outlier_channels else np.zeros(0, np.int64)
+    seeds = root.integers(0, 2**63 - 1, size=B * Hq + B * Hk)
+    qs, ks, vs = [], [], []
+    for bh in range(B * Hq):
+        rng = np.random.default_rng(int(seeds[bh]))
+        q = rng.standard_normal((Nq, D), dtype=np.float32)
+        if w.t_noise_scale:
+            q += (w.t_noise_scale * rng.standard_t(3, (Nq, D))).astype(np.float32)
+        if w.outlier_channels:
+            q[:, out_idx] *= np.float32(w.outlier_scale)
+        qs.append(round_to_bits(q, w.dtype))
+    for bh in range(B * Hk):
+        rng = np.random.default_rng(int(seeds[B * Hq + bh]))
+        k = rng.standard_normal((Nk, D), dtype=np.float32)
+        v = rng.standard_normal((Nk, D), dtype=np.float32)
+        if w.t_noise_scale:
+            k += (w.t_noise_scale * rng.standard_t(3, (Nk, D))).astype(np.float32)
+        if w.outlier_channels and w.outliers_in_k:
+            k[:, out_idx] *= np.float32(w.outlier_scale)
+        if w.k_offset_std:
+            k += (w.k_offset_std * rng.standard_normal(D)).astype(np.float32)[None, :]
+        if w.v_offset_std:
+            v += (w.v_offset_std * rng.standard_normal(D)).astype(np.float32)[None, :]
+        ks.append(round_to_bits(k, w.dtype))
+        vs.append(round_to_bits(v, w.dtype))
+    return (np.stack(qs).reshape(B, Hq, Nq, D), np.stack(ks).reshape(B, Hk, Nk, D),
+            np.stack(vs).reshape(B, Hk, Nk, D))
 
 
 @dataclass(frozen=True)

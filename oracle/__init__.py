@@ -22,6 +22,11 @@ something other than itself):
   * attn_mirror           -- equals attn_exact over the same quantized operands
                              when P~ is not quantized (online softmax identity);
                              special cases Q = 0, causal row 0, one dominant key.
+  * general geometry      -- (tests/test_oracle_geometry.py) cross-attention,
+                             decoding and grouped-query heads against a numpy
+                             fp64 brute force with the bottom-right causal mask;
+                             grouped heads equal repeated K/V heads bit for bit;
+                             a single query is its own block mean.
 Parity unpinned: the cosine similarity against FP32 attention is a property of
 the method on the synthetic inputs; the pages print no accuracy figure for it.
 """
@@ -77,13 +82,13 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [P, P, i64]
         L.oracle_e4m3_decode.argtypes = [P, P, i64]
         L.oracle_decode_input.argtypes = [P, i32, P, i64]
-        L.oracle_quant_smooth.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32] + [P] * 10 + [i32]
+        L.oracle_quant_smooth.argtypes = [P, P, P] + [i32] * 9 + [P] * 10 + [i32]
         L.oracle_quant_smooth.restype = i32
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
         L.oracle_qk_int32.restype = i32
-        L.oracle_attn_mirror.argtypes = [P] * 8 + [i32, i32, i32, i32, i32, f32, i32, P, i64, f32, P, P, P, i32]
+        L.oracle_attn_mirror.argtypes = [P] * 8 + [i32] * 7 + [f32, i32, P, i64, f32, P, P, P, i32]
         L.oracle_attn_mirror.restype = i32
-        L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 8 + [i32, i32, i32, i32, i32, f64, i32, P, i64, P, P, i32]
+        L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 8 + [i32] * 7 + [f64, i32, P, i64, P, P, i32]
         L.oracle_attn_exact.restype = i32
         _lib = L
     return _lib
@@ -120,36 +125,43 @@ def decode_input(bits: np.ndarray, dtype: int) -> np.ndarray:
 
 @dataclass
 class Quant:
-    """Canonical (unpacked, unpadded) prepass outputs."""
-    q_codes: np.ndarray   # int8  [B,H,N,D]
-    q_scale: np.ndarray   # fp32  [B,H,N]
-    k_codes: np.ndarray   # int8  [B,H,N,D]
-    k_scale: np.ndarray   # fp32  [B,H,2*ceil(N/32)]
-    q_mean: np.ndarray    # fp32  [B,H,ceil(N/128),D]
-    k_mean: np.ndarray    # fp32  [B,H,D]
-    v_codes: np.ndarray   # uint8 [B,H,N,D]
-    v_scale: np.ndarray   # fp32  [B,H,D]
-    delta_s: np.ndarray   # fp32  [B,H,ceil(N/128),N]
-    v_mean: np.ndarray = None   # fp32 [B,H,D]: V channel means (zeros without V smoothing)
+    """Canonical (unpacked, unpadded) prepass outputs.  Queries have Hq heads
+    and Nq tokens, keys/values Hkv heads and Nk tokens (Hq a multiple of Hkv);
+    for self-attention Hq == Hkv == H and Nq == Nk == N."""
+    q_codes: np.ndarray   # int8  [B,Hq,Nq,D]
+    q_scale: np.ndarray   # fp32  [B,Hq,Nq]
+    k_codes: np.ndarray   # int8  [B,Hkv,Nk,D]
+    k_scale: np.ndarray   # fp32  [B,Hkv,2*ceil(Nk/32)]
+    q_mean: np.ndarray    # fp32  [B,Hq,ceil(Nq/128),D]
+    k_mean: np.ndarray    # fp32  [B,Hkv,D]
+    v_codes: np.ndarray   # uint8 [B,Hkv,Nk,D]
+    v_scale: np.ndarray   # fp32  [B,Hkv,D]
+    delta_s: np.ndarray   # fp32  [B,Hq,ceil(Nq/128),Nk]
+    v_mean: np.ndarray = None   # fp32 [B,Hkv,D]: V channel means (zeros without V smoothing)
 
 
 def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True,
                  qk_bits: int = 4, smooth_v: bool = False) -> Quant:
     """Run the prepass; with_delta_s=False skips the (quadratic) compensation
     term and leaves ``delta_s`` as None.  qk_bits selects INT4 (4) or INT8 (8)
-    codes for Q and K; smooth_v subtracts the per-channel V mean before FP8."""
-    B, H, N, D = q_bits.shape
-    nqb = (N + BQ_MEAN - 1) // BQ_MEAN
-    G = 2 * ((N + 31) // 32)
+    codes for Q and K; smooth_v subtracts the per-channel V mean before FP8.
+    q_bits is [B,Hq,Nq,D]; k_bits and v_bits are [B,Hkv,Nk,D]."""
+    B, Hq, Nq, D = q_bits.shape
+    _, Hk, Nk, _ = k_bits.shape
+    if k_bits.shape != v_bits.shape or k_bits.shape[0] != B or k_bits.shape[3] != D:
+        raise ValueError("K and V must be [B, Hkv, Nk, D] with Q's B and D")
+    nqb = (Nq + BQ_MEAN - 1) // BQ_MEAN
+    G = 2 * ((Nk + 31) // 32)
     qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
     out = Quant(
-        q_codes=np.empty((B, H, N, D), np.int8), q_scale=np.empty((B, H, N), np.float32),
-        k_codes=np.empty((B, H, N, D), np.int8), k_scale=np.empty((B, H, G), np.float32),
-        q_mean=np.empty((B, H, nqb, D), np.float32), k_mean=np.empty((B, H, D), np.float32),
-        v_codes=np.empty((B, H, N, D), np.uint8), v_scale=np.empty((B, H, D), np.float32),
-        delta_s=np.empty((B, H, nqb, N), np.float32) if with_delta_s else None,
-        v_mean=np.empty((B, H, D), np.float32))
-    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, H, N, D, qk_bits, int(bool(smooth_v)),
+        q_codes=np.empty((B, Hq, Nq, D), np.int8), q_scale=np.empty((B, Hq, Nq), np.float32),
+        k_codes=np.empty((B, Hk, Nk, D), np.int8), k_scale=np.empty((B, Hk, G), np.float32),
+        q_mean=np.empty((B, Hq, nqb, D), np.float32), k_mean=np.empty((B, Hk, D), np.float32),
+        v_codes=np.empty((B, Hk, Nk, D), np.uint8), v_scale=np.empty((B, Hk, D), np.float32),
+        delta_s=np.empty((B, Hq, nqb, Nk), np.float32) if with_delta_s else None,
+        v_mean=np.empty((B, Hk, D), np.float32))
+    rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, Hq, Hk, Nq, Nk, D, qk_bits,
+                                   int(bool(smooth_v)),
                                    _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
                                    _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),
                                    _ptr(out.v_mean), _ptr(out.delta_s), _threads(nthreads))
@@ -171,8 +183,10 @@ def qk_int32(q_codes_head, k_codes_head, q0, k0, nq, nk) -> np.ndarray:
 
 def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bool = True,
                 eps: float = 0.0, nthreads: int = 0):
-    """Returns (O [nrows, D] fp32, slack [nrows] fp32, lse [nrows, 2] fp32)."""
+    """Returns (O [nrows, D] fp32, slack [nrows] fp32, lse [nrows, 2] fp32).
+    rows index the flattened [B, Hq, Nq] query grid."""
     B, H, N, D = qz.q_codes.shape
+    Hk, Nk = qz.k_codes.shape[1], qz.k_codes.shape[2]
     if rows is None:
         nrows = B * H * N
         rows_arr = None
@@ -184,7 +198,7 @@ def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bo
     lse = np.empty((nrows, 2), np.float32)
     rc = lib().oracle_attn_mirror(_ptr(qz.q_codes), _ptr(qz.q_scale), _ptr(qz.k_codes), _ptr(qz.k_scale),
                                   _ptr(qz.v_codes), _ptr(qz.v_scale), _ptr(qz.v_mean), _ptr(qz.delta_s),
-                                  B, H, N, D, int(causal), float(sm_scale),
+                                  B, H, Hk, N, Nk, D, int(causal), float(sm_scale),
                                   MIRROR_QUANT_P if quant_p else 0, _ptr(rows_arr), nrows, float(eps),
                                   _ptr(O), _ptr(slack), _ptr(lse), _threads(nthreads))
     if rc != 0:
@@ -194,8 +208,10 @@ def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bo
 
 def attn_exact(q_bits, k_bits, v_bits, dtype: int, causal: bool, sm_scale: float, flags: int,
                qz: Quant | None = None, rows=None, nthreads: int = 0):
-    """Returns (O [nrows, D] fp64, row sums of P [nrows] fp64)."""
+    """Returns (O [nrows, D] fp64, row sums of P [nrows] fp64).  q_bits is
+    [B,Hq,Nq,D], k_bits and v_bits [B,Hkv,Nk,D]; rows index [B, Hq, Nq]."""
     B, H, N, D = q_bits.shape
+    Hk, Nk = k_bits.shape[1], k_bits.shape[2]
     qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
     if rows is None:
         nrows = B * H * N
@@ -209,7 +225,7 @@ def attn_exact(q_bits, k_bits, v_bits, dtype: int, causal: bool, sm_scale: float
     rc = lib().oracle_attn_exact(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype,
                                  _ptr(z.q_codes), _ptr(z.q_scale), _ptr(z.k_codes), _ptr(z.k_scale),
                                  _ptr(z.v_codes), _ptr(z.v_scale), _ptr(z.v_mean), _ptr(z.delta_s),
-                                 B, H, N, D, int(causal), float(sm_scale), flags, _ptr(rows_arr), nrows,
+                                 B, H, Hk, N, Nk, D, int(causal), float(sm_scale), flags, _ptr(rows_arr), nrows,
                                  _ptr(O), _ptr(psum), _threads(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_exact rejected its arguments")

@@ -60,7 +60,7 @@
 
 namespace {
 
-constexpr int ORACLE_CONTRACT = 1;
+constexpr int ORACLE_CONTRACT = 2;
 constexpr int BQ_MEAN = 128;   // tokens per Q-smoothing block and per mean chunk
 constexpr int BK = 128;        // keys per online-softmax / two-level block
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -159,121 +159,139 @@ void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
   for (int64_t i = 0; i < n; i++) out[i] = in_to_f32(in, i, dtype);
 }
 
+// Geometry.  Queries: B batches x Hq heads x Nq tokens.  Keys and values:
+// B x Hkv heads x Nk tokens, with Hq a multiple of Hkv; query head h reads
+// key/value head h / (Hq / Hkv) (grouped-query attention; Hkv == Hq is plain
+// multi-head attention, Nk != Nq is cross-attention or decoding against a
+// key/value cache).  A causal mask is aligned at the bottom-right corner:
+// query i may attend key j iff j <= i + (Nk - Nq), so the last query sees every
+// key; causal calls require Nq <= Nk (every query then sees at least key 0).
+//
 // Prepass: smoothing statistics, INT4 codes and scales for Q and K, FP8 V with
 // per-channel scales, and the rank-1 compensation term.  All arrays are in the
 // canonical (unpacked, unpadded) layout:
-//   q_codes, k_codes : int8  [B,H,N,D]     values in [-7, 7] (qk_bits 4) or [-127, 127] (8)
-//   q_scale          : fp32  [B,H,N]
-//   k_scale          : fp32  [B,H,2*ceil(N/32)]
-//   q_mean           : fp32  [B,H,ceil(N/128),D]
-//   k_mean           : fp32  [B,H,D]
-//   v_codes          : uint8 [B,H,N,D]     e4m3fn bit patterns of (V - vmean)/vscale
-//   v_scale          : fp32  [B,H,D]
-//   v_mean           : fp32  [B,H,D]       per-channel V mean (zeros without smoothing)
-//   delta_s          : fp32  [B,H,ceil(N/128),N]
+//   q_codes          : int8  [B,Hq,Nq,D]    values in [-7, 7] (qk_bits 4) or [-127, 127] (8)
+//   q_scale          : fp32  [B,Hq,Nq]
+//   q_mean           : fp32  [B,Hq,ceil(Nq/128),D]
+//   k_codes          : int8  [B,Hkv,Nk,D]
+//   k_scale          : fp32  [B,Hkv,2*ceil(Nk/32)]
+//   k_mean           : fp32  [B,Hkv,D]
+//   v_codes          : uint8 [B,Hkv,Nk,D]   e4m3fn bit patterns of (V - vmean)/vscale
+//   v_scale          : fp32  [B,Hkv,D]
+//   v_mean           : fp32  [B,Hkv,D]      per-channel V mean (zeros without smoothing)
+//   delta_s          : fp32  [B,Hq,ceil(Nq/128),Nk]  (query head h against its K head)
 // Returns 0, or -1 for invalid arguments.
 int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
-                        int B, int H, int N, int D, int qk_bits, int smooth_v,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
                         int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
                         float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale, float* v_mean,
                         float* delta_s, int nthreads) {
-  if (!q || !k || !v || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
+  if (!q || !k || !v || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1) return -1;
+  if (dtype != 0 && dtype != 1) return -1;
   if (qk_bits != 4 && qk_bits != 8) return -1;
   if (smooth_v != 0 && smooth_v != 1) return -1;
   const float qmax = qk_bits == 4 ? 7.0f : 127.0f;
-  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
-  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
-  parallel_for((int64_t)B * H, nthreads, [&](int64_t bh) {
-    const int64_t base = bh * (int64_t)N * D;
-    // decode this head's inputs to fp32 (exact)
-    std::vector<float> Q((size_t)N * D), K((size_t)N * D), V((size_t)N * D);
-    for (int64_t i = 0; i < (int64_t)N * D; i++) {
-      Q[i] = in_to_f32(q, base + i, dtype);
+  const int64_t NQB = (Nq + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
+  const int group = Hq / Hkv;
+  // ---- key/value side, one (batch, K/V head) at a time.  The smoothed keys
+  // gK are kept for the compensation term of every query head of the group.
+  std::vector<std::vector<float>> gK_all((size_t)B * Hkv);
+  parallel_for((int64_t)B * Hkv, nthreads, [&](int64_t bhk) {
+    const int64_t base = bhk * (int64_t)Nk * D;
+    std::vector<float> K((size_t)Nk * D), V((size_t)Nk * D);
+    for (int64_t i = 0; i < (int64_t)Nk * D; i++) {
       K[i] = in_to_f32(k, base + i, dtype);
       V[i] = in_to_f32(v, base + i, dtype);
     }
-    // ---- K channel mean over all N tokens: chunk partials, then their sum.
+    // K channel mean over all Nk tokens: chunk partials, then their sum.
     std::vector<float> kbar(D);
     for (int c = 0; c < D; c++) {
       float total = 0.0f;
-      for (int64_t t0 = 0; t0 < N; t0 += BQ_MEAN) {
+      for (int64_t t0 = 0; t0 < Nk; t0 += BQ_MEAN) {
         float part = 0.0f;
-        for (int64_t j = t0; j < std::min<int64_t>(N, t0 + BQ_MEAN); j++) part = part + K[j * D + c];
+        for (int64_t j = t0; j < std::min<int64_t>(Nk, t0 + BQ_MEAN); j++) part = part + K[j * D + c];
         total = total + part;
       }
-      kbar[c] = total / (float)N;
-      if (k_mean) k_mean[bh * D + c] = kbar[c];
+      kbar[c] = total / (float)Nk;
+      if (k_mean) k_mean[bhk * D + c] = kbar[c];
     }
-    // ---- Q block means (128-token blocks, partial tail block).
-    std::vector<float> qbar((size_t)NQB * D);
-    for (int64_t qb = 0; qb < NQB; qb++) {
-      int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(N, i0 + BQ_MEAN);
-      for (int c = 0; c < D; c++) {
-        float s = 0.0f;
-        for (int64_t i = i0; i < i1; i++) s = s + Q[i * D + c];
-        qbar[qb * D + c] = s / (float)(i1 - i0);
-        if (q_mean) q_mean[(bh * NQB + qb) * D + c] = qbar[qb * D + c];
-      }
-    }
-    // ---- smoothed values
-    std::vector<float> gQ((size_t)N * D), gK((size_t)N * D);
-    for (int64_t i = 0; i < N; i++)
-      for (int c = 0; c < D; c++) {
-        gQ[i * D + c] = Q[i * D + c] - qbar[(i / BQ_MEAN) * D + c];
-        gK[i * D + c] = K[i * D + c] - kbar[c];
-      }
-    // ---- Q: one INT4 scale per token
-    for (int64_t i = 0; i < N; i++) {
-      float amax = 0.0f;
-      for (int c = 0; c < D; c++) amax = std::max(amax, std::fabs(gQ[i * D + c]));
-      float dq = amax / qmax;
-      if (q_scale) q_scale[bh * N + i] = dq;
-      if (q_codes)
-        for (int c = 0; c < D; c++) q_codes[base + i * D + c] = int_code(gQ[i * D + c], dq, qmax);
-    }
-    // ---- K: one INT4 scale per 16-key fragment group
+    std::vector<float>& gK = gK_all[bhk];
+    gK.resize((size_t)Nk * D);
+    for (int64_t j = 0; j < Nk; j++)
+      for (int c = 0; c < D; c++) gK[j * D + c] = K[j * D + c] - kbar[c];
+    // K: one scale per 16-key fragment group
     std::vector<float> gamax(G, 0.0f);
-    for (int64_t j = 0; j < N; j++) {
+    for (int64_t j = 0; j < Nk; j++) {
       int64_t g = k_group(j);
       for (int c = 0; c < D; c++) gamax[g] = std::max(gamax[g], std::fabs(gK[j * D + c]));
     }
     std::vector<float> dk(G);
     for (int64_t g = 0; g < G; g++) {
       dk[g] = gamax[g] / qmax;
-      if (k_scale) k_scale[bh * G + g] = dk[g];
+      if (k_scale) k_scale[bhk * G + g] = dk[g];
     }
     if (k_codes)
-      for (int64_t j = 0; j < N; j++)
+      for (int64_t j = 0; j < Nk; j++)
         for (int c = 0; c < D; c++) k_codes[base + j * D + c] = int_code(gK[j * D + c], dk[k_group(j)], qmax);
-    // ---- V: optional smoothing, then FP8 e4m3fn with one scale per channel
+    // V: optional smoothing, then FP8 e4m3fn with one scale per channel
     for (int c = 0; c < D; c++) {
       float vbar = 0.0f;
       if (smooth_v) {
         float total = 0.0f;
-        for (int64_t t0 = 0; t0 < N; t0 += BQ_MEAN) {
+        for (int64_t t0 = 0; t0 < Nk; t0 += BQ_MEAN) {
           float part = 0.0f;
-          for (int64_t j = t0; j < std::min<int64_t>(N, t0 + BQ_MEAN); j++) part = part + V[j * D + c];
+          for (int64_t j = t0; j < std::min<int64_t>(Nk, t0 + BQ_MEAN); j++) part = part + V[j * D + c];
           total = total + part;
         }
-        vbar = total / (float)N;
-        for (int64_t j = 0; j < N; j++) V[j * D + c] = V[j * D + c] - vbar;
+        vbar = total / (float)Nk;
+        for (int64_t j = 0; j < Nk; j++) V[j * D + c] = V[j * D + c] - vbar;
       }
-      if (v_mean) v_mean[bh * D + c] = vbar;
+      if (v_mean) v_mean[bhk * D + c] = vbar;
       float amax = 0.0f;
-      for (int64_t j = 0; j < N; j++) amax = std::max(amax, std::fabs(V[j * D + c]));
+      for (int64_t j = 0; j < Nk; j++) amax = std::max(amax, std::fabs(V[j * D + c]));
       float dv = amax / 448.0f;
-      if (v_scale) v_scale[bh * D + c] = dv;
+      if (v_scale) v_scale[bhk * D + c] = dv;
       if (v_codes)
-        for (int64_t j = 0; j < N; j++)
+        for (int64_t j = 0; j < Nk; j++)
           v_codes[base + j * D + c] = (dv == 0.0f) ? (uint8_t)0 : e4m3_encode(V[j * D + c] / dv);
     }
-    // ---- rank-1 compensation: DeltaS[qb][j] = qbar[qb] . gK[j]
+  });
+  // ---- query side, one (batch, query head) at a time.
+  parallel_for((int64_t)B * Hq, nthreads, [&](int64_t bhq) {
+    const int64_t base = bhq * (int64_t)Nq * D;
+    const std::vector<float>& gK = gK_all[(bhq / Hq) * Hkv + (bhq % Hq) / group];
+    std::vector<float> Q((size_t)Nq * D);
+    for (int64_t i = 0; i < (int64_t)Nq * D; i++) Q[i] = in_to_f32(q, base + i, dtype);
+    // Q block means (128-token blocks, partial tail block).
+    std::vector<float> qbar((size_t)NQB * D);
+    for (int64_t qb = 0; qb < NQB; qb++) {
+      int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(Nq, i0 + BQ_MEAN);
+      for (int c = 0; c < D; c++) {
+        float s = 0.0f;
+        for (int64_t i = i0; i < i1; i++) s = s + Q[i * D + c];
+        qbar[qb * D + c] = s / (float)(i1 - i0);
+        if (q_mean) q_mean[(bhq * NQB + qb) * D + c] = qbar[qb * D + c];
+      }
+    }
+    // Q: one scale per token, on the smoothed values
+    std::vector<float> gQ(D);
+    for (int64_t i = 0; i < Nq; i++) {
+      for (int c = 0; c < D; c++) gQ[c] = Q[i * D + c] - qbar[(i / BQ_MEAN) * D + c];
+      float amax = 0.0f;
+      for (int c = 0; c < D; c++) amax = std::max(amax, std::fabs(gQ[c]));
+      float dq = amax / qmax;
+      if (q_scale) q_scale[bhq * Nq + i] = dq;
+      if (q_codes)
+        for (int c = 0; c < D; c++) q_codes[base + i * D + c] = int_code(gQ[c], dq, qmax);
+    }
+    // rank-1 compensation: DeltaS[qb][j] = qbar[qb] . gK[j]
     if (delta_s)
       for (int64_t qb = 0; qb < NQB; qb++)
-        for (int64_t j = 0; j < N; j++) {
+        for (int64_t j = 0; j < Nk; j++) {
           double acc = 0.0;
           for (int c = 0; c < D; c++) acc += (double)qbar[qb * D + c] * (double)gK[j * D + c];
-          delta_s[(bh * NQB + qb) * N + j] = (float)acc;
+          delta_s[(bhq * NQB + qb) * Nk + j] = (float)acc;
         }
   });
   return 0;
@@ -297,38 +315,42 @@ int oracle_qk_int32(const int8_t* qc, const int8_t* kc, int D, int q0, int k0, i
 enum { MIRROR_QUANT_P = 1 };
 
 // Mirror mode: the method step by step, in the same fp32 operations the GPU
-// path performs, for a list of query rows.  rows[r] = (b*H + h)*N + i.
-// Inputs are the canonical prepass arrays.  Outputs: O[r][c] (fp32) and, per
-// row, slack[r]: an upper bound on how far O may move if any P~ element whose
-// value p' lies within relative distance eps of an FP8 rounding midpoint were
-// rounded the other way (used to tolerate exp2 implementation differences).
-// Optional lse[r] = (final running max m, final l') for diagnostics.
+// path performs, for a list of query rows.  rows[r] = (b*Hq + h)*Nq + i.
+// Inputs are the canonical prepass arrays (geometry as for the prepass).
+// Outputs: O[r][c] (fp32) and, per row, slack[r]: an upper bound on how far O
+// may move if any P~ element whose value p' lies within relative distance eps
+// of an FP8 rounding midpoint were rounded the other way (used to tolerate exp2
+// implementation differences).  Optional lse[r] = (final running max m, final
+// l') for diagnostics.
 int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                        const uint8_t* v_codes, const float* v_scale, const float* v_mean, const float* delta_s,
-                       int B, int H, int N, int D, int causal, float sm_scale, int flags,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, float sm_scale, int flags,
                        const int64_t* rows, int64_t nrows, float eps,
                        float* O, float* slack, float* lse, int nthreads) {
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !delta_s || !O) return -1;
-  if (B < 1 || H < 1 || N < 1 || D < 1 || !(sm_scale > 0.0f)) return -1;
-  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
-  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || !(sm_scale > 0.0f)) return -1;
+  if (causal && Nq > Nk) return -1;
+  const int64_t NQB = (Nq + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
+  const int group = Hq / Hkv;
   const float ks = sm_scale * LOG2E;
-  const int64_t total = rows ? nrows : (int64_t)B * H * N;
+  const int64_t total = rows ? nrows : (int64_t)B * Hq * Nq;
   parallel_for(total, nthreads, [&](int64_t r) {
     const int64_t flat = rows ? rows[r] : r;
-    const int64_t bh = flat / N, i = flat % N;
+    const int64_t bhq = flat / Nq, i = flat % Nq;
+    const int64_t bhk = (bhq / Hq) * Hkv + (bhq % Hq) / group;
     const int8_t* qi = q_codes + flat * D;
-    const int8_t* kh = k_codes + bh * (int64_t)N * D;
-    const uint8_t* vh = v_codes + bh * (int64_t)N * D;
-    const float* ds = delta_s + (bh * NQB + i / BQ_MEAN) * N;
-    const float* dvec = v_scale + bh * D;
+    const int8_t* kh = k_codes + bhk * (int64_t)Nk * D;
+    const uint8_t* vh = v_codes + bhk * (int64_t)Nk * D;
+    const float* ds = delta_s + (bhq * NQB + i / BQ_MEAN) * Nk;
+    const float* dvec = v_scale + bhk * D;
     const float dq = q_scale[flat];
     std::vector<float> Orun(D, 0.0f), R(D), s2(BK), p(BK);
     float m = -std::numeric_limits<float>::infinity();
     float l = 0.0f, slk = 0.0f;
-    const int64_t jend = causal ? i + 1 : N;  // keys j < jend are allowed
+    const int64_t jend = causal ? i + 1 + (Nk - Nq) : Nk;  // keys j < jend are allowed
     for (int64_t t0 = 0; t0 < jend; t0 += BK) {
-      const int64_t t1 = std::min<int64_t>(t0 + BK, N);
+      const int64_t t1 = std::min<int64_t>(t0 + BK, Nk);
       // scores in the log2 domain
       float bmax = -std::numeric_limits<float>::infinity();
       for (int64_t j = t0; j < t1; j++) {
@@ -336,7 +358,7 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
         if (j >= jend) { s = -std::numeric_limits<float>::infinity(); continue; }
         int32_t acc = 0;
         for (int c = 0; c < D; c++) acc += (int32_t)qi[c] * (int32_t)kh[j * D + c];
-        float cfac = (dq * k_scale[bh * G + k_group(j)]) * ks;
+        float cfac = (dq * k_scale[bhk * G + k_group(j)]) * ks;
         float d = ds[j] * ks;
         s = std::fma((float)acc, cfac, d);
         bmax = std::max(bmax, s);
@@ -378,7 +400,7 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
     }
     for (int c = 0; c < D; c++) {
       O[r * D + c] = (Orun[c] * dvec[c]) / l;
-      if (v_mean) O[r * D + c] = O[r * D + c] + v_mean[bh * D + c];
+      if (v_mean) O[r * D + c] = O[r * D + c] + v_mean[bhk * D + c];
     }
     if (slack) slack[r] = slk / l;
     if (lse) { lse[2 * r] = m; lse[2 * r + 1] = l; }
@@ -399,78 +421,92 @@ enum {
 //   S_ij = sm_scale * ( gQ_i . gK_j + [SMOOTH_Q] qmean_qb(i) . gK_j )
 // With EXACT_QUANT_QK they are built from the canonical prepass arrays:
 //   S_ij = sm_scale * ( (dq_i * qc_i) . (dk_g(j) * kc_j) + DeltaS[qb(i)][j] )
-// Outputs O[r][c] in fp64; optional P row sums in psum[r].
+// Geometry, head mapping and causal alignment as for the prepass; rows[r] =
+// (b*Hq + h)*Nq + i.  Outputs O[r][c] in fp64; optional P row sums in psum[r].
 int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
                       const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                       const uint8_t* v_codes, const float* v_scale, const float* v_mean, const float* delta_s,
-                      int B, int H, int N, int D, int causal, double sm_scale, int flags,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, double sm_scale, int flags,
                       const int64_t* rows, int64_t nrows, double* O, double* psum, int nthreads) {
-  if (!q || !k || !v || !O || B < 1 || H < 1 || N < 1 || D < 1 || (dtype != 0 && dtype != 1)) return -1;
+  if (!q || !k || !v || !O || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1) return -1;
+  if (dtype != 0 && dtype != 1) return -1;
+  if (causal && Nq > Nk) return -1;
   if ((flags & EXACT_QUANT_QK) && (!q_codes || !q_scale || !k_codes || !k_scale || !delta_s)) return -1;
   if ((flags & EXACT_QUANT_V) && (!v_codes || !v_scale)) return -1;
-  const int64_t NQB = (N + BQ_MEAN - 1) / BQ_MEAN;
-  const int64_t G = 2 * ((int64_t)(N + 31) / 32);
-  const int64_t total = rows ? nrows : (int64_t)B * H * N;
-  // per-head fp64 statistics, computed lazily per head
-  const int64_t nheads = (int64_t)B * H;
-  std::vector<std::vector<double>> kbar(nheads), qbar(nheads), vbar(nheads);
-  std::vector<char> need(nheads, rows ? 0 : 1);
+  const int64_t NQB = (Nq + BQ_MEAN - 1) / BQ_MEAN;
+  const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
+  const int group = Hq / Hkv;
+  const int64_t total = rows ? nrows : (int64_t)B * Hq * Nq;
+  // fp64 statistics: query-block means per query head, K and V channel means
+  // per K/V head; computed only for the heads the requested rows touch.
+  const int64_t nq_heads = (int64_t)B * Hq, nk_heads = (int64_t)B * Hkv;
+  auto kv_head = [&](int64_t bhq) { return (bhq / Hq) * Hkv + (bhq % Hq) / group; };
+  std::vector<std::vector<double>> kbar(nk_heads), vbar(nk_heads), qbar(nq_heads);
+  std::vector<char> need_q(nq_heads, rows ? 0 : 1), need_k(nk_heads, rows ? 0 : 1);
   if (rows)
-    for (int64_t r = 0; r < nrows; r++) need[rows[r] / N] = 1;
-  parallel_for(nheads, nthreads, [&](int64_t bh) {
-    if (!need[bh]) return;
-    const int64_t base = bh * (int64_t)N * D;
-    kbar[bh].assign(D, 0.0);
-    qbar[bh].assign(NQB * D, 0.0);
-    vbar[bh].assign(D, 0.0);
+    for (int64_t r = 0; r < nrows; r++) {
+      need_q[rows[r] / Nq] = 1;
+      need_k[kv_head(rows[r] / Nq)] = 1;
+    }
+  parallel_for(nk_heads, nthreads, [&](int64_t bhk) {
+    if (!need_k[bhk]) return;
+    const int64_t base = bhk * (int64_t)Nk * D;
+    kbar[bhk].assign(D, 0.0);
+    vbar[bhk].assign(D, 0.0);
     if ((flags & EXACT_SMOOTH_V) && !(flags & EXACT_QUANT_V))
       for (int c = 0; c < D; c++) {
         double s = 0.0;
-        for (int64_t j = 0; j < N; j++) s += in_to_f32(v, base + j * D + c, dtype);
-        vbar[bh][c] = s / N;
+        for (int64_t j = 0; j < Nk; j++) s += in_to_f32(v, base + j * D + c, dtype);
+        vbar[bhk][c] = s / Nk;
       }
     if (flags & EXACT_SMOOTH_K)
       for (int c = 0; c < D; c++) {
         double s = 0.0;
-        for (int64_t j = 0; j < N; j++) s += in_to_f32(k, base + j * D + c, dtype);
-        kbar[bh][c] = s / N;
+        for (int64_t j = 0; j < Nk; j++) s += in_to_f32(k, base + j * D + c, dtype);
+        kbar[bhk][c] = s / Nk;
       }
+  });
+  parallel_for(nq_heads, nthreads, [&](int64_t bhq) {
+    if (!need_q[bhq]) return;
+    const int64_t base = bhq * (int64_t)Nq * D;
+    qbar[bhq].assign(NQB * D, 0.0);
     if (flags & EXACT_SMOOTH_Q)
       for (int64_t qb = 0; qb < NQB; qb++) {
-        int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(N, i0 + BQ_MEAN);
+        int64_t i0 = qb * BQ_MEAN, i1 = std::min<int64_t>(Nq, i0 + BQ_MEAN);
         for (int c = 0; c < D; c++) {
           double s = 0.0;
           for (int64_t i = i0; i < i1; i++) s += in_to_f32(q, base + i * D + c, dtype);
-          qbar[bh][qb * D + c] = s / (double)(i1 - i0);
+          qbar[bhq][qb * D + c] = s / (double)(i1 - i0);
         }
       }
   });
   parallel_for(total, nthreads, [&](int64_t r) {
     const int64_t flat = rows ? rows[r] : r;
-    const int64_t bh = flat / N, i = flat % N, qb = i / BQ_MEAN;
-    const int64_t base = bh * (int64_t)N * D;
-    const int64_t jend = causal ? i + 1 : N;
+    const int64_t bhq = flat / Nq, i = flat % Nq, qb = i / BQ_MEAN;
+    const int64_t bhk = kv_head(bhq);
+    const int64_t qbase = bhq * (int64_t)Nq * D, kbase = bhk * (int64_t)Nk * D;
+    const int64_t jend = causal ? i + 1 + (Nk - Nq) : Nk;
     std::vector<double> S(jend);
     std::vector<double> qrow(D), qm(D);
     for (int c = 0; c < D; c++) {
       if (flags & EXACT_QUANT_QK) {
         qrow[c] = (double)q_scale[flat] * (double)q_codes[flat * D + c];
       } else {
-        double x = in_to_f32(q, base + i * D + c, dtype);
-        qm[c] = (flags & EXACT_SMOOTH_Q) ? qbar[bh][qb * D + c] : 0.0;
+        double x = in_to_f32(q, qbase + i * D + c, dtype);
+        qm[c] = (flags & EXACT_SMOOTH_Q) ? qbar[bhq][qb * D + c] : 0.0;
         qrow[c] = x - qm[c];
       }
     }
     for (int64_t j = 0; j < jend; j++) {
       double s = 0.0;
       if (flags & EXACT_QUANT_QK) {
-        double dk = k_scale[bh * G + k_group(j)];
-        for (int c = 0; c < D; c++) s += qrow[c] * (dk * (double)k_codes[base + j * D + c]);
-        s += (double)delta_s[(bh * NQB + qb) * N + j];
+        double dk = k_scale[bhk * G + k_group(j)];
+        for (int c = 0; c < D; c++) s += qrow[c] * (dk * (double)k_codes[kbase + j * D + c]);
+        s += (double)delta_s[(bhq * NQB + qb) * Nk + j];
       } else {
         double comp = 0.0;
         for (int c = 0; c < D; c++) {
-          double kj = (double)in_to_f32(k, base + j * D + c, dtype) - kbar[bh][c];
+          double kj = (double)in_to_f32(k, kbase + j * D + c, dtype) - kbar[bhk][c];
           s += qrow[c] * kj;
           comp += qm[c] * kj;
         }
@@ -488,14 +524,14 @@ int oracle_attn_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
       double pj = S[j] / denom;
       ps += pj;
       for (int c = 0; c < D; c++) {
-        double vj = (flags & EXACT_QUANT_V) ? (double)v_scale[bh * D + c] * (double)e4m3_decode(v_codes[base + j * D + c])
-                                            : (double)in_to_f32(v, base + j * D + c, dtype) - vbar[bh][c];
+        double vj = (flags & EXACT_QUANT_V) ? (double)v_scale[bhk * D + c] * (double)e4m3_decode(v_codes[kbase + j * D + c])
+                                            : (double)in_to_f32(v, kbase + j * D + c, dtype) - vbar[bhk][c];
         O[r * D + c] += pj * vj;
       }
     }
     for (int c = 0; c < D; c++) {
-      if (flags & EXACT_QUANT_V) O[r * D + c] += v_mean ? (double)v_mean[bh * D + c] : 0.0;
-      else O[r * D + c] += vbar[bh][c];
+      if (flags & EXACT_QUANT_V) O[r * D + c] += v_mean ? (double)v_mean[bhk * D + c] : 0.0;
+      else O[r * D + c] += vbar[bhk][c];
     }
     if (psum) psum[r] = ps;
   });

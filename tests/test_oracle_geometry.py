@@ -1,0 +1,164 @@
+"""Pins for the oracle's general geometry: queries and keys/values with their
+own lengths (cross-attention, decoding against a key/value cache, chunked
+prefill) and head counts (grouped-query attention), causal masks aligned at the
+bottom-right corner.
+
+Checks against: a direct fp64 softmax(QK^T)V in numpy with the bottom-right
+mask written out; grouped-query attention equal, bit for bit, to multi-head
+attention on key/value heads repeated along the head axis (a mapping of query
+head h to K/V head h % Hkv instead of h / (Hq / Hkv) fails it); the online
+softmax identity (mirror without P~ quantization equals the direct softmax over
+the same quantized operands); the smoothing invariants; and closed forms of
+decoding (one query: its block mean is the query itself, so its INT codes are
+zero and the compensation term carries the whole score).
+"""
+import numpy as np
+import pytest
+
+from fp8_attention_transformer_amd import workloads as wl
+
+
+def _brute(Q, K, V, causal, scale, group):
+    """fp64 attention; query head h uses K/V head h // group; query i sees key
+    j iff j <= i + (Nk - Nq) when causal."""
+    B, Hq, Nq, D = Q.shape
+    Nk = K.shape[2]
+    out = np.empty((B, Hq, Nq, D))
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    allowed = j <= i + (Nk - Nq)
+    for b in range(B):
+        for h in range(Hq):
+            S = (Q[b, h].astype(np.float64) @ K[b, h // group].astype(np.float64).T) * scale
+            if causal:
+                S = np.where(allowed, S, -np.inf)
+            S = S - S.max(1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(1, keepdims=True)
+            out[b, h] = P @ V[b, h // group].astype(np.float64)
+    return out
+
+
+GEOMS = [
+    # (B, Hq, Hkv, Nq, Nk, D)
+    (1, 2, 2, 70, 300, 64),      # chunked prefill / cross-attention, Nq < Nk
+    (1, 4, 2, 1, 257, 128),      # decode, grouped heads
+    (2, 4, 1, 130, 130, 64),     # multi-query attention, square
+    (1, 2, 1, 129, 517, 128),    # several query blocks and a ragged key tail
+]
+
+
+def _id(g):
+    B, Hq, Hk, Nq, Nk, D = g
+    return f"b{B}hq{Hq}hkv{Hk}nq{Nq}nk{Nk}d{D}"
+
+
+@pytest.mark.parametrize("g", GEOMS, ids=_id)
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_mode_is_plain_attention(oracle_lib, g, causal):
+    B, Hq, Hk, Nq, Nk, D = g
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=Nq + 3 * Nk, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    O, psum = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, 0)
+    Q, K, V = (oracle_lib.decode_input(a, 1) for a in (q, k, v))
+    ref = _brute(Q, K, V, causal, w.scale, Hq // Hk).reshape(-1, D)
+    assert np.allclose(O, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(psum, 1.0, atol=1e-12)
+    # smoothing K and Q leaves the exact scores unchanged (invariants)
+    Os, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale,
+                                  oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_SMOOTH_V)
+    assert np.allclose(Os, ref, rtol=1e-9, atol=1e-9)
+
+
+def test_noncausal_more_queries_than_keys(oracle_lib):
+    B, Hq, Hk, Nq, Nk, D = 1, 2, 1, 300, 70, 64
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=17, k_offset_std=2.0)
+    q, k, v = wl.generate(w)
+    O, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, 0)
+    Q, K, V = (oracle_lib.decode_input(a, 1) for a in (q, k, v))
+    assert np.allclose(O, _brute(Q, K, V, False, w.scale, 2).reshape(-1, D), rtol=1e-12, atol=1e-12)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    oracle_lib.attn_mirror(z, False, w.scale)
+    with pytest.raises(ValueError):
+        oracle_lib.attn_mirror(z, True, w.scale)
+    with pytest.raises(ValueError):
+        oracle_lib.attn_exact(q, k, v, 1, True, w.scale, 0)
+
+
+@pytest.mark.parametrize("qk_bits", [4, 8])
+@pytest.mark.parametrize("smooth_v", [False, True])
+def test_grouped_heads_equal_repeated_kv_heads(oracle_lib, qk_bits, smooth_v):
+    B, Hq, Hk, Nq, Nk, D = 2, 6, 3, 140, 200, 64
+    g = Hq // Hk
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=23, k_offset_std=3.0, v_offset_std=1.0)
+    q, k, v = wl.generate(w)
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    za = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=qk_bits, smooth_v=smooth_v)
+    zb = oracle_lib.quant_smooth(q, kr, vr, oracle_lib.DT_BF16, qk_bits=qk_bits, smooth_v=smooth_v)
+    for name in ("q_codes", "q_scale", "q_mean", "delta_s"):
+        assert np.array_equal(getattr(za, name), getattr(zb, name)), name
+    for name in ("k_codes", "k_scale", "k_mean", "v_codes", "v_scale", "v_mean"):
+        assert np.array_equal(np.repeat(getattr(za, name), g, axis=1), getattr(zb, name)), name
+    for causal in (False, True):
+        Oa, sa, la = oracle_lib.attn_mirror(za, causal, w.scale, eps=2.0 ** -16)
+        Ob, sb, lb = oracle_lib.attn_mirror(zb, causal, w.scale, eps=2.0 ** -16)
+        assert np.array_equal(Oa, Ob) and np.array_equal(sa, sb) and np.array_equal(la, lb)
+        Ea, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, 0)
+        Eb, _ = oracle_lib.attn_exact(q, kr, vr, 1, causal, w.scale, 0)
+        assert np.array_equal(Ea, Eb)
+
+
+@pytest.mark.parametrize("g", GEOMS, ids=_id)
+@pytest.mark.parametrize("causal", [False, True])
+def test_mirror_online_softmax_equals_direct_softmax(oracle_lib, g, causal):
+    B, Hq, Hk, Nq, Nk, D = g
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=5 * Nq + Nk, k_offset_std=4.0, outlier_channels=2,
+                  outlier_scale=10.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, smooth_v=True)
+    flags = (oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_QUANT_QK
+             | oracle_lib.EXACT_QUANT_V)
+    Oe, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, flags, qz=z)
+    Om, _, _ = oracle_lib.attn_mirror(z, causal, w.scale, quant_p=False)
+    vmax = np.abs(oracle_lib.e4m3_decode(z.v_codes) * z.v_scale[:, :, None, :]).max() + np.abs(z.v_mean).max()
+    assert np.abs(Om - Oe).max() <= 1e-5 * vmax
+
+
+def test_causal_last_query_sees_every_key(oracle_lib):
+    """Bottom-right alignment: the last query row of a causal call is the
+    non-causal row, bit for bit; the first row sees Nk - Nq + 1 keys."""
+    B, Hq, Hk, Nq, Nk, D = 1, 2, 2, 130, 400, 128
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=31, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    last = np.array([h * Nq + Nq - 1 for h in range(Hq)])
+    Oc, _, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=last)
+    On, _, _ = oracle_lib.attn_mirror(z, False, w.scale, rows=last)
+    assert np.array_equal(Oc, On)
+    # row 0 equals exact attention over the first Nk - Nq + 1 keys only
+    O0, _ = oracle_lib.attn_exact(q, k, v, 1, True, w.scale, 0, rows=[0])
+    Q, K, V = (oracle_lib.decode_input(a, 1) for a in (q, k, v))
+    n0 = Nk - Nq + 1
+    ref = _brute(Q[:, :1, :1], K[:, :1, :n0], V[:, :1, :n0], False, w.scale, 1).reshape(-1, D)
+    assert np.allclose(O0, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("qk_bits", [4, 8])
+def test_decode_query_is_its_own_block_mean(oracle_lib, qk_bits):
+    """One query token: Q smoothing subtracts the query itself, so its codes and
+    scale are zero and DeltaS = q . (K - mean K) holds the whole score.  The
+    quantized scores then differ from the exact ones only by fp32 rounding of
+    the K mean and of DeltaS, so the output (V unquantized) matches plain
+    attention to ~1e-6, far inside any INT4 error."""
+    B, Hq, Hk, Nq, Nk, D = 2, 4, 2, 1, 700, 128
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=41, k_offset_std=4.0, t_noise_scale=0.5)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=qk_bits)
+    Q = oracle_lib.decode_input(q, 1)
+    assert not z.q_codes.any() and not z.q_scale.any()
+    assert np.array_equal(z.q_mean[:, :, 0, :], Q[:, :, 0, :])
+    flags = oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_QUANT_QK
+    Oq, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, flags, qz=z)
+    Oe, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, 0)
+    V = oracle_lib.decode_input(v, 1)
+    assert np.abs(Oq - Oe).max() <= 1e-5 * np.abs(V).max()
