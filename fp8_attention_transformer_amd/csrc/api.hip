@@ -23,27 +23,34 @@ bool mul_ok(size_t a, size_t b, size_t* out) {
   return true;
 }
 
-bool shape_ok(int B, int H, int N, int D) {
-  if (B < 1 || H < 1 || N < 1) return false;
+// Queries [B, Hq, Nq, D], keys and values [B, Hkv, Nk, D].
+bool shape_ok(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return false;
+  if (Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
   // keep every index computed in 32-bit arithmetic inside the kernels in range
-  const long long NP = ((long long)N + 127) / 128 * 128;
-  if (NP > (1LL << 24)) return false;
-  if ((long long)B * H > 65535) return false;   // grid y dimension of the prepass
-  if ((long long)B * H * (NP / 128) > (1LL << 30)) return false;
+  const long long NPq = ((long long)Nq + 127) / 128 * 128, NPk = ((long long)Nk + 127) / 128 * 128;
+  if (NPq > (1LL << 24) || NPk > (1LL << 24)) return false;
+  if ((long long)B * Hq > 65535) return false;   // grid y dimension of the prepass
+  if ((long long)B * Hq * (NPq / 128) > (1LL << 30)) return false;
+  if ((long long)B * Hkv * (NPk / 128) > (1LL << 30)) return false;
   return true;
 }
 
 bool bits_ok(int qk_bits) { return qk_bits == 4 || qk_bits == 8; }
 
-Dims make_dims(int B, int H, int N, int D, int qk_bits = 8, int smooth_v = 0) {
+Dims make_dims(int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits = 8, int smooth_v = 0) {
   Dims d;
   d.B = B;
-  d.H = H;
-  d.N = N;
+  d.H = Hq;
+  d.N = Nq;
   d.D = D;
-  d.NP = (N + 127) / 128 * 128;
+  d.NP = (Nq + 127) / 128 * 128;
   d.NQB = d.NP / 128;
+  d.Hk = Hkv;
+  d.Nk = Nk;
+  d.NPk = (Nk + 127) / 128 * 128;
+  d.NQBk = d.NPk / 128;
   d.QB = qk_bits;
   d.SV = smooth_v;
   d.cu = nullptr;
@@ -56,21 +63,25 @@ constexpr int kNumArrays = 12;
 // Sizes of the workspace arrays, in the order of sage_quant_bufs.  The code
 // arrays are sized for 8-bit codes so that one layout serves both code widths.
 bool layout(const Dims& d, size_t sizes[kNumArrays]) {
-  const size_t bh = (size_t)d.B * d.H, np = (size_t)d.NP, nqb = (size_t)d.NQB, D = (size_t)d.D;
-  size_t rows, t;
-  if (!mul_ok(bh, np, &rows)) return false;
-  if (!mul_ok(rows, D, &sizes[0])) return false;            // q_codes
-  sizes[1] = sizes[0];                                       // k_codes
-  if (!mul_ok(rows, 4, &sizes[2])) return false;            // q_scale
-  sizes[3] = rows / 16 * 4;                                  // k_scale
-  if (!mul_ok(bh * nqb, D * 4, &sizes[4])) return false;    // q_mean
-  sizes[5] = bh * D * 4;                                     // k_mean
-  if (!mul_ok(rows, D, &sizes[6])) return false;            // v_codes
-  sizes[7] = bh * D * 4;                                     // v_scale
-  if (!mul_ok(bh * nqb, np, &t) || !mul_ok(t, 4, &sizes[8])) return false;  // delta_s
-  sizes[9] = 2 * sizes[4];                                   // k_part
-  sizes[10] = 2 * sizes[4];                                  // v_part
-  sizes[11] = bh * D * 4;                                    // v_mean
+  const size_t D = (size_t)d.D;
+  const size_t bhq = (size_t)d.B * d.H, bhk = (size_t)d.B * d.Hk;
+  size_t qrows, krows, qblk, kblk, t;
+  if (!mul_ok(bhq, (size_t)d.NP, &qrows) || !mul_ok(bhk, (size_t)d.NPk, &krows)) return false;
+  if (!mul_ok(bhq, (size_t)d.NQB, &qblk) || !mul_ok(bhk, (size_t)d.NQBk, &kblk)) return false;
+  if (!mul_ok(qrows, D, &sizes[0])) return false;           // q_codes
+  if (!mul_ok(krows, D, &sizes[1])) return false;           // k_codes
+  if (!mul_ok(qrows, 4, &sizes[2])) return false;           // q_scale
+  sizes[3] = krows / 16 * 4;                                 // k_scale
+  if (!mul_ok(qblk, D * 4, &sizes[4])) return false;        // q_mean
+  sizes[5] = bhk * D * 4;                                    // k_mean
+  if (!mul_ok(krows, D, &sizes[6])) return false;           // v_codes
+  sizes[7] = bhk * D * 4;                                    // v_scale
+  if (!mul_ok(qblk, (size_t)d.NPk, &t) || !mul_ok(t, 4, &sizes[8])) return false;  // delta_s
+  // per-chunk K/V statistics, later the bf16 pieces of the Q block means
+  if (!mul_ok(kblk, 2 * D * 4, &t)) return false;
+  sizes[9] = t > qblk * 2 * D * 2 ? t : qblk * 2 * D * 2;   // k_part
+  sizes[10] = t > qblk * D * 2 ? t : qblk * D * 2;          // v_part
+  sizes[11] = bhk * D * 4;                                   // v_mean
   return true;
 }
 
@@ -162,14 +173,15 @@ const char* sage_status_string(sage_status st) {
   return "unknown sage_status";
 }
 
-size_t sage_workspace_bytes(int B, int H, int N, int D) {
-  if (!shape_ok(B, H, N, D)) return 0;
-  return total_bytes(make_dims(B, H, N, D));
+size_t sage_workspace_bytes_cross(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
+  if (!shape_ok(B, Hq, Hkv, Nq, Nk, D)) return 0;
+  return total_bytes(make_dims(B, Hq, Hkv, Nq, Nk, D));
 }
 
-sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H, int N, int D, sage_quant_bufs* out) {
-  if (!ws || !out || !shape_ok(B, H, N, D)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D);
+sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, int Hq, int Hkv, int Nq, int Nk,
+                                                 int D, sage_quant_bufs* out) {
+  if (!ws || !out || !shape_ok(B, Hq, Hkv, Nq, Nk, D)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (bytes < need) return SAGE_ERR_WORKSPACE;
@@ -177,36 +189,43 @@ sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H,
   return SAGE_OK;
 }
 
-sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H, int N,
-                              int D, int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream) {
-  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
+                                    int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
+                                    const sage_quant_bufs* out, hipStream_t stream) {
+  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
+    return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D, qk_bits, smooth_v);
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), 1.0f, stream);
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
-                          int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
-                          sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
+                                int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v,
+                                sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
+    return SAGE_ERR_INVALID;
+  if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D, qk_bits, smooth_v);
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
-  size_t elems, obytes, ibytes;
-  if (!mul_ok((size_t)B * H * N, (size_t)D, &elems)) return SAGE_ERR_INVALID;
-  if (!mul_ok(elems, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(elems, 2, &ibytes)) return SAGE_ERR_INVALID;
-  if (ranges_overlap(o, obytes, q, ibytes) || ranges_overlap(o, obytes, k, ibytes) ||
-      ranges_overlap(o, obytes, v, ibytes) || ranges_overlap(o, obytes, workspace, need))
+  size_t qel, kel, obytes, qbytes, kbytes;
+  if (!mul_ok((size_t)B * Hq * Nq, (size_t)D, &qel) || !mul_ok((size_t)B * Hkv * Nk, (size_t)D, &kel))
+    return SAGE_ERR_INVALID;
+  if (!mul_ok(qel, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(qel, 2, &qbytes) || !mul_ok(kel, 2, &kbytes))
+    return SAGE_ERR_INVALID;
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kbytes) ||
+      ranges_overlap(o, obytes, v, kbytes) || ranges_overlap(o, obytes, workspace, need))
     return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
@@ -214,18 +233,20 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
   carve(workspace, d, &qb);
   const Bufs b = to_internal(qb);
   const float ks = sm_scale * 1.44269504088896340736f;
-  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, 1.0f, stream);
+  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, stream);
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_attn(b, d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
-sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
-                                float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream) {
-  if (!bufs_ok(qb) || !o || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B, int Hq, int Hkv, int Nq, int Nk,
+                                      int D, int causal, float sm_scale, int qk_bits, sage_dtype out_dtype,
+                                      hipStream_t stream) {
+  if (!bufs_ok(qb) || !o || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, H, N, D, qk_bits);
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
@@ -234,14 +255,38 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
+// Self-attention: the same calls with Hq = Hkv = H and Nq = Nk = N.
+size_t sage_workspace_bytes(int B, int H, int N, int D) { return sage_workspace_bytes_cross(B, H, H, N, N, D); }
+
+sage_status sage_quant_bufs_from_workspace(void* ws, size_t bytes, int B, int H, int N, int D, sage_quant_bufs* out) {
+  return sage_quant_bufs_from_workspace_cross(ws, bytes, B, H, H, N, N, D, out);
+}
+
+sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H, int N,
+                              int D, int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream) {
+  return sage_quant_smooth_cross(q, k, v, in_dtype, B, H, H, N, N, D, qk_bits, smooth_v, out, stream);
+}
+
+sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
+                          int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
+                          sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sage_attn_fwd_cross(q, k, v, o, B, H, H, N, N, D, causal, sm_scale, qk_bits, smooth_v, in_dtype, out_dtype,
+                             workspace, workspace_bytes, stream);
+}
+
+sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H, int N, int D, int causal,
+                                float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream) {
+  return sage_attn_quantized_cross(qb, o, B, H, H, N, N, D, causal, sm_scale, qk_bits, out_dtype, stream);
+}
+
 sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int qk_bits, int bh, int q0,
                                 int k0, int nq, int nk, int32_t* out, hipStream_t stream) {
-  if (!bufs_ok(qb) || !out || !shape_ok(B, H, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (!bufs_ok(qb) || !out || !shape_ok(B, H, H, N, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
   if (bh < 0 || bh >= B * H || q0 < 0 || k0 < 0 || nq < 1 || nk < 1) return SAGE_ERR_INVALID;
   if ((long long)q0 + nq > N || (long long)k0 + nk > N) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, N, D, qk_bits), bh, q0, k0, nq, nk, out, stream);
+  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, H, N, N, D, qk_bits), bh, q0, k0, nq, nk, out, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -250,7 +295,7 @@ sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, 
 // (nseq, H, max_seqlen, D).
 static bool varlen_ok(const int* cu, int nseq, int max_seqlen, int total, int H, int D) {
   // the prepass grids put the 128-token blocks in the y dimension (<= 65535)
-  return cu && total >= 1 && shape_ok(nseq, H, max_seqlen, D) && (max_seqlen + 127) / 128 <= 65535;
+  return cu && total >= 1 && shape_ok(nseq, H, H, max_seqlen, max_seqlen, D) && (max_seqlen + 127) / 128 <= 65535;
 }
 
 sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v, sage_dtype in_dtype,
@@ -260,13 +305,13 @@ sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v
     return SAGE_ERR_INVALID;
   if (!bits_ok(qk_bits) || (smooth_v != 0 && smooth_v != 1)) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
-  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits, smooth_v);
+  Dims d = make_dims(nseq, H, H, max_seqlen, max_seqlen, D, qk_bits, smooth_v);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   d.cu = cu_seqlens;
   d.T = total_tokens;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), 1.0f, stream);
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -280,7 +325,7 @@ sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits, smooth_v);
+  Dims d = make_dims(nseq, H, H, max_seqlen, max_seqlen, D, qk_bits, smooth_v);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
@@ -298,7 +343,7 @@ sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
   carve(workspace, d, &qb);
   const Bufs b = to_internal(qb);
   const float ks = sm_scale * 1.44269504088896340736f;
-  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, 1.0f, stream);
+  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, stream);
   if (e != hipSuccess) return SAGE_ERR_HIP;
   e = sage::launch_attn(b, d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
@@ -311,7 +356,7 @@ sage_status sage_attn_quantized_varlen(const sage_quant_bufs* qb, void* o, const
     return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  Dims d = make_dims(nseq, H, max_seqlen, D, qk_bits);
+  Dims d = make_dims(nseq, H, H, max_seqlen, max_seqlen, D, qk_bits);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   d.cu = cu_seqlens;
   d.T = total_tokens;

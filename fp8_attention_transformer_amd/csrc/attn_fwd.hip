@@ -253,14 +253,15 @@ __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, c
   }
 }
 
-// n: valid keys of the head; nqb: its key blocks.
+// nk: valid keys of the head; klim: the last key this lane's query may see
+// (causal); need_mask: some key of block t is masked for some query of the
+// workgroup (wave-uniform).
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
-                                             const float* cKS, float dq, float ks, int t, int qb, int qrow, int h,
-                                             int n, int nqb, v8i* P8, float& alpha) {
+                                             const float* cKS, float dq, float ks, int t, int klim, int h, int nk,
+                                             bool need_mask, v8i* P8, float& alpha) {
   float s2[4][16];
   float tmax[4];
-  const bool need_mask = (CAUSAL && t == qb) || (t == nqb - 1 && n != nqb * kBK);
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     const float c = (dq * cKS[2 * T + h]) * ks;
@@ -273,7 +274,7 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int key = t * kBK + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool bad = (key >= n) || (CAUSAL && key > qrow);
+        const bool bad = (key >= nk) || (CAUSAL && key > klim);
         if (bad) s2[T][r] = -__builtin_inff();
       }
     }
@@ -339,14 +340,14 @@ __device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8,
 template <int D, int BITS, bool CAUSAL>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
-                                           int t, int qb, int qrow, int n, int h, int nvalid, int nqb) {
+                                           int t, int klim, int n, int h, int nk, bool need_mask) {
   v16f S[4];
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   qk_part<D, BITS>(S, qop, cK, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   v8i P8[2];
   float alpha;
-  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, qb, qrow, h, nvalid, nqb, P8, alpha);
+  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -392,25 +393,35 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const int bh = d.cu ? logical % d.BH() : logical / d.NQB;
   const int jq = d.cu ? logical / d.BH() : logical % d.NQB;
   const int qb = CAUSAL ? d.NQB - 1 - jq : jq;
-  const HeadIO io = head_io(d, bh);
-  const int nqb = (io.n + kBQ - 1) / kBQ;        // query and key blocks of this head
+  const HeadIO io = head_io(d, bh);              // queries and outputs
+  const int nqb = (io.n + kBQ - 1) / kBQ;
   if (qb >= nqb) return;                         // past a shorter packed sequence (whole workgroup)
+  const int bhk = d.kv_head(bh);
+  const int nk = head_io_kv(d, bhk).n;           // keys of this head
+  const int nkb = (nk + kBK - 1) / kBK;
+  // causal mask aligned at the last key: query i sees keys j <= i + (nk - n)
+  const int off = nk - io.n;
   const int qrow = qb * kBQ + wave * 32 + n;     // padded query index of this lane
+  const int klim = qrow + off;
   const size_t hrowp = (size_t)bh * d.NP;
 
-  const float* dsrow = b.delta_s + ((size_t)bh * d.NQB + qb) * d.NP;
-  const uint8_t* kblk = b.k_codes + hrowp * ROWB;
-  const uint8_t* vblk = b.v_codes + (size_t)bh * d.NQB * D * kBK;
-  const float* kscl = b.k_scale + hrowp / kKGroup;
-  const int tend = CAUSAL ? qb + 1 : nqb;
+  const float* dsrow = b.delta_s + ((size_t)bh * d.NQB + qb) * d.NPk;
+  const uint8_t* kblk = b.k_codes + (size_t)bhk * d.NPk * ROWB;
+  const uint8_t* vblk = b.v_codes + (size_t)bhk * d.NQBk * D * kBK;
+  const float* kscl = b.k_scale + (size_t)bhk * d.NPk / kKGroup;
+  // key blocks: all, or (causal) up to the one holding the last valid query's
+  // last key; blocks past the first query's limit need the mask
+  const int tend = CAUSAL ? (min(qb * kBQ + kBQ, io.n) - 1 + off) / kBK + 1 : nkb;
+  const int tmask = CAUSAL ? (qb * kBQ + off) / kBK : nkb;   // first block with a causally masked key
+  const bool ragged = nk != nkb * kBK;
 
   // Every wave issues the same number of memory ops per block (the small
   // loads are unconditional, with in-range indices), so a vmcnt limit of
   // VM_PER_BLOCK * k waits exactly for all but the newest k blocks.
   float ds_reg[S - 1], ks_reg[S - 1];
   const uint32_t koff = k_src_offset<D, BITS>(wave, lane), voff = v_src_offset(wave, lane);
-  const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NP * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NP * D);
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NPk * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NPk * D);
   auto issue = [&](int t, int slot) {
     stage_kv_async<D, BITS>(bK(slot), bV(slot), rk, rv, t, wave, koff, voff);
     ds_reg[t % (S - 1)] = dsrow[t * kBK + (tid & (kBK - 1))];
@@ -445,8 +456,9 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     const int slot = t % S;
     const bool ahead = t + S - 1 < tend;          // block t+S-1 exists: stage it now
     if (ahead) issue(t + S - 1, (t + S - 1) % S);
-    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, qb, qrow, n, h, io.n,
-                                nqb);
+    const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
+    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, klim, n, h, nk,
+                                need_mask);
     if (t + 1 < tend) {
       // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
       if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
@@ -459,8 +471,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
   const int qi = qrow;
   if (qi < io.n) {
-    const float* vs = b.v_scale + (size_t)bh * D;
-    const float* vm = b.v_mean + (size_t)bh * D;
+    const float* vs = b.v_scale + (size_t)bhk * D;
+    const float* vm = b.v_mean + (size_t)bhk * D;
     const size_t orow = io.base + (size_t)qi * io.stride;
     const float inv_l = 1.0f / as.l;
 #pragma unroll
@@ -480,14 +492,13 @@ __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, in
                                                       int32_t* __restrict__ out) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
-  const size_t hrowp = (size_t)bh * d.NP;
   const int qloc = blockIdx.x * 32 + n;
   const int kbase = blockIdx.y * 32;
   const int qrow = min(q0 + qloc, d.NP - 1);
   QOperand<D, BITS> qop;
-  load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
-  const int krow = min(k0 + kbase + n, d.NP - 1);
-  const uint8_t* khead = b.k_codes + hrowp * ROWB;
+  load_q_operand<D, BITS>(b.q_codes + (size_t)bh * d.NP * ROWB, qrow, h, qop);
+  const int krow = min(k0 + kbase + n, d.NPk - 1);
+  const uint8_t* khead = b.k_codes + (size_t)d.kv_head(bh) * d.NPk * ROWB;
   v16f s;
   if constexpr (BITS == 4) {
     v8i a[D / 64];

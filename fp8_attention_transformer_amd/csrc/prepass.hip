@@ -7,48 +7,64 @@
 // readings taken where the pages are silent (block sizes, scale groups, mean
 // order, rounding) are the contract constants of sage_internal.h.
 //
-// All kernels here are HBM-bound except the compensation term (VALU-bound
+// All kernels here are HBM-bound except the compensation term (matrix-core
 // dot products); they are launched in order on the caller's stream:
 //   stats -> finalize -> quant -> delta_s.
+// Self-attention handles a token block of Q, K and V in one workgroup; with
+// separate query and key/value geometry (cross-attention, decoding, grouped
+// heads) the stats and quant steps run once for the query side and once for
+// the key/value side.
 #include "sage_internal.h"
 #include "sage_device.h"
 
 namespace sage {
 namespace {
 
+// Which inputs a prepass workgroup handles: the query side, the key/value
+// side, or both (self-attention, where a token block of Q, K and V is one
+// work item).
+enum Part { kPartQ = 1, kPartKV = 2, kPartBoth = 3 };
+
 // ---------------------------------------------------------------------------
 // stats: 256 threads, one channel pair per thread, 256/(D/2) chunks of 128
 // tokens per workgroup.  Each thread walks its chunk in token order (the sums
-// are sequential per channel); loads are issued 32 tokens ahead.
-template <int IN, int D>
+// are sequential per channel); loads are issued 32 tokens ahead.  Q side:
+// block means; K/V side: per-chunk K and V sums and V maxima and minima.
+template <int IN, int D, int PART>
 __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
   constexpr int LPC = D / 2;          // lanes per chunk
   constexpr int CPW = 256 / LPC;      // chunks per workgroup
   constexpr int U = 32;               // tokens in flight
+  constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
   const int tid = threadIdx.x, cp = tid % LPC;
   const int chunk = blockIdx.x * CPW + tid / LPC;
-  if (chunk >= d.BH() * d.NQB) return;
+  const int nh = DO_Q ? d.BH() : d.BHk(), nb = DO_Q ? d.NQB : d.NQBk;
+  if (chunk >= nh * nb) return;
   // dense: the chunks of a head are adjacent; packed [T, H, D]: the heads of a
   // token block are adjacent, so neighbouring workgroups read whole rows
-  const int bh = d.cu ? chunk % d.BH() : chunk / d.NQB, qb = d.cu ? chunk / d.BH() : chunk % d.NQB;
-  const HeadIO io = head_io(d, bh);
+  const int bh = d.cu ? chunk % nh : chunk / nb, qb = d.cu ? chunk / nh : chunk % nb;
+  const HeadIO io = DO_Q ? head_io(d, bh) : head_io_kv(d, bh);
   const int i0 = qb * kBQ, i1 = min(io.n, i0 + kBQ);   // i1 <= i0: empty chunk (short sequence)
   const size_t base = io.base + 2 * cp, rs = io.stride;
   float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
   float vx0 = -__builtin_inff(), vx1 = -__builtin_inff(), vn0 = __builtin_inff(), vn1 = __builtin_inff();
   auto add = [&](uint32_t qv, uint32_t kv, uint32_t vv) {
-    qs0 = qs0 + in_to_f32<IN>((uint16_t)(qv & 0xFFFF));
-    qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
-    ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
-    ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
-    const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
-    vs0 = vs0 + v0;
-    vs1 = vs1 + v1;
-    vx0 = fmaxf(vx0, v0);
-    vx1 = fmaxf(vx1, v1);
-    vn0 = fminf(vn0, v0);
-    vn1 = fminf(vn1, v1);
+    if constexpr (DO_Q) {
+      qs0 = qs0 + in_to_f32<IN>((uint16_t)(qv & 0xFFFF));
+      qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
+    }
+    if constexpr (DO_KV) {
+      ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
+      ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
+      const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
+      vs0 = vs0 + v0;
+      vs1 = vs1 + v1;
+      vx0 = fmaxf(vx0, v0);
+      vx1 = fmaxf(vx1, v1);
+      vn0 = fminf(vn0, v0);
+      vn1 = fminf(vn1, v1);
+    }
   };
   if (i1 - i0 == kBQ) {
     // full chunk: branch-free, U tokens of loads in flight
@@ -57,9 +73,9 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const size_t o = base + (size_t)(i + u) * rs;
-        qv[u] = *(const uint32_t*)(q + o);
-        kv[u] = *(const uint32_t*)(k + o);
-        vv[u] = *(const uint32_t*)(v + o);
+        qv[u] = DO_Q ? *(const uint32_t*)(q + o) : 0u;
+        kv[u] = DO_KV ? *(const uint32_t*)(k + o) : 0u;
+        vv[u] = DO_KV ? *(const uint32_t*)(v + o) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < U; u++) add(qv[u], kv[u], vv[u]);
@@ -67,39 +83,44 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   } else {
     for (int i = i0; i < i1; i++) {
       const size_t o = base + (size_t)i * rs;
-      add(*(const uint32_t*)(q + o), *(const uint32_t*)(k + o), *(const uint32_t*)(v + o));
+      add(DO_Q ? *(const uint32_t*)(q + o) : 0u, DO_KV ? *(const uint32_t*)(k + o) : 0u,
+          DO_KV ? *(const uint32_t*)(v + o) : 0u);
     }
   }
-  const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
-  const size_t o2 = ((size_t)bh * d.NQB + qb) * 2 * D + 2 * cp;
-  const float cnt = (float)(i1 - i0);
-  b.q_mean[o] = i1 > i0 ? qs0 / cnt : 0.0f;
-  b.q_mean[o + 1] = i1 > i0 ? qs1 / cnt : 0.0f;
-  b.k_part[o2] = ks0;
-  b.k_part[o2 + 1] = ks1;
-  b.k_part[o2 + D] = vs0;
-  b.k_part[o2 + D + 1] = vs1;
-  b.v_part[o2] = vx0;
-  b.v_part[o2 + 1] = vx1;
-  b.v_part[o2 + D] = vn0;
-  b.v_part[o2 + D + 1] = vn1;
+  if constexpr (DO_Q) {
+    const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
+    const float cnt = (float)(i1 - i0);
+    b.q_mean[o] = i1 > i0 ? qs0 / cnt : 0.0f;
+    b.q_mean[o + 1] = i1 > i0 ? qs1 / cnt : 0.0f;
+  }
+  if constexpr (DO_KV) {
+    const size_t o2 = ((size_t)bh * d.NQBk + qb) * 2 * D + 2 * cp;
+    b.k_part[o2] = ks0;
+    b.k_part[o2 + 1] = ks1;
+    b.k_part[o2 + D] = vs0;
+    b.k_part[o2 + D + 1] = vs1;
+    b.v_part[o2] = vx0;
+    b.v_part[o2 + 1] = vx1;
+    b.v_part[o2 + D] = vn0;
+    b.v_part[o2 + D + 1] = vn1;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// finalize: grid (B*H), D threads.  K mean = (sum of chunk sums, in chunk
-// order) / N; likewise the V mean when V is smoothed (else 0).  V scale =
+// finalize: grid (B*Hk), D threads.  K mean = (sum of chunk sums, in chunk
+// order) / Nk; likewise the V mean when V is smoothed (else 0).  V scale =
 // max|V - vmean| / 448, from the chunk maxima and minima: rounding is
 // monotonic, so max_j |fl(V_j - m)| = max(|fl(max V - m)|, |fl(min V - m)|).
 __global__ void finalize_kernel(Dims d, Bufs b) {
   constexpr int U = 8;
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
-  const size_t base = (size_t)bh * d.NQB * 2 * D + c;
+  const size_t base = (size_t)bh * d.NQBk * 2 * D + c;
   float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
-  for (int t = 0; t < d.NQB; t += U) {
+  for (int t = 0; t < d.NQBk; t += U) {
     float kp[U], vp[U], xp[U], np[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const bool ok = t + u < d.NQB;
+      const bool ok = t + u < d.NQBk;
       const size_t o = base + (size_t)(t + u) * 2 * D;
       kp[u] = ok ? b.k_part[o] : 0.0f;
       vp[u] = ok ? b.k_part[o + D] : 0.0f;
@@ -108,7 +129,7 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      if (t + u < d.NQB) {
+      if (t + u < d.NQBk) {
         tot = tot + kp[u];
         vtot = vtot + vp[u];
       }
@@ -116,7 +137,7 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
       vn = fminf(vn, np[u]);
     }
   }
-  const int n = head_io(d, bh).n;   // 0 only for an empty packed sequence
+  const int n = head_io_kv(d, bh).n;   // 0 only for an empty packed sequence
   b.k_mean[(size_t)bh * D + c] = n ? tot / (float)n : 0.0f;
   const float vbar = (d.SV && n) ? vtot / (float)n : 0.0f;
   b.v_mean[(size_t)bh * D + c] = vbar;
@@ -226,36 +247,41 @@ __device__ __forceinline__ void fp8_quotients(float* x, float dv) {
 }
 
 // ---------------------------------------------------------------------------
-// quant: grid (NQB, B*H), 256 threads.  One 128-token block of one head:
+// quant: 256 threads, one 128-token block of one head; grid (blocks, heads):
+// (NQB, B*H) for the query side and for self-attention, (NQBk, B*Hk) for the
+// key/value side.
 //  Q: one scale per token (D/16 lanes per token, 16 channels each);
 //  K: one scale per 16-key fragment group (one group = 16 keys x D/32 lanes);
 //  V: FP8 with the per-channel scale, written in the permuted channel-major
 //     layout through an LDS copy of the block.
-template <int IN, int D, int BITS>
+template <int IN, int D, int BITS, int PART>
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
   constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
-  __shared__ __align__(16) uint16_t sV[kBK * D];
-  // grid (NQB, B*H), or (B*H, NQB) for packed [T, H, D] inputs (heads of a
-  // token block adjacent)
+  constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
+  __shared__ __align__(16) uint16_t sV[DO_KV ? kBK * D : 8];
+  // packed [T, H, D] inputs: grid (B*H, NQB), heads of a token block adjacent
   const int qb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i0 = qb * kBQ;
-  const HeadIO io = head_io(d, bh);          // input tokens of this head
+  // input tokens of this head (query head, or key/value head for the K/V side)
+  const HeadIO io = DO_Q ? head_io(d, bh) : head_io_kv(d, bh);
   // past the end of a shorter packed sequence: nothing here is ever read
   if (d.cu && i0 >= io.n) return;
-  const size_t hrowp = (size_t)bh * d.NP;    // first padded row of this head
+  const size_t qrowp = (size_t)bh * d.NP;    // first padded query row of this head
+  const size_t krowp = (size_t)bh * d.NPk;   // first padded key row of this head
 
-  // ---- V block -> LDS (rows >= N are zero)
-  for (int e = tid; e < kBK * D / 8; e += 256) {
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    v4i val = {0, 0, 0, 0};
-    if (i0 + r < io.n) val = *(const v4i*)(v + io.base + (size_t)(i0 + r) * io.stride + 8 * c8);
-    *(v4i*)(sV + r * D + 8 * c8) = val;
-  }
+  // ---- V block -> LDS (rows >= Nk are zero)
+  if constexpr (DO_KV)
+    for (int e = tid; e < kBK * D / 8; e += 256) {
+      const int r = e / (D / 8), c8 = e % (D / 8);
+      v4i val = {0, 0, 0, 0};
+      if (i0 + r < io.n) val = *(const v4i*)(v + io.base + (size_t)(i0 + r) * io.stride + 8 * c8);
+      *(v4i*)(sV + r * D + 8 * c8) = val;
+    }
 
   // ---- Q: LPT lanes per token, 16 channels per lane
-  {
+  if constexpr (DO_Q) {
     constexpr int LPT = D / 16, TPP = 256 / LPT;
     const int sub = tid % LPT, c0 = 16 * sub;
     float qm[16];
@@ -300,7 +326,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
         uint32_t w[3];
         pack_fp6<16>(cq, w);
         const int hq = (c0 >> 5) & 1, odd = sub & 1;
-        uint32_t* chunk = (uint32_t*)(b.q_codes + fp6_chunk_offset(D, hrowp + i, hq));
+        uint32_t* chunk = (uint32_t*)(b.q_codes + fp6_chunk_offset(D, qrowp + i, hq));
         if constexpr (D == 128) {
           const int d0 = 6 * (c0 >> 6) + 3 * odd;
 #pragma unroll
@@ -323,14 +349,14 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
           for (int e = 0; e < 4; e++) word |= ((uint32_t)cq[4 * w + e] & 0xFFu) << (8 * e);
           pk[w] = (int)word;
         }
-        *(v4i*)(b.q_codes + (hrowp + i) * D + 16 * sub) = pk;
+        *(v4i*)(b.q_codes + (qrowp + i) * D + 16 * sub) = pk;
       }
-      if (sub == 0) b.q_scale[hrowp + i] = dq;
+      if (sub == 0) b.q_scale[qrowp + i] = dq;
     }
   }
   // ---- K: a group (T, hh) holds keys 32T + 8u + 4hh + w (u, w in 0..3);
   //      LPK lanes per key, 32 channels per lane.
-  {
+  if constexpr (DO_KV) {
     constexpr int LPK = D / 32, LPG = 16 * LPK;          // lanes per key / per group
     constexpr int GPW = 64 / LPG;                          // groups per wave
     const int sub = lane % LPK, c0 = 32 * sub;
@@ -363,7 +389,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
         uint32_t w[6];
         pack_fp6<32>(ck, w);
         const int hk = sub & 1;
-        uint8_t* chunk = b.k_codes + fp6_chunk_offset(D, hrowp + j, hk);
+        uint8_t* chunk = b.k_codes + fp6_chunk_offset(D, krowp + j, hk);
         if constexpr (D == 128) {
 #pragma unroll
           for (int k2 = 0; k2 < 3; k2++) {
@@ -390,16 +416,16 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
             for (int e = 0; e < 4; e++) word |= ((uint32_t)ck[16 * half + 4 * w + e] & 0xFFu) << (8 * e);
             pk[w] = (int)word;
           }
-          *(v4i*)(b.k_codes + (hrowp + j) * D + 32 * sub + 16 * half) = pk;
+          *(v4i*)(b.k_codes + (krowp + j) * D + 32 * sub + 16 * half) = pk;
         }
       }
-      if ((lane % LPG) == 0) b.k_scale[hrowp / kKGroup + (i0 / kKGroup) + grp] = dk;
+      if ((lane % LPG) == 0) b.k_scale[krowp / kKGroup + (i0 / kKGroup) + grp] = dk;
     }
   }
-  __syncthreads();
   // ---- V: 16-key chunks of one channel -> 16 FP8 bytes
-  {
-    uint8_t* vout = b.v_codes + ((size_t)bh * d.NQB + qb) * D * kBK;
+  if constexpr (DO_KV) {
+    __syncthreads();
+    uint8_t* vout = b.v_codes + ((size_t)bh * d.NQBk + qb) * D * kBK;
     for (int e = tid; e < D * 8; e += 256) {
       const int ch = e % D, c = e / D;
       const float dv = b.v_scale[(size_t)bh * D + ch];
@@ -421,23 +447,25 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// delta_s: grid (NQB key blocks, B*H), 256 threads; wave w owns keys
-// j0 + 32w .. +31 and all Q blocks.  DeltaS = qmean . gamma(K) on the bf16
-// matrix core: every fp32 operand is split into three bf16 pieces
-// (x = x1 + x2 + x3 up to 2^-24 |x|) and the six products x_a*y_b with
-// a + b <= 4 are accumulated in fp32, which reproduces an fp32 dot product to
-// within a few units in the last place.
+// delta_s: grid (NQBk key blocks, B*H query heads), 256 threads; wave w owns
+// keys j0 + 32w .. +31 of the query head's K/V head and all Q blocks.
+// DeltaS = qmean . gamma(K) on the bf16 matrix core: every fp32 operand is
+// split into three bf16 pieces (x = x1 + x2 + x3 up to 2^-24 |x|) and the six
+// products x_a*y_b with a + b <= 4 are accumulated in fp32, which reproduces
+// an fp32 dot product to within a few units in the last place.
 template <int IN, int D>
 __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
   constexpr int NK = D / 16;   // k-steps of the 32x32x16 bf16 MFMA
   const int kb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
   const int j = kb * kBK + 32 * wave + n;        // this lane's key (B operand column)
-  const HeadIO io = head_io(d, bh);
+  const int bhk = d.kv_head(bh);
+  const HeadIO io = head_io_kv(d, bhk);
   // packed sequences: only key blocks and query blocks inside the sequence
-  const int nqb = d.cu ? (io.n + kBQ - 1) / kBQ : d.NQB;
-  if (kb >= nqb) return;
-  const float* km = b.k_mean + (size_t)bh * D;
+  const int nkb = d.cu ? (io.n + kBK - 1) / kBK : d.NQBk;
+  const int nqb = d.cu ? (head_io(d, bh).n + kBQ - 1) / kBQ : d.NQB;
+  if (kb >= nkb) return;
+  const float* km = b.k_mean + (size_t)bhk * D;
   // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
   v8bf B1[NK], B2[NK], B3[NK];
 #pragma unroll
@@ -482,7 +510,7 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
                                        0, 0);
     }
   };
-  float* out = b.delta_s + (size_t)bh * d.NQB * d.NP + j;
+  float* out = b.delta_s + (size_t)bh * d.NQB * d.NPk + j;
   stage(0, sA0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -510,7 +538,7 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int q2 = qt + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (q2 < d.NQB) out[(size_t)q2 * d.NP] = acc[r];
+      if (q2 < d.NQB) out[(size_t)q2 * d.NPk] = acc[r];
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -526,32 +554,48 @@ __global__ void fp8_encode_kernel(const float* __restrict__ in, uint8_t* __restr
   }
 }
 
+template <int IN, int D, int BITS>
+void launch_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, const Dims& d, const Bufs& b,
+                  hipStream_t s) {
+  if (d.self_attention()) {
+    const dim3 grid = d.cu ? dim3(d.BH(), d.NQB) : dim3(d.NQB, d.BH());
+    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartBoth>), grid, dim3(256), 0, s, q, k, v, d, b);
+  } else {
+    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartQ>), dim3(d.NQB, d.BH()), dim3(256), 0, s, q, k, v, d, b);
+    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartKV>), dim3(d.NQBk, d.BHk()), dim3(256), 0, s, q, k, v, d, b);
+  }
+}
+
 template <int IN, int D>
-hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims& d, const Bufs& b, float ds_scale,
-                        hipStream_t s) {
-  (void)ds_scale;
-  const dim3 grid = d.cu ? dim3(d.BH(), d.NQB) : dim3(d.NQB, d.BH());
+hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims& d, const Bufs& b, hipStream_t s) {
   const uint16_t* q16 = (const uint16_t*)q;
   const uint16_t* k16 = (const uint16_t*)k;
   const uint16_t* v16 = (const uint16_t*)v;
   constexpr int CPW = 256 / (D / 2);
-  const unsigned nstat = (unsigned)((d.BH() * d.NQB + CPW - 1) / CPW);
-  hipLaunchKernelGGL((stats_kernel<IN, D>), dim3(nstat), dim3(256), 0, s, q16, k16, v16, d, b);
-  hipLaunchKernelGGL(finalize_kernel, dim3(d.BH()), dim3(D), 0, s, d, b);
-  if (d.QB == 8) hipLaunchKernelGGL((quant_kernel<IN, D, 8>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
-  else hipLaunchKernelGGL((quant_kernel<IN, D, 4>), grid, dim3(256), 0, s, q16, k16, v16, d, b);
-  hipLaunchKernelGGL((delta_s_kernel<IN, D>), grid, dim3(256), 0, s, k16, d, b);
+  auto nstat = [](long long chunks) { return dim3((unsigned)((chunks + CPW - 1) / CPW)); };
+  if (d.self_attention()) {
+    hipLaunchKernelGGL((stats_kernel<IN, D, kPartBoth>), nstat((long long)d.BH() * d.NQB), dim3(256), 0, s, q16, k16,
+                       v16, d, b);
+  } else {
+    hipLaunchKernelGGL((stats_kernel<IN, D, kPartQ>), nstat((long long)d.BH() * d.NQB), dim3(256), 0, s, q16, k16, v16,
+                       d, b);
+    hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s, q16, k16,
+                       v16, d, b);
+  }
+  hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(D), 0, s, d, b);
+  if (d.QB == 8) launch_quant<IN, D, 8>(q16, k16, v16, d, b, s);
+  else launch_quant<IN, D, 4>(q16, k16, v16, d, b, s);
+  const dim3 ds_grid = d.cu ? dim3(d.BH(), d.NQBk) : dim3(d.NQBk, d.BH());
+  hipLaunchKernelGGL((delta_s_kernel<IN, D>), ds_grid, dim3(256), 0, s, k16, d, b);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
-                          float ds_scale, hipStream_t s) {
-  if (in_dtype == kBF16) {
-    return d.D == 64 ? prepass_impl<1, 64>(q, k, v, d, b, ds_scale, s) : prepass_impl<1, 128>(q, k, v, d, b, ds_scale, s);
-  }
-  return d.D == 64 ? prepass_impl<0, 64>(q, k, v, d, b, ds_scale, s) : prepass_impl<0, 128>(q, k, v, d, b, ds_scale, s);
+                          hipStream_t s) {
+  if (in_dtype == kBF16) return d.D == 64 ? prepass_impl<1, 64>(q, k, v, d, b, s) : prepass_impl<1, 128>(q, k, v, d, b, s);
+  return d.D == 64 ? prepass_impl<0, 64>(q, k, v, d, b, s) : prepass_impl<0, 128>(q, k, v, d, b, s);
 }
 
 hipError_t launch_fp8_encode(const float* in, uint8_t* out, size_t n, hipStream_t s) {

@@ -40,17 +40,26 @@ __host__ __device__ inline int fp6_half_offset(int chunk_index, int half) {
 }
 
 struct Dims {
-  int B, H, N, D;
+  int B, H, N, D;   // queries: B batches x H heads x N tokens
   int NP;    // N rounded up to a multiple of 128
-  int NQB;   // NP / 128
+  int NQB;   // NP / 128: query blocks per head
+  // Keys and values: Hk heads (H is a multiple of Hk; query head h reads K/V
+  // head h / (H / Hk)) and Nk tokens.  Self-attention: Hk == H, Nk == N.
+  int Hk, Nk;
+  int NPk;   // Nk rounded up to a multiple of 128
+  int NQBk;  // NPk / 128: key blocks per head
   int QB;    // bits per Q/K code: 4 (INT4, stored as FP6) or 8 (INT8)
   int SV;    // 1: smooth V (subtract the per-channel V mean before FP8)
-  // Packed variable-length batches: when cu is not null, head b*H + h is
-  // sequence b, tokens cu[b] .. cu[b+1]-1 of a token-major [T, H, D] tensor,
-  // and N is the maximum length (it sets the workspace geometry).
+  // Packed variable-length batches (self-attention only): when cu is not
+  // null, head b*H + h is sequence b, tokens cu[b] .. cu[b+1]-1 of a
+  // token-major [T, H, D] tensor, and N is the maximum length (it sets the
+  // workspace geometry).
   const int* cu;
   int T;
   __host__ __device__ int BH() const { return B * H; }
+  __host__ __device__ int BHk() const { return B * Hk; }
+  __host__ __device__ bool self_attention() const { return Hk == H && Nk == N; }
+  __host__ __device__ int kv_head(int bh) const { return (bh / H) * Hk + (bh % H) / (H / Hk); }
 };
 
 // Where the tokens of head bh live in q, k, v and o: token i starts at element
@@ -61,6 +70,7 @@ struct HeadIO {
   int n;
   size_t base, stride;
 };
+// Query head bh (q and o).
 __device__ inline HeadIO head_io(const Dims& d, int bh) {
   HeadIO io;
   if (!d.cu) {
@@ -78,25 +88,37 @@ __device__ inline HeadIO head_io(const Dims& d, int bh) {
   io.stride = (size_t)d.H * d.D;
   return io;
 }
+// Key/value head bhk (k and v); packed batches have Hk == H and Nk == N.
+__device__ inline HeadIO head_io_kv(const Dims& d, int bhk) {
+  if (d.cu) return head_io(d, bhk);
+  HeadIO io;
+  io.n = d.Nk;
+  io.base = (size_t)bhk * d.Nk * d.D;
+  io.stride = (size_t)d.D;
+  return io;
+}
 
 // Device buffers written by the prepass and read by the attention kernel.
+// Query-side arrays use (H, NP, NQB), key/value-side arrays (Hk, NPk, NQBk).
 struct Bufs {
   uint8_t* q_codes;   // QB 4: FP6 tiles (above), QB 8: int8 [B,H,NP,D]
-  uint8_t* k_codes;   // same layout as q_codes
+  uint8_t* k_codes;   // same layout, [B,Hk,NPk,...]
   float* q_scale;     // [B,H,NP]
-  float* k_scale;     // [B,H,NP/16]
+  float* k_scale;     // [B,Hk,NPk/16]
   float* q_mean;      // [B,H,NQB,D]
-  float* k_mean;      // [B,H,D]
-  uint8_t* v_codes;   // [B,H,NQB,D,128] e4m3fn, keys permuted inside each 128-key block
-  float* v_scale;     // [B,H,D]
-  float* delta_s;     // [B,H,NQB,NP]   compensation term times ds_scale
-  float* k_part;      // [B,H,NQB,2,D]  per-chunk K and V channel sums; then bf16 q_mean pieces 1-2
-  float* v_part;      // [B,H,NQB,2,D]  per-chunk V channel max and min; then bf16 q_mean piece 3
-  float* v_mean;      // [B,H,D]        V channel means (zeros without V smoothing)
+  float* k_mean;      // [B,Hk,D]
+  uint8_t* v_codes;   // [B,Hk,NQBk,D,128] e4m3fn, keys permuted inside each 128-key block
+  float* v_scale;     // [B,Hk,D]
+  float* delta_s;     // [B,H,NQB,NPk]  compensation term
+  float* k_part;      // [B,Hk,NQBk,2,D] per-chunk K and V channel sums; then bf16 q_mean
+                      //                 pieces 1-2 as [B,H,NQB,2,D] (sized for the larger)
+  float* v_part;      // [B,Hk,NQBk,2,D] per-chunk V channel max and min; then bf16 q_mean
+                      //                 piece 3 as [B,H,NQB,D]
+  float* v_mean;      // [B,Hk,D]        V channel means (zeros without V smoothing)
 };
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d,
-                          const Bufs& b, float ds_scale, hipStream_t s);
+                          const Bufs& b, hipStream_t s);
 hipError_t launch_attn(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
                        hipStream_t s);
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk,

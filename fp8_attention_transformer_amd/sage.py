@@ -22,6 +22,8 @@ EXPORTED = [
     "sage_contract_version", "sage_status_string", "sage_workspace_bytes", "sage_quant_bufs_from_workspace",
     "sage_quant_smooth", "sage_attn_fwd", "sage_attn_quantized", "sage_qk_int32_debug", "sage_fp8_encode_debug",
     "sage_quant_smooth_varlen", "sage_attn_fwd_varlen", "sage_attn_quantized_varlen",
+    "sage_workspace_bytes_cross", "sage_quant_bufs_from_workspace_cross", "sage_quant_smooth_cross",
+    "sage_attn_fwd_cross", "sage_attn_quantized_cross",
 ]
 
 
@@ -76,6 +78,16 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_quantized_varlen.argtypes = [ctypes.POINTER(QuantBufs), P, P, i32, i32, i32, i32, i32, i32, f32,
                                                  i32, i32, P]
         L.sage_attn_quantized_varlen.restype = i32
+        L.sage_workspace_bytes_cross.argtypes = [i32] * 6
+        L.sage_workspace_bytes_cross.restype = sz
+        L.sage_quant_bufs_from_workspace_cross.argtypes = [P, sz] + [i32] * 6 + [ctypes.POINTER(QuantBufs)]
+        L.sage_quant_bufs_from_workspace_cross.restype = i32
+        L.sage_quant_smooth_cross.argtypes = [P, P, P] + [i32] * 9 + [ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth_cross.restype = i32
+        L.sage_attn_fwd_cross.argtypes = [P, P, P, P] + [i32] * 7 + [f32, i32, i32, i32, i32, P, sz, P]
+        L.sage_attn_fwd_cross.restype = i32
+        L.sage_attn_quantized_cross.argtypes = [ctypes.POINTER(QuantBufs), P] + [i32] * 7 + [f32, i32, i32, P]
+        L.sage_attn_quantized_cross.restype = i32
         _lib = L
     return _lib
 
@@ -157,6 +169,39 @@ def attn_fwd_varlen(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, cu_ptr: int,
                                       out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd_varlen")
 
 
+def workspace_bytes_cross(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int) -> int:
+    return lib().sage_workspace_bytes_cross(B, Hq, Hkv, Nq, Nk, D)
+
+
+def quant_bufs_from_workspace_cross(ws_ptr: int, nbytes: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                                    D: int) -> QuantBufs:
+    qb = QuantBufs()
+    _check(lib().sage_quant_bufs_from_workspace_cross(ws_ptr, nbytes, B, Hq, Hkv, Nq, Nk, D, ctypes.byref(qb)),
+           "sage_quant_bufs_from_workspace_cross")
+    return qb
+
+
+def quant_smooth_cross(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, Hq: int, Hkv: int, Nq: int,
+                       Nk: int, D: int, bufs: QuantBufs, stream: int = 0, qk_bits: int = 4,
+                       smooth_v: bool = False) -> None:
+    _check(lib().sage_quant_smooth_cross(q_ptr, k_ptr, v_ptr, in_dtype, B, Hq, Hkv, Nq, Nk, D, qk_bits,
+                                         int(bool(smooth_v)), ctypes.byref(bufs), stream), "sage_quant_smooth_cross")
+
+
+def attn_fwd_cross(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                   D: int, causal: bool, sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int,
+                   stream: int = 0, qk_bits: int = 4, smooth_v: bool = False) -> None:
+    _check(lib().sage_attn_fwd_cross(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
+                                     float(sm_scale), qk_bits, int(bool(smooth_v)), in_dtype, out_dtype, ws_ptr,
+                                     ws_bytes, stream), "sage_attn_fwd_cross")
+
+
+def attn_quantized_cross(bufs: QuantBufs, o_ptr: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int,
+                         causal: bool, sm_scale: float, out_dtype: int, stream: int = 0, qk_bits: int = 4) -> None:
+    _check(lib().sage_attn_quantized_cross(ctypes.byref(bufs), o_ptr, B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
+                                           float(sm_scale), qk_bits, out_dtype, stream), "sage_attn_quantized_cross")
+
+
 # ---------------------------------------------------------------- torch glue --
 # Device memory and the stream handle come from torch; nothing is computed here.
 
@@ -169,9 +214,11 @@ def _torch_dtype_code(t) -> int:
 class Workspace:
     tensor: object      # torch.uint8 device tensor
     B: int
-    H: int
-    N: int
+    H: int              # query heads
+    N: int              # query tokens
     D: int
+    Hkv: int = 0        # key/value heads (0: H)
+    Nk: int = 0         # key/value tokens (0: N)
 
     @property
     def ptr(self) -> int:
@@ -182,15 +229,16 @@ class Workspace:
         return self.tensor.numel()
 
     def bufs(self) -> QuantBufs:
-        return quant_bufs_from_workspace(self.ptr, self.nbytes, self.B, self.H, self.N, self.D)
+        return quant_bufs_from_workspace_cross(self.ptr, self.nbytes, self.B, self.H, self.Hkv or self.H, self.N,
+                                               self.Nk or self.N, self.D)
 
 
-def alloc_workspace(B: int, H: int, N: int, D: int, device="cuda") -> Workspace:
+def alloc_workspace(B: int, H: int, N: int, D: int, device="cuda", Hkv: int = 0, Nk: int = 0) -> Workspace:
     import torch
-    n = workspace_bytes(B, H, N, D)
+    n = workspace_bytes_cross(B, H, Hkv or H, N, Nk or N, D)
     if n == 0:
-        raise SageError(ERR_INVALID, "sage_workspace_bytes")
-    return Workspace(torch.empty(n, dtype=torch.uint8, device=device), B, H, N, D)
+        raise SageError(ERR_INVALID, "sage_workspace_bytes_cross")
+    return Workspace(torch.empty(n, dtype=torch.uint8, device=device), B, H, N, D, Hkv or H, Nk or N)
 
 
 def _stream_handle(device) -> int:
@@ -200,27 +248,35 @@ def _stream_handle(device) -> int:
 
 def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype=None, workspace: Workspace = None,
          out=None, qk_bits: int = 4, smooth_v: bool = False):
-    """Drop-in attention over [B, H, N, D] fp16/bf16 CUDA tensors (qk_bits 4: INT4 Q/K codes, 8: INT8;
-    smooth_v: subtract the V channel means before FP8)."""
+    """Drop-in attention: q [B, Hq, Nq, D], k and v [B, Hkv, Nk, D] fp16/bf16
+    device tensors (Hq a multiple of Hkv; Hq == Hkv and Nq == Nk for plain
+    self-attention).  qk_bits 4: INT4 Q/K codes, 8: INT8; smooth_v: subtract
+    the V channel means before FP8; a causal mask is aligned at the last key."""
     import torch
-    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
-        raise ValueError("q, k, v must share one [B, H, N, D] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Nq, D] and k, v one [B, Hkv, Nk, D] shape")
+    B, H, N, D = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q, k, v must share B and D")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
         raise ValueError("q, k, v must all be float16 or all bfloat16")
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
-    B, H, N, D = q.shape
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, H, N, D), dtype=out_dtype, device=q.device)
     if workspace is None:
-        workspace = alloc_workspace(B, H, N, D, q.device)
-    attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, causal, sm_scale,
-             _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr, workspace.nbytes,
-             _stream_handle(q.device), qk_bits, smooth_v)
+        workspace = alloc_workspace(B, H, N, D, q.device, Hkv=Hk, Nk=Nk)
+    args = (causal, sm_scale, _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.ptr,
+            workspace.nbytes, _stream_handle(q.device), qk_bits, smooth_v)
+    if Hk == H and Nk == N:
+        attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, D, *args)
+    else:
+        attn_fwd_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, N, Nk, D, *args)
     return out
 
 

@@ -177,6 +177,45 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
                                 float sm_scale, int qk_bits, sage_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Separate query and key/value geometry: cross-attention, decoding or chunked
+ * prefill against a key/value cache (Nq != Nk), and grouped-query / multi-
+ * query heads (Hq = g * Hkv).  The pages define the method for one attention
+ * call; these calls apply it unchanged to
+ *  q, o     [B, Hq, Nq, D]     k, v   [B, Hkv, Nk, D]
+ * with Hq a multiple of Hkv: query head h attends K/V head h / (Hq / Hkv).
+ * Smoothing statistics follow the tensors they describe: Q block means over
+ * the query tokens of each query head; the K mean, K scale groups, V scales
+ * and V mean over the Nk tokens of each K/V head; DeltaS per (query block,
+ * key).  Causal: the mask is aligned at the bottom-right corner, query i
+ * attends key j iff j <= i + (Nk - Nq) (the last query sees every key), and
+ * causal calls require Nq <= Nk (SAGE_ERR_INVALID otherwise).
+ * The buffers of sage_quant_bufs take the query-side shapes with (Hq, Nq):
+ * q_codes, q_scale, q_mean, and delta_s [B,Hq,NQB,NPk]; the key/value-side
+ * ones with (Hkv, Nk): k_codes, k_scale, k_mean, v_codes, v_scale, v_mean
+ * (NPk = Nk rounded up to 128).  Size the workspace with
+ * sage_workspace_bytes_cross.  With Hq = Hkv = H and Nq = Nk = N every call
+ * below is the self-attention call above (the same layout and results).
+ * Limits: B*Hq <= 65535, Nq and Nk rounded up to 128 at most 2^24.
+ */
+size_t sage_workspace_bytes_cross(int B, int Hq, int Hkv, int Nq, int Nk, int D);
+
+sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, int Hq, int Hkv, int Nq, int Nk,
+                                                 int D, sage_quant_bufs* out);
+
+sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
+                                    int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
+                                    const sage_quant_bufs* out, hipStream_t stream);
+
+sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
+                                int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v,
+                                sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B, int Hq, int Hkv, int Nq, int Nk,
+                                      int D, int causal, float sm_scale, int qk_bits, sage_dtype out_dtype,
+                                      hipStream_t stream);
+
+/*
  * Packed variable-length batches (the varlen form of the drop-in call; the
  * code record of the SageAttention2 paper names `sageattn_varlen`).  nseq
  * independent self-attention problems share one launch:

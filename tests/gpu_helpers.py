@@ -113,14 +113,16 @@ def unpermute_v(vcodes: np.ndarray, BH: int, NQB: int, D: int, N: int) -> np.nda
 
 
 class Readback:
-    """The prepass arrays of a workspace, copied to host in canonical form."""
+    """The prepass arrays of a workspace, copied to host in canonical form.
+    Query-side arrays use (H, N), key/value-side arrays (Hkv, Nk)."""
 
     def __init__(self, ws: sage.Workspace, qk_bits: int = 4, strict: bool = True):
         torch = torch_mod()
         B, H, N, D = ws.B, ws.H, ws.N, ws.D
-        BH = B * H
-        NP = (N + 127) // 128 * 128
-        NQB = NP // 128
+        Hk, Nk = ws.Hkv or H, ws.Nk or N
+        BH, BHk = B * H, B * Hk
+        NP, NPk = (N + 127) // 128 * 128, (Nk + 127) // 128 * 128
+        NQB, NQBk = NP // 128, NPk // 128
         qb = ws.bufs()
         host = ws.tensor.cpu().numpy()
         base = ws.tensor.data_ptr()
@@ -130,38 +132,47 @@ class Readback:
             return host[off:off + nbytes].view(dtype).reshape(shape)
 
         self.N, self.NP, self.NQB, self.D, self.BH = N, NP, NQB, D, BH
+        self.Nk, self.NPk, self.NQBk, self.BHk = Nk, NPk, NQBk, BHk
         self.qk_bits = qk_bits
         rowb = fp6_row_bytes(D) if qk_bits == 4 else D
         self.q_codes_raw = arr(qb.q_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
-        self.k_codes_raw = arr(qb.k_codes, BH * NP * rowb, np.uint8, (BH, NP * rowb))
+        self.k_codes_raw = arr(qb.k_codes, BHk * NPk * rowb, np.uint8, (BHk, NPk * rowb))
         self.q_codes_all = unpack_codes(self.q_codes_raw, NP, D, qk_bits, strict)   # padded rows included
-        self.k_codes_all = unpack_codes(self.k_codes_raw, NP, D, qk_bits, strict)
+        self.k_codes_all = unpack_codes(self.k_codes_raw, NPk, D, qk_bits, strict)
         self.q_codes = self.q_codes_all[:, :N]
-        self.k_codes = self.k_codes_all[:, :N]
+        self.k_codes = self.k_codes_all[:, :Nk]
         self.q_scale_p = arr(qb.q_scale, BH * NP * 4, np.float32, (BH, NP))
-        self.k_scale_p = arr(qb.k_scale, BH * NP // 16 * 4, np.float32, (BH, NP // 16))
+        self.k_scale_p = arr(qb.k_scale, BHk * NPk // 16 * 4, np.float32, (BHk, NPk // 16))
         self.q_mean = arr(qb.q_mean, BH * NQB * D * 4, np.float32, (BH, NQB, D))
-        self.k_mean = arr(qb.k_mean, BH * D * 4, np.float32, (BH, D))
-        self.v_codes_raw = arr(qb.v_codes, BH * NP * D, np.uint8, (BH, NQB, D, 128))
-        self.v_codes = unpermute_v(self.v_codes_raw, BH, NQB, D, N)
-        self.v_scale = arr(qb.v_scale, BH * D * 4, np.float32, (BH, D))
-        self.v_mean = arr(qb.v_mean, BH * D * 4, np.float32, (BH, D))
-        self.delta_s_p = arr(qb.delta_s, BH * NQB * NP * 4, np.float32, (BH, NQB, NP))
-        G = 2 * ((N + 31) // 32)
+        self.k_mean = arr(qb.k_mean, BHk * D * 4, np.float32, (BHk, D))
+        self.v_codes_raw = arr(qb.v_codes, BHk * NPk * D, np.uint8, (BHk, NQBk, D, 128))
+        self.v_codes = unpermute_v(self.v_codes_raw, BHk, NQBk, D, Nk)
+        self.v_scale = arr(qb.v_scale, BHk * D * 4, np.float32, (BHk, D))
+        self.v_mean = arr(qb.v_mean, BHk * D * 4, np.float32, (BHk, D))
+        self.delta_s_p = arr(qb.delta_s, BH * NQB * NPk * 4, np.float32, (BH, NQB, NPk))
+        G = 2 * ((Nk + 31) // 32)
         self.q_scale = self.q_scale_p[:, :N]
         self.k_scale = self.k_scale_p[:, :G]
-        self.delta_s = self.delta_s_p[:, :, :N]
+        self.delta_s = self.delta_s_p[:, :, :Nk]
         torch.cuda.synchronize()
 
 
 def run_quant_smooth(q_bits, k_bits, v_bits, dtype: str, qk_bits: int = 4, smooth_v: bool = False):
+    """Prepass into a poisoned workspace: the self-attention entry point when
+    Q and K/V share heads and length, the cross-geometry one otherwise."""
     torch = torch_mod()
     B, H, N, D = q_bits.shape
+    Hk, Nk = k_bits.shape[1], k_bits.shape[2]
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
-    ws = sage.alloc_workspace(B, H, N, D)
+    ws = sage.alloc_workspace(B, H, N, D, Hkv=Hk, Nk=Nk)
     ws.tensor.fill_(0xA5)  # poison: every array element the prepass owns must be written
-    sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code(dtype), B, H, N, D, ws.bufs(),
-                      torch.cuda.current_stream().cuda_stream, qk_bits=qk_bits, smooth_v=smooth_v)
+    sh = torch.cuda.current_stream().cuda_stream
+    if Hk == H and Nk == N:
+        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code(dtype), B, H, N, D, ws.bufs(), sh,
+                          qk_bits=qk_bits, smooth_v=smooth_v)
+    else:
+        sage.quant_smooth_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code(dtype), B, H, Hk, N, Nk, D,
+                                ws.bufs(), sh, qk_bits=qk_bits, smooth_v=smooth_v)
     torch.cuda.synchronize()
     return ws
 
@@ -170,8 +181,9 @@ def run_attn(q_bits, k_bits, v_bits, dtype: str, causal: bool, sm_scale: float, 
              smooth_v: bool = False):
     torch = torch_mod()
     B, H, N, D = q_bits.shape
+    Hk, Nk = k_bits.shape[1], k_bits.shape[2]
     q, k, v = (to_device(a, dtype) for a in (q_bits, k_bits, v_bits))
-    ws = sage.alloc_workspace(B, H, N, D)
+    ws = sage.alloc_workspace(B, H, N, D, Hkv=Hk, Nk=Nk)
     out = sage.attn(q, k, v, causal=causal, sm_scale=sm_scale, out_dtype=out_dtype or torch.float32, workspace=ws,
                     qk_bits=qk_bits, smooth_v=smooth_v)
     torch.cuda.synchronize()

@@ -179,3 +179,67 @@ def test_varlen_validation():
         args = list(base)
         args[i] = bad
         assert fwd(*args) == expect, (i, bad)
+
+
+def _sizes_cross(B, Hq, Hk, Nq, Nk, D):
+    NPq, NPk = (Nq + 127) // 128 * 128, (Nk + 127) // 128 * 128
+    NQB, NKB = NPq // 128, NPk // 128
+    BHq, BHk = B * Hq, B * Hk
+    part = BHk * NKB * 2 * D * 4
+    return [BHq * NPq * D, BHk * NPk * D, BHq * NPq * 4, BHk * NPk // 16 * 4, BHq * NQB * D * 4, BHk * D * 4,
+            BHk * NPk * D, BHk * D * 4, BHq * NQB * NPk * 4, max(part, BHq * NQB * 2 * D * 2),
+            max(part, BHq * NQB * D * 2), BHk * D * 4]
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 1, 8192, 128), (16, 32, 8, 1, 4096, 128), (2, 6, 3, 1000, 77, 64),
+                                   (1, 2, 2, 300, 300, 64)])
+def test_workspace_carving_cross(shape):
+    nbytes = sage.workspace_bytes_cross(*shape)
+    sizes = _sizes_cross(*shape)
+    assert nbytes >= sum(sizes)
+    base = 1 << 40
+    qb = sage.quant_bufs_from_workspace_cross(base, nbytes, *shape)
+    ptrs = [getattr(qb, f) for f, _ in sage.QuantBufs._fields_]
+    for p, s in zip(ptrs, sizes):
+        assert p % 256 == 0 and base <= p and p + s <= base + nbytes
+    spans = sorted(zip(ptrs, sizes))
+    for (p0, s0), (p1, _) in zip(spans, spans[1:]):
+        assert p0 + s0 <= p1
+    B, Hq, Hk, Nq, Nk, D = shape
+    if Hq == Hk and Nq == Nk:   # self-attention: the dense layout, byte for byte
+        assert nbytes == sage.workspace_bytes(B, Hq, Nq, D)
+        dense = sage.quant_bufs_from_workspace(base, nbytes, B, Hq, Nq, D)
+        assert [getattr(dense, f) for f, _ in sage.QuantBufs._fields_] == ptrs
+
+
+def test_cross_validation():
+    L = sage.lib()
+    ws = sage.workspace_bytes_cross
+    assert ws(1, 4, 3, 10, 10, 64) == 0          # Hq not a multiple of Hkv
+    assert ws(1, 4, 0, 10, 10, 64) == 0
+    assert ws(1, 4, 2, 10, 0, 64) == 0
+    assert ws(1, 4, 2, 0, 10, 64) == 0
+    assert ws(1, 4, 2, 10, 1 << 25, 64) == 0
+    assert ws(1, 4, 2, 10, 10, 96) == 0
+    assert ws(1, 4, 2, 1, 10, 64) > 0
+    qb = sage.QuantBufs(*([FAKE] * 12))
+    qs = L.sage_quant_smooth_cross
+    ok = (FAKE, FAKE, FAKE, sage.BF16, 1, 4, 2, 1, 300, 64, 4, 0, ctypes.byref(qb), None)
+    for i, bad in [(0, None), (3, sage.F32), (5, 3), (6, 3), (7, 0), (8, 0), (9, 96), (10, 5), (11, 2)]:
+        args = list(ok)
+        args[i] = bad
+        assert qs(*args) == sage.ERR_INVALID, (i, bad)
+    fwd = L.sage_attn_fwd_cross
+    wsb = ws(1, 4, 2, 100, 300, 64)
+    base = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), 1, 4, 2, 100, 300, 64, 1, 0.125, 4, 0,
+            sage.BF16, sage.F32, FAKE + (4 << 30), wsb, None]
+    for i, bad, expect in [(7, 301, sage.ERR_INVALID),       # causal with more queries than keys
+                           (5, 5, sage.ERR_INVALID), (11, 0.0, sage.ERR_INVALID), (17, 100, sage.ERR_WORKSPACE),
+                           (3, FAKE + 16, sage.ERR_INVALID), (12, 3, sage.ERR_INVALID), (13, 2, sage.ERR_INVALID)]:
+        args = list(base)
+        args[i] = bad
+        assert fwd(*args) == expect, (i, bad)
+    aq = L.sage_attn_quantized_cross
+    assert aq(ctypes.byref(qb), FAKE, 1, 4, 2, 301, 300, 64, 1, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
+    assert aq(ctypes.byref(qb), FAKE, 1, 4, 3, 10, 300, 64, 0, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
+    assert aq(None, FAKE, 1, 4, 2, 10, 300, 64, 0, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
