@@ -126,21 +126,34 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     torch.cuda.set_device(0)
     tdt = torch.float16 if w.dtype == wl.F16 else torch.bfloat16
     q, k, v = (torch.from_numpy(a.view(np.int16)).view(tdt).cuda() for a in wl.generate(w))
-    B, H, N, D = w.B, w.H, w.N, w.D
-    ws = sage.alloc_workspace(B, H, N, D)
+    B, H, N, D, Hk, Nk = w.B, w.H, w.N, w.D, w.hkv, w.nk
+    ws = sage.alloc_workspace(B, H, N, D, Hkv=Hk, Nk=Nk)
     bufs = ws.bufs()
     out = torch.empty((B, H, N, D), dtype=tdt, device="cuda")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     in_code = sage.F16 if tdt == torch.float16 else sage.BF16
 
-    def step():
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits,
-                          smooth_v=smooth_v)
-        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
+    # self-attention through the dense entry points, other geometries through
+    # the cross-geometry ones (the dense calls are the Hkv = H, Nk = N case)
+    def pre():
+        if w.self_attention:
+            sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh,
+                              qk_bits=qk_bits, smooth_v=smooth_v)
+        else:
+            sage.quant_smooth_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D, bufs, sh,
+                                    qk_bits=qk_bits, smooth_v=smooth_v)
+
+    def fused():
+        if w.self_attention:
+            sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
+        else:
+            sage.attn_quantized_cross(bufs, out.data_ptr(), B, H, Hk, N, Nk, D, w.causal, w.scale, in_code, sh,
+                                      qk_bits=qk_bits)
 
     for _ in range(warmup):
-        step()
+        pre()
+        fused()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -148,10 +161,9 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     start.record(stream)
     for i in range(steps):
         ev[i][0].record(stream)
-        sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh, qk_bits=qk_bits,
-                          smooth_v=smooth_v)
+        pre()
         ev[i][1].record(stream)
-        sage.attn_quantized(bufs, out.data_ptr(), B, H, N, D, w.causal, w.scale, in_code, sh, qk_bits=qk_bits)
+        fused()
         ev[i][2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -178,6 +190,10 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
                    "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale, "qk_bits": qk_bits,
                    "smooth_v": smooth_v},
+    }
+    if not w.self_attention:
+        rec["config"].update({"Hkv": Hk, "Nk": Nk, "ops": "4*B*H*N*Nk*D (causal: minus 2*B*H*N^2*D)"})
+    rec.update({
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tops, 1),
@@ -191,8 +207,8 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
         "breakdown": {"prepass_us": round(pre_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                       "e2e_frac_of_peak": round(value / PEAK_TOPS, 4)},
         "context": "pages: ~3x FlashAttention2 and ~4.5x xformers OPS on RTX4090; ~FlashAttention3(fp8) speed on Hopper",
-    }
-    if cpu:
+    })
+    if cpu and w.self_attention:
         o_host = out.float().cpu().numpy().reshape(B * H, N, D)[0]
         rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds, qk_bits, smooth_v)
     return rec

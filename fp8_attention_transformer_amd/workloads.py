@@ -93,7 +93,19 @@ def long_context(N: int, causal: bool) -> Workload:
 
 
 LONG = [long_context(n, c) for n in (8192, 16384, 32768) for c in (False, True)]
-ALL = [TINY, LLM, DIT, VIDEO] + LONG
+
+# Language-model inference against a key/value cache with grouped-query heads
+# (32 query heads sharing 8 K/V heads): one decoding step (one new token per
+# sequence) and one 512-token chunk of a chunked prefill (causal, aligned at
+# the last key); value structure of the LLM prefill family.
+DECODE = Workload("llm_decode_b16hq32hkv8_nk8192d128", 16, 32, 1, 128, BF16, False, seed=6, k_offset_std=4.0,
+                  outlier_channels=4, outlier_scale=20.0, Hkv=8, Nk=8192,
+                  note="decoding step: 1 query per sequence, 8192 cached keys, 4 query heads per K/V head")
+CHUNK = Workload("llm_chunk_b1hq32hkv8_nq512nk8192d128_causal", 1, 32, 512, 128, BF16, True, seed=7,
+                 k_offset_std=4.0, outlier_channels=4, outlier_scale=20.0, Hkv=8, Nk=8192,
+                 note="chunked prefill: the last 512 tokens of an 8192-token context")
+CROSS = [DECODE, CHUNK]
+ALL = [TINY, LLM, DIT, VIDEO] + LONG + CROSS
 BY_NAME = {w.name: w for w in ALL}
 # The configuration the headline throughput is quoted on: N = 16k, D = 128.
 HEADLINE = long_context(16384, False)

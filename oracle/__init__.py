@@ -86,7 +86,7 @@ def lib():
         L.oracle_quant_smooth.restype = i32
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
         L.oracle_qk_int32.restype = i32
-        L.oracle_attn_mirror.argtypes = [P] * 8 + [i32] * 7 + [f32, i32, P, i64, f32, P, P, P, i32]
+        L.oracle_attn_mirror.argtypes = [P] * 8 + [i32] * 7 + [f32, i32, i32, P, i64, f32, P, P, P, i32]
         L.oracle_attn_mirror.restype = i32
         L.oracle_attn_exact.argtypes = [P, P, P, i32] + [P] * 8 + [i32] * 7 + [f64, i32, P, i64, P, P, i32]
         L.oracle_attn_exact.restype = i32
@@ -182,9 +182,11 @@ def qk_int32(q_codes_head, k_codes_head, q0, k0, nq, nk) -> np.ndarray:
 
 
 def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bool = True,
-                eps: float = 0.0, nthreads: int = 0):
+                eps: float = 0.0, nthreads: int = 0, kv_split: int = 0):
     """Returns (O [nrows, D] fp32, slack [nrows] fp32, lse [nrows, 2] fp32).
-    rows index the flattened [B, Hq, Nq] query grid."""
+    rows index the flattened [B, Hq, Nq] query grid.  kv_split > 0 (a multiple
+    of 128): keys in ranges of kv_split, each with its own online softmax,
+    merged at the end (the split-key schedule)."""
     B, H, N, D = qz.q_codes.shape
     Hk, Nk = qz.k_codes.shape[1], qz.k_codes.shape[2]
     if rows is None:
@@ -199,7 +201,8 @@ def attn_mirror(qz: Quant, causal: bool, sm_scale: float, rows=None, quant_p: bo
     rc = lib().oracle_attn_mirror(_ptr(qz.q_codes), _ptr(qz.q_scale), _ptr(qz.k_codes), _ptr(qz.k_scale),
                                   _ptr(qz.v_codes), _ptr(qz.v_scale), _ptr(qz.v_mean), _ptr(qz.delta_s),
                                   B, H, Hk, N, Nk, D, int(causal), float(sm_scale),
-                                  MIRROR_QUANT_P if quant_p else 0, _ptr(rows_arr), nrows, float(eps),
+                                  MIRROR_QUANT_P if quant_p else 0, int(kv_split), _ptr(rows_arr), nrows,
+                                  float(eps),
                                   _ptr(O), _ptr(slack), _ptr(lse), _threads(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_mirror rejected its arguments")

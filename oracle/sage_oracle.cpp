@@ -322,18 +322,31 @@ enum { MIRROR_QUANT_P = 1 };
 // of an FP8 rounding midpoint were rounded the other way (used to tolerate exp2
 // implementation differences).  Optional lse[r] = (final running max m, final
 // l') for diagnostics.
+//
+// kv_split (0: none): keys are cut into consecutive ranges of kv_split keys (a
+// multiple of the 128-key block).  Each range runs the online softmax of the
+// method on its own, from an empty state (its own running max, so its P~
+// values are scaled to its own maximum before the FP8 rounding); the ranges
+// are then merged in order with fp32 weights w_s = exp2(m_s - M), M the
+// largest range maximum:  O = fma(w_s, O_s, O), l' = fma(w_s, l'_s, l').
+// Ranges holding no visible key are skipped.  One range is the plain
+// schedule, bit for bit.  (The pages fix the block-wise online softmax and
+// the per-block FP8 P~ but not the order in which key blocks are visited;
+// this is the schedule a split-key kernel uses.)
 int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes, const float* k_scale,
                        const uint8_t* v_codes, const float* v_scale, const float* v_mean, const float* delta_s,
                        int B, int Hq, int Hkv, int Nq, int Nk, int D, int causal, float sm_scale, int flags,
-                       const int64_t* rows, int64_t nrows, float eps,
+                       int kv_split, const int64_t* rows, int64_t nrows, float eps,
                        float* O, float* slack, float* lse, int nthreads) {
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !delta_s || !O) return -1;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1 || !(sm_scale > 0.0f)) return -1;
   if (causal && Nq > Nk) return -1;
+  if (kv_split < 0 || kv_split % BK) return -1;
   const int64_t NQB = (Nq + BQ_MEAN - 1) / BQ_MEAN;
   const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
   const int group = Hq / Hkv;
   const float ks = sm_scale * LOG2E;
+  const int64_t span = kv_split ? kv_split : Nk;
   const int64_t total = rows ? nrows : (int64_t)B * Hq * Nq;
   parallel_for(total, nthreads, [&](int64_t r) {
     const int64_t flat = rows ? rows[r] : r;
@@ -345,65 +358,87 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
     const float* ds = delta_s + (bhq * NQB + i / BQ_MEAN) * Nk;
     const float* dvec = v_scale + bhk * D;
     const float dq = q_scale[flat];
-    std::vector<float> Orun(D, 0.0f), R(D), s2(BK), p(BK);
-    float m = -std::numeric_limits<float>::infinity();
-    float l = 0.0f, slk = 0.0f;
     const int64_t jend = causal ? i + 1 + (Nk - Nq) : Nk;  // keys j < jend are allowed
-    for (int64_t t0 = 0; t0 < jend; t0 += BK) {
-      const int64_t t1 = std::min<int64_t>(t0 + BK, Nk);
-      // scores in the log2 domain
-      float bmax = -std::numeric_limits<float>::infinity();
-      for (int64_t j = t0; j < t1; j++) {
-        float& s = s2[j - t0];
-        if (j >= jend) { s = -std::numeric_limits<float>::infinity(); continue; }
-        int32_t acc = 0;
-        for (int c = 0; c < D; c++) acc += (int32_t)qi[c] * (int32_t)kh[j * D + c];
-        float cfac = (dq * k_scale[bhk * G + k_group(j)]) * ks;
-        float d = ds[j] * ks;
-        s = std::fma((float)acc, cfac, d);
-        bmax = std::max(bmax, s);
-      }
-      const float mnew = std::max(m, bmax);
-      const float alpha = std::exp2(m - mnew);
-      const float mm = mnew - LOG2_448;
-      float rowsum = 0.0f;
-      for (int64_t j = t0; j < t1; j++) {
-        float pj = (j < jend) ? std::exp2(s2[j - t0] - mm) : 0.0f;
-        p[j - t0] = pj;
-        rowsum = rowsum + pj;
-      }
-      // P~ -> FP8 and the level-1 partial R_t in a fresh fp32 buffer
-      std::fill(R.begin(), R.end(), 0.0f);
-      float blk_slack = 0.0f;
-      for (int64_t j = t0; j < t1; j++) {
-        float pj = p[j - t0];
-        float pq = (flags & MIRROR_QUANT_P) ? e4m3_decode(e4m3_encode(pj)) : pj;
-        if (pq == 0.0f && pj == 0.0f) continue;
-        for (int c = 0; c < D; c++) R[c] = R[c] + pq * e4m3_decode(vh[j * D + c]);
-        if ((flags & MIRROR_QUANT_P) && eps > 0.0f && pj > 0.0f) {
-          // Is a rounding midpoint of the FP8 grid within relative eps of pj?
-          float lo = pj * (1.0f - eps), hi = pj * (1.0f + eps);
-          uint8_t clo = e4m3_encode(lo), chi = e4m3_encode(hi);
-          if (clo != chi) {
-            float step = std::fabs(e4m3_decode(chi) - e4m3_decode(clo));
-            float vm = 0.0f;
-            for (int c = 0; c < D; c++) vm = std::max(vm, std::fabs(e4m3_decode(vh[j * D + c]) * dvec[c]));
-            blk_slack += step * vm;
+    // per-range states, merged below
+    std::vector<std::vector<float>> Os;
+    std::vector<float> ms, ls, slks;
+    std::vector<float> R(D), s2(BK), p(BK);
+    for (int64_t r0 = 0; r0 < jend; r0 += span) {
+      const int64_t r1 = std::min<int64_t>(r0 + span, Nk);
+      std::vector<float> Orun(D, 0.0f);
+      float m = -std::numeric_limits<float>::infinity();
+      float l = 0.0f, slk = 0.0f;
+      for (int64_t t0 = r0; t0 < std::min(r1, jend); t0 += BK) {
+        const int64_t t1 = std::min<int64_t>(t0 + BK, r1);
+        // scores in the log2 domain
+        float bmax = -std::numeric_limits<float>::infinity();
+        for (int64_t j = t0; j < t1; j++) {
+          float& s = s2[j - t0];
+          if (j >= jend) { s = -std::numeric_limits<float>::infinity(); continue; }
+          int32_t acc = 0;
+          for (int c = 0; c < D; c++) acc += (int32_t)qi[c] * (int32_t)kh[j * D + c];
+          float cfac = (dq * k_scale[bhk * G + k_group(j)]) * ks;
+          float d = ds[j] * ks;
+          s = std::fma((float)acc, cfac, d);
+          bmax = std::max(bmax, s);
+        }
+        const float mnew = std::max(m, bmax);
+        const float alpha = std::exp2(m - mnew);
+        const float mm = mnew - LOG2_448;
+        float rowsum = 0.0f;
+        for (int64_t j = t0; j < t1; j++) {
+          float pj = (j < jend) ? std::exp2(s2[j - t0] - mm) : 0.0f;
+          p[j - t0] = pj;
+          rowsum = rowsum + pj;
+        }
+        // P~ -> FP8 and the level-1 partial R_t in a fresh fp32 buffer
+        std::fill(R.begin(), R.end(), 0.0f);
+        float blk_slack = 0.0f;
+        for (int64_t j = t0; j < t1; j++) {
+          float pj = p[j - t0];
+          float pq = (flags & MIRROR_QUANT_P) ? e4m3_decode(e4m3_encode(pj)) : pj;
+          if (pq == 0.0f && pj == 0.0f) continue;
+          for (int c = 0; c < D; c++) R[c] = R[c] + pq * e4m3_decode(vh[j * D + c]);
+          if ((flags & MIRROR_QUANT_P) && eps > 0.0f && pj > 0.0f) {
+            // Is a rounding midpoint of the FP8 grid within relative eps of pj?
+            float lo = pj * (1.0f - eps), hi = pj * (1.0f + eps);
+            uint8_t clo = e4m3_encode(lo), chi = e4m3_encode(hi);
+            if (clo != chi) {
+              float step = std::fabs(e4m3_decode(chi) - e4m3_decode(clo));
+              float vm = 0.0f;
+              for (int c = 0; c < D; c++) vm = std::max(vm, std::fabs(e4m3_decode(vh[j * D + c]) * dvec[c]));
+              blk_slack += step * vm;
+            }
           }
         }
+        // level 2: fold the block into the fp32 running buffer
+        for (int c = 0; c < D; c++) Orun[c] = std::fma(alpha, Orun[c], R[c]);
+        l = alpha * l + rowsum;
+        slk = alpha * slk + blk_slack;
+        m = mnew;
       }
-      // level 2: fold the block into the fp32 running buffer
-      for (int c = 0; c < D; c++) Orun[c] = std::fma(alpha, Orun[c], R[c]);
-      l = alpha * l + rowsum;
-      slk = alpha * slk + blk_slack;
-      m = mnew;
+      Os.push_back(Orun);
+      ms.push_back(m);
+      ls.push_back(l);
+      slks.push_back(slk);
+    }
+    // merge the ranges (a single range passes through unchanged: w = 1)
+    float M = -std::numeric_limits<float>::infinity();
+    for (float m : ms) M = std::max(M, m);
+    std::vector<float> Ofin(D, 0.0f);
+    float l = 0.0f, slk = 0.0f;
+    for (size_t sidx = 0; sidx < ms.size(); sidx++) {
+      const float w = std::exp2(ms[sidx] - M);
+      for (int c = 0; c < D; c++) Ofin[c] = std::fma(w, Os[sidx][c], Ofin[c]);
+      l = std::fma(w, ls[sidx], l);
+      slk = std::fma(w, slks[sidx], slk);
     }
     for (int c = 0; c < D; c++) {
-      O[r * D + c] = (Orun[c] * dvec[c]) / l;
+      O[r * D + c] = (Ofin[c] * dvec[c]) / l;
       if (v_mean) O[r * D + c] = O[r * D + c] + v_mean[bhk * D + c];
     }
     if (slack) slack[r] = slk / l;
-    if (lse) { lse[2 * r] = m; lse[2 * r + 1] = l; }
+    if (lse) { lse[2 * r] = M; lse[2 * r + 1] = l; }
   });
   return 0;
 }

@@ -162,3 +162,33 @@ def test_decode_query_is_its_own_block_mean(oracle_lib, qk_bits):
     Oe, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, 0)
     V = oracle_lib.decode_input(v, 1)
     assert np.abs(Oq - Oe).max() <= 1e-5 * np.abs(V).max()
+
+
+@pytest.mark.parametrize("split", [128, 256, 640])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_key_schedule(oracle_lib, split, causal):
+    """Key ranges with their own online softmax, merged with weights
+    exp2(m_s - M): without P~ quantization every schedule is the direct
+    softmax (so a wrong merge weight or a missing rescale fails); one range
+    covering all keys is the plain schedule bit for bit."""
+    B, Hq, Hk, Nq, Nk, D = 1, 4, 2, 130, 1000, 128
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, seed=split + causal, k_offset_std=4.0, outlier_channels=2,
+                  outlier_scale=10.0)
+    q, k, v = wl.generate(w)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, smooth_v=True)
+    flags = (oracle_lib.EXACT_SMOOTH_K | oracle_lib.EXACT_SMOOTH_Q | oracle_lib.EXACT_QUANT_QK
+             | oracle_lib.EXACT_QUANT_V)
+    Oe, _ = oracle_lib.attn_exact(q, k, v, 1, causal, w.scale, flags, qz=z)
+    Os, _, _ = oracle_lib.attn_mirror(z, causal, w.scale, quant_p=False, kv_split=split)
+    vmax = np.abs(oracle_lib.e4m3_decode(z.v_codes) * z.v_scale[:, :, None, :]).max() + np.abs(z.v_mean).max()
+    assert np.abs(Os - Oe).max() <= 1e-5 * vmax
+    # with FP8 P~ the schedule changes the rounding only: close to the plain schedule
+    Op, sp, _ = oracle_lib.attn_mirror(z, causal, w.scale, eps=2.0 ** -16)
+    Oq, sq, _ = oracle_lib.attn_mirror(z, causal, w.scale, eps=2.0 ** -16, kv_split=split)
+    assert 0 < np.abs(Oq - Op).max() < 0.05 * vmax
+    big = (Nk + 127) // 128 * 128
+    Ob, sb, lb = oracle_lib.attn_mirror(z, causal, w.scale, eps=2.0 ** -16, kv_split=big)
+    _, _, lp = oracle_lib.attn_mirror(z, causal, w.scale, eps=2.0 ** -16)
+    assert np.array_equal(Ob, Op) and np.array_equal(sb, sp) and np.array_equal(lb, lp)
+    with pytest.raises(ValueError):
+        oracle_lib.attn_mirror(z, causal, w.scale, kv_split=100)
