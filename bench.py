@@ -214,6 +214,62 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     return rec
 
 
+def run_decode(w, steps: int, warmup: int, smooth_v: bool = False):
+    """A decoding step (one query token per head, Nq = 1) through sage_attn_decode:
+    K/V statistics, split-key attention, merge.  Memory-bound: the roofline is
+    HBM bandwidth over the step's algorithmic bytes, the 16-bit K and V read
+    twice (the statistics must see every key before any key is quantized) plus
+    q read and o written."""
+    import numpy as np
+    import torch
+
+    from fp8_attention_transformer_amd import sage
+    from fp8_attention_transformer_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    tdt = torch.float16 if w.dtype == wl.F16 else torch.bfloat16
+    q, k, v = (torch.from_numpy(a.view(np.int16)).view(tdt).cuda() for a in wl.generate(w))
+    B, H, D, Hk, Nk = w.B, w.H, w.D, w.hkv, w.nk
+    split = sage.decode_split_keys(B, H, Hk, Nk, D)
+    ws = torch.empty(sage.decode_workspace_bytes(B, H, Hk, Nk, D, split), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H, 1, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    in_code = sage.F16 if tdt == torch.float16 else sage.BF16
+
+    def step():
+        sage.attn_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, Nk, D, w.scale,
+                             in_code, in_code, ws.data_ptr(), ws.numel(), sh, smooth_v, split)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    kv_bytes = 2 * B * Hk * Nk * D * 2
+    alg_bytes = 2 * kv_bytes + 2 * B * H * D * 2
+    gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    value = w.ops / (ms_per_step * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 scores+fp8", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hk, "N": 1, "Nk": Nk, "D": D, "in_dtype": w.dtype,
+                   "out_dtype": w.dtype, "smooth_v": smooth_v, "split_keys": split, "entry": "sage_attn_decode",
+                   "ops": "4*B*H*Nk*D"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "decode step (stats, attention, merge)",
+                     "kernel_us": round(ms_per_step * 1e3, 2),
+                     "algorithmic_bytes": alg_bytes},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+    }
+
+
 def run_packed(pw, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = False):
     """A packed variable-length batch through the varlen entry points (prepass,
     then the fused kernel), timed like the dense workloads."""
@@ -325,6 +381,8 @@ def main():
     for w in todo:
         if isinstance(w, wl.PackedWorkload):
             rec = run_packed(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
+        elif w.N == 1 and not w.self_attention:
+            rec = run_decode(w, args.steps, args.warmup, args.smooth_v)
         else:
             rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits,
                       args.smooth_v)

@@ -156,6 +156,54 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// ---------------------------------------------------------------- decoding --
+// Workspace of a decoding step: K/V statistics (k_part, v_part, k_mean,
+// v_scale, v_mean) and the per-range partial outputs.
+constexpr int kDecodeArrays = 7;
+
+bool split_ok(int split_keys) { return split_keys >= 0 && split_keys % 128 == 0; }
+
+// The decoding kernel addresses one head's keys with 31-bit byte offsets.
+bool decode_shape_ok(int B, int Hq, int Hkv, int Nk, int D) {
+  return shape_ok(B, Hq, Hkv, 1, Nk, D) && (long long)Nk * D * 2 < (1LL << 31);
+}
+
+int default_split_keys(const Dims& d) {
+  const int g = d.H / d.Hk, hg = sage::decode_heads_per_group(g);
+  const long long wgy = (long long)d.BHk() * ((g + hg - 1) / hg);
+  // about 1024 workgroups (four rounds of one 8-wave workgroup per compute
+  // unit), at least one block per range
+  long long S = (1024 + wgy - 1) / wgy;
+  if (S > d.NQBk) S = d.NQBk;
+  if (S < 1) S = 1;
+  return 128 * (int)((d.NQBk + S - 1) / S);
+}
+
+bool decode_layout(const Dims& d, int split_keys, size_t sizes[kDecodeArrays]) {
+  const size_t D = (size_t)d.D, bhk = (size_t)d.BHk(), bhq = (size_t)d.BH();
+  const size_t S = ((size_t)d.Nk + split_keys - 1) / split_keys;
+  size_t t;
+  if (!mul_ok(bhk * (size_t)d.NQBk, 2 * D * 4, &sizes[0])) return false;   // k_part
+  sizes[1] = sizes[0];                                                     // v_part
+  sizes[2] = sizes[3] = sizes[4] = bhk * D * 4;                            // k_mean, v_scale, v_mean
+  if (!mul_ok(bhq * S, D * 4, &sizes[5])) return false;                    // part_o
+  if (!mul_ok(bhq * S, 8, &t)) return false;                               // part_ml
+  sizes[6] = t;
+  return true;
+}
+
+size_t decode_total(const Dims& d, int split_keys) {
+  size_t s[kDecodeArrays];
+  if (!decode_layout(d, split_keys, s)) return 0;
+  size_t tot = 0;
+  for (int i = 0; i < kDecodeArrays; i++) {
+    const size_t a = align_up(s[i]);
+    if (a < s[i] || tot + a < tot) return 0;
+    tot += a;
+  }
+  return tot;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +300,64 @@ sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B,
   if (dc != SAGE_OK) return dc;
   const float ks = sm_scale * 1.44269504088896340736f;
   const hipError_t e = sage::launch_attn(to_internal(*qb), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_decode_split_keys(int B, int Hq, int Hkv, int Nk, int D) {
+  if (!decode_shape_ok(B, Hq, Hkv, Nk, D)) return 0;
+  return default_split_keys(make_dims(B, Hq, Hkv, 1, Nk, D));
+}
+
+size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nk, int D, int split_keys) {
+  if (!decode_shape_ok(B, Hq, Hkv, Nk, D) || !split_ok(split_keys)) return 0;
+  const Dims d = make_dims(B, Hq, Hkv, 1, Nk, D);
+  return decode_total(d, split_keys ? split_keys : default_split_keys(d));
+}
+
+sage_status sage_attn_decode(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nk,
+                             int D, float sm_scale, int smooth_v, int split_keys, sage_dtype in_dtype,
+                             sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !decode_shape_ok(B, Hq, Hkv, Nk, D) || !split_ok(split_keys))
+    return SAGE_ERR_INVALID;
+  if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, Hq, Hkv, 1, Nk, D, 4, smooth_v);
+  const int sk = split_keys ? split_keys : default_split_keys(d);
+  const size_t need = decode_total(d, sk);
+  if (need == 0) return SAGE_ERR_INVALID;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  size_t qel, kel, obytes, qbytes, kbytes;
+  if (!mul_ok((size_t)B * Hq, (size_t)D, &qel) || !mul_ok((size_t)B * Hkv * Nk, (size_t)D, &kel))
+    return SAGE_ERR_INVALID;
+  if (!mul_ok(qel, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(qel, 2, &qbytes) || !mul_ok(kel, 2, &kbytes))
+    return SAGE_ERR_INVALID;
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kbytes) ||
+      ranges_overlap(o, obytes, v, kbytes) || ranges_overlap(o, obytes, workspace, need))
+    return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  size_t sz[kDecodeArrays];
+  decode_layout(d, sk, sz);
+  char* p = (char*)workspace;
+  float* arr[kDecodeArrays];
+  for (int i = 0; i < kDecodeArrays; i++) {
+    arr[i] = (float*)p;
+    p += align_up(sz[i]);
+  }
+  Bufs b = {};
+  b.k_part = arr[0];
+  b.v_part = arr[1];
+  b.k_mean = arr[2];
+  b.v_scale = arr[3];
+  b.v_mean = arr[4];
+  sage::DecodeBufs db;
+  db.part_o = arr[5];
+  db.part_ml = arr[6];
+  db.split_keys = sk;
+  const float ks = sm_scale * 1.44269504088896340736f;
+  const hipError_t e = sage::launch_decode(q, k, v, (int)in_dtype, d, b, db, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

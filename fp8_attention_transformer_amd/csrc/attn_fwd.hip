@@ -132,20 +132,6 @@ __device__ __forceinline__ v16f qk_tile_i8(const v4i* a, const QOperand<D, 8>& o
   return f;
 }
 
-__device__ __forceinline__ void store_out(void* o, size_t idx, float val, int out_dtype) {
-  if (out_dtype == kOutF32) {
-    ((float*)o)[idx] = val;
-  } else if (out_dtype == kOutBF16) {
-    const uint32_t u = __float_as_uint(val);
-    ((uint16_t*)o)[idx] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-  } else {
-    const _Float16 hv = (_Float16)val;
-    uint16_t bits;
-    __builtin_memcpy(&bits, &hv, 2);
-    ((uint16_t*)o)[idx] = bits;
-  }
-}
-
 // Map the hardware workgroup id to (head, query block).  Workgroups are
 // dealt round-robin to the 8 XCDs; renumbering gives every XCD a contiguous
 // range of logical ids, so the query blocks of one head share an L2.

@@ -1,0 +1,432 @@
+// SageAttention2 decoding step on gfx950: one query token per sequence and
+// query head against Nk cached keys and values, grouped-query heads.
+//
+// The method is the one of the fused kernel (SageAttention2 abstract, arXiv
+// 2411.10958 page): smoothed INT4 QK^T with the compensation term, online
+// softmax over 128-key blocks, FP8 P~ and V with the two-level accumulation.
+// With one query token its 128-token smoothing block holds that token alone,
+// so the block mean is the query itself: the smoothed query is zero, its
+// codes and scale are zero, and the score of key j is exactly the
+// compensation term DeltaS_j = q . (K_j - mean K) (the integer part
+// contributes fma(0, 0, DeltaS)).  Key codes are therefore never needed; the
+// kernel evaluates DeltaS in fp32 straight from the 16-bit keys.
+//
+// Memory-bound layout.  The prepass statistics (K channel means, V channel
+// means and scales) need every key, so a decoding step streams K and V twice:
+// the statistics kernels of the prepass, then this kernel, which reads K and V
+// once more in 16-bit form and never writes codes.  Parallelism comes from
+// splitting the keys: workgroup (split, K/V head) runs the online softmax of
+// all query heads of its group over one key range with its own running
+// maximum (the split-key schedule); a second kernel merges the ranges.
+//
+// Thread layout for one 128-key block (512 threads): thread (kg, cg) owns the
+// 8 channels 8cg..8cg+7 of the KPG keys of key group kg, loaded as 16-byte
+// row pieces (one load instruction covers 64/CG whole rows).  Groups of more
+// than four query heads per K/V head take several workgroups, each reading
+// the keys and values again.  Scores: the
+// 8-channel partial dot products are summed across the CG lanes of a key with
+// row shifts (DPP).  P~V: each thread keeps partial fp32 accumulators for its
+// keys and channels (the two-level recurrence is linear, so partials over key
+// subsets add up to the whole); they are summed once per split.
+#include "sage_internal.h"
+#include "sage_device.h"
+
+namespace sage {
+namespace {
+
+constexpr float kLog2_448 = 8.80735492205760410744f;
+
+struct DecodeArgs {
+  const uint16_t* q;   // [B, Hq, D]
+  const uint16_t* k;   // [B, Hk, Nk, D]
+  const uint16_t* v;
+  const float* k_mean;   // [B*Hk, D]
+  const float* v_scale;
+  const float* v_mean;
+  float* part_o;    // [B*Hq, S, D]  per-range unnormalised outputs
+  float* part_ml;   // [B*Hq, S, 2]  per-range running maximum (log2 domain) and row sum
+  int Hq, Hk, Nk, S, split_blocks, hgroups;
+  float ks;         // sm_scale * log2(e)
+};
+
+// Sum over groups of CG consecutive lanes (CG = 8 or 16, inside one 16-lane
+// row): with zero fill, after shifts by 1, 2, .., CG/2 the last lane of each
+// group holds the sum of its group.
+template <int SH>
+__device__ __forceinline__ float add_row_shr(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + SH, 0xF, 0xF, true));
+}
+// The same for NV independent values, one shift step at a time for all.
+template <int CG, int NV>
+__device__ __forceinline__ void group_sum_last_n(float* v) {
+  static_assert(CG == 8 || CG == 16, "lanes per group");
+#pragma unroll
+  for (int i = 0; i < NV; i++) v[i] = add_row_shr<1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < NV; i++) v[i] = add_row_shr<2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < NV; i++) v[i] = add_row_shr<4>(v[i]);
+  if constexpr (CG == 16) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) v[i] = add_row_shr<8>(v[i]);
+  }
+}
+
+// Whole-wave maximum and sum on the VALU (DPP): shifts inside each 16-lane
+// row, then row broadcasts 15 and 31 carry the partial results up to lane 63,
+// which is read back as a uniform value.  The maximum fills invalid source
+// lanes with the lane's own value, the sum with zero.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
+                                                             false)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = dpp_max<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_max<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_max<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_max<0x118, 0xF>(v);   // row_shr:8
+  v = dpp_max<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0x111, 0xF>(v);
+  v = dpp_add<0x112, 0xF>(v);
+  v = dpp_add<0x114, 0xF>(v);
+  v = dpp_add<0x118, 0xF>(v);
+  v = dpp_add<0x142, 0xA>(v);
+  v = dpp_add<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// e4m3 byte pair (bytes 0-1, or 2-3 with HI) -> two floats (exact).
+template <bool HI>
+__device__ __forceinline__ void fp8x2_decode(uint32_t w, float& a, float& b) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  a = f[0];
+  b = f[1];
+}
+
+// (V - vmean) / vscale for 8 channels with their own scales, bit-identical to
+// a true division per element: reciprocal multiply unless, in some lane of the
+// wave, a quotient lies within 8 ulps of an e4m3 rounding midpoint (its low
+// 20 bits within 8 of 0x80000) or is nonzero below the e4m3 normal range
+// (2^-6) -- then true divisions for the whole wave.
+__device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const float* dv) {
+  bool amb = false;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    y[e] = x[e] * rdv[e];
+    const uint32_t bits = __float_as_uint(y[e]);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    amb |= ((bits - 0x7FFF8u) & 0xFFFFFu) <= 16u;   // near a midpoint (sign bit is above bit 19)
+    amb |= mag - 1u < 0x3C7FFFFFu;                 // 0 < |y| < 2^-6
+  }
+  if (__any(amb)) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[e] = dv[e] == 0.0f ? 0.0f : x[e] / dv[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) x[e] = y[e];
+}
+
+template <int IN>
+__device__ __forceinline__ void decode8(const v4i& raw, float* x) {
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    x[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF));
+    x[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] >> 16));
+  }
+}
+
+// grid (S key ranges, B*Hk*hgroups), 512 threads (8 waves, two per SIMD);
+// HG <= 4 query heads per workgroup.  The keys and values of block t+1 are
+// loaded into registers while block t is processed.
+constexpr int kThreads = 512;
+
+template <int IN, int D, int HG>
+__global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
+  static_assert(HG >= 1 && HG <= 4, "heads per workgroup");
+  constexpr int CG = D / 8;            // 16-byte channel groups per row
+  constexpr int KG = kThreads / CG;    // key groups per block
+  constexpr int KPG = kBK / KG;        // keys per group: 4 (D = 128) or 2 (D = 64)
+  constexpr int NW = kThreads / 64;
+  __shared__ float sP[HG][kBK];        // scores, then decoded FP8 P~
+  __shared__ float sAlpha[HG];
+  __shared__ __align__(16) float sRed[NW][HG][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = lane % CG, kg = tid / CG;
+  const int split = blockIdx.x;
+  const int hgrp = blockIdx.y % a.hgroups, bhk = blockIdx.y / a.hgroups;
+  const int b = bhk / a.Hk, hk = bhk % a.Hk;
+  const int g = a.Hq / a.Hk;
+  const int h0 = hgrp * HG;                 // first head of this workgroup inside its K/V group
+  const int nh = min(HG, g - h0);           // heads in use
+  const int bhq0 = b * a.Hq + hk * g + h0;  // flat index of head h0
+  const size_t kvbase = (size_t)bhk * a.Nk * D;
+  const int nkb = (a.Nk + kBK - 1) / kBK;
+  const int t0 = split * a.split_blocks, t1 = min(nkb, t0 + a.split_blocks);
+
+  // per-thread constants for channels c = 8cg + e; the V scales themselves
+  // (needed only on the exact-division path) stay in LDS
+  __shared__ float sDV[D];
+  if (tid < D) sDV[tid] = a.v_scale[(size_t)bhk * D + tid];
+  float kbar[8], vbar[8], rdv[8], qv[HG][8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int c = 8 * cg + e;
+    kbar[e] = a.k_mean[(size_t)bhk * D + c];
+    vbar[e] = a.v_mean[(size_t)bhk * D + c];
+    const float dv = a.v_scale[(size_t)bhk * D + c];
+    rdv[e] = dv == 0.0f ? 0.0f : 1.0f / dv;
+  }
+#pragma unroll
+  for (int h = 0; h < HG; h++) {
+    v4i raw = {0, 0, 0, 0};
+    if (h < nh) raw = *(const v4i*)(a.q + (size_t)(bhq0 + h) * D + 8 * cg);
+    decode8<IN>(raw, qv[h]);
+  }
+  float O[HG][8];
+#pragma unroll
+  for (int h = 0; h < HG; h++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) O[h][e] = 0.0f;
+  float m = -__builtin_inff(), l = 0.0f;   // state of head `wave` (waves < HG)
+
+  // Buffer resources over this head's keys and values: rows at or past Nk
+  // read as zeros, and so does the out-of-range offset used for blocks past
+  // the end of the range, so every load is unconditional and in order (the
+  // waits before each block then cover exactly that block's loads).
+  constexpr int ROWB = 2 * D;
+  const uint32_t head_bytes = (uint32_t)a.Nk * ROWB;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k + kvbase), (short)0, (int)head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v + kvbase), (short)0, (int)head_bytes, 0x00020000);
+  const int lane_off = KPG * kg * ROWB + 16 * cg;
+  auto issue = [&](int t, v4i* kb, v4i* vb) {
+    const int base = t < t1 ? t * kBK * ROWB + lane_off : 0x7FFFFFF0;
+#pragma unroll
+    for (int kk = 0; kk < KPG; kk++) {
+      kb[kk] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, base + kk * ROWB, 0, 0));
+      vb[kk] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, base + kk * ROWB, 0, 0));
+    }
+  };
+
+  auto process = [&](int t, const v4i* kc, const v4i* vc) {
+    // ---- scores: DeltaS_j * ks for the HG heads.  Partial dot products over
+    //      this thread's 8 channels, then the KPG*HG independent sums over the
+    //      CG lanes of each key, step by step (the chains hide each other's
+    //      DPP latency); the last lane of each group stores its keys' scores.
+    float ps[KPG][HG];
+#pragma unroll
+    for (int kk = 0; kk < KPG; kk++) {
+      float x[8];
+      decode8<IN>(kc[kk], x);
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = x[e] - kbar[e];   // gamma(K) in fp32
+#pragma unroll
+      for (int h = 0; h < HG; h++) {
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) p = __builtin_fmaf(qv[h][e], x[e], p);
+        ps[kk][h] = p;
+      }
+    }
+    group_sum_last_n<CG, KPG * HG>(&ps[0][0]);
+    if (cg == CG - 1) {
+#pragma unroll
+      for (int h = 0; h < HG; h++) {
+        float sc[KPG];
+#pragma unroll
+        for (int kk = 0; kk < KPG; kk++)
+          sc[kk] = (t * kBK + KPG * kg + kk < a.Nk) ? ps[kk][h] * a.ks : -__builtin_inff();
+        if constexpr (KPG == 4) *(float4*)&sP[h][KPG * kg] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        else *(float2*)&sP[h][KPG * kg] = make_float2(sc[0], sc[1]);
+      }
+    }
+    __syncthreads();
+    // ---- online softmax of head h by wave h: block max, rescale, p', FP8 P~, row sum
+    if (wave < HG) {
+      const int h = wave;
+      const float x0 = sP[h][2 * lane], x1 = sP[h][2 * lane + 1];
+      const float bmax = wave_max_dpp(fmaxf(x0, x1));
+      const float mnew = fmaxf(m, bmax);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      const float mm = mnew - kLog2_448;
+      const float p0 = __builtin_amdgcn_exp2f(x0 - mm), p1 = __builtin_amdgcn_exp2f(x1 - mm);
+      const float rs = wave_sum_dpp(p0 + p1);
+      l = alpha * l + rs;
+      m = mnew;
+      float q0, q1;
+      fp8x2_decode<false>(fp8x2(p0, p1), q0, q1);
+      sP[h][2 * lane] = q0;
+      sP[h][2 * lane + 1] = q1;
+      if (lane == 0) sAlpha[h] = alpha;
+    }
+    __syncthreads();
+    // ---- P~V: V -> FP8 codes of the method (smoothed, per-channel scale),
+    //      level-1 partial R over this thread's keys, then O = alpha*O + R
+    float R[HG][8];
+#pragma unroll
+    for (int h = 0; h < HG; h++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) R[h][e] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KPG; kk++) {
+      const int key = KPG * kg + kk;
+      float x[8];
+      decode8<IN>(vc[kk], x);
+      const bool valid = t * kBK + key < a.Nk;
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = valid ? x[e] - vbar[e] : 0.0f;
+      fp8_quotients8(x, rdv, sDV + 8 * cg);
+      float vq[8];
+#pragma unroll
+      for (int w = 0; w < 2; w++) {
+        const uint32_t pk = fp8x4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
+        fp8x2_decode<false>(pk, vq[4 * w], vq[4 * w + 1]);
+        fp8x2_decode<true>(pk, vq[4 * w + 2], vq[4 * w + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < HG; h++) {
+        const float p = sP[h][key];
+#pragma unroll
+        for (int e = 0; e < 8; e++) R[h][e] = __builtin_fmaf(p, vq[e], R[h][e]);   // products of FP8 values are exact
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < HG; h++) {
+      const float alpha = sAlpha[h];
+#pragma unroll
+      for (int e = 0; e < 8; e++) O[h][e] = __builtin_fmaf(alpha, O[h][e], R[h][e]);
+    }
+    __syncthreads();
+  };
+
+  // two register buffers in turn: the next block loads while this one runs
+  v4i kA[KPG], vA[KPG], kB[KPG], vB[KPG];
+  issue(t0, kA, vA);
+  for (int t = t0; t < t1; t += 2) {
+    issue(t + 1, kB, vB);
+    process(t, kA, vA);
+    issue(t + 2, kA, vA);
+    if (t + 1 < t1) process(t + 1, kB, vB);
+  }
+
+  // ---- sum the partial outputs of the key groups: inside the wave (lanes
+  //      with the same channel group), then across the waves
+#pragma unroll
+  for (int h = 0; h < HG; h++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      float s = O[h][e];
+#pragma unroll
+      for (int o = CG; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
+      O[h][e] = s;
+    }
+  if (lane < CG) {
+#pragma unroll
+    for (int h = 0; h < HG; h++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) sRed[wave][h][8 * cg + e] = O[h][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < HG * D; i += kThreads) {
+    const int h = i / D, c = i % D;
+    if (h < nh) {
+      float s = sRed[0][h][c];
+#pragma unroll
+      for (int w = 1; w < NW; w++) s = s + sRed[w][h][c];
+      a.part_o[((size_t)(bhq0 + h) * a.S + split) * D + c] = s;
+    }
+  }
+  if (wave < nh && lane == 0) {
+    a.part_ml[((size_t)(bhq0 + wave) * a.S + split) * 2] = m;
+    a.part_ml[((size_t)(bhq0 + wave) * a.S + split) * 2 + 1] = l;
+  }
+}
+
+// Merge of the key ranges, one workgroup per query head, one thread per
+// channel: M = max m_s, w_s = exp2(m_s - M), O = fma(w_s, O_s, O) and
+// l' = fma(w_s, l'_s, l') in range order, then O * vscale / l' + vmean.
+__global__ void __launch_bounds__(128) decode_merge_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           const float* __restrict__ v_scale,
+                                                           const float* __restrict__ v_mean, int Hq, int Hk, int S,
+                                                           int D, void* __restrict__ o, int out_dtype) {
+  const int bhq = blockIdx.x, c = threadIdx.x;
+  if (c >= D) return;
+  const int g = Hq / Hk, bhk = (bhq / Hq) * Hk + (bhq % Hq) / g;
+  const float* ml = part_ml + (size_t)bhq * S * 2;
+  float M = -__builtin_inff();
+#pragma unroll 8
+  for (int s = 0; s < S; s++) M = fmaxf(M, ml[2 * s]);
+  float acc = 0.0f, l = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < S; s++) {
+    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    acc = __builtin_fmaf(w, part_o[((size_t)bhq * S + s) * D + c], acc);
+    l = __builtin_fmaf(w, ml[2 * s + 1], l);
+  }
+  const float val = (acc * v_scale[(size_t)bhk * D + c]) / l + v_mean[(size_t)bhk * D + c];
+  store_out(o, (size_t)bhq * D + c, val, out_dtype);
+}
+
+template <int IN, int D, int HG>
+void launch_decode_kernel(const DecodeArgs& a, int BHk, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<IN, D, HG>), dim3(a.S, BHk * a.hgroups), dim3(kThreads), 0, s, a);
+}
+
+template <int IN, int D>
+void launch_decode_hg(const DecodeArgs& a, int BHk, int hg, hipStream_t s) {
+  if (hg == 1) launch_decode_kernel<IN, D, 1>(a, BHk, s);
+  else if (hg == 2) launch_decode_kernel<IN, D, 2>(a, BHk, s);
+  else launch_decode_kernel<IN, D, 4>(a, BHk, s);
+}
+
+}  // namespace
+
+int decode_heads_per_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : 4; }
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
+                         const DecodeBufs& db, float ks, void* o, int out_dtype, hipStream_t s) {
+  hipError_t e = launch_kv_stats(k, v, in_dtype, d, b, s);
+  if (e != hipSuccess) return e;
+  const int g = d.H / d.Hk, hg = decode_heads_per_group(g);
+  DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.k_mean = b.k_mean;
+  a.v_scale = b.v_scale;
+  a.v_mean = b.v_mean;
+  a.part_o = db.part_o;
+  a.part_ml = db.part_ml;
+  a.Hq = d.H;
+  a.Hk = d.Hk;
+  a.Nk = d.Nk;
+  a.split_blocks = db.split_keys / kBK;
+  a.S = (d.NQBk + a.split_blocks - 1) / a.split_blocks;
+  a.hgroups = (g + hg - 1) / hg;
+  a.ks = ks;
+  if (in_dtype == kBF16) {
+    if (d.D == 64) launch_decode_hg<1, 64>(a, d.BHk(), hg, s);
+    else launch_decode_hg<1, 128>(a, d.BHk(), hg, s);
+  } else {
+    if (d.D == 64) launch_decode_hg<0, 64>(a, d.BHk(), hg, s);
+    else launch_decode_hg<0, 128>(a, d.BHk(), hg, s);
+  }
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(d.BH()), dim3(128), 0, s, db.part_o, db.part_ml, b.v_scale, b.v_mean,
+                     d.H, d.Hk, a.S, d.D, o, out_dtype);
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -112,30 +112,35 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
 // max|V - vmean| / 448, from the chunk maxima and minima: rounding is
 // monotonic, so max_j |fl(V_j - m)| = max(|fl(max V - m)|, |fl(min V - m)|).
 __global__ void finalize_kernel(Dims d, Bufs b) {
-  constexpr int U = 8;
+  constexpr int U = 16;   // chunks whose partials are loaded together
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
   const size_t base = (size_t)bh * d.NQBk * 2 * D + c;
   float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
-  for (int t = 0; t < d.NQBk; t += U) {
+  int t = 0;
+  for (; t + U <= d.NQBk; t += U) {   // whole batches: unconditional loads, then the in-order sums
     float kp[U], vp[U], xp[U], np[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const bool ok = t + u < d.NQBk;
       const size_t o = base + (size_t)(t + u) * 2 * D;
-      kp[u] = ok ? b.k_part[o] : 0.0f;
-      vp[u] = ok ? b.k_part[o + D] : 0.0f;
-      xp[u] = ok ? b.v_part[o] : -__builtin_inff();
-      np[u] = ok ? b.v_part[o + D] : __builtin_inff();
+      kp[u] = b.k_part[o];
+      vp[u] = b.k_part[o + D];
+      xp[u] = b.v_part[o];
+      np[u] = b.v_part[o + D];
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      if (t + u < d.NQBk) {
-        tot = tot + kp[u];
-        vtot = vtot + vp[u];
-      }
+      tot = tot + kp[u];
+      vtot = vtot + vp[u];
       vx = fmaxf(vx, xp[u]);
       vn = fminf(vn, np[u]);
     }
+  }
+  for (; t < d.NQBk; t++) {
+    const size_t o = base + (size_t)t * 2 * D;
+    tot = tot + b.k_part[o];
+    vtot = vtot + b.k_part[o + D];
+    vx = fmaxf(vx, b.v_part[o]);
+    vn = fminf(vn, b.v_part[o + D]);
   }
   const int n = head_io_kv(d, bh).n;   // 0 only for an empty packed sequence
   b.k_mean[(size_t)bh * D + c] = n ? tot / (float)n : 0.0f;
@@ -596,6 +601,24 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dt
                           hipStream_t s) {
   if (in_dtype == kBF16) return d.D == 64 ? prepass_impl<1, 64>(q, k, v, d, b, s) : prepass_impl<1, 128>(q, k, v, d, b, s);
   return d.D == 64 ? prepass_impl<0, 64>(q, k, v, d, b, s) : prepass_impl<0, 128>(q, k, v, d, b, s);
+}
+
+// Key/value statistics alone (K and V channel sums per chunk, then K means,
+// V means and V scales per K/V head): the first half of a decoding step.
+hipError_t launch_kv_stats(const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b, hipStream_t s) {
+  const uint16_t* k16 = (const uint16_t*)k;
+  const uint16_t* v16 = (const uint16_t*)v;
+  const int cpw = 256 / (d.D / 2);
+  const dim3 grid((unsigned)(((long long)d.BHk() * d.NQBk + cpw - 1) / cpw));
+  if (in_dtype == kBF16) {
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+  } else {
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+  }
+  hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(d.D), 0, s, d, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_encode(const float* in, uint8_t* out, size_t n, hipStream_t s) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sage_internal.h"
+
 namespace sage {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -55,6 +57,21 @@ __device__ __forceinline__ void pack_fp6(const int* c, uint32_t* w) {
     const int bit = 6 * e;
     w[bit / 32] |= f << (bit % 32);
     if (bit % 32 > 26) w[bit / 32 + 1] |= f >> (32 - bit % 32);
+  }
+}
+
+// One output element in the requested dtype (bf16 and fp16 with RNE).
+__device__ __forceinline__ void store_out(void* o, size_t idx, float val, int out_dtype) {
+  if (out_dtype == kOutF32) {
+    ((float*)o)[idx] = val;
+  } else if (out_dtype == kOutBF16) {
+    const uint32_t u = __float_as_uint(val);
+    ((uint16_t*)o)[idx] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    const _Float16 hv = (_Float16)val;
+    uint16_t bits;
+    __builtin_memcpy(&bits, &hv, 2);
+    ((uint16_t*)o)[idx] = bits;
   }
 }
 

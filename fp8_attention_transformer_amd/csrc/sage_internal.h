@@ -117,8 +117,24 @@ struct Bufs {
   float* v_mean;      // [B,Hk,D]        V channel means (zeros without V smoothing)
 };
 
+// Decoding step (one query token per head): per-range partial outputs.
+struct DecodeBufs {
+  float* part_o;    // [B*H, S, D] unnormalised outputs of each key range
+  float* part_ml;   // [B*H, S, 2] running maximum (log2 domain) and row sum of each range
+  int split_keys;   // keys per range (a multiple of 128); S = ceil(Nk / split_keys)
+};
+
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d,
                           const Bufs& b, hipStream_t s);
+// K/V statistics only: k_part, v_part (scratch) -> k_mean, v_scale, v_mean.
+hipError_t launch_kv_stats(const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
+                           hipStream_t s);
+// Decoding step: statistics, split-key attention (DeltaS in fp32 from the
+// 16-bit keys, FP8 V on the fly), merge of the ranges into o [B*H, D].
+hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
+                         const DecodeBufs& db, float ks, void* o, int out_dtype, hipStream_t s);
+// Query heads per decoding workgroup for a group of g query heads per K/V head.
+int decode_heads_per_group(int g);
 hipError_t launch_attn(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
                        hipStream_t s);
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk,

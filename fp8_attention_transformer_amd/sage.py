@@ -24,6 +24,7 @@ EXPORTED = [
     "sage_quant_smooth_varlen", "sage_attn_fwd_varlen", "sage_attn_quantized_varlen",
     "sage_workspace_bytes_cross", "sage_quant_bufs_from_workspace_cross", "sage_quant_smooth_cross",
     "sage_attn_fwd_cross", "sage_attn_quantized_cross",
+    "sage_decode_split_keys", "sage_decode_workspace_bytes", "sage_attn_decode",
 ]
 
 
@@ -88,6 +89,12 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd_cross.restype = i32
         L.sage_attn_quantized_cross.argtypes = [ctypes.POINTER(QuantBufs), P] + [i32] * 7 + [f32, i32, i32, P]
         L.sage_attn_quantized_cross.restype = i32
+        L.sage_decode_split_keys.argtypes = [i32] * 5
+        L.sage_decode_split_keys.restype = i32
+        L.sage_decode_workspace_bytes.argtypes = [i32] * 6
+        L.sage_decode_workspace_bytes.restype = sz
+        L.sage_attn_decode.argtypes = [P, P, P, P] + [i32] * 5 + [f32, i32, i32, i32, i32, P, sz, P]
+        L.sage_attn_decode.restype = i32
         _lib = L
     return _lib
 
@@ -202,6 +209,21 @@ def attn_quantized_cross(bufs: QuantBufs, o_ptr: int, B: int, Hq: int, Hkv: int,
                                            float(sm_scale), qk_bits, out_dtype, stream), "sage_attn_quantized_cross")
 
 
+def decode_split_keys(B: int, Hq: int, Hkv: int, Nk: int, D: int) -> int:
+    return lib().sage_decode_split_keys(B, Hq, Hkv, Nk, D)
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nk: int, D: int, split_keys: int = 0) -> int:
+    return lib().sage_decode_workspace_bytes(B, Hq, Hkv, Nk, D, split_keys)
+
+
+def attn_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, Hq: int, Hkv: int, Nk: int, D: int,
+                    sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int, stream: int = 0,
+                    smooth_v: bool = False, split_keys: int = 0) -> None:
+    _check(lib().sage_attn_decode(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, Nk, D, float(sm_scale), int(bool(smooth_v)),
+                                  split_keys, in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_decode")
+
+
 # ---------------------------------------------------------------- torch glue --
 # Device memory and the stream handle come from torch; nothing is computed here.
 
@@ -307,4 +329,38 @@ def attn_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False, sm_s
     attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu_seqlens.data_ptr(), nseq, max_seqlen,
                     T, H, D, causal, sm_scale, _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype),
                     workspace.ptr, workspace.nbytes, _stream_handle(q.device), qk_bits, smooth_v)
+    return out
+
+
+def attn_decode(q, k, v, sm_scale: float | None = None, out_dtype=None, workspace=None, out=None,
+                smooth_v: bool = False, split_keys: int = 0):
+    """One decoding step: q [B, Hq, 1, D], k and v [B, Hkv, Nk, D] fp16/bf16
+    device tensors (Hq a multiple of Hkv).  Returns [B, Hq, 1, D].  split_keys:
+    keys per range of the split-key schedule (a multiple of 128; 0 = the
+    library's choice, decode_split_keys)."""
+    import torch
+    if q.dim() != 4 or q.shape[2] != 1 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, 1, D] and k, v one [B, Hkv, Nk, D] shape")
+    B, H, _, D = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q, k, v must share B and D")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, 1, D), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        n = decode_workspace_bytes(B, H, Hk, Nk, D, split_keys)
+        if n == 0:
+            raise SageError(ERR_INVALID, "sage_decode_workspace_bytes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    attn_decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, Nk, D, sm_scale,
+                    _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.data_ptr(),
+                    workspace.numel(), _stream_handle(q.device), smooth_v, split_keys)
     return out

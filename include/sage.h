@@ -216,6 +216,40 @@ sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B,
                                       hipStream_t stream);
 
 /*
+ * Decoding step: one query token per sequence and query head against Nk
+ * cached keys and values (q [B, Hq, 1, D], k and v [B, Hkv, Nk, D], o
+ * [B, Hq, 1, D]; Hq a multiple of Hkv; no causal flag: the single query sees
+ * every key under the bottom-right alignment above).
+ * The method is unchanged; with one query token its smoothing block holds
+ * that token alone, so the smoothed query is zero, the Q codes and scale are
+ * zero for either code width (no qk_bits argument) and the score of key j is
+ * the compensation term q . (K_j - mean K) alone.  This call therefore skips
+ * the key codes: it computes the K/V statistics of the prepass (K mean, V mean
+ * with smooth_v, V scales), then evaluates the compensation term in fp32 from
+ * the 16-bit keys and the FP8 V codes of the method on the fly, reading K and
+ * V twice in all and writing no codes.
+ * Key blocks are processed in ranges of split_keys keys (a multiple of 128;
+ * 0 selects sage_decode_split_keys), each range with its own online softmax
+ * (its own running maximum scales its P~ before the FP8 rounding), merged at
+ * the end with weights exp2(m_s - M) in range order.  The result is that of
+ * the method under this schedule; it differs from sage_attn_fwd_cross on the
+ * same inputs by the FP8 rounding of P~ (one range covering every key gives
+ * the plain schedule).
+ * workspace: at least sage_decode_workspace_bytes(B, Hq, Hkv, Nk, D,
+ * split_keys) bytes, scratch for the call (its contents are unspecified
+ * afterwards).  Errors as for sage_attn_fwd; split_keys not a non-negative
+ * multiple of 128, or Nk * D * 2 >= 2^31 (one head's keys), is
+ * SAGE_ERR_INVALID.
+ */
+int sage_decode_split_keys(int B, int Hq, int Hkv, int Nk, int D);
+
+size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nk, int D, int split_keys);
+
+sage_status sage_attn_decode(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nk,
+                             int D, float sm_scale, int smooth_v, int split_keys, sage_dtype in_dtype,
+                             sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Packed variable-length batches (the varlen form of the drop-in call; the
  * code record of the SageAttention2 paper names `sageattn_varlen`).  nseq
  * independent self-attention problems share one launch:

@@ -243,3 +243,25 @@ def test_cross_validation():
     assert aq(ctypes.byref(qb), FAKE, 1, 4, 2, 301, 300, 64, 1, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
     assert aq(ctypes.byref(qb), FAKE, 1, 4, 3, 10, 300, 64, 0, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
     assert aq(None, FAKE, 1, 4, 2, 10, 300, 64, 0, 0.125, 4, sage.F32, None) == sage.ERR_INVALID
+
+
+def test_decode_validation():
+    L = sage.lib()
+    assert sage.decode_split_keys(16, 32, 8, 8192, 128) == 1024
+    assert sage.decode_split_keys(1, 4, 3, 100, 64) == 0
+    assert sage.decode_split_keys(1, 4, 2, 1, 64) == 128
+    assert sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 100) == 0
+    assert sage.decode_workspace_bytes(1, 4, 2, 1000, 128, -128) == 0
+    assert sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 256) > 0
+    # more ranges need more partial-output space
+    assert sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 128) > sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 1024)
+    wsb = sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 0)
+    base = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), 1, 4, 2, 1000, 128, 0.125, 0, 0, sage.BF16,
+            sage.F32, FAKE + (4 << 30), wsb, None]
+    for i, bad, expect in [(0, None, sage.ERR_INVALID), (6, 3, sage.ERR_INVALID), (7, 0, sage.ERR_INVALID),
+                           (8, 96, sage.ERR_INVALID), (9, 0.0, sage.ERR_INVALID), (10, 2, sage.ERR_INVALID),
+                           (11, 100, sage.ERR_INVALID), (12, sage.F32, sage.ERR_INVALID), (15, 64, sage.ERR_WORKSPACE),
+                           (3, FAKE + 16, sage.ERR_INVALID), (14, None, sage.ERR_INVALID)]:
+        args = list(base)
+        args[i] = bad
+        assert L.sage_attn_decode(*args) == expect, (i, bad)

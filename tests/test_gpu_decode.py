@@ -1,0 +1,98 @@
+"""GPU parity of the decoding-step entry point (one query token per head
+against Nk cached keys, grouped-query heads, split-key schedule).
+
+The oracle's mirror mode, run with the same key ranges (kv_split), is the
+reference: O within max-abs 2e-3 plus its FP8-midpoint slack.  With one range
+covering every key the schedule is the plain one, so the decode entry point
+and the general cross-geometry entry point then agree to the same bar.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from fp8_attention_transformer_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+EPS_TIE = 2.0 ** -14
+
+CASES = [
+    # (B, Hq, Hkv, Nk, D, split_keys, smooth_v)
+    (1, 4, 2, 1000, 128, 0, False),       # library's split
+    (2, 8, 2, 777, 64, 256, True),
+    (3, 6, 6, 300, 128, 128, False),      # one query head per K/V head
+    (1, 12, 1, 2000, 128, 512, False),    # 12 heads per K/V head: two workgroups of 8 and 4
+    (2, 4, 4, 1, 64, 0, True),            # a single cached key
+    (1, 32, 8, 4100, 128, 0, False),      # ragged last block
+    (2, 6, 2, 130, 64, 0, True),          # three heads per K/V head (one slot unused)
+    (1, 2, 1, 640, 128, 1024, False),     # one range covering every key
+]
+
+
+def _id(c):
+    B, Hq, Hk, Nk, D, sk, sv = c
+    return f"b{B}hq{Hq}hkv{Hk}nk{Nk}d{D}_s{sk}{'_sv' if sv else ''}"
+
+
+def _make(c, seed):
+    B, Hq, Hk, Nk, D, sk, sv = c
+    w = wl.custom(B, Hq, 1, D, Hkv=Hk, Nk=Nk, seed=seed, k_offset_std=4.0, v_offset_std=1.5, outlier_channels=2,
+                  outlier_scale=8.0, t_noise_scale=0.5)
+    return w, wl.generate(w)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_decode_parity(oracle_lib, case):
+    import torch
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    B, Hq, Hk, Nk, D, sk, sv = case
+    w, (q, k, v) = _make(case, seed=Nk + 13 * Hq)
+    split = sk or sage.decode_split_keys(B, Hq, Hk, Nk, D)
+    assert split > 0 and split % 128 == 0
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, smooth_v=sv)
+    assert not z.q_codes.any()   # one token per smoothing block: zero Q codes
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, False, w.scale, eps=EPS_TIE, kv_split=split)
+    qd, kd, vd = (gh.to_device(a, w.dtype) for a in (q, k, v))
+    out = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=torch.float32, smooth_v=sv, split_keys=sk)
+    torch.cuda.synchronize()
+    O_gpu = out.cpu().numpy().reshape(-1, D)
+    err = np.abs(O_gpu.astype(np.float64) - O_ref).max(1)
+    bad = np.nonzero(~(err <= O_TOL + slack))[0]
+    print(f"[{_id(case)}] split={split} maxerr={err.max():.3e}")
+    assert bad.size == 0, (bad[:5], err[bad[:5]], slack[bad[:5]])
+    O_fp, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, 0)
+    c_gpu, c_orc = gh.cos_sim(O_gpu, O_fp), gh.cos_sim(O_ref, O_fp)
+    print(f"[{_id(case)}] cos_sim gpu={c_gpu:.6f} oracle={c_orc:.6f}")
+    assert abs(c_gpu - c_orc) < 1e-4
+
+
+def test_decode_one_range_matches_general_path(oracle_lib):
+    """One range over all keys is the plain schedule: the decode entry point and
+    sage_attn_fwd_cross (Nq = 1) agree within the O bar."""
+    import torch
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    B, Hq, Hk, Nk, D = 2, 8, 2, 1500, 128
+    w, (q, k, v) = _make((B, Hq, Hk, Nk, D, 0, False), seed=5)
+    qd, kd, vd = (gh.to_device(a, w.dtype) for a in (q, k, v))
+    dec = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=torch.float32, split_keys=1536)
+    gen, _ = gh.run_attn(q, k, v, w.dtype, False, w.scale)
+    torch.cuda.synchronize()
+    assert float((dec - gen).abs().max()) <= 2 * O_TOL
+
+
+def test_decode_low_precision_outputs(oracle_lib):
+    import torch
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    B, Hq, Hk, Nk, D = 2, 4, 2, 700, 64
+    w, (q, k, v) = _make((B, Hq, Hk, Nk, D, 0, False), seed=6)
+    qd, kd, vd = (gh.to_device(a, w.dtype) for a in (q, k, v))
+    ref = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=torch.float32)
+    for dt in (torch.bfloat16, torch.float16):
+        o = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref.to(dt))
