@@ -349,6 +349,8 @@ def main():
     ap.add_argument("--qk-bits", type=int, default=4, choices=(4, 8),
                     help="width of the Q/K codes: 4 (INT4, the method's default) or 8 (INT8)")
     ap.add_argument("--smooth-v", action="store_true", help="subtract the V channel means before FP8 (added back to O)")
+    ap.add_argument("--general-path", action="store_true",
+                    help="run one-query (decoding) workloads through the general cross-geometry entry points")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -381,7 +383,7 @@ def main():
     for w in todo:
         if isinstance(w, wl.PackedWorkload):
             rec = run_packed(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
-        elif w.N == 1 and not w.self_attention:
+        elif w.N == 1 and not w.self_attention and not args.general_path:
             rec = run_decode(w, args.steps, args.warmup, args.smooth_v)
         else:
             rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits,
