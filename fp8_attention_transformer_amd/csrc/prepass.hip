@@ -203,17 +203,17 @@ __device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf&
 }
 
 // Integer codes rint(x/delta) of NV values sharing one scale (INT4: |code|
-// <= 7, INT8: <= 127), bit-identical to a true IEEE division per element:
-// multiply by the correctly rounded reciprocal (absolute error below 2^-19
-// for INT4 and 2^-15 for INT8 quotients), and if any lane of the wave lands
-// within twice that of a rounding midpoint (half-integer), redo the whole
-// wave with true divisions.  |x| <= qmax*delta makes the clamp unnecessary.
+// <= 7, INT8: <= 127), as floats, bit-identical to a true IEEE division per
+// element: multiply by the correctly rounded reciprocal (absolute error below
+// 2^-19 for INT4 and 2^-15 for INT8 quotients), and if any lane of the wave
+// lands within twice that of a rounding midpoint (half-integer), redo the
+// whole wave with true divisions.  |x| <= qmax*delta makes the clamp
+// unnecessary.  Adding +0 turns a rounded -0 into +0 (code 0 has one pattern).
 template <int NV, int BITS>
-__device__ __forceinline__ void int_codes(const float* x, float delta, int* code) {
+__device__ __forceinline__ void int_codes_f(const float* x, float delta, float* c) {
   constexpr float kWindow = BITS == 4 ? 0x1p-19f : 0x1p-14f;
   const float r = delta == 0.0f ? 0.0f : 1.0f / delta;
   bool amb = false;
-  float c[NV];
 #pragma unroll
   for (int e = 0; e < NV; e++) {
     const float q = x[e] * r;
@@ -225,7 +225,34 @@ __device__ __forceinline__ void int_codes(const float* x, float delta, int* code
     for (int e = 0; e < NV; e++) c[e] = delta == 0.0f ? 0.0f : rintf(x[e] / delta);
   }
 #pragma unroll
-  for (int e = 0; e < NV; e++) code[e] = (int)c[e];
+  for (int e = 0; e < NV; e++) c[e] = c[e] + 0.0f;
+}
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef int v6i_t __attribute__((ext_vector_type(6)));
+
+// NF (16 or 32) integer codes in [-7, 7], given as floats, -> 3*NF/16 words
+// of FP6 e2m3 fields (field e at bit 6e) with the gfx950 packing conversion
+// v_cvt_scalef32_2xpk16_fp6_f32.  It takes its 32 fields from two 16-value
+// operands interleaved (field 2i from the first, 2i+1 from the second), so
+// even and odd codes go to the two operands; integers of magnitude <= 7 are
+// exact in e2m3 (scale 1).  The instruction writes its result while it still
+// reads its sources, so the result registers must not overlap them: it is
+// issued with an early-clobber output (the builtin lets the register
+// allocator place the result on top of the operands), followed by wait
+// states before the result is read.
+template <int NF>
+__device__ __forceinline__ void pack_fp6_hw(const float* c, uint32_t* w) {
+  static_assert(NF == 16 || NF == 32, "one or two 16-field halves");
+  v16f_t ev, od;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    ev[i] = 2 * i < NF ? c[2 * i] : 0.0f;
+    od[i] = 2 * i + 1 < NF ? c[2 * i + 1] : 0.0f;
+  }
+  v6i_t r;
+  asm volatile("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0\n\ts_nop 4" : "=&v"(r) : "v"(ev), "v"(od));
+#pragma unroll
+  for (int i = 0; i < 3 * NF / 16; i++) w[i] = (uint32_t)r[i];
 }
 
 // x / dv for FP8 V codes: reciprocal multiply unless, in some lane of the wave,
@@ -323,13 +350,13 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPT>(amax);
       const float dq = amax / kQmax;
-      int cq[16];
-      int_codes<16, BITS>(g, dq, cq);
+      float cq[16];
+      int_codes_f<16, BITS>(g, dq, cq);
       if constexpr (BITS == 4) {
         // FP6 tile layout: this lane's 16 channels are fields 16*(sub&1)..+15
         // of group c0/64 in half (c0/32)&1 of the row's chunk
         uint32_t w[3];
-        pack_fp6<16>(cq, w);
+        pack_fp6_hw<16>(cq, w);
         const int hq = (c0 >> 5) & 1, odd = sub & 1;
         uint32_t* chunk = (uint32_t*)(b.q_codes + fp6_chunk_offset(D, qrowp + i, hq));
         if constexpr (D == 128) {
@@ -351,7 +378,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
         for (int w = 0; w < 4; w++) {
           uint32_t word = 0;
 #pragma unroll
-          for (int e = 0; e < 4; e++) word |= ((uint32_t)cq[4 * w + e] & 0xFFu) << (8 * e);
+          for (int e = 0; e < 4; e++) word |= ((uint32_t)(int)cq[4 * w + e] & 0xFFu) << (8 * e);
           pk[w] = (int)word;
         }
         *(v4i*)(b.q_codes + (qrowp + i) * D + 16 * sub) = pk;
@@ -387,12 +414,12 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       for (int e = 0; e < 32; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPG>(amax);
       const float dk = amax / kQmax;
-      int ck[32];
-      int_codes<32, BITS>(g, dk, ck);
+      float ck[32];
+      int_codes_f<32, BITS>(g, dk, ck);
       if constexpr (BITS == 4) {
         // FP6 tile layout: this lane's 32 channels are group sub/2 of half sub&1
         uint32_t w[6];
-        pack_fp6<32>(ck, w);
+        pack_fp6_hw<32>(ck, w);
         const int hk = sub & 1;
         uint8_t* chunk = b.k_codes + fp6_chunk_offset(D, krowp + j, hk);
         if constexpr (D == 128) {
@@ -418,7 +445,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
           for (int w = 0; w < 4; w++) {
             uint32_t word = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) word |= ((uint32_t)ck[16 * half + 4 * w + e] & 0xFFu) << (8 * e);
+            for (int e = 0; e < 4; e++) word |= ((uint32_t)(int)ck[16 * half + 4 * w + e] & 0xFFu) << (8 * e);
             pk[w] = (int)word;
           }
           *(v4i*)(b.k_codes + (krowp + j) * D + 32 * sub + 16 * half) = pk;

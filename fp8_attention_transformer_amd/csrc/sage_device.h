@@ -38,28 +38,6 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, in
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// FP6 e2m3 bit pattern of an integer c in [-7, 7]: magnitudes 0..7 encode as
-// 0, 8, 16, 20, 24, 26, 28, 30 (1.m x 2^(e-1) with e = 1..3), sign in bit 5.
-__device__ __forceinline__ uint32_t fp6_of_int(int c) {
-  const uint32_t a = (uint32_t)(c < 0 ? -c : c);
-  const uint32_t mag = (uint32_t)(0x1E1C1A1814100800ull >> (8 * a)) & 0x3Fu;
-  return c < 0 ? (mag | 32u) : mag;
-}
-// NF (a multiple of 16) FP6 codes -> 3*NF/16 words, field e at bit 6e.
-template <int NF>
-__device__ __forceinline__ void pack_fp6(const int* c, uint32_t* w) {
-  static_assert(NF % 16 == 0, "whole words");
-#pragma unroll
-  for (int i = 0; i < 3 * NF / 16; i++) w[i] = 0;
-#pragma unroll
-  for (int e = 0; e < NF; e++) {
-    const uint32_t f = fp6_of_int(c[e]);
-    const int bit = 6 * e;
-    w[bit / 32] |= f << (bit % 32);
-    if (bit % 32 > 26) w[bit / 32 + 1] |= f >> (32 - bit % 32);
-  }
-}
-
 // One output element in the requested dtype (bf16 and fp16 with RNE).
 __device__ __forceinline__ void store_out(void* o, size_t idx, float val, int out_dtype) {
   if (out_dtype == kOutF32) {
