@@ -270,6 +270,69 @@ def run_decode(w, steps: int, warmup: int, smooth_v: bool = False):
     }
 
 
+def run_split(w, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = False):
+    """A workload with few query blocks per head through sage_attn_fwd_split
+    (prepass, fused kernel over split key ranges, merge).  The prepass alone
+    (sage_quant_smooth_cross) is timed in a second loop; attn_us is the rest."""
+    import numpy as np
+    import torch
+
+    from fp8_attention_transformer_amd import sage
+    from fp8_attention_transformer_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    tdt = torch.float16 if w.dtype == wl.F16 else torch.bfloat16
+    q, k, v = (torch.from_numpy(a.view(np.int16)).view(tdt).cuda() for a in wl.generate(w))
+    B, H, N, D, Hk, Nk = w.B, w.H, w.N, w.D, w.hkv, w.nk
+    split = sage.split_keys(B, H, Hk, N, Nk, D)
+    ws = torch.empty(sage.split_workspace_bytes(B, H, Hk, N, Nk, D, split), dtype=torch.uint8, device="cuda")
+    bufs = sage.quant_bufs_from_workspace_cross(ws.data_ptr(), ws.numel(), B, H, Hk, N, Nk, D)
+    out = torch.empty((B, H, N, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    in_code = sage.F16 if tdt == torch.float16 else sage.BF16
+
+    def full():
+        sage.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, N, Nk, D, w.causal,
+                            w.scale, in_code, in_code, ws.data_ptr(), ws.numel(), sh, qk_bits, smooth_v, split)
+
+    def pre():
+        sage.quant_smooth_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D, bufs, sh,
+                                qk_bits=qk_bits, smooth_v=smooth_v)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_per_step = timed(full)
+    pre_ms = timed(pre)
+    attn_ms = max(ms_per_step - pre_ms, 1e-6)
+    value = w.ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = w.ops / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"int{qk_bits}+fp8", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hk, "N": N, "Nk": Nk, "D": D, "causal": w.causal,
+                   "in_dtype": w.dtype, "out_dtype": w.dtype, "qk_bits": qk_bits, "smooth_v": smooth_v,
+                   "split_keys": split, "entry": "sage_attn_fwd_split",
+                   "ops": "4*B*H*N*Nk*D (causal: minus 2*B*H*N^2*D)"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 1), "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tops / PEAK_TOPS, 4), "traffic": None,
+                     "kernel": "attn_kernel (split ranges) + merge", "kernel_us": round(attn_ms * 1e3, 2)},
+        "breakdown": {"prepass_us": round(pre_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                      "e2e_frac_of_peak": round(value / PEAK_TOPS, 4)},
+    }
+
+
 def run_packed(pw, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = False):
     """A packed variable-length batch through the varlen entry points (prepass,
     then the fused kernel), timed like the dense workloads."""
@@ -350,7 +413,8 @@ def main():
                     help="width of the Q/K codes: 4 (INT4, the method's default) or 8 (INT8)")
     ap.add_argument("--smooth-v", action="store_true", help="subtract the V channel means before FP8 (added back to O)")
     ap.add_argument("--general-path", action="store_true",
-                    help="run one-query (decoding) workloads through the general cross-geometry entry points")
+                    help="run decoding and chunked-prefill workloads through the general cross-geometry entry points "
+                         "(no decode kernel, no split key ranges)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -385,6 +449,8 @@ def main():
             rec = run_packed(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
         elif w.N == 1 and not w.self_attention and not args.general_path:
             rec = run_decode(w, args.steps, args.warmup, args.smooth_v)
+        elif not w.self_attention and not args.general_path:
+            rec = run_split(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
         else:
             rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits,
                       args.smooth_v)

@@ -204,6 +204,36 @@ size_t decode_total(const Dims& d, int split_keys) {
   return tot;
 }
 
+// ------------------------------------------------- split key ranges (fused) --
+int default_split_fused(const Dims& d) {
+  // about 1024 workgroups (two rounds of two per compute unit)
+  const long long wg = (long long)d.NQB * d.BH();
+  long long S = (1024 + wg - 1) / wg;
+  if (S > d.NQBk) S = d.NQBk;
+  if (S < 1) S = 1;
+  return 128 * (int)((d.NQBk + S - 1) / S);
+}
+
+// Partial-state arrays after the prepass buffers: O [B*H*N, S, D] and (m, l')
+// [B*H*N, S, 2], fp32.
+bool split_sizes(const Dims& d, int split_keys, size_t* o_bytes, size_t* ml_bytes) {
+  const size_t S = ((size_t)d.Nk + split_keys - 1) / split_keys;
+  const size_t rows = (size_t)d.BH() * d.N;
+  if ((long long)d.NQB * d.BH() * (long long)S >= (1LL << 31) || rows >= (1ULL << 31)) return false;
+  size_t t;
+  if (!mul_ok(rows * S, (size_t)d.D * 4, o_bytes) || !mul_ok(rows * S, 8, &t)) return false;
+  *ml_bytes = t;
+  return true;
+}
+
+size_t split_total(const Dims& d, int split_keys) {
+  size_t ob, mb;
+  const size_t base = total_bytes(d);
+  if (base == 0 || !split_sizes(d, split_keys, &ob, &mb)) return 0;
+  const size_t tot = base + align_up(ob) + align_up(mb);
+  return tot < base ? 0 : tot;
+}
+
 }  // namespace
 
 extern "C" {
@@ -358,6 +388,62 @@ sage_status sage_attn_decode(const void* q, const void* k, const void* v, void* 
   db.split_keys = sk;
   const float ks = sm_scale * 1.44269504088896340736f;
   const hipError_t e = sage::launch_decode(q, k, v, (int)in_dtype, d, b, db, ks, o, (int)out_dtype, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
+int sage_split_keys(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
+  if (!shape_ok(B, Hq, Hkv, Nq, Nk, D)) return 0;
+  return default_split_fused(make_dims(B, Hq, Hkv, Nq, Nk, D));
+}
+
+size_t sage_split_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int split_keys) {
+  if (!shape_ok(B, Hq, Hkv, Nq, Nk, D) || !split_ok(split_keys)) return 0;
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D);
+  return split_total(d, split_keys ? split_keys : default_split_fused(d));
+}
+
+sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
+                                int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v, int split_keys,
+                                sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (!q || !k || !v || !o || !workspace || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits) ||
+      !split_ok(split_keys))
+    return SAGE_ERR_INVALID;
+  if (causal && Nq > Nk) return SAGE_ERR_INVALID;
+  if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
+  if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
+  if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
+  const int sk = split_keys ? split_keys : default_split_fused(d);
+  const size_t need = split_total(d, sk);
+  if (need == 0) return SAGE_ERR_INVALID;
+  if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
+  size_t qel, kel, obytes, qbytes, kbytes;
+  if (!mul_ok((size_t)B * Hq * Nq, (size_t)D, &qel) || !mul_ok((size_t)B * Hkv * Nk, (size_t)D, &kel))
+    return SAGE_ERR_INVALID;
+  if (!mul_ok(qel, out_dtype == SAGE_F32 ? 4 : 2, &obytes) || !mul_ok(qel, 2, &qbytes) || !mul_ok(kel, 2, &kbytes))
+    return SAGE_ERR_INVALID;
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kbytes) ||
+      ranges_overlap(o, obytes, v, kbytes) || ranges_overlap(o, obytes, workspace, need))
+    return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  sage_quant_bufs qb;
+  carve(workspace, d, &qb);
+  const Bufs b = to_internal(qb);
+  size_t ob, mb;
+  split_sizes(d, sk, &ob, &mb);
+  char* p = (char*)workspace + total_bytes(d);
+  sage::SplitParts sp;
+  sp.part_o = (float*)p;
+  sp.part_ml = (float*)(p + align_up(ob));
+  sp.split_blocks = sk / 128;
+  sp.S = (d.NQBk + sp.split_blocks - 1) / sp.split_blocks;
+  const float ks = sm_scale * 1.44269504088896340736f;
+  hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, stream);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  e = sage::launch_attn_split(b, d, causal ? 1 : 0, ks, o, (int)out_dtype, sp, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

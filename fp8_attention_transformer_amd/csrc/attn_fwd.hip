@@ -242,7 +242,7 @@ __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, c
 // nk: valid keys of the head; klim: the last key this lane's query may see
 // (causal); need_mask: some key of block t is masked for some query of the
 // workgroup (wave-uniform).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
                                              const float* cKS, float dq, float ks, int t, int klim, int h, int nk,
                                              bool need_mask, v8i* P8, float& alpha) {
@@ -276,8 +276,11 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
   }
   const float bmax = pair_max(fmaxf(fmaxf(fmaxf(tmax[0], tmax[1]), tmax[2]), tmax[3]));
   const float mnew = fmaxf(as.m, bmax);
-  alpha = __builtin_amdgcn_exp2f(as.m - mnew);
-  const float mm = mnew - kLog2_448;
+  // Split key ranges: a query may see no key of a range yet (its running max
+  // stays -inf); referencing 0 then keeps alpha, p' and the state at 0.
+  const float mref = SPLIT ? (mnew == -__builtin_inff() ? 0.0f : mnew) : mnew;
+  alpha = __builtin_amdgcn_exp2f(as.m - mref);
+  const float mm = mref - kLog2_448;
   // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
   float part[4][4];   // independent partial row sums (tile, register quad)
 #pragma unroll
@@ -323,7 +326,7 @@ __device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8,
 }
 
 // One whole block in sequence (the four-wave kernel).
-template <int D, int BITS, bool CAUSAL>
+template <int D, int BITS, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
                                            int t, int klim, int n, int h, int nk, bool need_mask) {
@@ -333,7 +336,7 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   v8i P8[2];
   float alpha;
-  softmax_part<D, CAUSAL>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha);
+  softmax_part<D, CAUSAL, SPLIT>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -348,8 +351,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int BITS, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype) {
+// SPLIT: workgroup (head, key range, query block) runs the method over one
+// range of key blocks from an empty state and writes its unnormalised state
+// (O, running max, row sum) for a merge kernel (dense geometry only).
+template <int D, int BITS, bool CAUSAL, bool SPLIT>
+__global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype,
+                                                      SplitParts sp) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int NDT = D / 32;
   constexpr int S = SAGE_STAGES;
@@ -376,7 +383,11 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // Dense: head-major (the query blocks of a head share an XCD's L2).
   // Packed sequences of unequal length: query-block-major, so the heaviest
   // blocks of every sequence start first and no long sequence trails.
-  const int bh = d.cu ? logical % d.BH() : logical / d.NQB;
+  // Split: (head, range) pairs take the place of heads, so the query blocks
+  // of one key range share an L2.
+  const int hs = logical / d.NQB;
+  const int bh = d.cu ? logical % d.BH() : (SPLIT ? hs / sp.S : hs);
+  const int rng = SPLIT ? hs % sp.S : 0;
   const int jq = d.cu ? logical / d.BH() : logical % d.NQB;
   const int qb = CAUSAL ? d.NQB - 1 - jq : jq;
   const HeadIO io = head_io(d, bh);              // queries and outputs
@@ -400,6 +411,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const int tend = CAUSAL ? (min(qb * kBQ + kBQ, io.n) - 1 + off) / kBK + 1 : nkb;
   const int tmask = CAUSAL ? (qb * kBQ + off) / kBK : nkb;   // first block with a causally masked key
   const bool ragged = nk != nkb * kBK;
+  // key blocks of this workgroup: [tb, te)
+  const int tb = SPLIT ? rng * sp.split_blocks : 0;
+  const int te = SPLIT ? min(tend, tb + sp.split_blocks) : tend;
+  if (tb >= te) return;   // no query of this tile sees a key of the range (whole workgroup)
 
   // Every wave issues the same number of memory ops per block (the small
   // loads are unconditional, with in-range indices), so a vmcnt limit of
@@ -418,8 +433,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg[t % (S - 1)];
   };
 
-  issue(0, 0);
-  if (S > 2 && tend > 1) issue(1, 1);
+  issue(tb, 0);
+  if (S > 2 && te - tb > 1) issue(tb + 1, 1);
 
   QOperand<D, BITS> qop;
   load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
@@ -433,29 +448,46 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   as.m = -__builtin_inff();
   as.l = 0.0f;
 
-  if (S > 2 && tend > 1) wait_vmcnt<VM_PER_BLOCK>();
+  if (S > 2 && te - tb > 1) wait_vmcnt<VM_PER_BLOCK>();
   else wait_vmcnt<0>();
-  publish(0, 0);
+  publish(tb, 0);
   __syncthreads();
 
-  for (int t = 0; t < tend; t++) {
-    const int slot = t % S;
-    const bool ahead = t + S - 1 < tend;          // block t+S-1 exists: stage it now
-    if (ahead) issue(t + S - 1, (t + S - 1) % S);
+  for (int t = tb; t < te; t++) {
+    const int u = t - tb;                          // blocks done by this workgroup
+    const int slot = u % S;
+    const bool ahead = t + S - 1 < te;             // block t+S-1 exists: stage it now
+    if (ahead) issue(t + S - 1, (u + S - 1) % S);
     const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
-    attn_block<D, BITS, CAUSAL>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, klim, n, h, nk,
-                                need_mask);
-    if (t + 1 < tend) {
+    attn_block<D, BITS, CAUSAL, SPLIT>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, klim, n, h, nk,
+                                       need_mask);
+    if (t + 1 < te) {
       // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
       if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
       else wait_vmcnt<0>();
-      publish(t + 1, (t + 1) % S);
+      publish(t + 1, (u + 1) % S);
     }
     __syncthreads();
   }
 
-  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
   const int qi = qrow;
+  if constexpr (SPLIT) {
+    // ---- this range's state for the merge: O (before vscale), m, l'
+    if (qi < io.n) {
+      const size_t row = (size_t)bh * d.N + qi;
+      float* po = sp.part_o + (row * sp.S + rng) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) po[32 * dt + 8 * (r >> 2) + 4 * h + (r & 3)] = as.O[dt][r];
+      if (h == 0) {
+        sp.part_ml[(row * sp.S + rng) * 2] = as.m;
+        sp.part_ml[(row * sp.S + rng) * 2 + 1] = as.l;
+      }
+    }
+    return;
+  }
+  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
   if (qi < io.n) {
     const float* vs = b.v_scale + (size_t)bhk * D;
     const float* vm = b.v_mean + (size_t)bhk * D;
@@ -503,20 +535,62 @@ __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, in
   }
 }
 
-template <int D, int BITS>
-hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype, hipStream_t s) {
-  const dim3 grid(d.NQB * d.BH());
-  if (causal) hipLaunchKernelGGL((attn_kernel<D, BITS, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
-  else hipLaunchKernelGGL((attn_kernel<D, BITS, false>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype);
+// Merge of the key ranges: one workgroup per query row, one thread per
+// channel.  Row i reads the ranges holding a key it sees (range r starts at
+// key r*split_keys <= i + Nk - N when causal), M = max m_r, w_r = exp2(m_r - M),
+// O = fma(w_r, O_r, O) and l' = fma(w_r, l'_r, l') in range order, then the
+// fused kernel's epilogue (O * vscale) * (1 / l') + vmean.  One range gives
+// the unsplit kernel's result bit for bit (w = 1).
+__global__ void __launch_bounds__(128) split_merge_kernel(Bufs b, Dims d, int causal, SplitParts sp, void* o,
+                                                          int out_dtype) {
+  const int row = blockIdx.x, c = threadIdx.x;
+  if (c >= d.D) return;
+  const int bh = row / d.N, i = row % d.N, bhk = d.kv_head(bh);
+  const int limit = causal ? i + (d.Nk - d.N) : d.Nk - 1;   // last key row i sees
+  const int rlast = min(sp.S - 1, limit / (sp.split_blocks * kBK));
+  const float* ml = sp.part_ml + (size_t)row * sp.S * 2;
+  float M = -__builtin_inff();
+  for (int r = 0; r <= rlast; r++) M = fmaxf(M, ml[2 * r]);
+  float acc = 0.0f, l = 0.0f;
+  for (int r = 0; r <= rlast; r++) {
+    const float w = __builtin_amdgcn_exp2f(ml[2 * r] - M);
+    acc = __builtin_fmaf(w, sp.part_o[((size_t)row * sp.S + r) * d.D + c], acc);
+    l = __builtin_fmaf(w, ml[2 * r + 1], l);
+  }
+  const float inv_l = 1.0f / l;
+  const float val = (acc * b.v_scale[(size_t)bhk * d.D + c]) * inv_l + b.v_mean[(size_t)bhk * d.D + c];
+  store_out(o, (size_t)row * d.D + c, val, out_dtype);
+}
+
+template <int D, int BITS, bool SPLIT>
+hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype, const SplitParts& sp,
+                     hipStream_t s) {
+  const dim3 grid(d.NQB * d.BH() * (SPLIT ? sp.S : 1));
+  if (causal) hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+  else hipLaunchKernelGGL((attn_kernel<D, BITS, false, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+  if (SPLIT) hipLaunchKernelGGL(split_merge_kernel, dim3(d.BH() * d.N), dim3(128), 0, s, b, d, causal, sp, o, out_dtype);
   return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t attn_dispatch(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
+                         const SplitParts& sp, hipStream_t s) {
+  if (d.QB == 8)
+    return d.D == 64 ? attn_impl<64, 8, SPLIT>(b, d, causal, ks, o, out_dtype, sp, s)
+                     : attn_impl<128, 8, SPLIT>(b, d, causal, ks, o, out_dtype, sp, s);
+  return d.D == 64 ? attn_impl<64, 4, SPLIT>(b, d, causal, ks, o, out_dtype, sp, s)
+                   : attn_impl<128, 4, SPLIT>(b, d, causal, ks, o, out_dtype, sp, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype, hipStream_t s) {
-  if (d.QB == 8)
-    return d.D == 64 ? attn_impl<64, 8>(b, d, causal, ks, o, out_dtype, s) : attn_impl<128, 8>(b, d, causal, ks, o, out_dtype, s);
-  return d.D == 64 ? attn_impl<64, 4>(b, d, causal, ks, o, out_dtype, s) : attn_impl<128, 4>(b, d, causal, ks, o, out_dtype, s);
+  return attn_dispatch<false>(b, d, causal, ks, o, out_dtype, SplitParts{}, s);
+}
+
+hipError_t launch_attn_split(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
+                             const SplitParts& sp, hipStream_t s) {
+  return attn_dispatch<true>(b, d, causal, ks, o, out_dtype, sp, s);
 }
 
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk, int32_t* out,

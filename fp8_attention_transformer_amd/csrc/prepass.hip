@@ -498,28 +498,6 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
   const int nqb = d.cu ? (head_io(d, bh).n + kBQ - 1) / kBQ : d.NQB;
   if (kb >= nkb) return;
   const float* km = b.k_mean + (size_t)bhk * D;
-  // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
-  v8bf B1[NK], B2[NK], B3[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; kk++) {
-    const int c0 = 16 * kk + 8 * h;
-    const float4 m0 = *(const float4*)(km + c0);
-    const float4 m1 = *(const float4*)(km + c0 + 4);
-    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float g[8];
-    if (j < io.n) {
-      const v4i raw = *(const v4i*)(k + io.base + (size_t)j * io.stride + c0);
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF)) - mv[2 * w];
-        g[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] >> 16)) - mv[2 * w + 1];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; e++) g[e] = 0.0f;
-    }
-    split8(g, B1[kk], B2[kk], B3[kk]);
-  }
   // A operands: the three bf16 pieces of the Q-block means (pieces 1, 2:
   // [NQB][2][D] in k_part; piece 3: [NQB][D] in v_part), staged per 32-block
   // Q tile into LDS by direct copies, double-buffered.  LDS tile layout
@@ -542,8 +520,31 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
                                        0, 0);
     }
   };
-  float* out = b.delta_s + (size_t)bh * d.NQB * d.NPk + j;
+  // the first Q tile streams into LDS while this lane's keys load and split
   stage(0, sA0);
+  // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
+  v8bf B1[NK], B2[NK], B3[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; kk++) {
+    const int c0 = 16 * kk + 8 * h;
+    const float4 m0 = *(const float4*)(km + c0);
+    const float4 m1 = *(const float4*)(km + c0 + 4);
+    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float g[8];
+    if (j < io.n) {
+      const v4i raw = *(const v4i*)(k + io.base + (size_t)j * io.stride + c0);
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF)) - mv[2 * w];
+        g[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] >> 16)) - mv[2 * w + 1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[e] = 0.0f;
+    }
+    split8(g, B1[kk], B2[kk], B3[kk]);
+  }
+  float* out = b.delta_s + (size_t)bh * d.NQB * d.NPk + j;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int qt = 0, it = 0; qt < nqb; qt += 32, it++) {

@@ -137,6 +137,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dty
 int decode_heads_per_group(int g);
 hipError_t launch_attn(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
                        hipStream_t s);
+// Split key ranges for the fused kernel (dense geometry): per-range states and
+// their merge into o.
+struct SplitParts {
+  float* part_o;     // [B*H*N, S, D] unnormalised O of each range (before vscale)
+  float* part_ml;    // [B*H*N, S, 2] running maximum (log2 domain) and row sum
+  int split_blocks;  // 128-key blocks per range
+  int S;             // ranges: ceil(NQBk / split_blocks)
+};
+hipError_t launch_attn_split(const Bufs& b, const Dims& d, int causal, float ks, void* o, int out_dtype,
+                             const SplitParts& sp, hipStream_t s);
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk,
                            int32_t* out, hipStream_t s);
 hipError_t launch_fp8_encode(const float* in, uint8_t* out, size_t n, hipStream_t s);

@@ -25,6 +25,7 @@ EXPORTED = [
     "sage_workspace_bytes_cross", "sage_quant_bufs_from_workspace_cross", "sage_quant_smooth_cross",
     "sage_attn_fwd_cross", "sage_attn_quantized_cross",
     "sage_decode_split_keys", "sage_decode_workspace_bytes", "sage_attn_decode",
+    "sage_split_keys", "sage_split_workspace_bytes", "sage_attn_fwd_split",
 ]
 
 
@@ -95,6 +96,12 @@ def lib() -> ctypes.CDLL:
         L.sage_decode_workspace_bytes.restype = sz
         L.sage_attn_decode.argtypes = [P, P, P, P] + [i32] * 5 + [f32, i32, i32, i32, i32, P, sz, P]
         L.sage_attn_decode.restype = i32
+        L.sage_split_keys.argtypes = [i32] * 6
+        L.sage_split_keys.restype = i32
+        L.sage_split_workspace_bytes.argtypes = [i32] * 7
+        L.sage_split_workspace_bytes.restype = sz
+        L.sage_attn_fwd_split.argtypes = [P, P, P, P] + [i32] * 7 + [f32, i32, i32, i32, i32, i32, P, sz, P]
+        L.sage_attn_fwd_split.restype = i32
         _lib = L
     return _lib
 
@@ -222,6 +229,22 @@ def attn_decode_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, Hq: 
                     smooth_v: bool = False, split_keys: int = 0) -> None:
     _check(lib().sage_attn_decode(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, Nk, D, float(sm_scale), int(bool(smooth_v)),
                                   split_keys, in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_decode")
+
+
+def split_keys(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int) -> int:
+    return lib().sage_split_keys(B, Hq, Hkv, Nq, Nk, D)
+
+
+def split_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, D: int, split_keys: int = 0) -> int:
+    return lib().sage_split_workspace_bytes(B, Hq, Hkv, Nq, Nk, D, split_keys)
+
+
+def attn_fwd_split(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                   D: int, causal: bool, sm_scale: float, in_dtype: int, out_dtype: int, ws_ptr: int, ws_bytes: int,
+                   stream: int = 0, qk_bits: int = 4, smooth_v: bool = False, split_keys: int = 0) -> None:
+    _check(lib().sage_attn_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
+                                     float(sm_scale), qk_bits, int(bool(smooth_v)), split_keys, in_dtype, out_dtype,
+                                     ws_ptr, ws_bytes, stream), "sage_attn_fwd_split")
 
 
 # ---------------------------------------------------------------- torch glue --
@@ -364,3 +387,36 @@ def attn_decode(q, k, v, sm_scale: float | None = None, out_dtype=None, workspac
                     _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.data_ptr(),
                     workspace.numel(), _stream_handle(q.device), smooth_v, split_keys)
     return out
+
+
+def attn_split(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype=None, out=None,
+               qk_bits: int = 4, smooth_v: bool = False, split_keys: int = 0, workspace=None):
+    """attn() with split key ranges (sage_attn_fwd_split): q [B, Hq, Nq, D],
+    k and v [B, Hkv, Nk, D].  Returns (out, workspace tensor); the workspace
+    starts with the prepass buffers of the cross geometry."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Nq, D] and k, v one [B, Hkv, Nk, D] shape")
+    B, H, N, D = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q, k, v must share B and D")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        nbytes = split_workspace_bytes(B, H, Hk, N, Nk, D, split_keys)
+        if nbytes == 0:
+            raise SageError(ERR_INVALID, "sage_split_workspace_bytes")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, N, Nk, D, causal, sm_scale,
+                   _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.data_ptr(), workspace.numel(),
+                   _stream_handle(q.device), qk_bits, smooth_v, split_keys)
+    return out, workspace

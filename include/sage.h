@@ -216,6 +216,33 @@ sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B,
                                       hipStream_t stream);
 
 /*
+ * The full call with split key ranges, for shapes with few 128-query blocks
+ * per head (a prefill chunk against a long cache, cross-attention with few
+ * queries), where one workgroup per query block leaves the chip idle.
+ * Arguments, geometry and errors as for sage_attn_fwd_cross, plus
+ * split_keys: keys per range (a non-negative multiple of 128; 0 selects
+ * sage_split_keys).  Each (query block, key range) is processed by its own
+ * workgroup running the method over that range from an empty state (its own
+ * running maximum scales its P~ before the FP8 rounding); a merge then
+ * combines, for each query, the ranges holding a key it sees, in order, with
+ * weights exp2(m_r - M) (M the largest range maximum) and applies the
+ * epilogue.  One range covering every key gives sage_attn_fwd_cross's result
+ * bit for bit; more ranges change the FP8 rounding of P~ only.
+ * workspace: at least sage_split_workspace_bytes(...) bytes: the
+ * sage_quant_bufs of the cross geometry first (as written by the prepass, the
+ * layout of sage_quant_bufs_from_workspace_cross), then scratch for the range
+ * states (contents unspecified afterwards).
+ */
+int sage_split_keys(int B, int Hq, int Hkv, int Nq, int Nk, int D);
+
+size_t sage_split_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int D, int split_keys);
+
+sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
+                                int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v, int split_keys,
+                                sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * Decoding step: one query token per sequence and query head against Nk
  * cached keys and values (q [B, Hq, 1, D], k and v [B, Hkv, Nk, D], o
  * [B, Hq, 1, D]; Hq a multiple of Hkv; no causal flag: the single query sees

@@ -265,3 +265,22 @@ def test_decode_validation():
         args = list(base)
         args[i] = bad
         assert L.sage_attn_decode(*args) == expect, (i, bad)
+
+
+def test_split_validation():
+    L = sage.lib()
+    assert sage.split_keys(1, 32, 8, 512, 8192, 128) == 1024
+    assert sage.split_keys(1, 4, 3, 10, 10, 64) == 0
+    assert sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 100) == 0
+    ws_one = sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 1024)
+    assert ws_one > sage.workspace_bytes_cross(1, 4, 2, 100, 1000, 128)
+    assert sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 128) > ws_one
+    wsb = sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 0)
+    base = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), 1, 4, 2, 100, 1000, 128, 1, 0.125, 4, 0, 0,
+            sage.BF16, sage.F32, FAKE + (4 << 30), wsb, None]
+    for i, bad, expect in [(7, 1001, sage.ERR_INVALID), (5, 5, sage.ERR_INVALID), (11, 0.0, sage.ERR_INVALID),
+                           (14, 100, sage.ERR_INVALID), (14, -128, sage.ERR_INVALID), (12, 3, sage.ERR_INVALID),
+                           (18, 100, sage.ERR_WORKSPACE), (3, FAKE + 16, sage.ERR_INVALID)]:
+        args = list(base)
+        args[i] = bad
+        assert L.sage_attn_fwd_split(*args) == expect, (i, bad)

@@ -152,3 +152,37 @@ def test_cross_split_calls_equal_fwd(oracle_lib):
     sage.attn_quantized_cross(bufs, out.data_ptr(), B, Hq, Hk, Nq, Nk, D, True, w.scale, sage.F32, sh)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_chunk_full_size(oracle_lib, bits):
+    """The benchmark's chunked-prefill workload (512 queries against 8192 cached
+    keys, 32 query heads on 8 K/V heads, causal) through the cross-geometry
+    entry points: every head's prepass bit-exact; compensation term and O on
+    sampled rows of the first and last query heads."""
+    import gpu_helpers as gh
+    w = wl.CHUNK
+    q, k, v = wl.generate(w)
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits)
+    rb = gh.Readback(ws, qk_bits=bits)
+    z_all = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, with_delta_s=False, qk_bits=bits)
+    fq = lambda a: a.reshape((w.B * w.H,) + a.shape[2:])
+    fk = lambda a: a.reshape((w.B * w.hkv,) + a.shape[2:])
+    for name in ("q_codes", "q_scale", "q_mean"):
+        assert np.array_equal(getattr(rb, name), fq(getattr(z_all, name))), name
+    for name in ("k_codes", "k_scale", "k_mean", "v_codes", "v_scale", "v_mean"):
+        assert np.array_equal(getattr(rb, name), fk(getattr(z_all, name))), name
+    del z_all
+    O_gpu = out.cpu().numpy().reshape(w.B * w.H, w.N, w.D)
+    g = w.H // w.hkv
+    rng = np.random.default_rng(7)
+    for h in (0, w.H - 1):
+        qs, ks, vs = q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1]
+        z = oracle_lib.quant_smooth(qs, ks, vs, oracle_lib.DT_BF16, qk_bits=bits)
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1], rng.integers(0, w.N, 60)]))
+        O_ref, slack, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=EPS_TIE)
+        _compare_o(O_gpu[h][rows], O_ref, slack, f"{w.name}/int{bits}/h{h}")
+        O_fp, _ = oracle_lib.attn_exact(qs, ks, vs, 1, True, w.scale, 0, rows=rows)
+        c_gpu, c_orc = gh.cos_sim(O_gpu[h][rows], O_fp), gh.cos_sim(O_ref, O_fp)
+        print(f"[{w.name}/int{bits}/h{h}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+        assert abs(c_gpu - c_orc) < 1e-3

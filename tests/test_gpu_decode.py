@@ -96,3 +96,29 @@ def test_decode_low_precision_outputs(oracle_lib):
         o = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=dt)
         torch.cuda.synchronize()
         assert torch.equal(o, ref.to(dt))
+
+
+def test_decode_full_size(oracle_lib):
+    """The benchmark's decoding workload and launch (B16, 32 query heads on 8
+    K/V heads, 8192 keys, the library's key ranges): every output row against
+    the oracle's mirror with the same ranges."""
+    import torch
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    w = wl.DECODE
+    q, k, v = wl.generate(w)
+    split = sage.decode_split_keys(w.B, w.H, w.hkv, w.nk, w.D)
+    qd, kd, vd = (gh.to_device(a, w.dtype) for a in (q, k, v))
+    out = sage.attn_decode(qd, kd, vd, sm_scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O_gpu = out.cpu().numpy().reshape(-1, w.D)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16)
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, False, w.scale, eps=EPS_TIE, kv_split=split)
+    err = np.abs(O_gpu.astype(np.float64) - O_ref).max(1)
+    bad = np.nonzero(~(err <= O_TOL + slack))[0]
+    print(f"[{w.name}] split={split} rows={err.size} maxerr={err.max():.3e}")
+    assert bad.size == 0, (bad[:5], err[bad[:5]])
+    O_fp, _ = oracle_lib.attn_exact(q, k, v, 1, False, w.scale, 0)
+    c_gpu, c_orc = gh.cos_sim(O_gpu, O_fp), gh.cos_sim(O_ref, O_fp)
+    print(f"[{w.name}] cos_sim gpu={c_gpu:.6f} oracle={c_orc:.6f}")
+    assert abs(c_gpu - c_orc) < 1e-4

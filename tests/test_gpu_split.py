@@ -1,0 +1,104 @@
+"""GPU parity of the full call with split key ranges (sage_attn_fwd_split).
+
+The oracle's mirror with the same key ranges (kv_split) is the reference: O
+within max-abs 2e-3 plus its FP8-midpoint slack; the prepass buffers at the
+front of the workspace bit-exact.  One range covering every key is the plain
+schedule, so it must reproduce sage_attn_fwd_cross bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from fp8_attention_transformer_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3
+EPS_TIE = 2.0 ** -14
+
+CASES = [
+    # (B, Hq, Hkv, Nq, Nk, D, causal, qk_bits, smooth_v, split_keys)
+    (1, 4, 2, 130, 1000, 128, True, 4, False, 256),
+    (2, 2, 2, 300, 300, 64, True, 8, True, 128),       # square self-attention, one block per range
+    (1, 6, 3, 64, 2000, 128, False, 4, False, 0),      # library's split
+    (1, 2, 1, 200, 777, 64, True, 4, True, 384),       # ragged last range
+    (1, 4, 4, 129, 129, 128, False, 8, False, 128),
+]
+
+
+def _id(c):
+    B, Hq, Hk, Nq, Nk, D, causal, bits, sv, sk = c
+    return f"b{B}hq{Hq}hkv{Hk}nq{Nq}nk{Nk}d{D}{'_c' if causal else ''}_int{bits}{'_sv' if sv else ''}_s{sk}"
+
+
+def _run(q, k, v, w, causal, bits, sv, sk):
+    import torch
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    qd, kd, vd = (gh.to_device(a, w.dtype) for a in (q, k, v))
+    out, ws_t = sage.attn_split(qd, kd, vd, causal=causal, sm_scale=w.scale, out_dtype=torch.float32, qk_bits=bits,
+                                smooth_v=sv, split_keys=sk)
+    torch.cuda.synchronize()
+    ws = sage.Workspace(ws_t, w.B, w.H, w.N, w.D, w.hkv, w.nk)
+    return out, ws
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_split_parity(oracle_lib, case):
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    B, Hq, Hk, Nq, Nk, D, causal, bits, sv, sk = case
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, causal=causal, seed=Nq + 11 * Nk, k_offset_std=3.0,
+                  v_offset_std=1.5, outlier_channels=2, outlier_scale=8.0)
+    q, k, v = wl.generate(w)
+    split = sk or sage.split_keys(B, Hq, Hk, Nq, Nk, D)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=bits, smooth_v=sv)
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, causal, w.scale, eps=EPS_TIE, kv_split=split)
+    out, ws = _run(q, k, v, w, causal, bits, sv, sk)
+    rb = gh.Readback(ws, qk_bits=bits)
+    fq = lambda a: a.reshape((B * Hq,) + a.shape[2:])
+    fk = lambda a: a.reshape((B * Hk,) + a.shape[2:])
+    for name in ("q_codes", "q_scale", "q_mean"):
+        assert np.array_equal(getattr(rb, name), fq(getattr(z, name))), name
+    for name in ("k_codes", "k_scale", "k_mean", "v_codes", "v_scale", "v_mean"):
+        assert np.array_equal(getattr(rb, name), fk(getattr(z, name))), name
+    O_gpu = out.cpu().numpy().reshape(-1, D)
+    err = np.abs(O_gpu.astype(np.float64) - O_ref).max(1)
+    bad = np.nonzero(~(err <= O_TOL + slack))[0]
+    print(f"[{_id(case)}] split={split} maxerr={err.max():.3e}")
+    assert bad.size == 0, (bad[:5], err[bad[:5]], slack[bad[:5]])
+
+
+def test_split_one_range_equals_cross(oracle_lib):
+    """A range covering every key is the plain schedule: bit-identical output."""
+    import gpu_helpers as gh
+    B, Hq, Hk, Nq, Nk, D = 2, 4, 2, 257, 700, 128
+    w = wl.custom(B, Hq, Nq, D, Hkv=Hk, Nk=Nk, causal=True, seed=81, k_offset_std=3.0)
+    q, k, v = wl.generate(w)
+    ref, _ = gh.run_attn(q, k, v, w.dtype, True, w.scale)
+    out, _ = _run(q, k, v, w, True, 4, False, 768)
+    assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy())
+
+
+def test_chunk_split_full_size(oracle_lib):
+    """The benchmark's chunked-prefill workload through the split call with the
+    library's ranges: sampled rows of the first and last query heads."""
+    import gpu_helpers as gh
+    from fp8_attention_transformer_amd import sage
+    w = wl.CHUNK
+    q, k, v = wl.generate(w)
+    split = sage.split_keys(w.B, w.H, w.hkv, w.N, w.nk, w.D)
+    out, _ = _run(q, k, v, w, True, 4, False, 0)
+    O_gpu = out.cpu().numpy().reshape(w.B * w.H, w.N, w.D)
+    g = w.H // w.hkv
+    rng = np.random.default_rng(8)
+    for h in (0, w.H - 1):
+        qs, ks, vs = q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1]
+        z = oracle_lib.quant_smooth(qs, ks, vs, oracle_lib.DT_BF16)
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1], rng.integers(0, w.N, 60)]))
+        O_ref, slack, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=EPS_TIE, kv_split=split)
+        err = np.abs(O_gpu[h][rows].astype(np.float64) - O_ref).max(1)
+        bad = np.nonzero(~(err <= O_TOL + slack))[0]
+        print(f"[{w.name}/split{split}/h{h}] maxerr={err.max():.3e}")
+        assert bad.size == 0, (h, rows[bad[:5]], err[bad[:5]])
