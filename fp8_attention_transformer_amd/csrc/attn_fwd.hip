@@ -3,7 +3,11 @@
 // Method (SageAttention2 abstract, arXiv 2411.10958 page): INT4 QK^T with
 // fine-grained scales, online softmax, FP8 P~ and V, and a two-level
 // accumulation of P~V (a per-block partial in a fresh FP32 buffer, then added
-// into an FP32 running buffer).
+// into an FP32 running buffer).  The two levels exist because FP8 tensor
+// cores elsewhere accumulate in reduced precision; the gfx950 FP8 matrix core
+// accumulates in fp32, so here the running buffer is rescaled by alpha and the
+// block's products are accumulated into it by the matrix core directly (same
+// precision; the fp32 rounding order differs from the separate partial).
 //
 // gfx950 mapping.  A workgroup owns one 128-query block of one head (4 waves x
 // 32 queries).  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
@@ -216,8 +220,8 @@ struct AttnState {
 // The three parts of one 128-key block for this wave.  qk_part: S^T tiles
 // (exact integer dot products as floats).  softmax_part: dequantization into
 // the log2 domain, masking, online-softmax update, P~ -> e4m3 matrix-core
-// operands.  pv_part: two-level P~V (a fresh FP32 partial R per d-tile, then
-// O = alpha*O + R).
+// operands.  pv_part: O = alpha*O, then O += P~V on the FP8 matrix core (fp32
+// accumulation into the running buffer).
 template <int D, int BITS>
 __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, const uint8_t* cK, int n, int h) {
 #pragma unroll
@@ -309,19 +313,16 @@ __device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8,
 #pragma unroll
   for (int dt = 0; dt < D / 32; dt++) {
     const int row = 32 * dt + n;
-    v16f R;
 #pragma unroll
-    for (int r = 0; r < 16; r++) R[r] = 0.0f;
+    for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
 #pragma unroll
     for (int kh = 0; kh < 2; kh++) {
       const int c0 = 4 * kh + 2 * h;
       const v4i lo = *(const v4i*)(cV + row * kBK + 16 * (c0 ^ vswz(row)));
       const v4i hi = *(const v4i*)(cV + row * kBK + 16 * ((c0 + 1) ^ vswz(row)));
       const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      R = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], R, 0, 0, 0, 0, 0, 0);
+      as.O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], as.O[dt], 0, 0, 0, 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 16; r++) as.O[dt][r] = __builtin_fmaf(alpha, as.O[dt][r], R[r]);
   }
 }
 
