@@ -183,12 +183,6 @@ __device__ __forceinline__ uint32_t v_src_offset(int wave, int lane) {
   return (uint32_t)(r * kBK + 16 * c - 1024 * wave);
 }
 
-// Buffer resource over one head's array: raw addressing, `bytes` records (the
-// hardware returns zeros beyond them), default gfx9 data format word.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // The copies use buffer loads straight to LDS: the per-lane offset is one VGPR
 // and block, round and wave offsets stay scalar.
 template <int D, int BITS>
@@ -343,14 +337,6 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
   if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
 }
 
-
-// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // SPLIT: workgroup (head, key range, query block) runs the method over one
 // range of key blocks from an empty state and writes its unnormalised state

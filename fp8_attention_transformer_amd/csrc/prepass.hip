@@ -17,6 +17,8 @@
 #include "sage_internal.h"
 #include "sage_device.h"
 
+#include <type_traits>
+
 namespace sage {
 namespace {
 
@@ -158,11 +160,9 @@ __device__ __forceinline__ int vperm_key(int p) {
   return 64 * (p >> 6) + 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * ((p & 63) >> 5) + (s & 3);
 }
 
-// 16 consecutive 16-bit inputs (32 bytes) -> fp32
+// 16 consecutive 16-bit inputs (two 16-byte words) -> fp32
 template <int IN>
-__device__ __forceinline__ void load16(const uint16_t* p, float* x) {
-  const v4i a = *(const v4i*)p;
-  const v4i c = *(const v4i*)(p + 8);
+__device__ __forceinline__ void cvt16(const v4i a, const v4i c, float* x) {
 #pragma unroll
   for (int w = 0; w < 4; w++) {
     x[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)a[w] & 0xFFFF));
@@ -174,28 +174,34 @@ __device__ __forceinline__ void load16(const uint16_t* p, float* x) {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> their three-piece bf16 splits x = p1 + p2 + p3, each
+// piece rounded to nearest even from the residual of the ones before
+// (v_cvt_pk_bf16_f32 converts a pair per instruction).
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) {   // low bf16 of a packed word, as fp32
+  // byte permute (0x0c: zero byte): [0, 0, b0, b1]; a plain shift would be
+  // rewritten by the compiler into a second conversion of the low value
+  return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu));
 }
-__device__ __forceinline__ void split3(float x, uint32_t& a, uint32_t& bb, uint32_t& c) {
-  a = bf16_rne_bits(x);
-  const float r1 = x - __uint_as_float(a << 16);
-  bb = bf16_rne_bits(r1);
-  const float r2 = r1 - __uint_as_float(bb << 16);
-  c = bf16_rne_bits(r2);
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ void split3x2(float x0, float x1, uint32_t& p1, uint32_t& p2, uint32_t& p3) {
+  p1 = __builtin_bit_cast(uint32_t, v2bf{(__bf16)x0, (__bf16)x1});
+  const float r0 = x0 - bf16_lo_f32(p1), r1 = x1 - bf16_hi_f32(p1);
+  p2 = __builtin_bit_cast(uint32_t, v2bf{(__bf16)r0, (__bf16)r1});
+  const float t0 = r0 - bf16_lo_f32(p2), t1 = r1 - bf16_hi_f32(p2);
+  p3 = __builtin_bit_cast(uint32_t, v2bf{(__bf16)t0, (__bf16)t1});
 }
 // 8 fp32 values -> three v8bf operands
 __device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf& p3) {
   v4i w1, w2, w3;
 #pragma unroll
   for (int e = 0; e < 4; e++) {
-    uint32_t a0, b0, c0, a1, b1, c1;
-    split3(x[2 * e], a0, b0, c0);
-    split3(x[2 * e + 1], a1, b1, c1);
-    w1[e] = (int)(a0 | (a1 << 16));
-    w2[e] = (int)(b0 | (b1 << 16));
-    w3[e] = (int)(c0 | (c1 << 16));
+    uint32_t a, bb, c;
+    split3x2(x[2 * e], x[2 * e + 1], a, bb, c);
+    w1[e] = (int)a;
+    w2[e] = (int)bb;
+    w3[e] = (int)c;
   }
   p1 = __builtin_bit_cast(v8bf, w1);
   p2 = __builtin_bit_cast(v8bf, w2);
@@ -292,6 +298,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
   constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
   __shared__ __align__(16) uint16_t sV[DO_KV ? kBK * D : 8];
+  __shared__ __align__(16) float sKM[DO_KV ? D : 4];   // K means of the head
   // packed [T, H, D] inputs: grid (B*H, NQB), heads of a token block adjacent
   const int qb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -303,18 +310,57 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   const size_t qrowp = (size_t)bh * d.NP;    // first padded query row of this head
   const size_t krowp = (size_t)bh * d.NPk;   // first padded key row of this head
 
-  // ---- V block -> LDS (rows >= Nk are zero)
-  if constexpr (DO_KV)
-    for (int e = tid; e < kBK * D / 8; e += 256) {
+  // Every global load of the block is issued up front (one memory round
+  // trip): V by direct copies into LDS, this thread's Q and K rows into
+  // registers.  Rows past the head's tokens load its last row instead; Q and
+  // K zero them below, the V codes mask them by key.
+  const int nlast = io.n - 1;
+  const bool ragged = i0 + kBQ > io.n;   // the block holds rows past the head's tokens
+  constexpr int LPT = D / 16, TPP = 256 / LPT, NQP = kBQ / TPP;   // Q: lanes per token, tokens per pass, passes
+  constexpr int LPK = D / 32, LPG = 16 * LPK;                      // K: lanes per key / per scale group
+  constexpr int GPW = 64 / LPG, NKI = kBK / kKGroup / (4 * GPW);   // K: groups per wave, rounds
+  if constexpr (DO_KV) {
+    constexpr int VPT = kBK * D / 8 / 256;   // 16-byte chunks per thread
+#pragma unroll
+    for (int p = 0; p < VPT; p++) {
+      const int wbase = 256 * p + 64 * wave, e = wbase + lane;
       const int r = e / (D / 8), c8 = e % (D / 8);
-      v4i val = {0, 0, 0, 0};
-      if (i0 + r < io.n) val = *(const v4i*)(v + io.base + (size_t)(i0 + r) * io.stride + 8 * c8);
-      *(v4i*)(sV + r * D + 8 * c8) = val;
+      const uint16_t* src = v + io.base + (size_t)min(i0 + r, nlast) * io.stride + 8 * c8;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(sV + 8 * wbase), 16,
+                                       0, 0);
     }
+    if (wave == 0 && lane < D / 4)
+      __builtin_amdgcn_global_load_lds((const void*)(b.k_mean + (size_t)bh * D + 4 * lane),
+                                       (__attribute__((address_space(3))) void*)sKM, 16, 0, 0);
+  }
+  // V scale and mean of this thread's channel in the FP8 step (ch = tid mod D)
+  const float dv_ch = DO_KV ? b.v_scale[(size_t)bh * D + tid % D] : 0.0f;
+  const float vbar_ch = DO_KV ? b.v_mean[(size_t)bh * D + tid % D] : 0.0f;   // 0 without V smoothing
+  v4i qraw[DO_Q ? NQP : 1][2];
+  if constexpr (DO_Q) {
+    const int c0 = 16 * (tid % LPT);
+#pragma unroll
+    for (int p = 0; p < NQP; p++) {
+      const uint16_t* src = q + io.base + (size_t)min(i0 + tid / LPT + TPP * p, nlast) * io.stride + c0;
+      qraw[p][0] = *(const v4i*)src;
+      qraw[p][1] = *(const v4i*)(src + 8);
+    }
+  }
+  v4i kraw[DO_KV ? NKI : 1][4];
+  if constexpr (DO_KV) {
+    const int c0 = 32 * (lane % LPK), ki = (lane % LPG) / LPK;
+#pragma unroll
+    for (int it = 0; it < NKI; it++) {
+      const int grp = wave * GPW + lane / LPG + 4 * GPW * it, T = grp >> 1, hh = grp & 1;
+      const int j = i0 + 32 * T + 8 * (ki >> 2) + 4 * hh + (ki & 3);
+      const uint16_t* src = k + io.base + (size_t)min(j, nlast) * io.stride + c0;
+#pragma unroll
+      for (int w = 0; w < 4; w++) kraw[it][w] = *(const v4i*)(src + 8 * w);
+    }
+  }
 
   // ---- Q: LPT lanes per token, 16 channels per lane
   if constexpr (DO_Q) {
-    constexpr int LPT = D / 16, TPP = 256 / LPT;
     const int sub = tid % LPT, c0 = 16 * sub;
     float qm[16];
 #pragma unroll
@@ -326,24 +372,24 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       uint16_t* p12 = (uint16_t*)b.k_part + ((size_t)bh * d.NQB + qb) * 2 * D;
       uint16_t* p3s = (uint16_t*)b.v_part + ((size_t)bh * d.NQB + qb) * D;
 #pragma unroll
-      for (int e = 0; e < 16; e++) {
+      for (int e = 0; e < 16; e += 2) {
         uint32_t p1, p2, p3;
-        split3(qm[e], p1, p2, p3);
-        p12[c0 + e] = (uint16_t)p1;
-        p12[D + c0 + e] = (uint16_t)p2;
-        p3s[c0 + e] = (uint16_t)p3;
+        split3x2(qm[e], qm[e + 1], p1, p2, p3);
+        *(uint32_t*)(p12 + c0 + e) = p1;
+        *(uint32_t*)(p12 + D + c0 + e) = p2;
+        *(uint32_t*)(p3s + c0 + e) = p3;
       }
     }
-    for (int r = tid / LPT; r < kBQ; r += TPP) {
-      const int i = i0 + r;
+#pragma unroll
+    for (int p = 0; p < NQP; p++) {
+      const int i = i0 + tid / LPT + TPP * p;
       float g[16];
-      if (i < io.n) {
-        load16<IN>(q + io.base + (size_t)i * io.stride + c0, g);
+      cvt16<IN>(qraw[p][0], qraw[p][1], g);
 #pragma unroll
-        for (int e = 0; e < 16; e++) g[e] = g[e] - qm[e];
-      } else {
+      for (int e = 0; e < 16; e++) g[e] = g[e] - qm[e];
+      if (ragged) {
 #pragma unroll
-        for (int e = 0; e < 16; e++) g[e] = 0.0f;
+        for (int e = 0; e < 16; e++) g[e] = i < io.n ? g[e] : 0.0f;
       }
       float amax = 0.0f;
 #pragma unroll
@@ -389,25 +435,31 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   // ---- K: a group (T, hh) holds keys 32T + 8u + 4hh + w (u, w in 0..3);
   //      LPK lanes per key, 32 channels per lane.
   if constexpr (DO_KV) {
-    constexpr int LPK = D / 32, LPG = 16 * LPK;          // lanes per key / per group
-    constexpr int GPW = 64 / LPG;                          // groups per wave
     const int sub = lane % LPK, c0 = 32 * sub;
     const int ki = (lane % LPG) / LPK;
+    wait_vmcnt<0>();   // the V and K-mean copies (and this thread's loads) have landed
+    __syncthreads();
     float km[32];
 #pragma unroll
-    for (int e = 0; e < 32; e++) km[e] = b.k_mean[(size_t)bh * D + c0 + e];
-    for (int grp = wave * GPW + lane / LPG; grp < kBK / kKGroup; grp += 4 * GPW) {
-      const int T = grp >> 1, hh = grp & 1;
+    for (int e = 0; e < 32; e += 4) {
+      const float4 m = *(const float4*)(sKM + c0 + e);
+      km[e] = m.x;
+      km[e + 1] = m.y;
+      km[e + 2] = m.z;
+      km[e + 3] = m.w;
+    }
+#pragma unroll
+    for (int it = 0; it < NKI; it++) {
+      const int grp = wave * GPW + lane / LPG + 4 * GPW * it, T = grp >> 1, hh = grp & 1;
       const int j = i0 + 32 * T + 8 * (ki >> 2) + 4 * hh + (ki & 3);
       float g[32];
-      if (j < io.n) {
-        load16<IN>(k + io.base + (size_t)j * io.stride + c0, g);
-        load16<IN>(k + io.base + (size_t)j * io.stride + c0 + 16, g + 16);
+      cvt16<IN>(kraw[it][0], kraw[it][1], g);
+      cvt16<IN>(kraw[it][2], kraw[it][3], g + 16);
 #pragma unroll
-        for (int e = 0; e < 32; e++) g[e] = g[e] - km[e];
-      } else {
+      for (int e = 0; e < 32; e++) g[e] = g[e] - km[e];
+      if (ragged) {
 #pragma unroll
-        for (int e = 0; e < 32; e++) g[e] = 0.0f;
+        for (int e = 0; e < 32; e++) g[e] = j < io.n ? g[e] : 0.0f;
       }
       float amax = 0.0f;
 #pragma unroll
@@ -454,22 +506,25 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       if ((lane % LPG) == 0) b.k_scale[krowp / kKGroup + (i0 / kKGroup) + grp] = dk;
     }
   }
-  // ---- V: 16-key chunks of one channel -> 16 FP8 bytes
+  // ---- V: 16-key chunks of one channel -> 16 FP8 bytes (channel tid mod D,
+  //      chunks tid / D + (256 / D) i); the block is in LDS since the K step
   if constexpr (DO_KV) {
-    __syncthreads();
+    static_assert(256 % D == 0, "whole channels per pass");
     uint8_t* vout = b.v_codes + ((size_t)bh * d.NQBk + qb) * D * kBK;
-    for (int e = tid; e < D * 8; e += 256) {
-      const int ch = e % D, c = e / D;
-      const float dv = b.v_scale[(size_t)bh * D + ch];
-      const float vbar = b.v_mean[(size_t)bh * D + ch];   // 0 without V smoothing
+    const int ch = tid % D;
+#pragma unroll
+    for (int c = tid / D; c < kBK / 16; c += 256 / D) {
+      uint16_t raw[16];
+#pragma unroll
+      for (int u = 0; u < 16; u++) raw[u] = sV[vperm_key(16 * c + u) * D + ch];
       float x[16];
 #pragma unroll
       for (int u = 0; u < 16; u++) {
         // padding keys stay exactly zero (also when V is smoothed)
         const int key = vperm_key(16 * c + u);
-        x[u] = i0 + key < io.n ? in_to_f32<IN>(sV[key * D + ch]) - vbar : 0.0f;
+        x[u] = i0 + key < io.n ? in_to_f32<IN>(raw[u]) - vbar_ch : 0.0f;
       }
-      fp8_quotients<16>(x, dv);
+      fp8_quotients<16>(x, dv_ch);
       v4i pk;
 #pragma unroll
       for (int w = 0; w < 4; w++) pk[w] = (int)fp8x4(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
@@ -486,7 +541,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 // products x_a*y_b with a + b <= 4 are accumulated in fp32, which reproduces
 // an fp32 dot product to within a few units in the last place.
 template <int IN, int D>
-__global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
+__global__ void __launch_bounds__(256, 3) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
   constexpr int NK = D / 16;   // k-steps of the 32x32x16 bf16 MFMA
   const int kb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
@@ -520,34 +575,46 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
                                        0, 0);
     }
   };
-  // the first Q tile streams into LDS while this lane's keys load and split
+  // The first Q tile and the K means stream into LDS while this lane's key
+  // row loads: all eight 16-byte chunks at once, from a valid row (keys past
+  // the head read its last row and are zeroed below).
+  __shared__ __align__(16) float sM[D];
   stage(0, sA0);
-  // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel 16kk + 8h + s)
-  v8bf B1[NK], B2[NK], B3[NK];
+  if (tid < D) sM[tid] = km[tid];
+  const bool valid = j < io.n, ragged = kb * kBK + kBK > io.n;   // ragged: this block has keys past the head
+  const uint16_t* krow = k + io.base + (size_t)min(j, io.n - 1) * io.stride + 8 * h;
+  v4i raw[NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; kk++) {
-    const int c0 = 16 * kk + 8 * h;
-    const float4 m0 = *(const float4*)(km + c0);
-    const float4 m1 = *(const float4*)(km + c0 + 4);
-    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float g[8];
-    if (j < io.n) {
-      const v4i raw = *(const v4i*)(k + io.base + (size_t)j * io.stride + c0);
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] & 0xFFFF)) - mv[2 * w];
-        g[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[w] >> 16)) - mv[2 * w + 1];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; e++) g[e] = 0.0f;
-    }
-    split8(g, B1[kk], B2[kk], B3[kk]);
-  }
-  float* out = b.delta_s + (size_t)bh * d.NQB * d.NPk + j;
+  for (int kk = 0; kk < NK; kk++) raw[kk] = *(const v4i*)(krow + 16 * kk);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = 0, it = 0; qt < nqb; qt += 32, it++) {
+  // B operands: gamma(K) pieces for all k-steps (slot s of step kk = channel
+  // 16kk + 8h + s), built during the first Q tile just before the k-step that
+  // uses them, so this VALU work overlaps the tile's matrix-core work.
+  v8bf B1[NK], B2[NK], B3[NK];
+  auto build_b = [&](int kk) {
+    const int c0 = 16 * kk + 8 * h;
+    const float4 m0 = *(const float4*)(sM + c0);
+    const float4 m1 = *(const float4*)(sM + c0 + 4);
+    const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float g[8];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      g[2 * w] = in_to_f32<IN>((uint16_t)((uint32_t)raw[kk][w] & 0xFFFF)) - mv[2 * w];
+      g[2 * w + 1] = in_to_f32<IN>((uint16_t)((uint32_t)raw[kk][w] >> 16)) - mv[2 * w + 1];
+    }
+    if (ragged) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[e] = valid ? g[e] : 0.0f;
+    }
+    split8(g, B1[kk], B2[kk], B3[kk]);
+  };
+  // Output rows [NQB][NPk] of this head through one buffer resource: a 32-bit
+  // per-lane offset (key, and the row half h) instead of a 64-bit address per
+  // store; the row of each store is a scalar offset.  Every store is in range.
+  const __amdgpu_buffer_rsrc_t ro = head_rsrc(b.delta_s + (size_t)bh * d.NQB * d.NPk, (uint32_t)d.NQB * d.NPk * 4);
+  const uint32_t obase = ((uint32_t)(4 * h) * d.NPk + j) * 4;
+  auto tile = [&](int qt, int it, auto first) {
     const bool more = qt + 32 < nqb;
     if (more) stage(qt + 32, (it & 1) ? sA0 : sA1);
     const uint16_t* A = (it & 1) ? sA1 : sA0;
@@ -556,6 +623,7 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
     for (int r = 0; r < 16; r++) acc[r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NK; kk++) {
+      if constexpr (decltype(first)::value) build_b(kk);
       const int c = (2 * kk + h) ^ (n & (CPR - 1));
       const v8bf A1 = __builtin_bit_cast(v8bf, *(const v4i*)(A + (0 * 32 + n) * D + 8 * c));
       const v8bf A2 = __builtin_bit_cast(v8bf, *(const v4i*)(A + (1 * 32 + n) * D + 8 * c));
@@ -568,14 +636,35 @@ __global__ void __launch_bounds__(256) delta_s_kernel(const uint16_t* __restrict
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B2[kk], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1[kk], acc, 0, 0, 0);
     }
+    if (more) {
+      // A whole tile: exactly 16 stores, issued after the next tile's copies.
+      // The wait below lets those stores stay in flight and holds only for
+      // the copies (the counter retires in issue order).
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int q2 = qt + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (q2 < d.NQB) out[(size_t)q2 * d.NPk] = acc[r];
+      for (int r = 0; r < 16; r++) {
+        const uint32_t row = (uint32_t)(qt + 8 * (r >> 2) + (r & 3));
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, 0);
+      }
+      wait_vmcnt<16>();
+      // A bare barrier: the release fence of __syncthreads() would wait for
+      // every outstanding store as well.  Every LDS read of this tile has
+      // returned (its matrix-core instructions consumed them), and the memory
+      // clobber keeps the compiler from moving LDS accesses across it.
+      asm volatile("s_barrier" ::: "memory");
+    } else {
+      // the last tile (possibly partial): rows past the head's query blocks are not stored
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int q2 = qt + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (q2 < nqb) {
+          const uint32_t row = (uint32_t)(qt + 8 * (r >> 2) + (r & 3));
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, 0);
+        }
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  };
+  tile(0, 0, std::true_type{});
+  for (int qt = 32, it = 1; qt < nqb; qt += 32, it++) tile(qt, it, std::false_type{});
 }
 
 __global__ void fp8_encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out, size_t n) {

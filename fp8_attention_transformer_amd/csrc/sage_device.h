@@ -66,4 +66,20 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Buffer resource over one head's array: raw addressing, `bytes` records (the
+// hardware returns zeros beyond them), default gfx9 data format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at
+// max).  On gfx9 the counter retires loads and stores in issue order, so
+// vmcnt(n) means: all but the last n vector-memory instructions are done.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace sage
