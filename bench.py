@@ -216,10 +216,10 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
 
 def run_decode(w, steps: int, warmup: int, smooth_v: bool = False):
     """A decoding step (one query token per head, Nq = 1) through sage_attn_decode:
-    K/V statistics, split-key attention, merge.  Memory-bound: the roofline is
-    HBM bandwidth over the step's algorithmic bytes, the 16-bit K and V read
-    twice (the statistics must see every key before any key is quantized) plus
-    q read and o written."""
+    V statistics, split-key attention, merge.  Memory-bound: the roofline is
+    HBM bandwidth over the step's algorithmic bytes, the 16-bit V read twice
+    (its statistics must see every value before any is quantized), the 16-bit
+    K read once (the scores need no K mean), q read and o written."""
     import numpy as np
     import torch
 
@@ -251,8 +251,8 @@ def run_decode(w, steps: int, warmup: int, smooth_v: bool = False):
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / steps
-    kv_bytes = 2 * B * Hk * Nk * D * 2
-    alg_bytes = 2 * kv_bytes + 2 * B * H * D * 2
+    head_bytes = B * Hk * Nk * D * 2          # one 16-bit K or V tensor
+    alg_bytes = 3 * head_bytes + 2 * B * H * D * 2
     gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
     value = w.ops / (ms_per_step * 1e-3) / 1e12
     return {

@@ -158,8 +158,6 @@ __device__ __forceinline__ int kswz(int r) {
 }
 __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // Direct HBM/L2 -> LDS copy of one 128-key block: K codes and FP8 V.  Lane l
 // of a wave writes LDS chunk (wave base + l); it fetches the global chunk whose
 // swizzled position that is.  Chunk e = 256*i + 64*wave + lane of either array

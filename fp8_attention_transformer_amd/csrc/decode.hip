@@ -8,13 +8,19 @@
 // so the block mean is the query itself: the smoothed query is zero, its
 // codes and scale are zero, and the score of key j is exactly the
 // compensation term DeltaS_j = q . (K_j - mean K) (the integer part
-// contributes fma(0, 0, DeltaS)).  Key codes are therefore never needed; the
-// kernel evaluates DeltaS in fp32 straight from the 16-bit keys.
+// contributes fma(0, 0, DeltaS)).  Key codes are therefore never needed.
+// DeltaS_j = q . K_j - q . mean K, and the second term is one constant per
+// query head: the softmax cancels it (the same invariance that lets the
+// method smooth K at all).  The kernel therefore scores q . K_j in fp32
+// straight from the 16-bit keys, with no K mean: every running maximum (and
+// every range maximum of the merge) moves by that constant, and the
+// max-subtracted exponents, P~, the row sums and O are those of the method
+// up to fp32 rounding.
 //
-// Memory-bound layout.  The prepass statistics (K channel means, V channel
-// means and scales) need every key, so a decoding step streams K and V twice:
-// the statistics kernels of the prepass, then this kernel, which reads K and V
-// once more in 16-bit form and never writes codes.  Parallelism comes from
+// Memory-bound layout.  The V statistics (channel means and scales) need
+// every value, so a decoding step streams V twice and K once: the statistics
+// kernel of the prepass over V alone, then this kernel, which reads K and V
+// in 16-bit form and never writes codes.  Parallelism comes from
 // splitting the keys: workgroup (split, K/V head) runs the online softmax of
 // all query heads of its group over one key range with its own running
 // maximum (the split-key schedule); a second kernel merges the ranges.
@@ -40,8 +46,7 @@ struct DecodeArgs {
   const uint16_t* q;   // [B, Hq, D]
   const uint16_t* k;   // [B, Hk, Nk, D]
   const uint16_t* v;
-  const float* k_mean;   // [B*Hk, D]
-  const float* v_scale;
+  const float* v_scale;   // [B*Hk, D]
   const float* v_mean;
   float* part_o;    // [B*Hq, S, D]  per-range unnormalised outputs
   float* part_ml;   // [B*Hq, S, 2]  per-range running maximum (log2 domain) and row sum
@@ -115,8 +120,8 @@ __device__ __forceinline__ void fp8x2_decode(uint32_t w, float& a, float& b) {
 // (V - vmean) / vscale for 8 channels with their own scales, bit-identical to
 // a true division per element: reciprocal multiply unless, in some lane of the
 // wave, a quotient lies within 8 ulps of an e4m3 rounding midpoint (its low
-// 20 bits within 8 of 0x80000) or is nonzero below the e4m3 normal range
-// (2^-6) -- then true divisions for the whole wave.
+// 20 bits within 8 of 0x80000) or below the e4m3 normal range (|y| < 2^-6,
+// zero included: one compare) -- then true divisions for the whole wave.
 __device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const float* dv) {
   bool amb = false;
   float y[8];
@@ -124,9 +129,8 @@ __device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const
   for (int e = 0; e < 8; e++) {
     y[e] = x[e] * rdv[e];
     const uint32_t bits = __float_as_uint(y[e]);
-    const uint32_t mag = bits & 0x7FFFFFFFu;
     amb |= ((bits - 0x7FFF8u) & 0xFFFFFu) <= 16u;   // near a midpoint (sign bit is above bit 19)
-    amb |= mag - 1u < 0x3C7FFFFFu;                 // 0 < |y| < 2^-6
+    amb |= fabsf(y[e]) < 0x1p-6f;
   }
   if (__any(amb)) {
 #pragma unroll
@@ -134,6 +138,18 @@ __device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const
   }
 #pragma unroll
   for (int e = 0; e < 8; e++) x[e] = y[e];
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi over packed 16-bit pairs (bf16 or fp16), the
+// products exact in fp32
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+template <int IN>
+__device__ __forceinline__ float dot2(int a, int b, float acc) {
+  if constexpr (IN == kBF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf_t, a), __builtin_bit_cast(v2bf_t, b), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h_t, a), __builtin_bit_cast(v2h_t, b), acc, false);
 }
 
 template <int IN>
@@ -146,9 +162,21 @@ __device__ __forceinline__ void decode8(const v4i& raw, float* x) {
 }
 
 // grid (S key ranges, B*Hk*hgroups), 512 threads (8 waves, two per SIMD);
-// HG <= 4 query heads per workgroup.  The keys and values of block t+1 are
-// loaded into registers while block t is processed.
+// HG <= 4 query heads per workgroup.  A range is processed in chunks of up to
+// kChunkBlocks key blocks, each in four phases separated by barriers:
+//  S  scores of every block of the chunk into LDS;
+//  M  the maximum of each (head, block), one wave per pair;
+//  E  per (head, block): the running maximum after that block (from the
+//     carried maximum and the block maxima before it, exactly the online
+//     recurrence), alpha, p' = exp2(s - m + log2 448), its FP8 rounding
+//     (decoded in place of the score) and the block's row sum;
+//  V  FP8 codes of V on the fly, O = alpha*O, then O += P~ V block by block;
+//     one thread per head carries the running maximum and l' = alpha*l' +
+//     rowsum into the next chunk.
+// K (phase S) and V (phase V) stream through registers, the next block's
+// rows loading while one is processed.
 constexpr int kThreads = 512;
+constexpr int kChunkBlocks = 8;
 
 template <int IN, int D, int HG>
 __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
@@ -157,11 +185,15 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   constexpr int KG = kThreads / CG;    // key groups per block
   constexpr int KPG = kBK / KG;        // keys per group: 4 (D = 128) or 2 (D = 64)
   constexpr int NW = kThreads / 64;
-  __shared__ float sP[HG][kBK];        // scores, then decoded FP8 P~
-  __shared__ float sAlpha[HG];
-  __shared__ __align__(16) float sRed[NW][HG][D];
+  constexpr int ROWB = 2 * D;          // bytes per 16-bit row
+  constexpr int CB = kChunkBlocks, CK = CB * kBK;
+  static_assert(NW * D <= CK, "the final reduction fits the score buffer");
+  __shared__ float sS[HG][CK];         // scores, then decoded FP8 P~; at the end the cross-wave sums
+  __shared__ float sBmax[HG][CB], sAlpha[HG][CB], sRs[HG][CB];
+  __shared__ float sM[HG], sL[HG];     // carried running maximum and row sum per head
+  __shared__ float sDV[D], sRDV[D], sVB[D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cg = lane % CG, kg = tid / CG;
   const int split = blockIdx.x;
   const int hgrp = blockIdx.y % a.hgroups, bhk = blockIdx.y / a.hgroups;
@@ -174,69 +206,52 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   const int nkb = (a.Nk + kBK - 1) / kBK;
   const int t0 = split * a.split_blocks, t1 = min(nkb, t0 + a.split_blocks);
 
-  // per-thread constants for channels c = 8cg + e; the V scales themselves
-  // (needed only on the exact-division path) stay in LDS
-  __shared__ float sDV[D];
-  if (tid < D) sDV[tid] = a.v_scale[(size_t)bhk * D + tid];
-  float kbar[8], vbar[8], rdv[8], qv[HG][8];
-#pragma unroll
-  for (int e = 0; e < 8; e++) {
-    const int c = 8 * cg + e;
-    kbar[e] = a.k_mean[(size_t)bhk * D + c];
-    vbar[e] = a.v_mean[(size_t)bhk * D + c];
-    const float dv = a.v_scale[(size_t)bhk * D + c];
-    rdv[e] = dv == 0.0f ? 0.0f : 1.0f / dv;
+  // V scale, its reciprocal and the V mean per channel (LDS: read per key)
+  if (tid < D) {
+    const float dv = a.v_scale[(size_t)bhk * D + tid];
+    sDV[tid] = dv;
+    sRDV[tid] = dv == 0.0f ? 0.0f : 1.0f / dv;
+    sVB[tid] = a.v_mean[(size_t)bhk * D + tid];
   }
-#pragma unroll
-  for (int h = 0; h < HG; h++) {
-    v4i raw = {0, 0, 0, 0};
-    if (h < nh) raw = *(const v4i*)(a.q + (size_t)(bhq0 + h) * D + 8 * cg);
-    decode8<IN>(raw, qv[h]);
+  if (tid < HG) {
+    sM[tid] = -__builtin_inff();
+    sL[tid] = 0.0f;
   }
   float O[HG][8];
 #pragma unroll
   for (int h = 0; h < HG; h++)
 #pragma unroll
     for (int e = 0; e < 8; e++) O[h][e] = 0.0f;
-  float m = -__builtin_inff(), l = 0.0f;   // state of head `wave` (waves < HG)
 
   // Buffer resources over this head's keys and values: rows at or past Nk
   // read as zeros, and so does the out-of-range offset used for blocks past
-  // the end of the range, so every load is unconditional and in order (the
-  // waits before each block then cover exactly that block's loads).
-  constexpr int ROWB = 2 * D;
+  // the end of a chunk, so every load is unconditional.
   const uint32_t head_bytes = (uint32_t)a.Nk * ROWB;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k + kvbase), (short)0, (int)head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v + kvbase), (short)0, (int)head_bytes, 0x00020000);
   const int lane_off = KPG * kg * ROWB + 16 * cg;
-  auto issue = [&](int t, v4i* kb, v4i* vb) {
-    const int base = t < t1 ? t * kBK * ROWB + lane_off : 0x7FFFFFF0;
+  auto issue = [&](__amdgpu_buffer_rsrc_t r, int t, int tend, v4i* buf) {
+    const int base = t < tend ? t * kBK * ROWB + lane_off : 0x7FFFFFF0;
 #pragma unroll
-    for (int kk = 0; kk < KPG; kk++) {
-      kb[kk] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rk, base + kk * ROWB, 0, 0));
-      vb[kk] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rv, base + kk * ROWB, 0, 0));
-    }
+    for (int kk = 0; kk < KPG; kk++)
+      buf[kk] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, base + kk * ROWB, 0, 0));
   };
 
-  auto process = [&](int t, const v4i* kc, const v4i* vc) {
-    // ---- scores: DeltaS_j * ks for the HG heads.  Partial dot products over
-    //      this thread's 8 channels, then the KPG*HG independent sums over the
-    //      CG lanes of each key, step by step (the chains hide each other's
-    //      DPP latency); the last lane of each group stores its keys' scores.
+  // ---- scores of block t (slot i of the chunk): partial dot products over
+  //      this thread's 8 channels, then the KPG*HG independent sums over the
+  //      CG lanes of each key, step by step (the chains hide each other's DPP
+  //      latency); the last lane of each group stores its keys' scores.
+  auto scores = [&](int t, int i, const v4i* kc, const v4i* qw) {
     float ps[KPG][HG];
 #pragma unroll
     for (int kk = 0; kk < KPG; kk++) {
-      float x[8];
-      decode8<IN>(kc[kk], x);
-#pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = x[e] - kbar[e];   // gamma(K) in fp32
 #pragma unroll
       for (int h = 0; h < HG; h++) {
         float p = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) p = __builtin_fmaf(qv[h][e], x[e], p);
+        for (int w = 0; w < 4; w++) p = dot2<IN>(qw[h][w], kc[kk][w], p);
         ps[kk][h] = p;
       }
     }
@@ -248,45 +263,42 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KPG; kk++)
           sc[kk] = (t * kBK + KPG * kg + kk < a.Nk) ? ps[kk][h] * a.ks : -__builtin_inff();
-        if constexpr (KPG == 4) *(float4*)&sP[h][KPG * kg] = make_float4(sc[0], sc[1], sc[2], sc[3]);
-        else *(float2*)&sP[h][KPG * kg] = make_float2(sc[0], sc[1]);
+        if constexpr (KPG == 4) *(float4*)&sS[h][i * kBK + KPG * kg] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        else *(float2*)&sS[h][i * kBK + KPG * kg] = make_float2(sc[0], sc[1]);
       }
     }
-    __syncthreads();
-    // ---- online softmax of head h by wave h: block max, rescale, p', FP8 P~, row sum
-    if (wave < HG) {
-      const int h = wave;
-      const float x0 = sP[h][2 * lane], x1 = sP[h][2 * lane + 1];
-      const float bmax = wave_max_dpp(fmaxf(x0, x1));
-      const float mnew = fmaxf(m, bmax);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      const float mm = mnew - kLog2_448;
-      const float p0 = __builtin_amdgcn_exp2f(x0 - mm), p1 = __builtin_amdgcn_exp2f(x1 - mm);
-      const float rs = wave_sum_dpp(p0 + p1);
-      l = alpha * l + rs;
-      m = mnew;
-      float q0, q1;
-      fp8x2_decode<false>(fp8x2(p0, p1), q0, q1);
-      sP[h][2 * lane] = q0;
-      sP[h][2 * lane + 1] = q1;
-      if (lane == 0) sAlpha[h] = alpha;
+  };
+
+  // ---- P~V of block t (slot i): O = alpha*O, then V -> FP8 codes of the
+  //      method (smoothed, per-channel scale) and O += P~ V over this
+  //      thread's keys (the one-level form: the block's products accumulate
+  //      into the rescaled running sum)
+  auto pv = [&](int t, int i, const v4i* vc) {
+    const bool ragged = (t + 1) * kBK > a.Nk;   // the block holds keys past the end
+#pragma unroll
+    for (int h = 0; h < HG; h++) {
+      const float alpha = sAlpha[h][i];
+#pragma unroll
+      for (int e = 0; e < 8; e++) O[h][e] = O[h][e] * alpha;
     }
-    __syncthreads();
-    // ---- P~V: V -> FP8 codes of the method (smoothed, per-channel scale),
-    //      level-1 partial R over this thread's keys, then O = alpha*O + R
-    float R[HG][8];
+    float vbar[8], rdv[8];
 #pragma unroll
-    for (int h = 0; h < HG; h++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) R[h][e] = 0.0f;
+    for (int e = 0; e < 8; e += 4) {
+      *(float4*)&vbar[e] = *(const float4*)&sVB[8 * cg + e];
+      *(float4*)&rdv[e] = *(const float4*)&sRDV[8 * cg + e];
+    }
 #pragma unroll
     for (int kk = 0; kk < KPG; kk++) {
       const int key = KPG * kg + kk;
       float x[8];
       decode8<IN>(vc[kk], x);
-      const bool valid = t * kBK + key < a.Nk;
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = valid ? x[e] - vbar[e] : 0.0f;
+      for (int e = 0; e < 8; e++) x[e] = x[e] - vbar[e];
+      if (ragged) {   // padding keys stay exactly zero
+        const bool valid = t * kBK + key < a.Nk;
+#pragma unroll
+        for (int e = 0; e < 8; e++) x[e] = valid ? x[e] : 0.0f;
+      }
       fp8_quotients8(x, rdv, sDV + 8 * cg);
       float vq[8];
 #pragma unroll
@@ -297,28 +309,82 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < HG; h++) {
-        const float p = sP[h][key];
+        const float p = sS[h][i * kBK + key];
 #pragma unroll
-        for (int e = 0; e < 8; e++) R[h][e] = __builtin_fmaf(p, vq[e], R[h][e]);   // products of FP8 values are exact
+        for (int e = 0; e < 8; e++) O[h][e] = __builtin_fmaf(p, vq[e], O[h][e]);   // products of FP8 values are exact
       }
     }
-#pragma unroll
-    for (int h = 0; h < HG; h++) {
-      const float alpha = sAlpha[h];
-#pragma unroll
-      for (int e = 0; e < 8; e++) O[h][e] = __builtin_fmaf(alpha, O[h][e], R[h][e]);
-    }
-    __syncthreads();
   };
 
-  // two register buffers in turn: the next block loads while this one runs
-  v4i kA[KPG], vA[KPG], kB[KPG], vB[KPG];
-  issue(t0, kA, vA);
-  for (int t = t0; t < t1; t += 2) {
-    issue(t + 1, kB, vB);
-    process(t, kA, vA);
-    issue(t + 2, kA, vA);
-    if (t + 1 < t1) process(t + 1, kB, vB);
+  v4i kA[KPG], kB[KPG], vA[KPG], vB[KPG];
+  issue(rk, t0, t1, kA);
+  __syncthreads();   // sM, sL and the V constants
+  for (int tc = t0; tc < t1; tc += CB) {
+    const int te = min(t1, tc + CB), nb = te - tc;
+    // ---- S (kA holds block tc); the query rows are reloaded per chunk (they
+    //      would otherwise hold registers through the V phase)
+    {
+      v4i qw[HG];   // this thread's 8 query channels per head, packed pairs
+#pragma unroll
+      for (int h = 0; h < HG; h++) {
+        qw[h] = v4i{0, 0, 0, 0};
+        if (h < nh) qw[h] = *(const v4i*)(a.q + (size_t)(bhq0 + h) * D + 8 * cg);
+      }
+      for (int i = 0; i < nb; i += 2) {
+        issue(rk, tc + i + 1, te, kB);
+        scores(tc + i, i, kA, qw);
+        issue(rk, tc + i + 2, te, kA);
+        if (i + 1 < nb) scores(tc + i + 1, i + 1, kB, qw);
+      }
+    }
+    issue(rv, tc, te, vA);   // the chunk's first V block loads during M and E
+    __syncthreads();
+    // ---- M: block maxima, pairs (head p % HG, block p / HG) over the waves
+    for (int pr = wave; pr < HG * nb; pr += NW) {
+      const int h = pr % HG, i = pr / HG;
+      const float bmax = wave_max_dpp(fmaxf(sS[h][i * kBK + 2 * lane], sS[h][i * kBK + 2 * lane + 1]));
+      if (lane == 0) sBmax[h][i] = bmax;
+    }
+    __syncthreads();
+    // ---- E: running maximum after block i, alpha, FP8 P~ and row sum
+    for (int pr = wave; pr < HG * nb; pr += NW) {
+      const int h = pr % HG, i = pr / HG;
+      float mprev = sM[h];
+      for (int u = 0; u < i; u++) mprev = fmaxf(mprev, sBmax[h][u]);
+      const float mnew = fmaxf(mprev, sBmax[h][i]);
+      const float alpha = __builtin_amdgcn_exp2f(mprev - mnew);
+      const float mm = mnew - kLog2_448;
+      float* row = &sS[h][i * kBK + 2 * lane];
+      const float p0 = __builtin_amdgcn_exp2f(row[0] - mm), p1 = __builtin_amdgcn_exp2f(row[1] - mm);
+      const float rs = wave_sum_dpp(p0 + p1);
+      float q0, q1;
+      fp8x2_decode<false>(fp8x2(p0, p1), q0, q1);
+      row[0] = q0;
+      row[1] = q1;
+      if (lane == 0) {
+        sAlpha[h][i] = alpha;
+        sRs[h][i] = rs;
+      }
+    }
+    __syncthreads();
+    // ---- V; one thread per head carries the state into the next chunk
+    if (tid < HG) {
+      float m = sM[tid], l = sL[tid];
+      for (int i = 0; i < nb; i++) {
+        m = fmaxf(m, sBmax[tid][i]);
+        l = sAlpha[tid][i] * l + sRs[tid][i];
+      }
+      sM[tid] = m;
+      sL[tid] = l;
+    }
+    for (int i = 0; i < nb; i += 2) {
+      issue(rv, tc + i + 1, te, vB);
+      pv(tc + i, i, vA);
+      issue(rv, tc + i + 2, te, vA);
+      if (i + 1 < nb) pv(tc + i + 1, i + 1, vB);
+    }
+    issue(rk, te, t1, kA);   // the next chunk's first K block
+    __syncthreads();
   }
 
   // ---- sum the partial outputs of the key groups: inside the wave (lanes
@@ -332,25 +398,26 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       for (int o = CG; o < 64; o <<= 1) s = s + __shfl_xor(s, o);
       O[h][e] = s;
     }
+  float* sRed = &sS[0][0];   // [NW][HG][D]
   if (lane < CG) {
 #pragma unroll
     for (int h = 0; h < HG; h++)
 #pragma unroll
-      for (int e = 0; e < 8; e++) sRed[wave][h][8 * cg + e] = O[h][e];
+      for (int e = 0; e < 8; e++) sRed[(wave * HG + h) * D + 8 * cg + e] = O[h][e];
   }
   __syncthreads();
   for (int i = tid; i < HG * D; i += kThreads) {
     const int h = i / D, c = i % D;
     if (h < nh) {
-      float s = sRed[0][h][c];
+      float s = sRed[h * D + c];
 #pragma unroll
-      for (int w = 1; w < NW; w++) s = s + sRed[w][h][c];
+      for (int w = 1; w < NW; w++) s = s + sRed[(w * HG + h) * D + c];
       a.part_o[((size_t)(bhq0 + h) * a.S + split) * D + c] = s;
     }
   }
-  if (wave < nh && lane == 0) {
-    a.part_ml[((size_t)(bhq0 + wave) * a.S + split) * 2] = m;
-    a.part_ml[((size_t)(bhq0 + wave) * a.S + split) * 2 + 1] = l;
+  if (tid < nh) {
+    a.part_ml[((size_t)(bhq0 + tid) * a.S + split) * 2] = sM[tid];
+    a.part_ml[((size_t)(bhq0 + tid) * a.S + split) * 2 + 1] = sL[tid];
   }
 }
 
@@ -398,14 +465,13 @@ int decode_heads_per_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : 4; }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
                          const DecodeBufs& db, float ks, void* o, int out_dtype, hipStream_t s) {
-  hipError_t e = launch_kv_stats(k, v, in_dtype, d, b, s);
+  hipError_t e = launch_v_stats(v, in_dtype, d, b, s);
   if (e != hipSuccess) return e;
   const int g = d.H / d.Hk, hg = decode_heads_per_group(g);
   DecodeArgs a;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
-  a.k_mean = b.k_mean;
   a.v_scale = b.v_scale;
   a.v_mean = b.v_mean;
   a.part_o = db.part_o;

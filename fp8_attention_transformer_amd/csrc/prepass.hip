@@ -24,8 +24,9 @@ namespace {
 
 // Which inputs a prepass workgroup handles: the query side, the key/value
 // side, or both (self-attention, where a token block of Q, K and V is one
-// work item).
-enum Part { kPartQ = 1, kPartKV = 2, kPartBoth = 3 };
+// work item); kPartV: the V statistics alone (a decoding step, whose scores
+// need no K mean).
+enum Part { kPartQ = 1, kPartKV = 2, kPartBoth = 3, kPartV = 4 };
 
 // ---------------------------------------------------------------------------
 // stats: 256 threads, one channel pair per thread, 256/(D/2) chunks of 128
@@ -38,7 +39,7 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   constexpr int LPC = D / 2;          // lanes per chunk
   constexpr int CPW = 256 / LPC;      // chunks per workgroup
   constexpr int U = 32;               // tokens in flight
-  constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
+  constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & (kPartKV | kPartV), DO_K = PART & kPartKV;
   const int tid = threadIdx.x, cp = tid % LPC;
   const int chunk = blockIdx.x * CPW + tid / LPC;
   const int nh = DO_Q ? d.BH() : d.BHk(), nb = DO_Q ? d.NQB : d.NQBk;
@@ -57,8 +58,10 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
       qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
     }
     if constexpr (DO_KV) {
-      ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
-      ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
+      if constexpr (DO_K) {
+        ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
+        ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
+      }
       const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
       vs0 = vs0 + v0;
       vs1 = vs1 + v1;
@@ -76,7 +79,7 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
       for (int u = 0; u < U; u++) {
         const size_t o = base + (size_t)(i + u) * rs;
         qv[u] = DO_Q ? *(const uint32_t*)(q + o) : 0u;
-        kv[u] = DO_KV ? *(const uint32_t*)(k + o) : 0u;
+        kv[u] = DO_K ? *(const uint32_t*)(k + o) : 0u;
         vv[u] = DO_KV ? *(const uint32_t*)(v + o) : 0u;
       }
 #pragma unroll
@@ -85,7 +88,7 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   } else {
     for (int i = i0; i < i1; i++) {
       const size_t o = base + (size_t)i * rs;
-      add(DO_Q ? *(const uint32_t*)(q + o) : 0u, DO_KV ? *(const uint32_t*)(k + o) : 0u,
+      add(DO_Q ? *(const uint32_t*)(q + o) : 0u, DO_K ? *(const uint32_t*)(k + o) : 0u,
           DO_KV ? *(const uint32_t*)(v + o) : 0u);
     }
   }
@@ -720,19 +723,19 @@ hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dt
   return d.D == 64 ? prepass_impl<0, 64>(q, k, v, d, b, s) : prepass_impl<0, 128>(q, k, v, d, b, s);
 }
 
-// Key/value statistics alone (K and V channel sums per chunk, then K means,
-// V means and V scales per K/V head): the first half of a decoding step.
-hipError_t launch_kv_stats(const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b, hipStream_t s) {
-  const uint16_t* k16 = (const uint16_t*)k;
+// Value statistics alone (V channel sums, maxima and minima per chunk, then V
+// means and V scales per K/V head; the K sums and so the K means are left
+// zero): the first half of a decoding step.
+hipError_t launch_v_stats(const void* v, int in_dtype, const Dims& d, const Bufs& b, hipStream_t s) {
   const uint16_t* v16 = (const uint16_t*)v;
   const int cpw = 256 / (d.D / 2);
   const dim3 grid((unsigned)(((long long)d.BHk() * d.NQBk + cpw - 1) / cpw));
   if (in_dtype == kBF16) {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
   } else {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartKV>), grid, dim3(256), 0, s, nullptr, k16, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(d.D), 0, s, d, b);
   return hipGetLastError();

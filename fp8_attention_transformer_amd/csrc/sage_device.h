@@ -66,6 +66,9 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// LDS destination of the direct memory-to-LDS copies
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // Buffer resource over one head's array: raw addressing, `bytes` records (the
 // hardware returns zeros beyond them), default gfx9 data format word.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {

@@ -126,10 +126,9 @@ struct DecodeBufs {
 
 hipError_t launch_prepass(const void* q, const void* k, const void* v, int in_dtype, const Dims& d,
                           const Bufs& b, hipStream_t s);
-// K/V statistics only: k_part, v_part (scratch) -> k_mean, v_scale, v_mean.
-hipError_t launch_kv_stats(const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
-                           hipStream_t s);
-// Decoding step: statistics, split-key attention (DeltaS in fp32 from the
+// V statistics only: k_part, v_part (scratch) -> v_scale, v_mean (k_mean 0).
+hipError_t launch_v_stats(const void* v, int in_dtype, const Dims& d, const Bufs& b, hipStream_t s);
+// Decoding step: V statistics, split-key attention (scores in fp32 from the
 // 16-bit keys, FP8 V on the fly), merge of the ranges into o [B*H, D].
 hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dtype, const Dims& d, const Bufs& b,
                          const DecodeBufs& db, float ks, void* o, int out_dtype, hipStream_t s);

@@ -250,11 +250,13 @@ sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, voi
  * The method is unchanged; with one query token its smoothing block holds
  * that token alone, so the smoothed query is zero, the Q codes and scale are
  * zero for either code width (no qk_bits argument) and the score of key j is
- * the compensation term q . (K_j - mean K) alone.  This call therefore skips
- * the key codes: it computes the K/V statistics of the prepass (K mean, V mean
- * with smooth_v, V scales), then evaluates the compensation term in fp32 from
- * the 16-bit keys and the FP8 V codes of the method on the fly, reading K and
- * V twice in all and writing no codes.
+ * the compensation term q . (K_j - mean K) alone.  Its second part is one
+ * constant per query head, which the softmax does not see (the invariance
+ * behind smoothing K), so this call scores q . K_j in fp32 from the 16-bit
+ * keys with no K mean and skips the key codes: it computes the V statistics
+ * of the prepass (V mean with smooth_v, V scales), then the scores and the
+ * FP8 V codes of the method on the fly, reading K once and V twice in all and
+ * writing no codes.  The result equals the method's up to fp32 rounding.
  * Key blocks are processed in ranges of split_keys keys (a multiple of 128;
  * 0 selects sage_decode_split_keys), each range with its own online softmax
  * (its own running maximum scales its P~ before the FP8 rounding), merged at
