@@ -117,27 +117,18 @@ __device__ __forceinline__ void fp8x2_decode(uint32_t w, float& a, float& b) {
   b = f[1];
 }
 
-// (V - vmean) / vscale for 8 channels with their own scales, bit-identical to
-// a true division per element: reciprocal multiply unless, in some lane of the
-// wave, a quotient lies within 8 ulps of an e4m3 rounding midpoint (its low
-// 20 bits within 8 of 0x80000) or below the e4m3 normal range (|y| < 2^-6,
-// zero included: one compare) -- then true divisions for the whole wave.
-__device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const float* dv) {
-  bool amb = false;
-  float y[8];
+// (V - vmean) / vscale for 8 channels with their own scales, correctly
+// rounded in fp32 with the sign of zero kept (div_rn_signed), or by true
+// divisions when the workgroup holds a zero scale or one outside div_rn's
+// exact case (slow: one flag per workgroup, set up front).
+__device__ __forceinline__ void fp8_quotients8(float* x, const float* rdv, const float* dv, bool slow) {
+  if (slow) {
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    y[e] = x[e] * rdv[e];
-    const uint32_t bits = __float_as_uint(y[e]);
-    amb |= ((bits - 0x7FFF8u) & 0xFFFFFu) <= 16u;   // near a midpoint (sign bit is above bit 19)
-    amb |= fabsf(y[e]) < 0x1p-6f;
+    for (int e = 0; e < 8; e++) x[e] = dv[e] == 0.0f ? 0.0f : x[e] / dv[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = div_rn_signed(x[e], dv[e], rdv[e]);
   }
-  if (__any(amb)) {
-#pragma unroll
-    for (int e = 0; e < 8; e++) y[e] = dv[e] == 0.0f ? 0.0f : x[e] / dv[e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; e++) x[e] = y[e];
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi over packed 16-bit pairs (bf16 or fp16), the
@@ -207,8 +198,11 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   const int t0 = split * a.split_blocks, t1 = min(nkb, t0 + a.split_blocks);
 
   // V scale, its reciprocal and the V mean per channel (LDS: read per key)
+  int hard = 0;        // a scale outside div_rn's exact case: true divisions for this workgroup
+  bool vslow = false;  // the workgroup-wide verdict, set at the first barrier
   if (tid < D) {
     const float dv = a.v_scale[(size_t)bhk * D + tid];
+    hard = (dv == 0.0f || div_rn_hard(dv)) ? 1 : 0;
     sDV[tid] = dv;
     sRDV[tid] = dv == 0.0f ? 0.0f : 1.0f / dv;
     sVB[tid] = a.v_mean[(size_t)bhk * D + tid];
@@ -281,11 +275,12 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e++) O[h][e] = O[h][e] * alpha;
     }
-    float vbar[8], rdv[8];
+    float vbar[8], rdv[8], dvv[8];
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {
       *(float4*)&vbar[e] = *(const float4*)&sVB[8 * cg + e];
       *(float4*)&rdv[e] = *(const float4*)&sRDV[8 * cg + e];
+      *(float4*)&dvv[e] = *(const float4*)&sDV[8 * cg + e];
     }
 #pragma unroll
     for (int kk = 0; kk < KPG; kk++) {
@@ -299,7 +294,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e++) x[e] = valid ? x[e] : 0.0f;
       }
-      fp8_quotients8(x, rdv, sDV + 8 * cg);
+      fp8_quotients8(x, rdv, dvv, vslow);
       float vq[8];
 #pragma unroll
       for (int w = 0; w < 2; w++) {
@@ -318,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
 
   v4i kA[KPG], kB[KPG], vA[KPG], vB[KPG];
   issue(rk, t0, t1, kA);
-  __syncthreads();   // sM, sL and the V constants
+  vslow = __syncthreads_or(hard) != 0;   // also publishes sM, sL and the V constants
   for (int tc = t0; tc < t1; tc += CB) {
     const int te = min(t1, tc + CB), nb = te - tc;
     // ---- S (kA holds block tc); the query rows are reloaded per chunk (they

@@ -213,25 +213,20 @@ __device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf&
 
 // Integer codes rint(x/delta) of NV values sharing one scale (INT4: |code|
 // <= 7, INT8: <= 127), as floats, bit-identical to a true IEEE division per
-// element: multiply by the correctly rounded reciprocal (absolute error below
-// 2^-19 for INT4 and 2^-15 for INT8 quotients), and if any lane of the wave
-// lands within twice that of a rounding midpoint (half-integer), redo the
-// whole wave with true divisions.  |x| <= qmax*delta makes the clamp
-// unnecessary.  Adding +0 turns a rounded -0 into +0 (code 0 has one pattern).
+// element: the correctly rounded quotient from the reciprocal and one
+// remainder correction (div_rn), a true division for the whole wave only when
+// some lane's scale is outside the exact case.  |x| <= qmax*delta makes the
+// clamp unnecessary.  Adding +0 turns a rounded -0 into +0 (code 0 has one
+// pattern).
 template <int NV, int BITS>
 __device__ __forceinline__ void int_codes_f(const float* x, float delta, float* c) {
-  constexpr float kWindow = BITS == 4 ? 0x1p-19f : 0x1p-14f;
   const float r = delta == 0.0f ? 0.0f : 1.0f / delta;
-  bool amb = false;
-#pragma unroll
-  for (int e = 0; e < NV; e++) {
-    const float q = x[e] * r;
-    c[e] = rintf(q);
-    amb |= fabsf(fabsf(q - c[e]) - 0.5f) < kWindow;
-  }
-  if (__any(amb)) {
+  if (__any(div_rn_hard(delta))) {
 #pragma unroll
     for (int e = 0; e < NV; e++) c[e] = delta == 0.0f ? 0.0f : rintf(x[e] / delta);
+  } else {
+#pragma unroll
+    for (int e = 0; e < NV; e++) c[e] = rintf(div_rn(x[e], delta, r));
   }
 #pragma unroll
   for (int e = 0; e < NV; e++) c[e] = c[e] + 0.0f;
@@ -264,27 +259,19 @@ __device__ __forceinline__ void pack_fp6_hw(const float* c, uint32_t* w) {
   for (int i = 0; i < 3 * NF / 16; i++) w[i] = (uint32_t)r[i];
 }
 
-// x / dv for FP8 V codes: reciprocal multiply unless, in some lane of the wave,
-// the quotient lies within 2^-21 (relative) of an e4m3 rounding midpoint or
-// below the e4m3 normal range -- then true division for the whole wave.
+// x / dv for FP8 V codes, correctly rounded in fp32 with the sign of zero
+// kept (div_rn_signed); a true division for the whole wave when some lane's
+// scale is zero (an all-zero channel: +0 codes) or outside the exact case.
 template <int NV>
 __device__ __forceinline__ void fp8_quotients(float* x, float dv) {
   const float r = dv == 0.0f ? 0.0f : 1.0f / dv;
-  bool amb = false;
-  float y[NV];
+  if (__any(dv == 0.0f || div_rn_hard(dv))) {
 #pragma unroll
-  for (int e = 0; e < NV; e++) {
-    y[e] = x[e] * r;
-    const float a = fabsf(y[e]);
-    const int low = (int)(__float_as_uint(a) & 0xFFFFFu) - 0x80000;
-    amb |= (a != 0.0f) && (a < 0.015625f || (low <= 8 && low >= -8));
+    for (int e = 0; e < NV; e++) x[e] = dv == 0.0f ? 0.0f : x[e] / dv;
+  } else {
+#pragma unroll
+    for (int e = 0; e < NV; e++) x[e] = div_rn_signed(x[e], dv, r);
   }
-  if (__any(amb)) {
-#pragma unroll
-    for (int e = 0; e < NV; e++) y[e] = dv == 0.0f ? 0.0f : x[e] / dv;
-  }
-#pragma unroll
-  for (int e = 0; e < NV; e++) x[e] = y[e];
 }
 
 // ---------------------------------------------------------------------------

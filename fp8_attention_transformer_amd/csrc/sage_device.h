@@ -66,6 +66,25 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// x / d rounded to nearest in fp32, from r = RN(1/d): the product q = RN(x*r)
+// corrected once with the exact remainder fma(-q, d, x) (Markstein's
+// correction step) is the correctly rounded quotient whenever d is normal,
+// not above 2^126 and its significand is not all ones; d = 0 (r = 0) gives 0.
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+  const float q = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, d, x), r, q);
+}
+// The same with the sign of x kept on a zero quotient (-0 / d = -0; the two
+// FMAs above add +0 and -0 to +0), for d != 0.
+__device__ __forceinline__ float div_rn_signed(float x, float d, float r) {
+  return __builtin_copysignf(div_rn(x, d, r), x);
+}
+// divisors outside the case above (a true division is used for them)
+__device__ __forceinline__ bool div_rn_hard(float d) {
+  const uint32_t b = __float_as_uint(d) & 0x7FFFFFFFu;
+  return b != 0u && (b < 0x00800000u || b >= 0x7E800000u || (b & 0x7FFFFFu) == 0x7FFFFFu);
+}
+
 // LDS destination of the direct memory-to-LDS copies
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 

@@ -316,3 +316,30 @@ def test_smooth_v_full_size_dit(oracle_lib):
         rows = _sample_rows(w, 1, rng)
         O_ref, slack, _ = oracle_lib.attn_mirror(z, w.causal, w.scale, rows=rows, eps=EPS_TIE)
         _compare_o(O_gpu_all[bh][rows], O_ref, slack, f"{w.name}/smooth_v/bh{bh}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("smooth_v", [False, True])
+def test_signed_zeros_and_zero_channels(oracle_lib, bits, smooth_v):
+    """Codes of signed zeros: V entries of -0 keep the sign of their FP8 code
+    (0x80), a V channel of zeros only (scale 0) gives +0 codes, and Q/K zeros
+    give code 0; every prepass array bit-exact against the oracle."""
+    import gpu_helpers as gh
+    w = wl.custom(2, 2, 300, 128, seed=131, k_offset_std=2.0, v_offset_std=0.0)
+    q, k, v = (a.copy() for a in wl.generate(w))
+    rng = np.random.default_rng(5)
+    for a in (q, k, v):
+        m = rng.random(a.shape) < 0.05
+        a[m] = np.where(rng.random(m.sum()) < 0.5, 0x8000, 0x0000)       # bf16 -0 / +0
+    v[0, 1, :, 7] = np.where(rng.random(w.N) < 0.5, 0x8000, 0x0000)      # an all-zero V channel
+    k[1, 0, :, 3] = 0x8000                                                 # an all -0 K channel
+    out, ws = gh.run_attn(q, k, v, w.dtype, w.causal, w.scale, qk_bits=bits, smooth_v=smooth_v)
+    rb = gh.Readback(ws, qk_bits=bits)
+    z = oracle_lib.quant_smooth(q, k, v, _sdt(w), qk_bits=bits, smooth_v=smooth_v)
+    _check_prepass(rb, z)
+    if not smooth_v:
+        assert (rb.v_codes == 0x80).any(), "the case holds -0 V codes"
+    assert np.all(rb.v_codes[2 * 0 + 1, :, 7] == 0), "zero channel"
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, False, w.scale, eps=2.0 ** -14)
+    err = np.abs(out.cpu().numpy().reshape(-1, w.D).astype(np.float64) - O_ref).max(1)
+    assert np.all(err <= 2e-3 + slack)
