@@ -354,6 +354,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK], sV2[S > 2 ? D * kBK : 16];
   __shared__ float sDS0[kBK], sDS1[kBK], sDS2[S > 2 ? kBK : 1];
   __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup], sKS2[S > 2 ? kBK / kKGroup : 1];
+  __shared__ float sVS[D], sVM[D];   // V scales and means of the head, for the epilogue
   auto bK = [&](int i) { return i == 0 ? sK0 : (i == 1 ? sK1 : sK2); };
   auto bV = [&](int i) { return i == 0 ? sV0 : (i == 1 ? sV1 : sV2); };
   auto bDS = [&](int i) { return i == 0 ? sDS0 : (i == 1 ? sDS1 : sDS2); };
@@ -418,6 +419,13 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg[t % (S - 1)];
   };
 
+  // The head's V scales and means (read by the epilogue) load first, so every
+  // wait below that covers block tb's copies covers them too.
+  float vs_reg = 0.0f, vm_reg = 0.0f;
+  if (tid < D) {
+    vs_reg = b.v_scale[(size_t)bhk * D + tid];
+    vm_reg = b.v_mean[(size_t)bhk * D + tid];
+  }
   issue(tb, 0);
   if (S > 2 && te - tb > 1) issue(tb + 1, 1);
 
@@ -436,6 +444,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   if (S > 2 && te - tb > 1) wait_vmcnt<VM_PER_BLOCK>();
   else wait_vmcnt<0>();
   publish(tb, 0);
+  if (tid < D) {
+    sVS[tid] = vs_reg;
+    sVM[tid] = vm_reg;
+  }
   __syncthreads();
 
   for (int t = tb; t < te; t++) {
@@ -464,7 +476,9 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) po[32 * dt + 8 * (r >> 2) + 4 * h + (r & 3)] = as.O[dt][r];
+        for (int q4 = 0; q4 < 4; q4++)   // 4 consecutive channels per 16-byte store
+          *(float4*)(po + 32 * dt + 8 * q4 + 4 * h) =
+              make_float4(as.O[dt][4 * q4], as.O[dt][4 * q4 + 1], as.O[dt][4 * q4 + 2], as.O[dt][4 * q4 + 3]);
       if (h == 0) {
         sp.part_ml[(row * sp.S + rng) * 2] = as.m;
         sp.part_ml[(row * sp.S + rng) * 2 + 1] = as.l;
@@ -472,18 +486,35 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     }
     return;
   }
-  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean
+  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean.  The scales and
+  //      means come from LDS (global loads here would each wait behind the
+  //      stores before them: the output may alias them as far as the compiler
+  //      knows); a lane's registers 4q..4q+3 of a tile are 4 consecutive
+  //      channels, stored with one 8-byte (16-bit outputs) or 16-byte (fp32)
+  //      store when the output is 16-byte aligned.
   if (qi < io.n) {
-    const float* vs = b.v_scale + (size_t)bhk * D;
-    const float* vm = b.v_mean + (size_t)bhk * D;
     const size_t orow = io.base + (size_t)qi * io.stride;
     const float inv_l = 1.0f / as.l;
+    const bool vec = ((uintptr_t)o & 15) == 0;
 #pragma unroll
     for (int dt = 0; dt < NDT; dt++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int ch = 32 * dt + 8 * (r >> 2) + 4 * h + (r & 3);
-        store_out(o, orow + ch, (as.O[dt][r] * vs[ch]) * inv_l + vm[ch], out_dtype);
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int c0 = 32 * dt + 8 * q4 + 4 * h;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) y[j] = (as.O[dt][4 * q4 + j] * sVS[c0 + j]) * inv_l + sVM[c0 + j];
+        if (!vec) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) store_out(o, orow + c0 + j, y[j], out_dtype);
+        } else if (out_dtype == kOutF32) {
+          *(float4*)((float*)o + orow + c0) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+          uint32_t hb[4];
+#pragma unroll
+          for (int j = 0; j < 4; j++) hb[j] = out_bits16(y[j], out_dtype);
+          *(uint2*)((uint16_t*)o + orow + c0) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        }
       }
   }
 }

@@ -39,6 +39,18 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, in
 }
 
 // One output element in the requested dtype (bf16 and fp16 with RNE).
+// The 16-bit output pattern of val (kOutBF16: round to nearest even; kOutF16).
+__device__ __forceinline__ uint32_t out_bits16(float val, int out_dtype) {
+  if (out_dtype == kOutBF16) {
+    const uint32_t u = __float_as_uint(val);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  }
+  const _Float16 hv = (_Float16)val;
+  uint16_t bits;
+  __builtin_memcpy(&bits, &hv, 2);
+  return bits;
+}
+
 __device__ __forceinline__ void store_out(void* o, size_t idx, float val, int out_dtype) {
   if (out_dtype == kOutF32) {
     ((float*)o)[idx] = val;
