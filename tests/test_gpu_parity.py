@@ -343,3 +343,28 @@ def test_signed_zeros_and_zero_channels(oracle_lib, bits, smooth_v):
     O_ref, slack, _ = oracle_lib.attn_mirror(z, False, w.scale, eps=2.0 ** -14)
     err = np.abs(out.cpu().numpy().reshape(-1, w.D).astype(np.float64) - O_ref).max(1)
     assert np.all(err <= 2e-3 + slack)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_unaligned_output_equals_aligned(out):
+    """The epilogue stores four channels per instruction when the output is
+    16-byte aligned and one element at a time otherwise: an output one
+    element off alignment gets the same values, bit for bit."""
+    import torch
+    from fp8_attention_transformer_amd import sage
+    import gpu_helpers as gh
+    w = wl.custom(1, 2, 300, 128, causal=True, seed=141, k_offset_std=3.0)
+    q, k, v = (gh.to_device(a, w.dtype) for a in wl.generate(w))
+    odt, code = (torch.bfloat16, sage.BF16) if out == "bf16" else (torch.float32, sage.F32)
+    n = w.B * w.H * w.N * w.D
+    ws = sage.alloc_workspace(w.B, w.H, w.N, w.D).tensor
+    base = torch.full((n + 8,), 7.0, dtype=odt, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    args = (w.B, w.H, w.N, w.D, w.causal, w.scale, sage.BF16, code, ws.data_ptr(), ws.numel(), sh)
+    sage.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), base.data_ptr(), *args)
+    aligned = base[:n].clone()
+    base.fill_(7.0)
+    sage.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), base[1:].data_ptr(), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(base[1:n + 1], aligned)
+    assert base[0].item() == 7.0 and torch.all(base[n + 1:] == 7.0)   # nothing written outside
