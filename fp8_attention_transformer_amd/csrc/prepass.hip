@@ -28,87 +28,80 @@ namespace {
 // need no K mean).
 enum Part { kPartQ = 1, kPartKV = 2, kPartBoth = 3, kPartV = 4 };
 
+// Workgroup barrier for LDS written with ds_write: waits for this wave's LDS
+// operations only, so vector-memory loads and stores (including copies into
+// LDS that nothing reads yet) stay in flight across it; __syncthreads()
+// would wait for those too.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // stats: 256 threads, one channel pair per thread, 256/(D/2) chunks of 128
 // tokens per workgroup.  Each thread walks its chunk in token order (the sums
-// are sequential per channel); loads are issued 32 tokens ahead.  Q side:
-// block means; K/V side: per-chunk K and V sums and V maxima and minima.
+// are sequential per channel); loads are issued 32 tokens ahead.  Per chunk:
+// the K and V sums and the V maxima and minima (kPartV: V only).  The Q block
+// means are formed by the quant kernel, which holds the block anyway.
 template <int IN, int D, int PART>
-__global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v, Dims d, Bufs b) {
+__global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                    Dims d, Bufs b) {
   constexpr int LPC = D / 2;          // lanes per chunk
   constexpr int CPW = 256 / LPC;      // chunks per workgroup
   constexpr int U = 32;               // tokens in flight
-  constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & (kPartKV | kPartV), DO_K = PART & kPartKV;
+  constexpr bool DO_K = PART == kPartKV;
+  static_assert(PART == kPartKV || PART == kPartV, "stats cover the key/value side");
   const int tid = threadIdx.x, cp = tid % LPC;
   const int chunk = blockIdx.x * CPW + tid / LPC;
-  const int nh = DO_Q ? d.BH() : d.BHk(), nb = DO_Q ? d.NQB : d.NQBk;
+  const int nh = d.BHk(), nb = d.NQBk;
   if (chunk >= nh * nb) return;
   // dense: the chunks of a head are adjacent; packed [T, H, D]: the heads of a
   // token block are adjacent, so neighbouring workgroups read whole rows
   const int bh = d.cu ? chunk % nh : chunk / nb, qb = d.cu ? chunk / nh : chunk % nb;
-  const HeadIO io = DO_Q ? head_io(d, bh) : head_io_kv(d, bh);
+  const HeadIO io = head_io_kv(d, bh);
   const int i0 = qb * kBQ, i1 = min(io.n, i0 + kBQ);   // i1 <= i0: empty chunk (short sequence)
   const size_t base = io.base + 2 * cp, rs = io.stride;
-  float qs0 = 0.0f, qs1 = 0.0f, ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
+  float ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
   float vx0 = -__builtin_inff(), vx1 = -__builtin_inff(), vn0 = __builtin_inff(), vn1 = __builtin_inff();
-  auto add = [&](uint32_t qv, uint32_t kv, uint32_t vv) {
-    if constexpr (DO_Q) {
-      qs0 = qs0 + in_to_f32<IN>((uint16_t)(qv & 0xFFFF));
-      qs1 = qs1 + in_to_f32<IN>((uint16_t)(qv >> 16));
+  auto add = [&](uint32_t kv, uint32_t vv) {
+    if constexpr (DO_K) {
+      ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
+      ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
     }
-    if constexpr (DO_KV) {
-      if constexpr (DO_K) {
-        ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
-        ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
-      }
-      const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
-      vs0 = vs0 + v0;
-      vs1 = vs1 + v1;
-      vx0 = fmaxf(vx0, v0);
-      vx1 = fmaxf(vx1, v1);
-      vn0 = fminf(vn0, v0);
-      vn1 = fminf(vn1, v1);
-    }
+    const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
+    vs0 = vs0 + v0;
+    vs1 = vs1 + v1;
+    vx0 = fmaxf(vx0, v0);
+    vx1 = fmaxf(vx1, v1);
+    vn0 = fminf(vn0, v0);
+    vn1 = fminf(vn1, v1);
   };
   if (i1 - i0 == kBQ) {
     // full chunk: branch-free, U tokens of loads in flight
     for (int i = i0; i < i1; i += U) {
-      uint32_t qv[U], kv[U], vv[U];
+      uint32_t kv[U], vv[U];
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const size_t o = base + (size_t)(i + u) * rs;
-        qv[u] = DO_Q ? *(const uint32_t*)(q + o) : 0u;
         kv[u] = DO_K ? *(const uint32_t*)(k + o) : 0u;
-        vv[u] = DO_KV ? *(const uint32_t*)(v + o) : 0u;
+        vv[u] = *(const uint32_t*)(v + o);
       }
 #pragma unroll
-      for (int u = 0; u < U; u++) add(qv[u], kv[u], vv[u]);
+      for (int u = 0; u < U; u++) add(kv[u], vv[u]);
     }
   } else {
     for (int i = i0; i < i1; i++) {
       const size_t o = base + (size_t)i * rs;
-      add(DO_Q ? *(const uint32_t*)(q + o) : 0u, DO_K ? *(const uint32_t*)(k + o) : 0u,
-          DO_KV ? *(const uint32_t*)(v + o) : 0u);
+      add(DO_K ? *(const uint32_t*)(k + o) : 0u, *(const uint32_t*)(v + o));
     }
   }
-  if constexpr (DO_Q) {
-    const size_t o = ((size_t)bh * d.NQB + qb) * D + 2 * cp;
-    const float cnt = (float)(i1 - i0);
-    b.q_mean[o] = i1 > i0 ? qs0 / cnt : 0.0f;
-    b.q_mean[o + 1] = i1 > i0 ? qs1 / cnt : 0.0f;
-  }
-  if constexpr (DO_KV) {
-    const size_t o2 = ((size_t)bh * d.NQBk + qb) * 2 * D + 2 * cp;
-    b.k_part[o2] = ks0;
-    b.k_part[o2 + 1] = ks1;
-    b.k_part[o2 + D] = vs0;
-    b.k_part[o2 + D + 1] = vs1;
-    b.v_part[o2] = vx0;
-    b.v_part[o2 + 1] = vx1;
-    b.v_part[o2 + D] = vn0;
-    b.v_part[o2 + D + 1] = vn1;
-  }
+  const size_t o2 = ((size_t)bh * d.NQBk + qb) * 2 * D + 2 * cp;
+  b.k_part[o2] = ks0;
+  b.k_part[o2 + 1] = ks1;
+  b.k_part[o2 + D] = vs0;
+  b.k_part[o2 + D + 1] = vs1;
+  b.v_part[o2] = vx0;
+  b.v_part[o2 + 1] = vx1;
+  b.v_part[o2 + D] = vn0;
+  b.v_part[o2 + D + 1] = vn1;
 }
 
 // ---------------------------------------------------------------------------
@@ -289,6 +282,8 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
   __shared__ __align__(16) uint16_t sV[DO_KV ? kBK * D : 8];
   __shared__ __align__(16) float sKM[DO_KV ? D : 4];   // K means of the head
+  __shared__ __align__(16) uint16_t sQ[DO_Q ? 64 * D : 8];   // half a block of raw Q rows
+  __shared__ __align__(16) float sQM[DO_Q ? D : 4];          // the block's Q means
   // packed [T, H, D] inputs: grid (B*H, NQB), heads of a token block adjacent
   const int qb = d.cu ? blockIdx.y : blockIdx.x, bh = d.cu ? blockIdx.x : blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -352,9 +347,55 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   // ---- Q: LPT lanes per token, 16 channels per lane
   if constexpr (DO_Q) {
     const int sub = tid % LPT, c0 = 16 * sub;
+    // Block means: thread c < D sums channel c over the block's tokens in
+    // token order (fp32, one chain), then divides once by the count.  The raw
+    // rows pass through LDS in two halves of 64 tokens; rows past the head's
+    // tokens are staged too but not summed.
+    const int nval = min(kBQ, io.n - i0);
+    constexpr int PPH = NQP / 2;   // Q passes per half (64 tokens)
+    static_assert(PPH * TPP == 64, "a half is 64 tokens");
+    float qs = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      if (h) lds_barrier();   // the first half has been summed
+#pragma unroll
+      for (int p = 0; p < PPH; p++) {
+        uint16_t* dst = sQ + (tid / LPT + TPP * p) * D + c0;
+        *(v4i*)dst = qraw[PPH * h + p][0];
+        *(v4i*)(dst + 8) = qraw[PPH * h + p][1];
+      }
+      lds_barrier();
+      if (tid < D) {
+        const int nh = min(64, nval - 64 * h);   // tokens of this half to sum (may be <= 0)
+        if (nh == 64) {
+#pragma unroll
+          for (int t0 = 0; t0 < 64; t0 += 16) {
+            uint16_t x[16];
+#pragma unroll
+            for (int t = 0; t < 16; t++) x[t] = sQ[(t0 + t) * D + tid];
+#pragma unroll
+            for (int t = 0; t < 16; t++) qs = qs + in_to_f32<IN>(x[t]);
+          }
+        } else {
+          for (int t = 0; t < nh; t++) qs = qs + in_to_f32<IN>(sQ[t * D + tid]);
+        }
+      }
+    }
+    if (tid < D) {
+      const float m = qs / (float)nval;
+      sQM[tid] = m;
+      b.q_mean[((size_t)bh * d.NQB + qb) * D + tid] = m;
+    }
+    lds_barrier();
     float qm[16];
 #pragma unroll
-    for (int e = 0; e < 16; e++) qm[e] = b.q_mean[((size_t)bh * d.NQB + qb) * D + c0 + e];
+    for (int e = 0; e < 16; e += 4) {
+      const float4 m = *(const float4*)(sQM + c0 + e);
+      qm[e] = m.x;
+      qm[e + 1] = m.y;
+      qm[e + 2] = m.z;
+      qm[e + 3] = m.w;
+    }
     // three bf16 pieces of this block's channel means for the compensation
     // kernel: pieces 1 and 2 in k_part, piece 3 in v_part (both are free once
     // the K means and V scales are final)
@@ -685,15 +726,8 @@ hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims&
   const uint16_t* v16 = (const uint16_t*)v;
   constexpr int CPW = 256 / (D / 2);
   auto nstat = [](long long chunks) { return dim3((unsigned)((chunks + CPW - 1) / CPW)); };
-  if (d.self_attention()) {
-    hipLaunchKernelGGL((stats_kernel<IN, D, kPartBoth>), nstat((long long)d.BH() * d.NQB), dim3(256), 0, s, q16, k16,
-                       v16, d, b);
-  } else {
-    hipLaunchKernelGGL((stats_kernel<IN, D, kPartQ>), nstat((long long)d.BH() * d.NQB), dim3(256), 0, s, q16, k16, v16,
-                       d, b);
-    hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s, q16, k16,
-                       v16, d, b);
-  }
+  hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s, k16, v16,
+                     d, b);
   hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(D), 0, s, d, b);
   if (d.QB == 8) launch_quant<IN, D, 8>(q16, k16, v16, d, b, s);
   else launch_quant<IN, D, 4>(q16, k16, v16, d, b, s);
@@ -718,11 +752,11 @@ hipError_t launch_v_stats(const void* v, int in_dtype, const Dims& d, const Bufs
   const int cpw = 256 / (d.D / 2);
   const dim3 grid((unsigned)(((long long)d.BHk() * d.NQBk + cpw - 1) / cpw));
   if (in_dtype == kBF16) {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
   } else {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartV>), grid, dim3(256), 0, s, nullptr, nullptr, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
   }
   hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(d.D), 0, s, d, b);
   return hipGetLastError();
