@@ -318,6 +318,16 @@ __device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8,
   }
 }
 
+// Two outputs as one packed pair of 16-bit values, each rounded to nearest
+// even (one conversion instruction per pair on gfx950); the same bits as
+// store_out's per-element rounding for finite values.
+__device__ __forceinline__ uint32_t out_pack2(float a, float b, int out_dtype) {
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+  if (out_dtype == kOutBF16) return __builtin_bit_cast(uint32_t, v2bf_t{(__bf16)a, (__bf16)b});
+  return __builtin_bit_cast(uint32_t, v2h_t{(_Float16)a, (_Float16)b});
+}
+
 // One whole block in sequence (the four-wave kernel).
 template <int D, int BITS, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
@@ -483,7 +493,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     }
     return;
   }
-  // ---- epilogue: O = (O_run * vscale) * (1 / l') + vmean.  The scales and
+  // ---- epilogue: O = fma(O_run * vscale, 1 / l', vmean).  The scales and
   //      means come from LDS (global loads here would each wait behind the
   //      stores before them: the output may alias them as far as the compiler
   //      knows); a lane's registers 4q..4q+3 of a tile are 4 consecutive
@@ -500,17 +510,14 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
         const int c0 = 32 * dt + 8 * q4 + 4 * h;
         float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) y[j] = (as.O[dt][4 * q4 + j] * sVS[c0 + j]) * inv_l + sVM[c0 + j];
+        for (int j = 0; j < 4; j++) y[j] = __builtin_fmaf(as.O[dt][4 * q4 + j] * sVS[c0 + j], inv_l, sVM[c0 + j]);
         if (!vec) {
 #pragma unroll
           for (int j = 0; j < 4; j++) store_out(o, orow + c0 + j, y[j], out_dtype);
         } else if (out_dtype == kOutF32) {
           *(float4*)((float*)o + orow + c0) = make_float4(y[0], y[1], y[2], y[3]);
         } else {
-          uint32_t hb[4];
-#pragma unroll
-          for (int j = 0; j < 4; j++) hb[j] = out_bits16(y[j], out_dtype);
-          *(uint2*)((uint16_t*)o + orow + c0) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+          *(uint2*)((uint16_t*)o + orow + c0) = make_uint2(out_pack2(y[0], y[1], out_dtype), out_pack2(y[2], y[3], out_dtype));
         }
       }
   }
@@ -525,20 +532,41 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // sequences of unequal length query-block-major, so the heaviest blocks of
   // every sequence start first; split: (head, range) pairs take the place of
   // heads, so the query blocks of one key range share an L2.
+  // D = 128: one call site of item(), so its code (the key loop with the
+  // masked and unmasked softmax) exists once; inlined at each of three call
+  // sites the causal kernel took 80 KB and outgrew the instruction cache.
+  // D = 64 keeps two call sites: its code is smaller, and the loop would cost
+  // it 35 registers and its third wave per SIMD.
+  int bh, rng = 0, qb0, qb1 = -1;
   if (CAUSAL && !SPLIT && !d.cu && (int)gridDim.x != d.NQB * d.BH()) {
     const int npair = (d.NQB + 1) / 2;
-    const int bh = logical / npair, p = logical % npair;
-    item(bh, 0, d.NQB - 1 - p);
-    if (p != d.NQB - 1 - p) {
-      __syncthreads();
-      item(bh, 0, p);
-    }
+    const int p = logical % npair;
+    bh = logical / npair;
+    qb0 = d.NQB - 1 - p;
+    if (p != qb0) qb1 = p;
   } else {
     const int hs = logical / d.NQB;
-    const int bh = d.cu ? logical % d.BH() : (SPLIT ? hs / sp.S : hs);
-    const int rng = SPLIT ? hs % sp.S : 0;
+    bh = d.cu ? logical % d.BH() : (SPLIT ? hs / sp.S : hs);
+    rng = SPLIT ? hs % sp.S : 0;
     const int jq = d.cu ? logical / d.BH() : logical % d.NQB;
-    item(bh, rng, CAUSAL ? d.NQB - 1 - jq : jq);
+    qb0 = CAUSAL ? d.NQB - 1 - jq : jq;
+  }
+  if constexpr (!CAUSAL || SPLIT) {
+    item(bh, rng, qb0);
+  } else if constexpr (D == 64) {
+    item(bh, rng, qb0);
+    if (qb1 >= 0) {
+      __syncthreads();
+      item(bh, rng, qb1);
+    }
+  } else {
+#pragma clang loop unroll(disable)
+    for (int k = 0; k < 2; k++) {
+      const int qb = k == 0 ? qb0 : qb1;
+      if (qb < 0) break;
+      if (k) __syncthreads();
+      item(bh, rng, qb);
+    }
   }
 }
 
@@ -578,7 +606,7 @@ __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, in
 // channel.  Row i reads the ranges holding a key it sees (range r starts at
 // key r*split_keys <= i + Nk - N when causal), M = max m_r, w_r = exp2(m_r - M),
 // O = fma(w_r, O_r, O) and l' = fma(w_r, l'_r, l') in range order, then the
-// fused kernel's epilogue (O * vscale) * (1 / l') + vmean.  One range gives
+// fused kernel's epilogue fma(O * vscale, 1 / l', vmean).  One range gives
 // the unsplit kernel's result bit for bit (w = 1).
 __global__ void __launch_bounds__(128) split_merge_kernel(Bufs b, Dims d, int causal, SplitParts sp, void* o,
                                                           int out_dtype) {
@@ -597,7 +625,7 @@ __global__ void __launch_bounds__(128) split_merge_kernel(Bufs b, Dims d, int ca
     l = __builtin_fmaf(w, ml[2 * r + 1], l);
   }
   const float inv_l = 1.0f / l;
-  const float val = (acc * b.v_scale[(size_t)bhk * d.D + c]) * inv_l + b.v_mean[(size_t)bhk * d.D + c];
+  const float val = __builtin_fmaf(acc * b.v_scale[(size_t)bhk * d.D + c], inv_l, b.v_mean[(size_t)bhk * d.D + c]);
   store_out(o, (size_t)row * d.D + c, val, out_dtype);
 }
 
