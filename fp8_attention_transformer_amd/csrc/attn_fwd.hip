@@ -328,6 +328,11 @@ __device__ __forceinline__ uint32_t out_pack2(float a, float b, int out_dtype) {
   return __builtin_bit_cast(uint32_t, v2h_t{(_Float16)a, (_Float16)b});
 }
 
+// Workgroup barrier for LDS only: waits for this wave's LDS operations, not
+// for its vector-memory loads and stores (as __syncthreads() would).  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One whole block in sequence (the four-wave kernel).
 template <int D, int BITS, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
@@ -532,6 +537,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   // sequences of unequal length query-block-major, so the heaviest blocks of
   // every sequence start first; split: (head, range) pairs take the place of
   // heads, so the query blocks of one key range share an L2.
+  // Between the items of a pair only LDS needs ordering (the second one's
+  // prologue rewrites the slots and the V statistics the first one's
+  // epilogue read): the first one's output stores drain while the second
+  // one's prologue loads are in flight.
   // D = 128: one call site of item(), so its code (the key loop with the
   // masked and unmasked softmax) exists once; inlined at each of three call
   // sites the causal kernel took 80 KB and outgrew the instruction cache.
@@ -556,7 +565,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   } else if constexpr (D == 64) {
     item(bh, rng, qb0);
     if (qb1 >= 0) {
-      __syncthreads();
+      lds_barrier();
       item(bh, rng, qb1);
     }
   } else {
@@ -564,7 +573,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     for (int k = 0; k < 2; k++) {
       const int qb = k == 0 ? qb0 : qb1;
       if (qb < 0) break;
-      if (k) __syncthreads();
+      if (k) lds_barrier();
       item(bh, rng, qb);
     }
   }
