@@ -247,7 +247,7 @@ def test_cross_validation():
 
 def test_decode_validation():
     L = sage.lib()
-    assert sage.decode_split_keys(16, 32, 8, 8192, 128) == 1024
+    assert sage.decode_split_keys(16, 32, 8, 8192, 128) == 4096   # 256 workgroups: one per compute unit
     assert sage.decode_split_keys(1, 4, 3, 100, 64) == 0
     assert sage.decode_split_keys(1, 4, 2, 1, 64) == 128
     assert sage.decode_workspace_bytes(1, 4, 2, 1000, 128, 100) == 0
@@ -269,7 +269,7 @@ def test_decode_validation():
 
 def test_split_validation():
     L = sage.lib()
-    assert sage.split_keys(1, 32, 8, 512, 8192, 128) == 1024
+    assert sage.split_keys(1, 32, 8, 512, 8192, 128) == 2048   # 512 workgroups: two per compute unit
     assert sage.split_keys(1, 4, 3, 10, 10, 64) == 0
     assert sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 100) == 0
     ws_one = sage.split_workspace_bytes(1, 4, 2, 100, 1000, 128, 1024)
