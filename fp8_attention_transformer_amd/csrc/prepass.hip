@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
 // max|V - vmean| / 448, from the chunk maxima and minima: rounding is
 // monotonic, so max_j |fl(V_j - m)| = max(|fl(max V - m)|, |fl(min V - m)|).
 __global__ void finalize_kernel(Dims d, Bufs b) {
-  constexpr int U = 16;   // chunks whose partials are loaded together
+  constexpr int U = 32;   // chunks whose partials are loaded together
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
   const size_t base = (size_t)bh * d.NQBk * 2 * D + c;
   float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
