@@ -112,7 +112,7 @@ void carve(void* ws, const Dims& d, sage_quant_bufs* out) {
 }
 
 Bufs to_internal(const sage_quant_bufs& q) {
-  Bufs b;
+  Bufs b = {};
   b.q_codes = q.q_codes;
   b.k_codes = q.k_codes;
   b.q_scale = q.q_scale;
