@@ -611,31 +611,51 @@ __global__ void __launch_bounds__(64) qk_debug_kernel(Bufs b, Dims d, int bh, in
   }
 }
 
-// Merge of the key ranges: one workgroup per query row, one thread per
-// channel.  Row i reads the ranges holding a key it sees (range r starts at
-// key r*split_keys <= i + Nk - N when causal), M = max m_r, w_r = exp2(m_r - M),
+// Merge of the key ranges: D/4 threads per query row, four channels each
+// (16-byte loads of the partial outputs), 256/(D/4) rows per workgroup.  Row
+// i reads the ranges holding a key it sees (range r starts at key
+// r*split_keys <= i + Nk - N when causal), M = max m_r, w_r = exp2(m_r - M),
 // O = fma(w_r, O_r, O) and l' = fma(w_r, l'_r, l') in range order, then the
 // fused kernel's epilogue fma(O * vscale, 1 / l', vmean).  One range gives
 // the unsplit kernel's result bit for bit (w = 1).
-__global__ void __launch_bounds__(128) split_merge_kernel(Bufs b, Dims d, int causal, SplitParts sp, void* o,
+__global__ void __launch_bounds__(256) split_merge_kernel(Bufs b, Dims d, int causal, SplitParts sp, void* o,
                                                           int out_dtype) {
-  const int row = blockIdx.x, c = threadIdx.x;
-  if (c >= d.D) return;
+  const int tpr = d.D / 4;                                  // threads per row
+  const int row = blockIdx.x * (256 / tpr) + threadIdx.x / tpr;
+  const int c0 = 4 * (threadIdx.x % tpr);
+  if (row >= d.BH() * d.N) return;
   const int bh = row / d.N, i = row % d.N, bhk = d.kv_head(bh);
   const int limit = causal ? i + (d.Nk - d.N) : d.Nk - 1;   // last key row i sees
   const int rlast = min(sp.S - 1, limit / (sp.split_blocks * kBK));
   const float* ml = sp.part_ml + (size_t)row * sp.S * 2;
   float M = -__builtin_inff();
   for (int r = 0; r <= rlast; r++) M = fmaxf(M, ml[2 * r]);
-  float acc = 0.0f, l = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, l = 0.0f;
   for (int r = 0; r <= rlast; r++) {
     const float w = __builtin_amdgcn_exp2f(ml[2 * r] - M);
-    acc = __builtin_fmaf(w, sp.part_o[((size_t)row * sp.S + r) * d.D + c], acc);
+    const float4 p = *(const float4*)(sp.part_o + ((size_t)row * sp.S + r) * d.D + c0);
+    acc[0] = __builtin_fmaf(w, p.x, acc[0]);
+    acc[1] = __builtin_fmaf(w, p.y, acc[1]);
+    acc[2] = __builtin_fmaf(w, p.z, acc[2]);
+    acc[3] = __builtin_fmaf(w, p.w, acc[3]);
     l = __builtin_fmaf(w, ml[2 * r + 1], l);
   }
   const float inv_l = 1.0f / l;
-  const float val = __builtin_fmaf(acc * b.v_scale[(size_t)bhk * d.D + c], inv_l, b.v_mean[(size_t)bhk * d.D + c]);
-  store_out(o, (size_t)row * d.D + c, val, out_dtype);
+  const float4 vs = *(const float4*)(b.v_scale + (size_t)bhk * d.D + c0);
+  const float4 vm = *(const float4*)(b.v_mean + (size_t)bhk * d.D + c0);
+  const float y0 = __builtin_fmaf(acc[0] * vs.x, inv_l, vm.x), y1 = __builtin_fmaf(acc[1] * vs.y, inv_l, vm.y);
+  const float y2 = __builtin_fmaf(acc[2] * vs.z, inv_l, vm.z), y3 = __builtin_fmaf(acc[3] * vs.w, inv_l, vm.w);
+  const size_t oi = (size_t)row * d.D + c0;
+  if (((uintptr_t)o & 15) != 0) {
+    store_out(o, oi, y0, out_dtype);
+    store_out(o, oi + 1, y1, out_dtype);
+    store_out(o, oi + 2, y2, out_dtype);
+    store_out(o, oi + 3, y3, out_dtype);
+  } else if (out_dtype == kOutF32) {
+    *(float4*)((float*)o + oi) = make_float4(y0, y1, y2, y3);
+  } else {
+    *(uint2*)((uint16_t*)o + oi) = make_uint2(out_pack2(y0, y1, out_dtype), out_pack2(y2, y3, out_dtype));
+  }
 }
 
 template <int D, int BITS, bool SPLIT>
@@ -646,7 +666,11 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   const dim3 grid(qunits * d.BH() * (SPLIT ? sp.S : 1));
   if (causal) hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
   else hipLaunchKernelGGL((attn_kernel<D, BITS, false, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
-  if (SPLIT) hipLaunchKernelGGL(split_merge_kernel, dim3(d.BH() * d.N), dim3(128), 0, s, b, d, causal, sp, o, out_dtype);
+  if (SPLIT) {
+    const long long rows = (long long)d.BH() * d.N, rpw = 256 / (d.D / 4);
+    hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, s, b, d, causal, sp,
+                       o, out_dtype);
+  }
   return hipGetLastError();
 }
 
