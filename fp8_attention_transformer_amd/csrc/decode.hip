@@ -416,30 +416,41 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the key ranges, one workgroup per query head, one thread per
-// channel: M = max m_s, w_s = exp2(m_s - M), O = fma(w_s, O_s, O) and
+// Merge of the key ranges: D/4 threads per query head, four channels each
+// (16-byte loads of the partial outputs), 256/(D/4) heads per workgroup.
+// Per channel: M = max m_s, w_s = exp2(m_s - M), O = fma(w_s, O_s, O) and
 // l' = fma(w_s, l'_s, l') in range order, then O * vscale / l' + vmean.
-__global__ void __launch_bounds__(128) decode_merge_kernel(const float* __restrict__ part_o,
+__global__ void __launch_bounds__(256) decode_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            const float* __restrict__ v_scale,
-                                                           const float* __restrict__ v_mean, int Hq, int Hk, int S,
-                                                           int D, void* __restrict__ o, int out_dtype) {
-  const int bhq = blockIdx.x, c = threadIdx.x;
-  if (c >= D) return;
+                                                           const float* __restrict__ v_mean, int BHq, int Hq, int Hk,
+                                                           int S, int D, void* __restrict__ o, int out_dtype) {
+  const int tpr = D / 4;
+  const int bhq = blockIdx.x * (256 / tpr) + threadIdx.x / tpr, c0 = 4 * (threadIdx.x % tpr);
+  if (bhq >= BHq) return;
   const int g = Hq / Hk, bhk = (bhq / Hq) * Hk + (bhq % Hq) / g;
   const float* ml = part_ml + (size_t)bhq * S * 2;
   float M = -__builtin_inff();
 #pragma unroll 8
   for (int s = 0; s < S; s++) M = fmaxf(M, ml[2 * s]);
-  float acc = 0.0f, l = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, l = 0.0f;
 #pragma unroll 8
   for (int s = 0; s < S; s++) {
     const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    acc = __builtin_fmaf(w, part_o[((size_t)bhq * S + s) * D + c], acc);
+    const float4 p = *(const float4*)(part_o + ((size_t)bhq * S + s) * D + c0);
+    acc[0] = __builtin_fmaf(w, p.x, acc[0]);
+    acc[1] = __builtin_fmaf(w, p.y, acc[1]);
+    acc[2] = __builtin_fmaf(w, p.z, acc[2]);
+    acc[3] = __builtin_fmaf(w, p.w, acc[3]);
     l = __builtin_fmaf(w, ml[2 * s + 1], l);
   }
-  const float val = (acc * v_scale[(size_t)bhk * D + c]) / l + v_mean[(size_t)bhk * D + c];
-  store_out(o, (size_t)bhq * D + c, val, out_dtype);
+  const float4 vs = *(const float4*)(v_scale + (size_t)bhk * D + c0);
+  const float4 vm = *(const float4*)(v_mean + (size_t)bhk * D + c0);
+  const size_t oi = (size_t)bhq * D + c0;
+  store_out(o, oi, (acc[0] * vs.x) / l + vm.x, out_dtype);
+  store_out(o, oi + 1, (acc[1] * vs.y) / l + vm.y, out_dtype);
+  store_out(o, oi + 2, (acc[2] * vs.z) / l + vm.z, out_dtype);
+  store_out(o, oi + 3, (acc[3] * vs.w) / l + vm.w, out_dtype);
 }
 
 template <int IN, int D, int HG>
@@ -485,8 +496,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int in_dty
     if (d.D == 64) launch_decode_hg<0, 64>(a, d.BHk(), hg, s);
     else launch_decode_hg<0, 128>(a, d.BHk(), hg, s);
   }
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(d.BH()), dim3(128), 0, s, db.part_o, db.part_ml, b.v_scale, b.v_mean,
-                     d.H, d.Hk, a.S, d.D, o, out_dtype);
+  const int hpw = 256 / (d.D / 4);   // query heads per merge workgroup
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((d.BH() + hpw - 1) / hpw), dim3(256), 0, s, db.part_o, db.part_ml,
+                     b.v_scale, b.v_mean, d.BH(), d.H, d.Hk, a.S, d.D, o, out_dtype);
   return hipGetLastError();
 }
 
