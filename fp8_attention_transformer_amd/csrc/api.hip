@@ -128,9 +128,16 @@ Bufs to_internal(const sage_quant_bufs& q) {
   return b;
 }
 
+// 16-byte boundary: the kernels read inputs, codes and workspace arrays in
+// 16-byte pieces
+bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool a16(const void* a, const void* b, const void* c) { return a16(a) && a16(b) && a16(c); }
+
 bool bufs_ok(const sage_quant_bufs* q) {
   return q && q->q_codes && q->k_codes && q->q_scale && q->k_scale && q->q_mean && q->k_mean && q->v_codes &&
-         q->v_scale && q->delta_s && q->k_part && q->v_part && q->v_mean;
+         q->v_scale && q->delta_s && q->k_part && q->v_part && q->v_mean && a16(q->q_codes, q->k_codes, q->q_scale) &&
+         a16(q->k_scale, q->q_mean, q->k_mean) && a16(q->v_codes, q->v_scale, q->delta_s) &&
+         a16(q->k_part, q->v_part, q->v_mean);
 }
 
 // gfx950 check, cached once per device.
@@ -264,7 +271,7 @@ size_t sage_workspace_bytes_cross(int B, int Hq, int Hkv, int Nq, int Nk, int D)
 
 sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, int Hq, int Hkv, int Nq, int Nk,
                                                  int D, sage_quant_bufs* out) {
-  if (!ws || !out || !shape_ok(B, Hq, Hkv, Nq, Nk, D)) return SAGE_ERR_INVALID;
+  if (!ws || !out || !a16(ws) || !shape_ok(B, Hq, Hkv, Nq, Nk, D)) return SAGE_ERR_INVALID;
   const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
@@ -276,7 +283,7 @@ sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, 
 sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
                                     int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
                                     const sage_quant_bufs* out, hipStream_t stream) {
-  if (!q || !k || !v || !bufs_ok(out) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
+  if (!q || !k || !v || !a16(q, k, v) || !bufs_ok(out) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
     return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
@@ -292,7 +299,8 @@ sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, voi
                                 int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v,
                                 sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
+  if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) ||
+      !bits_ok(qk_bits))
     return SAGE_ERR_INVALID;
   if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
@@ -353,7 +361,8 @@ size_t sage_decode_workspace_bytes(int B, int Hq, int Hkv, int Nk, int D, int sp
 sage_status sage_attn_decode(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nk,
                              int D, float sm_scale, int smooth_v, int split_keys, sage_dtype in_dtype,
                              sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !decode_shape_ok(B, Hq, Hkv, Nk, D) || !split_ok(split_keys))
+  if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) || !decode_shape_ok(B, Hq, Hkv, Nk, D) ||
+      !split_ok(split_keys))
     return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
@@ -412,8 +421,8 @@ sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, voi
                                 int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v, int split_keys,
                                 sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits) ||
-      !split_ok(split_keys))
+  if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) ||
+      !bits_ok(qk_bits) || !split_ok(split_keys))
     return SAGE_ERR_INVALID;
   if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
@@ -499,7 +508,7 @@ static bool varlen_ok(const int* cu, int nseq, int max_seqlen, int total, int H,
 sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v, sage_dtype in_dtype,
                                      const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens, int H, int D,
                                      int qk_bits, int smooth_v, const sage_quant_bufs* out, hipStream_t stream) {
-  if (!q || !k || !v || !bufs_ok(out) || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
+  if (!q || !k || !v || !a16(q, k, v) || !bufs_ok(out) || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
     return SAGE_ERR_INVALID;
   if (!bits_ok(qk_bits) || (smooth_v != 0 && smooth_v != 1)) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
@@ -517,7 +526,8 @@ sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
                                  int nseq, int max_seqlen, int total_tokens, int H, int D, int causal, float sm_scale,
                                  int qk_bits, int smooth_v, sage_dtype in_dtype, sage_dtype out_dtype,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !o || !workspace || !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
+  if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) ||
+      !varlen_ok(cu_seqlens, nseq, max_seqlen, total_tokens, H, D))
     return SAGE_ERR_INVALID;
   if (!bits_ok(qk_bits) || (smooth_v != 0 && smooth_v != 1)) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;

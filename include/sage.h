@@ -13,6 +13,10 @@
  * Conventions for every entry point
  *  - Tensors are contiguous, row-major [B, H, N, D] device buffers (self
  *    attention: queries and keys share N).  D must be 64 or 128; B, H, N >= 1.
+ *  - q, k, v and workspaces start on a 16-byte boundary (the
+ *    kernels read them in 16-byte pieces), as do the arrays of a
+ *    sage_quant_bufs; otherwise the call returns SAGE_ERR_INVALID.  Outputs
+ *    may start anywhere (a misaligned one is written element by element).
  *  - Every buffer is owned by the caller.  The library allocates no device
  *    memory, keeps no pointer after returning and holds no mutable state
  *    (the gfx950 check is cached once per device).

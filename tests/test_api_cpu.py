@@ -95,6 +95,9 @@ def _attn(**kw):
     (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID), (dict(qk_bits=0), sage.ERR_INVALID),
     (dict(qk_bits=2), sage.ERR_INVALID), (dict(qk_bits=6), sage.ERR_INVALID), (dict(qk_bits=16), sage.ERR_INVALID),
     (dict(smooth_v=2), sage.ERR_INVALID), (dict(smooth_v=-1), sage.ERR_INVALID),
+    # inputs and workspace start on a 16-byte boundary (read in 16-byte pieces)
+    (dict(q=FAKE + 2), sage.ERR_INVALID), (dict(k=FAKE + (1 << 30) + 8), sage.ERR_INVALID),
+    (dict(v=FAKE + (2 << 30) + 4), sage.ERR_INVALID), (dict(ws=FAKE + (4 << 30) + 8), sage.ERR_INVALID),
 ])
 def test_attn_fwd_validation(kw, expect):
     assert _attn(**kw) == expect
@@ -107,6 +110,14 @@ def test_quant_smooth_and_debug_validation():
     assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, 4, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
     bad = sage.QuantBufs(*([FAKE] * 11 + [0]))
     assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(bad), None) == sage.ERR_INVALID
+    for i in range(12):   # every array of the buffer set on a 16-byte boundary
+        off = [FAKE] * 12
+        off[i] = FAKE + 4
+        mis = sage.QuantBufs(*off)
+        assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(mis),
+                                   None) == sage.ERR_INVALID, i
+    assert L.sage_quant_smooth(FAKE + 2, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(qb),
+                               None) == sage.ERR_INVALID
     assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, None, None) == sage.ERR_INVALID
     dbg = L.sage_qk_int32_debug
     assert dbg(ctypes.byref(qb), 1, 1, 100, 64, 4, 0, 0, 0, 101, 4, FAKE, None) == sage.ERR_INVALID
@@ -261,7 +272,9 @@ def test_decode_validation():
     for i, bad, expect in [(0, None, sage.ERR_INVALID), (6, 3, sage.ERR_INVALID), (7, 0, sage.ERR_INVALID),
                            (8, 96, sage.ERR_INVALID), (9, 0.0, sage.ERR_INVALID), (10, 2, sage.ERR_INVALID),
                            (11, 100, sage.ERR_INVALID), (12, sage.F32, sage.ERR_INVALID), (15, 64, sage.ERR_WORKSPACE),
-                           (3, FAKE + 16, sage.ERR_INVALID), (14, None, sage.ERR_INVALID)]:
+                           (3, FAKE + 16, sage.ERR_INVALID), (14, None, sage.ERR_INVALID),
+                           (0, FAKE + 2, sage.ERR_INVALID), (2, FAKE + (2 << 30) + 8, sage.ERR_INVALID),
+                           (14, FAKE + (4 << 30) + 4, sage.ERR_INVALID)]:
         args = list(base)
         args[i] = bad
         assert L.sage_attn_decode(*args) == expect, (i, bad)
