@@ -10,10 +10,10 @@
 // All kernels here are HBM-bound except the compensation term (matrix-core
 // dot products); they are launched in order on the caller's stream:
 //   stats -> finalize -> quant -> delta_s.
-// Self-attention handles a token block of Q, K and V in one workgroup; with
-// separate query and key/value geometry (cross-attention, decoding, grouped
-// heads) the stats and quant steps run once for the query side and once for
-// the key/value side.
+// The statistics cover the key/value side (the Q block means come from the
+// quant step, which holds each block anyway); the quant step runs once for
+// the query side and once for the key/value side, except for packed
+// sequences, where one workgroup handles a token block of Q, K and V.
 #include "sage_internal.h"
 #include "sage_device.h"
 
@@ -23,9 +23,9 @@ namespace sage {
 namespace {
 
 // Which inputs a prepass workgroup handles: the query side, the key/value
-// side, or both (self-attention, where a token block of Q, K and V is one
-// work item); kPartV: the V statistics alone (a decoding step, whose scores
-// need no K mean).
+// side, or both (packed self-attention, where a token block of Q, K and V is
+// one work item); kPartV: the V statistics alone (a decoding step, whose
+// scores need no K mean).
 enum Part { kPartQ = 1, kPartKV = 2, kPartBoth = 3, kPartV = 4 };
 
 // Workgroup barrier for LDS written with ds_write: waits for this wave's LDS
