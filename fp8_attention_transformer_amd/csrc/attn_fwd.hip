@@ -31,15 +31,6 @@
 #include "sage_internal.h"
 #include "sage_device.h"
 
-// Pipeline depth of the K/V staging (LDS buffers in flight) and whether the
-// matrix-core issue phases run at raised wave priority.
-#ifndef SAGE_STAGES
-#define SAGE_STAGES 2
-#endif
-#ifndef SAGE_SETPRIO
-#define SAGE_SETPRIO 0
-#endif
-
 namespace sage {
 namespace {
 
@@ -91,14 +82,17 @@ struct QOperand<D, 8> {
 // The FP6 operands of one lane chunk (`ci` = its chunk index in the tile).
 template <int D>
 __device__ __forceinline__ void load_fp6_chunk(const uint8_t* chunk, int ci, v8i* a) {
+  // Dwords 6-7 of an FP6 operand are not read by the instruction: leaving
+  // them undefined lets the 12 loaded dwords serve as both operands in place.
   if constexpr (D == 128) {
     const v4i u0 = *(const v4i*)chunk, u1 = *(const v4i*)(chunk + 16), u2 = *(const v4i*)(chunk + 32);
-    a[0] = (v8i){u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], 0, 0};
-    a[1] = (v8i){u1[2], u1[3], u2[0], u2[1], u2[2], u2[3], 0, 0};
+    const v8i w01 = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+    a[0] = __builtin_shufflevector(w01, w01, 0, 1, 2, 3, 4, 5, -1, -1);
+    a[1] = __builtin_shufflevector(u1, u2, 2, 3, 4, 5, 6, 7, -1, -1);
   } else {
     const v4i lo = *(const v4i*)(chunk + fp6_half_offset(ci, 0));
     const v4i hi = *(const v4i*)(chunk + fp6_half_offset(ci, 1));
-    a[0] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    a[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, -1, -1);
   }
 }
 
@@ -339,15 +333,11 @@ __device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOper
                                            const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
                                            int t, int klim, int n, int h, int nk, bool need_mask) {
   v16f S[4];
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   qk_part<D, BITS>(S, qop, cK, n, h);
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
   v8i P8[2];
   float alpha;
   softmax_part<D, CAUSAL, SPLIT>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha);
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(1);
   pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
-  if (SAGE_SETPRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 
@@ -364,21 +354,18 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
                                                       SplitParts sp) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int NDT = D / 32;
-  constexpr int S = SAGE_STAGES;
-  // vector-memory ops one block's staging issues per wave: K and V chunks via
-  // direct-to-LDS copies, plus the compensation and K-scale loads
-  constexpr int VM_PER_BLOCK = kBK * ROWB / 16 / 256 + D * kBK / 16 / 256 + 2;
-  // LDS buffers as separate arrays, so the compiler can tell the block being
-  // read from the blocks being filled by the asynchronous copies.
-  __shared__ __align__(16) uint8_t sK0[kBK * ROWB], sK1[kBK * ROWB], sK2[S > 2 ? kBK * ROWB : 16];
-  __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK], sV2[S > 2 ? D * kBK : 16];
-  __shared__ float sDS0[kBK], sDS1[kBK], sDS2[S > 2 ? kBK : 1];
-  __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup], sKS2[S > 2 ? kBK / kKGroup : 1];
+  // K/V staging: two LDS stages of one 128-key block each (double buffer),
+  // as separate arrays so the compiler can tell the block being read from the
+  // block being filled by the asynchronous copies.
+  __shared__ __align__(16) uint8_t sK0[kBK * ROWB], sK1[kBK * ROWB];
+  __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK];
+  __shared__ float sDS0[kBK], sDS1[kBK];
+  __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup];
   __shared__ float sVS[D], sVM[D];   // V scales and means of the head, for the epilogue
-  auto bK = [&](int i) { return i == 0 ? sK0 : (i == 1 ? sK1 : sK2); };
-  auto bV = [&](int i) { return i == 0 ? sV0 : (i == 1 ? sV1 : sV2); };
-  auto bDS = [&](int i) { return i == 0 ? sDS0 : (i == 1 ? sDS1 : sDS2); };
-  auto bKS = [&](int i) { return i == 0 ? sKS0 : (i == 1 ? sKS1 : sKS2); };
+  auto bK = [&](int i) { return i == 0 ? sK0 : sK1; };
+  auto bV = [&](int i) { return i == 0 ? sV0 : sV1; };
+  auto bDS = [&](int i) { return i == 0 ? sDS0 : sDS1; };
+  auto bKS = [&](int i) { return i == 0 ? sKS0 : sKS1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,24 +401,22 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const int te = SPLIT ? min(tend, tb + sp.split_blocks) : tend;
   if (tb >= te) return;   // no query of this tile sees a key of the range (whole workgroup)
 
-  // Every wave issues the same number of memory ops per block (the small
-  // loads are unconditional, with in-range indices), so a vmcnt limit of
-  // VM_PER_BLOCK * k waits exactly for all but the newest k blocks.
-  float ds_reg[S - 1], ks_reg[S - 1];
+  // the small loads are unconditional, with in-range indices
+  float ds_reg, ks_reg;
   const uint32_t koff = k_src_offset<D, BITS>(wave, lane), voff = v_src_offset(wave, lane);
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NPk * ROWB);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NPk * D);
   auto issue = [&](int t, int slot) {
     stage_kv_async<D, BITS>(bK(slot), bV(slot), rk, rv, t, wave, koff, voff);
-    ds_reg[t % (S - 1)] = dsrow[t * kBK + (tid & (kBK - 1))];
-    ks_reg[t % (S - 1)] = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
+    ds_reg = dsrow[t * kBK + (tid & (kBK - 1))];
+    ks_reg = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
   };
-  auto publish = [&](int t, int slot) {   // compensation row and K scales of block t -> LDS
-    if (tid < kBK) bDS(slot)[tid] = ds_reg[t % (S - 1)] * ks;
-    if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg[t % (S - 1)];
+  auto publish = [&](int slot) {   // compensation row and K scales of the block -> LDS
+    if (tid < kBK) bDS(slot)[tid] = ds_reg * ks;
+    if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg;
   };
 
-  // The head's V scales and means (read by the epilogue) load first, so every
+  // The head's V scales and means (read by the epilogue) load first, so the
   // wait below that covers block tb's copies covers them too.
   float vs_reg = 0.0f, vm_reg = 0.0f;
   if (tid < D) {
@@ -439,7 +424,6 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     vm_reg = b.v_mean[(size_t)bhk * D + tid];
   }
   issue(tb, 0);
-  if (S > 2 && te - tb > 1) issue(tb + 1, 1);
 
   QOperand<D, BITS> qop;
   load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
@@ -453,9 +437,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   as.m = -__builtin_inff();
   as.l = 0.0f;
 
-  if (S > 2 && te - tb > 1) wait_vmcnt<VM_PER_BLOCK>();
-  else wait_vmcnt<0>();
-  publish(tb, 0);
+  wait_vmcnt<0>();
+  publish(0);
   if (tid < D) {
     sVS[tid] = vs_reg;
     sVM[tid] = vm_reg;
@@ -463,18 +446,15 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   __syncthreads();
 
   for (int t = tb; t < te; t++) {
-    const int u = t - tb;                          // blocks done by this workgroup
-    const int slot = u % S;
-    const bool ahead = t + S - 1 < te;             // block t+S-1 exists: stage it now
-    if (ahead) issue(t + S - 1, (u + S - 1) % S);
+    const int slot = (t - tb) & 1;
+    const bool ahead = t + 1 < te;                 // block t+1 exists: stage it now
+    if (ahead) issue(t + 1, slot ^ 1);
     const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
     attn_block<D, BITS, CAUSAL, SPLIT>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, klim, n, h, nk,
                                        need_mask);
-    if (t + 1 < te) {
-      // block t+1 must have landed; block t+S-1 (issued above) may stay in flight
-      if (ahead && S > 2) wait_vmcnt<VM_PER_BLOCK * (S > 2 ? S - 2 : 0)>();
-      else wait_vmcnt<0>();
-      publish(t + 1, (u + 1) % S);
+    if (ahead) {
+      wait_vmcnt<0>();   // block t+1 has landed (this wave's copies)
+      publish(slot ^ 1);
     }
     __syncthreads();
   }

@@ -208,11 +208,13 @@ __device__ __forceinline__ void split8(const float* x, v8bf& p1, v8bf& p2, v8bf&
 // <= 7, INT8: <= 127), as floats, bit-identical to a true IEEE division per
 // element: the correctly rounded quotient from the reciprocal and one
 // remainder correction (div_rn), a true division for the whole wave only when
-// some lane's scale is outside the exact case.  |x| <= qmax*delta makes the
-// clamp unnecessary.  Adding +0 turns a rounded -0 into +0 (code 0 has one
-// pattern).
+// some lane's scale is outside the exact case.  The codes are clamped to
+// [-qmax, qmax]: |x| <= amax, but delta = amax/qmax rounds below the exact
+// quotient when it falls among the fp32 subnormals, and x/delta can then
+// exceed qmax.  Adding +0 turns a rounded -0 into +0 (code 0 has one pattern).
 template <int NV, int BITS>
 __device__ __forceinline__ void int_codes_f(const float* x, float delta, float* c) {
+  constexpr float qmax = BITS == 4 ? 7.0f : 127.0f;
   const float r = delta == 0.0f ? 0.0f : 1.0f / delta;
   if (__any(div_rn_hard(delta))) {
 #pragma unroll
@@ -222,7 +224,7 @@ __device__ __forceinline__ void int_codes_f(const float* x, float delta, float* 
     for (int e = 0; e < NV; e++) c[e] = rintf(div_rn(x[e], delta, r));
   }
 #pragma unroll
-  for (int e = 0; e < NV; e++) c[e] = c[e] + 0.0f;
+  for (int e = 0; e < NV; e++) c[e] = fminf(fmaxf(c[e], -qmax), qmax) + 0.0f;
 }
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef int v6i_t __attribute__((ext_vector_type(6)));

@@ -194,3 +194,58 @@ def cos_sim(a, b) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()
     return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+# The output bar: max-abs 2e-3 against the oracle's mirror of the method.
+O_TOL = 2e-3
+# Relative window around FP8 rounding midpoints inside which the mirror marks
+# a P~ element as one whose code the GPU's exp2 or compensation rounding could
+# flip; reported for diagnosis only, it widens no bar.
+EPS_TIE = 2.0 ** -14
+
+
+def output_rounding(O_ref, out_dtype: str) -> np.ndarray:
+    """Half a unit in the last place of a 16-bit output format at the size of
+    |O| (plus the bar): the rounding of the fp32 result to the output dtype."""
+    if out_dtype == "f32":
+        return np.zeros(O_ref.shape)
+    mant = 7 if out_dtype == "bf16" else 10
+    mag = np.maximum(np.abs(O_ref.astype(np.float64)) + O_TOL, 2.0 ** -24)
+    return np.exp2(np.floor(np.log2(mag)) - mant - 1)
+
+
+def compare_o(O_gpu, O_ref, label: str, out_dtype: str = "f32", slack=None):
+    """Element-wise |O_gpu - O_ref| <= 2e-3, plus (16-bit outputs only) the
+    output rounding.  NaN fails.  Prints the largest error and, if the mirror's
+    midpoint slack is given, how many rows hold a P~ element near an FP8
+    midpoint (diagnostic)."""
+    g = np.asarray(O_gpu, np.float64)
+    r = np.asarray(O_ref, np.float64)
+    err = np.abs(g - r)
+    allowed = O_TOL + output_rounding(r, out_dtype)
+    bad_el = ~(err <= allowed)
+    bad = np.nonzero(bad_el.reshape(bad_el.shape[0], -1).any(1))[0]
+    extra = ""
+    if slack is not None:
+        extra = f" rows_near_fp8_midpoint={int(np.sum(np.asarray(slack) > 0))}"
+    print(f"[{label}] rows={r.shape[0]} maxerr={err.max():.3e} out={out_dtype}{extra}")
+    assert bad.size == 0, (label, bad[:5], err.reshape(err.shape[0], -1).max(1)[bad[:5]])
+    return float(err.max())
+
+
+def sample_rows(N: int, heads: int, rng, per_head: int = 4, pair_blocks: bool = True) -> np.ndarray:
+    """Query rows of every head (flattened head*N + i): the first and last rows,
+    the first block's edge, the start and last row of the tail block, the
+    middle, one row in query block p and one in its causal pair partner
+    NQB-1-p (p varies with the head), and per_head random rows."""
+    nqb = (N + 127) // 128
+    rows = []
+    for hh in range(heads):
+        pick = {0, 1, 127, 128, N // 2, N - 1, (nqb - 1) * 128}
+        if pair_blocks and nqb > 1:
+            p = hh % nqb
+            pick.add(p * 128 + int(rng.integers(0, 128)))
+            pick.add((nqb - 1 - p) * 128 + int(rng.integers(0, 128)))
+        pick.update(rng.integers(0, N, per_head).tolist())
+        rows.extend(hh * N + np.array(sorted(i for i in pick if 0 <= i < N)))
+    return np.array(rows, np.int64)

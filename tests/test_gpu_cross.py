@@ -4,7 +4,7 @@ and multi-query heads (Hq = g * Hkv), causal masks aligned at the last key.
 
 Bar: prepass codes, scales, means and FP8 V bit-exact against the oracle; the
 compensation term within the fp32-chain bound of its bf16x3 evaluation; O
-within max-abs 2e-3 plus the FP8-midpoint slack of the oracle's mirror mode.
+within max-abs 2e-3 of the oracle's mirror mode (element-wise, fp32 output).
 """
 from __future__ import annotations
 
@@ -76,10 +76,8 @@ def _check_prepass(rb, z, k_bits, oracle_lib):
 
 
 def _compare_o(O_gpu, O_ref, slack, label):
-    err = np.abs(O_gpu.astype(np.float64) - O_ref.astype(np.float64)).max(1)
-    bad = np.nonzero(~(err <= O_TOL + slack))[0]   # NaN rows fail too
-    print(f"[{label}] rows={err.size} maxerr={err.max():.3e}")
-    assert bad.size == 0, (label, bad[:5], err[bad[:5]], slack[bad[:5]])
+    import gpu_helpers as gh
+    gh.compare_o(O_gpu, O_ref, label, slack=slack)
 
 
 @pytest.mark.parametrize("case", CASES, ids=_id)
@@ -158,8 +156,8 @@ def test_cross_split_calls_equal_fwd(oracle_lib):
 def test_chunk_full_size(oracle_lib, bits):
     """The benchmark's chunked-prefill workload (512 queries against 8192 cached
     keys, 32 query heads on 8 K/V heads, causal) through the cross-geometry
-    entry points: every head's prepass bit-exact; compensation term and O on
-    sampled rows of the first and last query heads."""
+    entry points: every head's prepass bit-exact; O on rows of every query
+    head."""
     import gpu_helpers as gh
     w = wl.CHUNK
     q, k, v = wl.generate(w)
@@ -173,16 +171,12 @@ def test_chunk_full_size(oracle_lib, bits):
     for name in ("k_codes", "k_scale", "k_mean", "v_codes", "v_scale", "v_mean"):
         assert np.array_equal(getattr(rb, name), fk(getattr(z_all, name))), name
     del z_all
-    O_gpu = out.cpu().numpy().reshape(w.B * w.H, w.N, w.D)
-    g = w.H // w.hkv
-    rng = np.random.default_rng(7)
-    for h in (0, w.H - 1):
-        qs, ks, vs = q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1]
-        z = oracle_lib.quant_smooth(qs, ks, vs, oracle_lib.DT_BF16, qk_bits=bits)
-        rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1], rng.integers(0, w.N, 60)]))
-        O_ref, slack, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=EPS_TIE)
-        _compare_o(O_gpu[h][rows], O_ref, slack, f"{w.name}/int{bits}/h{h}")
-        O_fp, _ = oracle_lib.attn_exact(qs, ks, vs, 1, True, w.scale, 0, rows=rows)
-        c_gpu, c_orc = gh.cos_sim(O_gpu[h][rows], O_fp), gh.cos_sim(O_ref, O_fp)
-        print(f"[{w.name}/int{bits}/h{h}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
-        assert abs(c_gpu - c_orc) < 1e-3
+    O_gpu = out.cpu().numpy().reshape(w.B * w.H * w.N, w.D)
+    z = oracle_lib.quant_smooth(q, k, v, oracle_lib.DT_BF16, qk_bits=bits)
+    rows = gh.sample_rows(w.N, w.B * w.H, np.random.default_rng(7))
+    O_ref, slack, _ = oracle_lib.attn_mirror(z, True, w.scale, rows=rows, eps=EPS_TIE)
+    _compare_o(O_gpu[rows], O_ref, slack, f"{w.name}/int{bits}/all_heads")
+    O_fp, _ = oracle_lib.attn_exact(q, k, v, 1, True, w.scale, 0, rows=rows)
+    c_gpu, c_orc = gh.cos_sim(O_gpu[rows], O_fp), gh.cos_sim(O_ref, O_fp)
+    print(f"[{w.name}/int{bits}] cos_sim gpu={c_gpu:.5f} oracle={c_orc:.5f}")
+    assert abs(c_gpu - c_orc) < 1e-3

@@ -5,7 +5,7 @@ A packed batch is nseq independent self-attention problems in token-major
 separate varlen mode: each sequence is checked against the dense oracle run on
 that sequence alone ([1, H, N_s, D]), which is what the entry point promises.
 Bit-exact: codes, scales, means, FP8 V per sequence; O within the same bar as
-the dense tests (max-abs 2e-3 plus the FP8-midpoint slack).
+the dense tests (max-abs 2e-3, element-wise, fp32 output).
 """
 from __future__ import annotations
 
@@ -106,10 +106,7 @@ def test_varlen_parity(oracle_lib, case):
             assert not vcodes[n:npad].any() and not rb.q_codes_all[bh, n:npad].any(), (s, h, "padding")
         O_ref, slack, _ = oracle_lib.attn_mirror(z, causal, scale, eps=EPS_TIE)
         O_gpu = np.transpose(O_all[cu[s]:cu[s + 1]], (1, 0, 2)).reshape(-1, D)
-        err = np.abs(O_gpu.astype(np.float64) - O_ref).max(1)
-        bad = np.nonzero(~(err <= O_TOL + slack))[0]
-        print(f"[seq {s} n={n}] maxerr={err.max():.3e}")
-        assert bad.size == 0, (s, bad[:5], err[bad[:5]])
+        gh.compare_o(O_gpu, O_ref, f"seq {s} n={n}", slack=slack)
 
 
 def test_varlen_single_sequence_equals_dense(oracle_lib):

@@ -262,3 +262,57 @@ def test_v_smoothing_restores_offset_exactly(oracle_lib):
     ref = _brute_force(Q, K, Vo, False, scale).reshape(-1, D)
     Om, _, _ = oracle_lib.attn_mirror(z, False, scale, quant_p=False)
     assert np.abs(Om - ref).max() <= 5e-6 * np.abs(Vo).max()
+
+
+def _one_row_quant(oracle_lib, ds_keys, v_rows, v_scale, sm_scale):
+    """A single query (zero codes, so its scores are the compensation term
+    alone: s2_j = (DeltaS_j * sm_scale * log2 e)) against len(ds_keys) keys with
+    the given FP8 V codes and channel scales."""
+    Nk, D = len(ds_keys), v_rows.shape[1]
+    return oracle_lib.Quant(
+        q_codes=np.zeros((1, 1, 1, D), np.int8), q_scale=np.zeros((1, 1, 1), np.float32),
+        k_codes=np.zeros((1, 1, Nk, D), np.int8), k_scale=np.zeros((1, 1, 2 * ((Nk + 31) // 32)), np.float32),
+        q_mean=np.zeros((1, 1, 1, D), np.float32), k_mean=np.zeros((1, 1, D), np.float32),
+        v_codes=np.ascontiguousarray(v_rows[None, None], np.uint8), v_scale=np.asarray(v_scale, np.float32)[None, None],
+        delta_s=np.asarray(ds_keys, np.float32)[None, None, None], v_mean=np.zeros((1, 1, D), np.float32))
+
+
+def test_midpoint_slack_is_the_code_flip_effect(oracle_lib):
+    """The mirror's diagnostic slack: with exactly one P~ element within the
+    window of an e4m3 rounding midpoint, the slack equals the effect on O of
+    rounding that element the other way, max_c |step * v_c * vscale_c| / l';
+    with no element near a midpoint it is zero."""
+    D, scale = 64, 0.5
+    ks = np.float32(scale) * np.float32(1.44269504088896340736)
+    log2_448 = np.float32(8.80735492205760410744)
+    rng = np.random.default_rng(3)
+    v_rows = rng.integers(0, 0x7F, (2, D)).astype(np.uint8)          # finite e4m3 codes
+    v_scale = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    vdec = oracle_lib.e4m3_decode(v_rows).astype(np.float64) * v_scale
+
+    def row(target_p):
+        # key 0 holds the maximum (s2 = 0, p' = 448); key 1 is placed at p' = target_p
+        s2_1 = np.float32(np.log2(np.float64(target_p) / 448.0))
+        ds1 = np.float32(s2_1 / ks)
+        z = _one_row_quant(oracle_lib, [0.0, ds1], v_rows, v_scale, scale)
+        O, slack, lse = oracle_lib.attn_mirror(z, False, scale, eps=2.0 ** -14)
+        # the p' of key 1 as the mirror forms it
+        s2 = np.float32(ds1 * ks)
+        mm = np.float32(np.float32(0.0) - log2_448)
+        p1 = np.float32(np.exp2(np.float64(np.float32(s2 - mm))))
+        return O[0], float(slack[0]), float(lse[0, 1]), p1
+
+    # p' = 272 is the midpoint of the e4m3 neighbours 256 and 288
+    O, slack, l, p1 = row(272.0)
+    assert abs(p1 / 272.0 - 1) < 2.0 ** -16
+    step = 288.0 - 256.0
+    flip = step * np.abs(vdec[1]).max() / l            # effect of rounding p'_1 the other way
+    assert slack == pytest.approx(flip, rel=1e-5)
+    # the same number from the two outputs: both roundings of P~_1, normalised by l'
+    O_lo = (448.0 * vdec[0] + 256.0 * vdec[1]) / l
+    O_hi = (448.0 * vdec[0] + 288.0 * vdec[1]) / l
+    assert np.abs(O_hi - O_lo).max() == pytest.approx(slack, rel=1e-5)
+    assert min(np.abs(O - O_lo).max(), np.abs(O - O_hi).max()) <= 1e-6 * np.abs(O_lo).max()
+    # away from any midpoint (p' = 300, between the midpoints 272 and 304): no slack
+    _, slack0, _, _ = row(300.0)
+    assert slack0 == 0.0
