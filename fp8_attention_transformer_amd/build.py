@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsage.so")
-SOURCES = ["api.hip", "prepass.hip", "attn_fwd.hip", "decode.hip"]
+SOURCES = ["api.hip", "prepass.hip", "attn_fwd.hip", "decode.hip", "static_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -25,8 +25,9 @@ EXPORTED = [
     "sage_workspace_bytes_cross", "sage_quant_bufs_from_workspace_cross", "sage_quant_smooth_cross",
     "sage_attn_fwd_cross", "sage_attn_quantized_cross",
     "sage_decode_split_keys", "sage_decode_workspace_bytes", "sage_attn_decode",
-    "sage_split_keys", "sage_split_workspace_bytes", "sage_attn_fwd_split",
+    "sage_split_keys", "sage_split_workspace_bytes", "sage_attn_fwd_split", "sage_attn_fwd_static",
 ]
+STATIC_SCRATCH_BYTES = 128 << 20   # SAGE_STATIC_SCRATCH_BYTES
 
 
 class QuantBufs(ctypes.Structure):
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.sage_split_workspace_bytes.restype = sz
         L.sage_attn_fwd_split.argtypes = [P, P, P, P] + [i32] * 7 + [f32, i32, i32, i32, i32, i32, P, sz, P]
         L.sage_attn_fwd_split.restype = i32
+        L.sage_attn_fwd_static.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, P]
+        L.sage_attn_fwd_static.restype = i32
         _lib = L
     return _lib
 
@@ -141,6 +144,16 @@ def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: 
              qk_bits: int = 4, smooth_v: bool = False) -> None:
     _check(lib().sage_attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale), qk_bits,
                                int(bool(smooth_v)), in_dtype, out_dtype, ws_ptr, ws_bytes, stream), "sage_attn_fwd")
+
+
+def attn_fwd_static(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool,
+                    sm_scale: float, in_dtype: int, out_dtype: int, stream: int = 0, qk_bits: int = 4,
+                    smooth_v: bool = False) -> None:
+    """sage_attn_fwd_static: the forward with the library's fixed device scratch
+    array as its workspace (nothing is allocated)."""
+    _check(lib().sage_attn_fwd_static(q_ptr, k_ptr, v_ptr, o_ptr, B, H, N, D, int(bool(causal)), float(sm_scale),
+                                      qk_bits, int(bool(smooth_v)), in_dtype, out_dtype, stream),
+           "sage_attn_fwd_static")
 
 
 def attn_quantized(bufs: QuantBufs, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool, sm_scale: float,

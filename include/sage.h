@@ -170,6 +170,23 @@ sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, 
                           sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sage_attn_fwd without a workspace argument.  The prepass buffers live in a
+ * fixed device array of SAGE_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing.
+ * Shapes whose sage_workspace_bytes exceeds the array return
+ * SAGE_ERR_WORKSPACE (128 MiB: for example B1 H16 N8192 D128 fits, B1 H16
+ * N16384 D128 does not).  All calls on one GPU share its array and it keeps
+ * the last call's buffers: calls that overlap on one GPU (several streams or
+ * threads) race.  Other arguments, results and errors as for sage_attn_fwd.
+ */
+#define SAGE_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+sage_status sage_attn_fwd_static(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
+                                 int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
+                                 sage_dtype out_dtype, hipStream_t stream);
+
+/*
  * The fused attention kernel alone, over prepass buffers already written by
  * sage_quant_smooth (or by an earlier sage_attn_fwd): INT4 QK^T,
  * dequantization with the compensation term, online softmax, FP8 P~V with

@@ -297,3 +297,16 @@ def test_split_validation():
         args = list(base)
         args[i] = bad
         assert L.sage_attn_fwd_split(*args) == expect, (i, bad)
+
+
+def test_static_entry_rejects_before_any_device_call():
+    """sage_attn_fwd_static: a shape whose workspace exceeds the fixed scratch
+    array returns SAGE_ERR_WORKSPACE, an invalid shape SAGE_ERR_INVALID, both
+    before anything touches a device."""
+    L = sage.lib()
+    big = (1, 16, 16384, 128)
+    assert sage.workspace_bytes(*big) > sage.STATIC_SCRATCH_BYTES
+    assert sage.workspace_bytes(1, 16, 8192, 128) <= sage.STATIC_SCRATCH_BYTES
+    args = lambda shape: (FAKE, FAKE, FAKE, FAKE + (1 << 30)) + shape + (0, 0.1, 4, 0, sage.BF16, sage.BF16, None)
+    assert L.sage_attn_fwd_static(*args(big)) == sage.ERR_WORKSPACE
+    assert L.sage_attn_fwd_static(*args((1, 1, 10, 96))) == sage.ERR_INVALID
