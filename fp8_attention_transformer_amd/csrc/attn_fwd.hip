@@ -176,20 +176,23 @@ __device__ __forceinline__ uint32_t v_src_offset(int wave, int lane) {
 }
 
 // The copies use buffer loads straight to LDS: the per-lane offset is one VGPR
-// and block, round and wave offsets stay scalar.
+// and block, round and wave offsets stay scalar.  K codes and V bytes of a
+// block are staged at different times (see the key loop), so separately.
 template <int D, int BITS>
-__device__ __forceinline__ void stage_kv_async(uint8_t* sK, uint8_t* sV, __amdgpu_buffer_rsrc_t rk,
-                                               __amdgpu_buffer_rsrc_t rv, int t, int wave, uint32_t koff,
-                                               uint32_t voff) {
+__device__ __forceinline__ void stage_k_async(uint8_t* sK, __amdgpu_buffer_rsrc_t rk, int t, int wave, uint32_t koff) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
-  constexpr int KCH = kBK * ROWB / 16 / 256, VCH = D * kBK / 16 / 256;
+  constexpr int KCH = kBK * ROWB / 16 / 256;
   static_assert(KCH * 16 * 256 == kBK * ROWB, "whole copy rounds");
   const uint32_t kb = (uint32_t)t * (kBK * ROWB) + 1024u * wave;
-  const uint32_t vb = (uint32_t)t * (D * kBK) + 1024u * wave;
 #pragma unroll
   for (int i = 0; i < KCH; i++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(sK + 4096 * i + 1024 * wave), 16, koff, kb + 4096 * i, 0,
                                              0);
+}
+template <int D>
+__device__ __forceinline__ void stage_v_async(uint8_t* sV, __amdgpu_buffer_rsrc_t rv, int t, int wave, uint32_t voff) {
+  constexpr int VCH = D * kBK / 16 / 256;
+  const uint32_t vb = (uint32_t)t * (D * kBK) + 1024u * wave;
 #pragma unroll
   for (int i = 0; i < VCH; i++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sV + 4096 * i + 1024 * wave), 16, voff, vb + 4096 * i, 0,
@@ -203,11 +206,11 @@ struct AttnState {
   float m, l;
 };
 
-// The three parts of one 128-key block for this wave.  qk_part: S^T tiles
-// (exact integer dot products as floats).  softmax_part: dequantization into
-// the log2 domain, masking, online-softmax update, P~ -> e4m3 matrix-core
-// operands.  pv_part: O = alpha*O, then O += P~V on the FP8 matrix core (fp32
-// accumulation into the running buffer).
+// The parts of one 128-key block for this wave.  qk_part: S^T tiles (exact
+// integer dot products as floats).  softmax_part: dequantization into the
+// log2 domain, masking, online-softmax update, P~ -> e4m3 matrix-core
+// operands.  rescale and pv_mfma: O = alpha*O, then O += P~V on the FP8
+// matrix core (fp32 accumulation into the running buffer).
 template <int D, int BITS>
 __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, const uint8_t* cK, int n, int h) {
 #pragma unroll
@@ -229,13 +232,45 @@ __device__ __forceinline__ void qk_part(v16f* S, const QOperand<D, BITS>& qop, c
   }
 }
 
-// nk: valid keys of the head; klim: the last key this lane's query may see
-// (causal); need_mask: some key of block t is masked for some query of the
-// workgroup (wave-uniform).
-template <int D, bool CAUSAL, bool SPLIT>
+// One FP8 matrix-core product of P~V: O[dt] += V(channels 32dt.., keys of
+// half kh) * P~(keys of half kh)^T, V read from the block's LDS slot.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void pv_mfma(AttnState<D, CAUSAL>& as, const v8i* P8, const uint8_t* cV, int n, int h,
+                                        int dt, int kh) {
+  const int row = 32 * dt + n;
+  const int c0 = 4 * kh + 2 * h;
+  const v4i lo = *(const v4i*)(cV + row * kBK + 16 * (c0 ^ vswz(row)));
+  const v4i hi = *(const v4i*)(cV + row * kBK + 16 * ((c0 + 1) ^ vswz(row)));
+  const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  as.O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], as.O[dt], 0, 0, 0, 0, 0, 0);
+}
+
+// Quarter T of the previous block's P~V products, pinned in the schedule next
+// to the vector work of score tile T (the scheduler would otherwise gather
+// them).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void pv_quarter(AttnState<D, CAUSAL>& as, const v8i* P8p, const uint8_t* cVp, int n, int h,
+                                           int T) {
+  constexpr int NPV = 2 * (D / 32);   // products per block: (kh, dt) kh-major
+#pragma unroll
+  for (int j = T * NPV / 4; j < (T + 1) * NPV / 4; j++) pv_mfma<D, CAUSAL>(as, P8p, cVp, n, h, j % (D / 32), j / (D / 32));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The softmax of block t.  nk: valid keys of the head; klim: the last key
+// this lane's query may see (causal); need_mask: some key of block t is
+// masked for some query of the workgroup (wave-uniform).  PIPE (the
+// pipelined key loop): P8p and cVp are the previous block's P~ and V slot:
+// its 2*D/32 P~V products (which accumulate
+// into O, already rescaled by that block's alpha) are spread over this
+// block's exponentials, so the matrix core works on them while the vector
+// unit works here.  For the first block of a range P8p is zero (the products
+// add exactly zero).
+template <int D, bool CAUSAL, bool SPLIT, bool PIPE>
 __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
                                              const float* cKS, float dq, float ks, int t, int klim, int h, int nk,
-                                             bool need_mask, v8i* P8, float& alpha) {
+                                             bool need_mask, v8i* P8, float& alpha, const v8i* P8p,
+                                             const uint8_t* cVp, int n) {
   float s2[4][16];
   float tmax[4];
 #pragma unroll
@@ -284,6 +319,7 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
     for (int w = 0; w < 4; w++)
       P8[T >> 1][4 * (T & 1) + w] =
           (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3], __float_as_int(s2[T][4 * w]));
+    if constexpr (PIPE) pv_quarter<D, CAUSAL>(as, P8p, cVp, n, h, T);
   }
   float tsum[4];
 #pragma unroll
@@ -293,23 +329,13 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
   as.m = mnew;
 }
 
+// O = alpha * O (the running buffer, once the previous block's products are in it)
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void pv_part(AttnState<D, CAUSAL>& as, const v8i* P8, float alpha, const uint8_t* cV, int n,
-                                        int h) {
+__device__ __forceinline__ void rescale(AttnState<D, CAUSAL>& as, float alpha) {
 #pragma unroll
-  for (int dt = 0; dt < D / 32; dt++) {
-    const int row = 32 * dt + n;
+  for (int dt = 0; dt < D / 32; dt++)
 #pragma unroll
     for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
-#pragma unroll
-    for (int kh = 0; kh < 2; kh++) {
-      const int c0 = 4 * kh + 2 * h;
-      const v4i lo = *(const v4i*)(cV + row * kBK + 16 * (c0 ^ vswz(row)));
-      const v4i hi = *(const v4i*)(cV + row * kBK + 16 * ((c0 + 1) ^ vswz(row)));
-      const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      as.O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, P8[kh], as.O[dt], 0, 0, 0, 0, 0, 0);
-    }
-  }
 }
 
 // Two outputs as one packed pair of 16-bit values, each rounded to nearest
@@ -327,29 +353,18 @@ __device__ __forceinline__ uint32_t out_pack2(float a, float b, int out_dtype) {
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One whole block in sequence (the four-wave kernel).
-template <int D, int BITS, bool CAUSAL, bool SPLIT>
-__device__ __forceinline__ void attn_block(AttnState<D, CAUSAL>& as, const QOperand<D, BITS>& qop, const uint8_t* cK,
-                                           const uint8_t* cV, const float* cDS, const float* cKS, float dq, float ks,
-                                           int t, int klim, int n, int h, int nk, bool need_mask) {
-  v16f S[4];
-  qk_part<D, BITS>(S, qop, cK, n, h);
-  v8i P8[2];
-  float alpha;
-  softmax_part<D, CAUSAL, SPLIT>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha);
-  pv_part<D, CAUSAL>(as, P8, alpha, cV, n, h);
-}
-
-
 // Dense causal calls with at most this many query blocks per head pair the
 // blocks in workgroups (measured: +4-7% at 32 and 64 blocks, -1-2% at 128
 // and 256, where the finer units balance better).
 constexpr int kPairMaxBlocks = 64;
+// Key ranges of at most this many 128-key blocks on average run the
+// pipelined key loop (D = 128 only).
+constexpr int kPipeMaxBlocks = 96;
 
 // SPLIT: workgroup (head, key range, query block) runs the method over one
 // range of key blocks from an empty state and writes its unnormalised state
 // (O, running max, row sum) for a merge kernel (dense geometry only).
-template <int D, int BITS, bool CAUSAL, bool SPLIT>
+template <int D, int BITS, bool CAUSAL, bool SPLIT, bool PIPE>
 __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype,
                                                       SplitParts sp) {
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
@@ -406,8 +421,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const uint32_t koff = k_src_offset<D, BITS>(wave, lane), voff = v_src_offset(wave, lane);
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NPk * ROWB);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NPk * D);
-  auto issue = [&](int t, int slot) {
-    stage_kv_async<D, BITS>(bK(slot), bV(slot), rk, rv, t, wave, koff, voff);
+  auto issue_k = [&](int t, int slot) {   // K codes, compensation row and K scales of block t
+    stage_k_async<D, BITS>(bK(slot), rk, t, wave, koff);
     ds_reg = dsrow[t * kBK + (tid & (kBK - 1))];
     ks_reg = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
   };
@@ -423,7 +438,8 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     vs_reg = b.v_scale[(size_t)bhk * D + tid];
     vm_reg = b.v_mean[(size_t)bhk * D + tid];
   }
-  issue(tb, 0);
+  issue_k(tb, 0);
+  stage_v_async<D>(bV(0), rv, tb, wave, voff);
 
   QOperand<D, BITS> qop;
   load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
@@ -445,18 +461,76 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   }
   __syncthreads();
 
-  for (int t = tb; t < te; t++) {
-    const int slot = (t - tb) & 1;
-    const bool ahead = t + 1 < te;                 // block t+1 exists: stage it now
-    if (ahead) issue(t + 1, slot ^ 1);
-    const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
-    attn_block<D, BITS, CAUSAL, SPLIT>(as, qop, bK(slot), bV(slot), bDS(slot), bKS(slot), dq, ks, t, klim, n, h, nk,
-                                       need_mask);
-    if (ahead) {
-      wait_vmcnt<0>();   // block t+1 has landed (this wave's copies)
-      publish(slot ^ 1);
+  if constexpr (!PIPE) {
+    // Plain key loop: iteration t stages block t+1 (K codes and V bytes) and
+    // runs block t's S^T tiles, softmax and P~V in sequence.
+    for (int t = tb; t < te; t++) {
+      const int slot = (t - tb) & 1;
+      const bool ahead = t + 1 < te;   // block t+1 exists: stage it now
+      if (ahead) {
+        issue_k(t + 1, slot ^ 1);
+        stage_v_async<D>(bV(slot ^ 1), rv, t + 1, wave, voff);
+      }
+      const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
+      v16f S[4];
+      qk_part<D, BITS>(S, qop, bK(slot), n, h);
+      v8i P8[2];
+      float alpha;
+      softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha,
+                                            nullptr, nullptr, n);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
+        pv_mfma<D, CAUSAL>(as, P8, bV(slot), n, h, dt, 0);
+        pv_mfma<D, CAUSAL>(as, P8, bV(slot), n, h, dt, 1);
+      }
+      if (ahead) {
+        wait_vmcnt<0>();   // block t+1 has landed (this wave's copies)
+        publish(slot ^ 1);
+      }
+      __syncthreads();
     }
+  } else {
+    // Software-pipelined key loop.  Iteration t computes block t's S^T tiles,
+    // rescales O by block t-1's alpha, and runs block t's softmax (vector unit)
+    // with block t-1's P~V products spread through it (matrix core).  Block t's
+    // V bytes are therefore read one iteration after its K codes, and staged
+    // one iteration later: K codes of block t+1 and V bytes of block t are
+    // copied during iteration t (two LDS slots each; a slot is rewritten only
+    // after the barrier that follows its last read).
+    v8i P8p[2] = {};       // P~ of the previous block (zero before the first)
+    float alpha_p = 1.0f;  // alpha of the previous block
+  #pragma clang loop unroll(disable)
+    for (int t = tb; t < te; t++) {
+      const int slot = (t - tb) & 1;
+      const bool ahead = t + 1 < te;
+      if (t > tb) __syncthreads();   // block t's K codes, compensation row and scales are in LDS
+      if (ahead) issue_k(t + 1, slot ^ 1);
+      if (t > tb) stage_v_async<D>(bV(slot), rv, t, wave, voff);
+      v16f S[4];
+      qk_part<D, BITS>(S, qop, bK(slot), n, h);
+      rescale<D, CAUSAL>(as, alpha_p);
+      const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
+      v8i P8[2];
+      // the previous block's V slot; in the first iteration any valid slot (its
+      // products with P8p = 0 add zero)
+      const uint8_t* cVp = bV(t > tb ? slot ^ 1 : 0);
+      softmax_part<D, CAUSAL, SPLIT, true>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha_p, P8p,
+                                       cVp, n);
+      P8p[0] = P8[0];
+      P8p[1] = P8[1];
+      wait_vmcnt<0>();   // K codes of block t+1 and V bytes of block t have landed (this wave's copies)
+      if (ahead) publish(slot ^ 1);
+    }
+    // the last block's P~V
+    rescale<D, CAUSAL>(as, alpha_p);
     __syncthreads();
+    {
+      const uint8_t* cVl = bV((te - 1 - tb) & 1);
+  #pragma unroll
+      for (int j = 0; j < 2 * NDT; j++) pv_mfma<D, CAUSAL>(as, P8p, cVl, n, h, j % NDT, j / NDT);
+    }
   }
 
   const int qi = qrow;
@@ -644,8 +718,28 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   // dense causal with few query blocks: one workgroup per pair (see the kernel)
   const int qunits = (causal && !SPLIT && !d.cu && d.NQB <= kPairMaxBlocks) ? (d.NQB + 1) / 2 : d.NQB;
   const dim3 grid(qunits * d.BH() * (SPLIT ? sp.S : 1));
-  if (causal) hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
-  else hipLaunchKernelGGL((attn_kernel<D, BITS, false, SPLIT>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+  // The pipelined key loop pays off on short key ranges (measured at D = 128:
+  // LLM prefill N 4096 causal +4-8%, DiT N 4608 +2-8%, N 16384 causal +7%)
+  // and costs ~2% on long ones (N 16384 non-causal, N 32768 causal); at D = 64
+  // its extra registers cost the INT8 kernel its third wave.  Both loops give
+  // bit-identical results.
+  const int mean_blocks = SPLIT ? sp.split_blocks : (causal ? (d.NQBk + 1) / 2 : d.NQBk);
+  bool launched = false;
+  if constexpr (D == 128) {
+    if (mean_blocks <= kPipeMaxBlocks) {
+      if (causal)
+        hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+      else
+        hipLaunchKernelGGL((attn_kernel<D, BITS, false, SPLIT, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+      launched = true;
+    }
+  }
+  if (!launched) {
+    if (causal)
+      hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT, false>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+    else
+      hipLaunchKernelGGL((attn_kernel<D, BITS, false, SPLIT, false>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);
+  }
   if (SPLIT) {
     const long long rows = (long long)d.BH() * d.N, rpw = 256 / (d.D / 4);
     hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, s, b, d, causal, sp,
