@@ -82,7 +82,9 @@ def lib():
         L.oracle_e4m3_encode.argtypes = [P, P, i64]
         L.oracle_e4m3_decode.argtypes = [P, P, i64]
         L.oracle_decode_input.argtypes = [P, i32, P, i64]
-        L.oracle_quant_smooth.argtypes = [P, P, P] + [i32] * 9 + [P] * 10 + [i32]
+        L.oracle_quant_smooth.argtypes = [P, P, P] + [i32] * 9 + [P] * 11 + [i32]
+        L.oracle_adaptive_bits.argtypes = [P, P, P] + [i32] * 7 + [f32, P, P, i32]
+        L.oracle_adaptive_bits.restype = i32
         L.oracle_quant_smooth.restype = i32
         L.oracle_qk_int32.argtypes = [P, P, i32, i32, i32, i32, i32, P]
         L.oracle_qk_int32.restype = i32
@@ -140,12 +142,30 @@ class Quant:
     v_mean: np.ndarray = None   # fp32 [B,Hkv,D]: V channel means (zeros without V smoothing)
 
 
+def adaptive_bits(q_bits, k_bits, v_bits, dtype: int, sm_scale: float, nthreads: int = 0):
+    """The adaptive code width of every key/value head (the rule in the header
+    of sage_oracle.cpp).  Returns (head_bits int32 [B,Hkv] of 4 or 8,
+    stats fp32 [B,Hkv,6] = A_Q, E_Q, A_K, E_K, EV, V2)."""
+    B, Hq, Nq, D = q_bits.shape
+    _, Hk, Nk, _ = k_bits.shape
+    qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
+    bits = np.empty((B, Hk), np.int32)
+    stats = np.empty((B, Hk, 6), np.float32)
+    rc = lib().oracle_adaptive_bits(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, Hq, Hk, Nq, Nk, D, float(sm_scale),
+                                    _ptr(bits), _ptr(stats), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_adaptive_bits rejected its arguments")
+    return bits, stats
+
+
 def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_delta_s: bool = True,
-                 qk_bits: int = 4, smooth_v: bool = False) -> Quant:
+                 qk_bits: int = 4, smooth_v: bool = False, head_bits=None, sm_scale: float | None = None) -> Quant:
     """Run the prepass; with_delta_s=False skips the (quadratic) compensation
     term and leaves ``delta_s`` as None.  qk_bits selects INT4 (4) or INT8 (8)
-    codes for Q and K; smooth_v subtracts the per-channel V mean before FP8.
-    q_bits is [B,Hq,Nq,D]; k_bits and v_bits are [B,Hkv,Nk,D]."""
+    codes for Q and K, or 0: the width of each key/value head (and its query
+    heads) from head_bits [B,Hkv], or, if head_bits is None, from
+    adaptive_bits(..., sm_scale); smooth_v subtracts the per-channel V mean
+    before FP8.  q_bits is [B,Hq,Nq,D]; k_bits and v_bits are [B,Hkv,Nk,D]."""
     B, Hq, Nq, D = q_bits.shape
     _, Hk, Nk, _ = k_bits.shape
     if k_bits.shape != v_bits.shape or k_bits.shape[0] != B or k_bits.shape[3] != D:
@@ -153,6 +173,13 @@ def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_del
     nqb = (Nq + BQ_MEAN - 1) // BQ_MEAN
     G = 2 * ((Nk + 31) // 32)
     qb_, kb_, vb_ = (np.ascontiguousarray(a, dtype=np.uint16) for a in (q_bits, k_bits, v_bits))
+    hb = None
+    if qk_bits == 0:
+        if head_bits is None:
+            if sm_scale is None:
+                raise ValueError("qk_bits 0 needs head_bits or sm_scale")
+            head_bits, _ = adaptive_bits(q_bits, k_bits, v_bits, dtype, sm_scale, nthreads)
+        hb = np.ascontiguousarray(head_bits, dtype=np.int32).reshape(B, Hk)
     out = Quant(
         q_codes=np.empty((B, Hq, Nq, D), np.int8), q_scale=np.empty((B, Hq, Nq), np.float32),
         k_codes=np.empty((B, Hk, Nk, D), np.int8), k_scale=np.empty((B, Hk, G), np.float32),
@@ -161,7 +188,7 @@ def quant_smooth(q_bits, k_bits, v_bits, dtype: int, nthreads: int = 0, with_del
         delta_s=np.empty((B, Hq, nqb, Nk), np.float32) if with_delta_s else None,
         v_mean=np.empty((B, Hk, D), np.float32))
     rc = lib().oracle_quant_smooth(_ptr(qb_), _ptr(kb_), _ptr(vb_), dtype, B, Hq, Hk, Nq, Nk, D, qk_bits,
-                                   int(bool(smooth_v)),
+                                   int(bool(smooth_v)), _ptr(hb),
                                    _ptr(out.q_codes), _ptr(out.q_scale), _ptr(out.k_codes), _ptr(out.k_scale),
                                    _ptr(out.q_mean), _ptr(out.k_mean), _ptr(out.v_codes), _ptr(out.v_scale),
                                    _ptr(out.v_mean), _ptr(out.delta_s), _threads(nthreads))

@@ -25,6 +25,31 @@
 //     The adaptive alternative for Q and K ("adaptive quantization method",
 //     technical-report summary, Key Contribution 3; 8-bit codes as in the
 //     SageAttention v1 page) uses the same rule with 127 in place of 7.
+//   - Adaptive width (qk_bits 0): the summary page names an "adaptive
+//     quantization method" that keeps end-to-end metrics but does not define
+//     it.  Reading: per key/value head (with its query heads), predict the
+//     error INT4 adds to the softmax logits and fall back to INT8 where that
+//     error would cost more than 0.01 of cosine similarity.  A code error is
+//     modelled as uniform over +-delta/2 (variance delta^2/12, delta =
+//     amax/7), so a logit q.k gains variance
+//        sigma^2 = sm^2/12 * (amax_q^2/49 * |gK|^2 + amax_k^2/49 * |gQ|^2)
+//     on average over queries and keys.  Logit noise sigma moves O by about
+//     sigma * (spread of the V rows), so the cosine loss against unquantized
+//     attention is at most ~ sigma^2/2 * rho with rho = E|V - vbar|^2 /
+//     (E|V - vbar|^2 + |vbar|^2) (attention concentrated on one key).  INT4
+//     iff sigma^2 * rho <= 0.02.  Statistics (fp32, fixed order):
+//       A_Q = sum over query blocks (in order) of the block's sum, in token
+//             order, of amax_i^2 (amax of the smoothed token);
+//       E_Q = sum over query blocks of sum_c max(0, SSQ_c - SQ_c * qmean_c)
+//             (SQ, SSQ: the block's sequential sums of Q and Q^2);
+//       A_K = sum over 128-key blocks of the block's sum, in key order, of
+//             amax_g(j)^2 (the key's scale group);
+//       E_K = sum_c max(0, SSK_c - SK_c * kmean_c), EV likewise for V with
+//             vbar_c = SV_c / Nk, V2 = sum_c SV_c * vbar_c (SK, SSK, SV, SSV:
+//             chunked sums as for the means);
+//     A_Q and E_Q summed over the group's query heads in head order.  Then in
+//     fp64: INT4 iff sm^2 * (A_Q*E_K + A_K*E_Q) * EV <= 11.76 * (G*Nq) * Nk *
+//     (EV + V2) (11.76 = 0.02 * 12 * 49; G query heads per K/V head).
 //   - Q: one scale per token.  K: one scale per 16-key group; inside every
 //     32-key tile, group h (0 or 1) holds the keys whose offset o satisfies
 //     (o / 4) % 2 == h.  These are the keys that one half of a 64-lane wave holds
@@ -181,16 +206,28 @@ void oracle_decode_input(const uint16_t* in, int dtype, float* out, int64_t n) {
 //   v_mean           : fp32  [B,Hkv,D]      per-channel V mean (zeros without smoothing)
 //   delta_s          : fp32  [B,Hq,ceil(Nq/128),Nk]  (query head h against its K head)
 // Returns 0, or -1 for invalid arguments.
+// qk_bits 4 or 8 for every head, or 0: the width of K/V head bhk (and of its
+// query heads) is head_bits[bhk] (4 or 8), as chosen by oracle_adaptive_bits.
 int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
                         int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
+                        const int32_t* head_bits,
                         int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale,
                         float* q_mean, float* k_mean, uint8_t* v_codes, float* v_scale, float* v_mean,
                         float* delta_s, int nthreads) {
   if (!q || !k || !v || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1) return -1;
   if (dtype != 0 && dtype != 1) return -1;
-  if (qk_bits != 4 && qk_bits != 8) return -1;
+  if (qk_bits != 4 && qk_bits != 8 && qk_bits != 0) return -1;
+  if (qk_bits == 0) {
+    if (!head_bits) return -1;
+    for (int64_t i = 0; i < (int64_t)B * Hkv; i++)
+      if (head_bits[i] != 4 && head_bits[i] != 8) return -1;
+  }
   if (smooth_v != 0 && smooth_v != 1) return -1;
-  const float qmax = qk_bits == 4 ? 7.0f : 127.0f;
+  // the largest code of K/V head bhk and of its query heads
+  auto qmax_of = [&](int64_t bhk) {
+    const int bits = qk_bits ? qk_bits : head_bits[bhk];
+    return bits == 4 ? 7.0f : 127.0f;
+  };
   const int64_t NQB = (Nq + BQ_MEAN - 1) / BQ_MEAN;
   const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
   const int group = Hq / Hkv;
@@ -199,6 +236,7 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   std::vector<std::vector<float>> gK_all((size_t)B * Hkv);
   parallel_for((int64_t)B * Hkv, nthreads, [&](int64_t bhk) {
     const int64_t base = bhk * (int64_t)Nk * D;
+    const float qmax = qmax_of(bhk);
     std::vector<float> K((size_t)Nk * D), V((size_t)Nk * D);
     for (int64_t i = 0; i < (int64_t)Nk * D; i++) {
       K[i] = in_to_f32(k, base + i, dtype);
@@ -260,7 +298,9 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // ---- query side, one (batch, query head) at a time.
   parallel_for((int64_t)B * Hq, nthreads, [&](int64_t bhq) {
     const int64_t base = bhq * (int64_t)Nq * D;
-    const std::vector<float>& gK = gK_all[(bhq / Hq) * Hkv + (bhq % Hq) / group];
+    const int64_t bhk = (bhq / Hq) * Hkv + (bhq % Hq) / group;
+    const std::vector<float>& gK = gK_all[bhk];
+    const float qmax = qmax_of(bhk);
     std::vector<float> Q((size_t)Nq * D);
     for (int64_t i = 0; i < (int64_t)Nq * D; i++) Q[i] = in_to_f32(q, base + i, dtype);
     // Q block means (128-token blocks, partial tail block).
@@ -293,6 +333,108 @@ int oracle_quant_smooth(const uint16_t* q, const uint16_t* k, const uint16_t* v,
           for (int c = 0; c < D; c++) acc += (double)qbar[qb * D + c] * (double)gK[j * D + c];
           delta_s[(bhq * NQB + qb) * Nk + j] = (float)acc;
         }
+  });
+  return 0;
+}
+
+// Adaptive width (header comment): the statistics and the choice for every
+// key/value head.  head_bits[B*Hkv] receives 4 or 8; stats (optional)
+// [B*Hkv][6] receives the group totals A_Q, E_Q, A_K, E_K, EV, V2.
+int oracle_adaptive_bits(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int D, float sm_scale, int32_t* head_bits, float* stats, int nthreads) {
+  if (!q || !k || !v || !head_bits || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || Nq < 1 || Nk < 1 || D < 1) return -1;
+  if (dtype != 0 && dtype != 1) return -1;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return -1;
+  const int group = Hq / Hkv;
+  // query side: A_Q and E_Q of every query head
+  std::vector<float> AQ((size_t)B * Hq), EQ((size_t)B * Hq);
+  parallel_for((int64_t)B * Hq, nthreads, [&](int64_t bhq) {
+    const int64_t base = bhq * (int64_t)Nq * D;
+    float a_tot = 0.0f, e_tot = 0.0f;
+    for (int64_t i0 = 0; i0 < Nq; i0 += BQ_MEAN) {
+      const int64_t i1 = std::min<int64_t>(Nq, i0 + BQ_MEAN);
+      std::vector<float> mean(D);
+      float e_blk = 0.0f;
+      for (int c = 0; c < D; c++) {
+        float sq = 0.0f, ssq = 0.0f;
+        for (int64_t i = i0; i < i1; i++) {
+          const float x = in_to_f32(q, base + i * D + c, dtype);
+          sq = sq + x;
+          ssq = ssq + x * x;
+        }
+        mean[c] = sq / (float)(i1 - i0);
+        e_blk = e_blk + std::max(ssq - sq * mean[c], 0.0f);
+      }
+      float a_blk = 0.0f;
+      for (int64_t i = i0; i < i1; i++) {
+        float amax = 0.0f;
+        for (int c = 0; c < D; c++) amax = std::max(amax, std::fabs(in_to_f32(q, base + i * D + c, dtype) - mean[c]));
+        a_blk = a_blk + amax * amax;
+      }
+      a_tot = a_tot + a_blk;
+      e_tot = e_tot + e_blk;
+    }
+    AQ[bhq] = a_tot;
+    EQ[bhq] = e_tot;
+  });
+  // key/value side and the choice
+  parallel_for((int64_t)B * Hkv, nthreads, [&](int64_t bhk) {
+    const int64_t base = bhk * (int64_t)Nk * D;
+    std::vector<float> kbar(D);
+    float EK = 0.0f, EV = 0.0f, V2 = 0.0f;
+    for (int c = 0; c < D; c++) {
+      float sk = 0.0f, ssk = 0.0f, sv = 0.0f, ssv = 0.0f;
+      for (int64_t t0 = 0; t0 < Nk; t0 += BQ_MEAN) {
+        float pk = 0.0f, pkk = 0.0f, pv = 0.0f, pvv = 0.0f;
+        for (int64_t j = t0; j < std::min<int64_t>(Nk, t0 + BQ_MEAN); j++) {
+          const float xk = in_to_f32(k, base + j * D + c, dtype), xv = in_to_f32(v, base + j * D + c, dtype);
+          pk = pk + xk;
+          pkk = pkk + xk * xk;
+          pv = pv + xv;
+          pvv = pvv + xv * xv;
+        }
+        sk = sk + pk;
+        ssk = ssk + pkk;
+        sv = sv + pv;
+        ssv = ssv + pvv;
+      }
+      kbar[c] = sk / (float)Nk;
+      const float vbar = sv / (float)Nk;
+      EK = EK + std::max(ssk - sk * kbar[c], 0.0f);
+      EV = EV + std::max(ssv - sv * vbar, 0.0f);
+      V2 = V2 + sv * vbar;
+    }
+    // per-group amax of the smoothed keys
+    const int64_t G = 2 * ((int64_t)(Nk + 31) / 32);
+    std::vector<float> gamax(G, 0.0f);
+    for (int64_t j = 0; j < Nk; j++)
+      for (int c = 0; c < D; c++)
+        gamax[k_group(j)] = std::max(gamax[k_group(j)], std::fabs(in_to_f32(k, base + j * D + c, dtype) - kbar[c]));
+    float AK = 0.0f;
+    for (int64_t j0 = 0; j0 < Nk; j0 += BK) {
+      float part = 0.0f;
+      for (int64_t j = j0; j < std::min<int64_t>(Nk, j0 + BK); j++) part = part + gamax[k_group(j)] * gamax[k_group(j)];
+      AK = AK + part;
+    }
+    float AQg = 0.0f, EQg = 0.0f;
+    const int64_t b = bhk / Hkv, hk = bhk % Hkv;
+    for (int g = 0; g < group; g++) {
+      AQg = AQg + AQ[b * Hq + hk * group + g];
+      EQg = EQg + EQ[b * Hq + hk * group + g];
+    }
+    const double sm = (double)sm_scale;
+    const double num = (sm * sm) * ((double)AQg * (double)EK + (double)AK * (double)EQg) * (double)EV;
+    const double den = 11.76 * ((double)group * (double)Nq * (double)Nk) * ((double)EV + (double)V2);
+    head_bits[bhk] = num <= den ? 4 : 8;
+    if (stats) {
+      float* st = stats + bhk * 6;
+      st[0] = AQg;
+      st[1] = EQg;
+      st[2] = AK;
+      st[3] = EK;
+      st[4] = EV;
+      st[5] = V2;
+    }
   });
   return 0;
 }
