@@ -38,8 +38,11 @@ bool shape_ok(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
 }
 
 bool bits_ok(int qk_bits) { return qk_bits == 4 || qk_bits == 8; }
+// also 0, the adaptive width (dense entry points; the codes use the 8-bit layout)
+bool bits_ok_ad(int qk_bits) { return qk_bits == 0 || bits_ok(qk_bits); }
 
-Dims make_dims(int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits = 8, int smooth_v = 0) {
+Dims make_dims(int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits = 8, int smooth_v = 0,
+               float sm_scale = 0.0f) {
   Dims d;
   d.B = B;
   d.H = Hq;
@@ -51,14 +54,16 @@ Dims make_dims(int B, int Hq, int Hkv, int Nq, int Nk, int D, int qk_bits = 8, i
   d.Nk = Nk;
   d.NPk = (Nk + 127) / 128 * 128;
   d.NQBk = d.NPk / 128;
-  d.QB = qk_bits;
+  d.QB = qk_bits ? qk_bits : 8;
   d.SV = smooth_v;
+  d.AD = qk_bits == 0;
+  d.sm = sm_scale;
   d.cu = nullptr;
   d.T = 0;
   return d;
 }
 
-constexpr int kNumArrays = 12;
+constexpr int kNumArrays = 15;
 
 // Sizes of the workspace arrays, in the order of sage_quant_bufs.  The code
 // arrays are sized for 8-bit codes so that one layout serves both code widths.
@@ -82,6 +87,10 @@ bool layout(const Dims& d, size_t sizes[kNumArrays]) {
   sizes[9] = t > qblk * 2 * D * 2 ? t : qblk * 2 * D * 2;   // k_part
   sizes[10] = t > qblk * D * 2 ? t : qblk * D * 2;          // v_part
   sizes[11] = bhk * D * 4;                                   // v_mean
+  // adaptive width: per-chunk sums of squares, statistics, chosen widths
+  sizes[12] = t;                                             // m2_part
+  if (!mul_ok(bhk * 8 + qblk * 2 + kblk, 4, &sizes[13])) return false;   // adapt_stat
+  sizes[14] = bhk * 4;                                       // head_bits
   return true;
 }
 
@@ -104,14 +113,18 @@ void carve(void* ws, const Dims& d, sage_quant_bufs* out) {
   void** slots[kNumArrays] = {(void**)&out->q_codes, (void**)&out->k_codes, (void**)&out->q_scale,
                               (void**)&out->k_scale, (void**)&out->q_mean,  (void**)&out->k_mean,
                               (void**)&out->v_codes, (void**)&out->v_scale, (void**)&out->delta_s,
-                              (void**)&out->k_part,  (void**)&out->v_part,  (void**)&out->v_mean};
+                              (void**)&out->k_part,  (void**)&out->v_part,  (void**)&out->v_mean,
+                              (void**)&out->m2_part, (void**)&out->adapt_stat, (void**)&out->head_bits};
   for (int i = 0; i < kNumArrays; i++) {
     *slots[i] = p;
     p += align_up(s[i]);
   }
 }
 
-Bufs to_internal(const sage_quant_bufs& q) {
+// The buffer set of shape d (the adaptive statistics are carved from
+// adapt_stat: [B*Hkv][8] per head, [B*Hq*NQB][2] per query block, [B*Hkv*NQBk]
+// per key block).
+Bufs to_internal(const sage_quant_bufs& q, const Dims& d) {
   Bufs b = {};
   b.q_codes = q.q_codes;
   b.k_codes = q.k_codes;
@@ -125,6 +138,11 @@ Bufs to_internal(const sage_quant_bufs& q) {
   b.k_part = q.k_part;
   b.v_part = q.v_part;
   b.v_mean = q.v_mean;
+  b.m2_part = q.m2_part;
+  b.stat_head = q.adapt_stat;
+  b.stat_qblk = q.adapt_stat + (size_t)d.BHk() * 8;
+  b.stat_kblk = b.stat_qblk + (size_t)d.BH() * d.NQB * 2;
+  b.head_bits = q.head_bits;
   return b;
 }
 
@@ -135,9 +153,10 @@ bool a16(const void* a, const void* b, const void* c) { return a16(a) && a16(b) 
 
 bool bufs_ok(const sage_quant_bufs* q) {
   return q && q->q_codes && q->k_codes && q->q_scale && q->k_scale && q->q_mean && q->k_mean && q->v_codes &&
-         q->v_scale && q->delta_s && q->k_part && q->v_part && q->v_mean && a16(q->q_codes, q->k_codes, q->q_scale) &&
-         a16(q->k_scale, q->q_mean, q->k_mean) && a16(q->v_codes, q->v_scale, q->delta_s) &&
-         a16(q->k_part, q->v_part, q->v_mean);
+         q->v_scale && q->delta_s && q->k_part && q->v_part && q->v_mean && q->m2_part && q->adapt_stat &&
+         q->head_bits && a16(q->q_codes, q->k_codes, q->q_scale) && a16(q->k_scale, q->q_mean, q->k_mean) &&
+         a16(q->v_codes, q->v_scale, q->delta_s) && a16(q->k_part, q->v_part, q->v_mean) &&
+         a16(q->m2_part, q->adapt_stat, q->head_bits);
 }
 
 // gfx950 check, cached once per device.
@@ -280,19 +299,40 @@ sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, 
   return SAGE_OK;
 }
 
-sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
-                                    int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
-                                    const sage_quant_bufs* out, hipStream_t stream) {
-  if (!q || !k || !v || !a16(q, k, v) || !bufs_ok(out) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits))
+}  // extern "C"
+
+namespace {
+// The prepass into caller buffers; qk_bits 0 (adaptive width) uses sm_scale.
+sage_status quant_smooth_impl(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
+                              int Hkv, int Nq, int Nk, int D, int qk_bits, float sm_scale, int smooth_v,
+                              const sage_quant_bufs* out, hipStream_t stream) {
+  if (!q || !k || !v || !a16(q, k, v) || !bufs_ok(out) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok_ad(qk_bits))
     return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
+  if (qk_bits == 0 && (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))) return SAGE_ERR_INVALID;
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v, sm_scale);
   if (total_bytes(d) == 0) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), stream);
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out, d), stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
+                                    int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
+                                    const sage_quant_bufs* out, hipStream_t stream) {
+  if (!bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  return quant_smooth_impl(q, k, v, in_dtype, B, Hq, Hkv, Nq, Nk, D, qk_bits, 0.0f, smooth_v, out, stream);
+}
+
+sage_status sage_quant_smooth_adaptive_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B,
+                                             int Hq, int Hkv, int Nq, int Nk, int D, float sm_scale, int smooth_v,
+                                             const sage_quant_bufs* out, hipStream_t stream) {
+  return quant_smooth_impl(q, k, v, in_dtype, B, Hq, Hkv, Nq, Nk, D, 0, sm_scale, smooth_v, out, stream);
 }
 
 sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
@@ -300,14 +340,14 @@ sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, voi
                                 sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) ||
-      !bits_ok(qk_bits))
+      !bits_ok_ad(qk_bits))
     return SAGE_ERR_INVALID;
   if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v, sm_scale);
   const size_t need = total_bytes(d);
   if (need == 0) return SAGE_ERR_INVALID;
   if (workspace_bytes < need) return SAGE_ERR_WORKSPACE;
@@ -323,7 +363,7 @@ sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, voi
   if (dc != SAGE_OK) return dc;
   sage_quant_bufs qb;
   carve(workspace, d, &qb);
-  const Bufs b = to_internal(qb);
+  const Bufs b = to_internal(qb, d);
   const float ks = sm_scale * 1.44269504088896340736f;
   hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, stream);
   if (e != hipSuccess) return SAGE_ERR_HIP;
@@ -334,7 +374,7 @@ sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, voi
 sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B, int Hq, int Hkv, int Nq, int Nk,
                                       int D, int causal, float sm_scale, int qk_bits, sage_dtype out_dtype,
                                       hipStream_t stream) {
-  if (!bufs_ok(qb) || !o || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (!bufs_ok(qb) || !o || !shape_ok(B, Hq, Hkv, Nq, Nk, D) || !bits_ok_ad(qk_bits)) return SAGE_ERR_INVALID;
   if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
@@ -343,7 +383,7 @@ sage_status sage_attn_quantized_cross(const sage_quant_bufs* qb, void* o, int B,
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
   const float ks = sm_scale * 1.44269504088896340736f;
-  const hipError_t e = sage::launch_attn(to_internal(*qb), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  const hipError_t e = sage::launch_attn(to_internal(*qb, d), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -422,14 +462,14 @@ sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, voi
                                 sage_dtype in_dtype, sage_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   if (!q || !k || !v || !o || !workspace || !a16(q, k, v) || !a16(workspace) || !shape_ok(B, Hq, Hkv, Nq, Nk, D) ||
-      !bits_ok(qk_bits) || !split_ok(split_keys))
+      !bits_ok_ad(qk_bits) || !split_ok(split_keys))
     return SAGE_ERR_INVALID;
   if (causal && Nq > Nk) return SAGE_ERR_INVALID;
   if (smooth_v != 0 && smooth_v != 1) return SAGE_ERR_INVALID;
   if (in_dtype != SAGE_F16 && in_dtype != SAGE_BF16) return SAGE_ERR_INVALID;
   if (out_dtype != SAGE_F16 && out_dtype != SAGE_BF16 && out_dtype != SAGE_F32) return SAGE_ERR_INVALID;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID;
-  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v);
+  const Dims d = make_dims(B, Hq, Hkv, Nq, Nk, D, qk_bits, smooth_v, sm_scale);
   const int sk = split_keys ? split_keys : default_split_fused(d);
   const size_t need = split_total(d, sk);
   if (need == 0) return SAGE_ERR_INVALID;
@@ -446,7 +486,7 @@ sage_status sage_attn_fwd_split(const void* q, const void* k, const void* v, voi
   if (dc != SAGE_OK) return dc;
   sage_quant_bufs qb;
   carve(workspace, d, &qb);
-  const Bufs b = to_internal(qb);
+  const Bufs b = to_internal(qb, d);
   size_t ob, mb;
   split_sizes(d, sk, &ob, &mb);
   char* p = (char*)workspace + total_bytes(d);
@@ -474,6 +514,12 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
   return sage_quant_smooth_cross(q, k, v, in_dtype, B, H, H, N, N, D, qk_bits, smooth_v, out, stream);
 }
 
+sage_status sage_quant_smooth_adaptive(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H,
+                                       int N, int D, float sm_scale, int smooth_v, const sage_quant_bufs* out,
+                                       hipStream_t stream) {
+  return sage_quant_smooth_adaptive_cross(q, k, v, in_dtype, B, H, H, N, N, D, sm_scale, smooth_v, out, stream);
+}
+
 sage_status sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int D,
                           int causal, float sm_scale, int qk_bits, int smooth_v, sage_dtype in_dtype,
                           sage_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -488,12 +534,13 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
 
 sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, int D, int qk_bits, int bh, int q0,
                                 int k0, int nq, int nk, int32_t* out, hipStream_t stream) {
-  if (!bufs_ok(qb) || !out || !shape_ok(B, H, H, N, N, D) || !bits_ok(qk_bits)) return SAGE_ERR_INVALID;
+  if (!bufs_ok(qb) || !out || !shape_ok(B, H, H, N, N, D) || !bits_ok_ad(qk_bits)) return SAGE_ERR_INVALID;
   if (bh < 0 || bh >= B * H || q0 < 0 || k0 < 0 || nq < 1 || nk < 1) return SAGE_ERR_INVALID;
   if ((long long)q0 + nq > N || (long long)k0 + nk > N) return SAGE_ERR_INVALID;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_qk_debug(to_internal(*qb), make_dims(B, H, H, N, N, D, qk_bits), bh, q0, k0, nq, nk, out, stream);
+  const Dims d = make_dims(B, H, H, N, N, D, qk_bits);
+  const hipError_t e = sage::launch_qk_debug(to_internal(*qb, d), d, bh, q0, k0, nq, nk, out, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -518,7 +565,7 @@ sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v
   d.T = total_tokens;
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
-  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out), stream);
+  const hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, to_internal(*out, d), stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
@@ -549,7 +596,7 @@ sage_status sage_attn_fwd_varlen(const void* q, const void* k, const void* v, vo
   if (dc != SAGE_OK) return dc;
   sage_quant_bufs qb;
   carve(workspace, d, &qb);
-  const Bufs b = to_internal(qb);
+  const Bufs b = to_internal(qb, d);
   const float ks = sm_scale * 1.44269504088896340736f;
   hipError_t e = sage::launch_prepass(q, k, v, (int)in_dtype, d, b, stream);
   if (e != hipSuccess) return SAGE_ERR_HIP;
@@ -571,7 +618,7 @@ sage_status sage_attn_quantized_varlen(const sage_quant_bufs* qb, void* o, const
   const sage_status dc = device_check();
   if (dc != SAGE_OK) return dc;
   const float ks = sm_scale * 1.44269504088896340736f;
-  const hipError_t e = sage::launch_attn(to_internal(*qb), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
+  const hipError_t e = sage::launch_attn(to_internal(*qb, d), d, causal ? 1 : 0, ks, o, (int)out_dtype, stream);
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 

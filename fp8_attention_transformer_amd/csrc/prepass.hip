@@ -41,7 +41,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // are sequential per channel); loads are issued 32 tokens ahead.  Per chunk:
 // the K and V sums and the V maxima and minima (kPartV: V only).  The Q block
 // means are formed by the quant kernel, which holds the block anyway.
-template <int IN, int D, int PART>
+// M2 (adaptive width): also the per-chunk sums of squares of K and V, in the
+// same token order, for the width statistics.
+template <int IN, int D, int PART, bool M2>
 __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                     Dims d, Bufs b) {
   constexpr int LPC = D / 2;          // lanes per chunk
@@ -61,14 +63,24 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   const size_t base = io.base + 2 * cp, rs = io.stride;
   float ks0 = 0.0f, ks1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
   float vx0 = -__builtin_inff(), vx1 = -__builtin_inff(), vn0 = __builtin_inff(), vn1 = __builtin_inff();
+  float kq0 = 0.0f, kq1 = 0.0f, vq0 = 0.0f, vq1 = 0.0f;   // sums of squares (M2)
   auto add = [&](uint32_t kv, uint32_t vv) {
     if constexpr (DO_K) {
-      ks0 = ks0 + in_to_f32<IN>((uint16_t)(kv & 0xFFFF));
-      ks1 = ks1 + in_to_f32<IN>((uint16_t)(kv >> 16));
+      const float k0 = in_to_f32<IN>((uint16_t)(kv & 0xFFFF)), k1 = in_to_f32<IN>((uint16_t)(kv >> 16));
+      ks0 = ks0 + k0;
+      ks1 = ks1 + k1;
+      if constexpr (M2) {
+        kq0 = kq0 + k0 * k0;
+        kq1 = kq1 + k1 * k1;
+      }
     }
     const float v0 = in_to_f32<IN>((uint16_t)(vv & 0xFFFF)), v1 = in_to_f32<IN>((uint16_t)(vv >> 16));
     vs0 = vs0 + v0;
     vs1 = vs1 + v1;
+    if constexpr (M2) {
+      vq0 = vq0 + v0 * v0;
+      vq1 = vq1 + v1 * v1;
+    }
     vx0 = fmaxf(vx0, v0);
     vx1 = fmaxf(vx1, v1);
     vn0 = fminf(vn0, v0);
@@ -102,6 +114,12 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   b.v_part[o2 + 1] = vx1;
   b.v_part[o2 + D] = vn0;
   b.v_part[o2 + D + 1] = vn1;
+  if constexpr (M2) {
+    b.m2_part[o2] = kq0;
+    b.m2_part[o2 + 1] = kq1;
+    b.m2_part[o2 + D] = vq0;
+    b.m2_part[o2 + D + 1] = vq1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,14 +127,21 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
 // order) / Nk; likewise the V mean when V is smoothed (else 0).  V scale =
 // max|V - vmean| / 448, from the chunk maxima and minima: rounding is
 // monotonic, so max_j |fl(V_j - m)| = max(|fl(max V - m)|, |fl(min V - m)|).
+// AD (adaptive width): also the channel's sums of squares of K and V (chunk
+// partials in the same order), its centred sums of squares
+// max(0, SS - S * mean) and V mean term S * mean (the V mean S/Nk also
+// without V smoothing), summed over channels in channel order into E_K, EV
+// and V2 of the head.
+template <bool AD>
 __global__ void finalize_kernel(Dims d, Bufs b) {
   constexpr int U = 32;   // chunks whose partials are loaded together
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
   const size_t base = (size_t)bh * d.NQBk * 2 * D + c;
   float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
+  float ssk = 0.0f, ssv = 0.0f;
   int t = 0;
   for (; t + U <= d.NQBk; t += U) {   // whole batches: unconditional loads, then the in-order sums
-    float kp[U], vp[U], xp[U], np[U];
+    float kp[U], vp[U], xp[U], np[U], kq[AD ? U : 1], vq[AD ? U : 1];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const size_t o = base + (size_t)(t + u) * 2 * D;
@@ -124,6 +149,10 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
       vp[u] = b.k_part[o + D];
       xp[u] = b.v_part[o];
       np[u] = b.v_part[o + D];
+      if constexpr (AD) {
+        kq[u] = b.m2_part[o];
+        vq[u] = b.m2_part[o + D];
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -131,6 +160,10 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
       vtot = vtot + vp[u];
       vx = fmaxf(vx, xp[u]);
       vn = fminf(vn, np[u]);
+      if constexpr (AD) {
+        ssk = ssk + kq[u];
+        ssv = ssv + vq[u];
+      }
     }
   }
   for (; t < d.NQBk; t++) {
@@ -139,12 +172,71 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
     vtot = vtot + b.k_part[o + D];
     vx = fmaxf(vx, b.v_part[o]);
     vn = fminf(vn, b.v_part[o + D]);
+    if constexpr (AD) {
+      ssk = ssk + b.m2_part[o];
+      ssv = ssv + b.m2_part[o + D];
+    }
   }
   const int n = head_io_kv(d, bh).n;   // 0 only for an empty packed sequence
-  b.k_mean[(size_t)bh * D + c] = n ? tot / (float)n : 0.0f;
+  const float kbar = n ? tot / (float)n : 0.0f;
+  b.k_mean[(size_t)bh * D + c] = kbar;
   const float vbar = (d.SV && n) ? vtot / (float)n : 0.0f;
   b.v_mean[(size_t)bh * D + c] = vbar;
   b.v_scale[(size_t)bh * D + c] = n ? fmaxf(fabsf(vx - vbar), fabsf(vn - vbar)) / 448.0f : 0.0f;
+  if constexpr (AD) {
+    const float vbs = vtot / (float)n;
+    __shared__ float sEK[128], sEV[128], sV2[128];
+    sEK[c] = fmaxf(ssk - tot * kbar, 0.0f);
+    sEV[c] = fmaxf(ssv - vtot * vbs, 0.0f);
+    sV2[c] = vtot * vbs;
+    __syncthreads();
+    if (c == 0) {
+      float ek = 0.0f, ev = 0.0f, v2 = 0.0f;
+      for (int cc = 0; cc < D; cc++) {
+        ek = ek + sEK[cc];
+        ev = ev + sEV[cc];
+        v2 = v2 + sV2[cc];
+      }
+      b.stat_head[(size_t)bh * 8 + 3] = ek;
+      b.stat_head[(size_t)bh * 8 + 4] = ev;
+      b.stat_head[(size_t)bh * 8 + 5] = v2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decide (adaptive width): grid (B*Hk), one thread per K/V head sums the block
+// statistics in order (key blocks; the group's query heads in head order,
+// each over its query blocks) and chooses, in fp64: INT4 iff
+//   sm^2 * (A_Q*E_K + A_K*E_Q) * EV <= 11.76 * (G*Nq) * Nk * (EV + V2),
+// i.e. the predicted INT4 logit variance sigma^2 (uniform rounding,
+// delta = amax/7) times rho = EV / (EV + V2) is at most 0.02.
+__global__ void decide_kernel(Dims d, Bufs b) {
+  if (threadIdx.x != 0) return;
+  const int bhk = blockIdx.x, G = d.H / d.Hk;
+  const int bb = bhk / d.Hk, hk = bhk % d.Hk;
+  float ak = 0.0f;
+  for (int kb = 0; kb < d.NQBk; kb++) ak = ak + b.stat_kblk[(size_t)bhk * d.NQBk + kb];
+  float aq = 0.0f, eq = 0.0f;
+  for (int g = 0; g < G; g++) {
+    const size_t bh = (size_t)bb * d.H + (size_t)hk * G + g;
+    float a = 0.0f, e = 0.0f;
+    for (int qb = 0; qb < d.NQB; qb++) {
+      a = a + b.stat_qblk[(bh * d.NQB + qb) * 2];
+      e = e + b.stat_qblk[(bh * d.NQB + qb) * 2 + 1];
+    }
+    aq = aq + a;
+    eq = eq + e;
+  }
+  float* st = b.stat_head + (size_t)bhk * 8;
+  const float ek = st[3], ev = st[4], v2 = st[5];
+  const double sm = (double)d.sm;
+  const double num = (sm * sm) * ((double)aq * (double)ek + (double)ak * (double)eq) * (double)ev;
+  const double den = 11.76 * ((double)G * (double)d.N * (double)d.Nk) * ((double)ev + (double)v2);
+  b.head_bits[bhk] = num <= den ? 4 : 8;
+  st[0] = aq;
+  st[1] = eq;
+  st[2] = ak;
 }
 
 // Position p (0..127) inside a 128-key block of the FP8 V layout holds key
@@ -277,12 +369,23 @@ __device__ __forceinline__ void fp8_quotients(float* x, float dv) {
 //  K: one scale per 16-key fragment group (one group = 16 keys x D/32 lanes);
 //  V: FP8 with the per-channel scale, written in the permuted channel-major
 //     layout through an LDS copy of the block.
-template <int IN, int D, int BITS, int PART>
+// MODE 0: codes of width BITS.  Adaptive width (BITS 8 layout): MODE 1 writes
+// INT8 codes for every head and the block statistics of the width rule
+// (per query block: the sum of amax^2 over its tokens in token order and the
+// sum over channels of max(0, SSQ - SQ * mean); per key block: the sum of the
+// keys' group amax^2 in key order); MODE 2 rewrites, for the heads the rule
+// gave INT4, the Q and K codes and scales with qmax 7 in the same layout (V
+// and the Q block means are unchanged).
+template <int IN, int D, int BITS, int PART, int MODE>
 __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, Dims d, Bufs b) {
-  constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
+  static_assert(MODE == 0 || (BITS == 8 && PART != kPartBoth), "adaptive width: int8 layout, dense geometry");
+  constexpr int CB = MODE == 2 ? 4 : BITS;   // code width of this pass
+  constexpr float kQmax = CB == 4 ? 7.0f : 127.0f;
   constexpr bool DO_Q = PART & kPartQ, DO_KV = PART & kPartKV;
-  __shared__ __align__(16) uint16_t sV[DO_KV ? kBK * D : 8];
+  constexpr bool DO_V = DO_KV && MODE != 2;
+  __shared__ __align__(16) uint16_t sV[DO_V ? kBK * D : 8];
+  __shared__ float sStat[MODE == 1 ? kBQ + D : 1];   // amax^2 per token or key; centred squares per channel
   __shared__ __align__(16) float sKM[DO_KV ? D : 4];   // K means of the head
   __shared__ __align__(16) uint16_t sQ[DO_Q ? 64 * D : 8];   // half a block of raw Q rows
   __shared__ __align__(16) float sQM[DO_Q ? D : 4];          // the block's Q means
@@ -294,6 +397,9 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   const HeadIO io = DO_Q ? head_io(d, bh) : head_io_kv(d, bh);
   // past the end of a shorter packed sequence: nothing here is ever read
   if (d.cu && i0 >= io.n) return;
+  if constexpr (MODE == 2) {
+    if (b.head_bits[DO_Q ? d.kv_head(bh) : bh] != 4) return;   // an INT8 head keeps the first pass
+  }
   const size_t qrowp = (size_t)bh * d.NP;    // first padded query row of this head
   const size_t krowp = (size_t)bh * d.NPk;   // first padded key row of this head
 
@@ -306,7 +412,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
   constexpr int LPT = D / 16, TPP = 256 / LPT, NQP = kBQ / TPP;   // Q: lanes per token, tokens per pass, passes
   constexpr int LPK = D / 32, LPG = 16 * LPK;                      // K: lanes per key / per scale group
   constexpr int GPW = 64 / LPG, NKI = kBK / kKGroup / (4 * GPW);   // K: groups per wave, rounds
-  if constexpr (DO_KV) {
+  if constexpr (DO_V) {
     constexpr int VPT = kBK * D / 8 / 256;   // 16-byte chunks per thread
 #pragma unroll
     for (int p = 0; p < VPT; p++) {
@@ -316,13 +422,15 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(sV + 8 * wbase), 16,
                                        0, 0);
     }
+  }
+  if constexpr (DO_KV) {
     if (wave == 0 && lane < D / 4)
       __builtin_amdgcn_global_load_lds((const void*)(b.k_mean + (size_t)bh * D + 4 * lane),
                                        (__attribute__((address_space(3))) void*)sKM, 16, 0, 0);
   }
   // V scale and mean of this thread's channel in the FP8 step (ch = tid mod D)
-  const float dv_ch = DO_KV ? b.v_scale[(size_t)bh * D + tid % D] : 0.0f;
-  const float vbar_ch = DO_KV ? b.v_mean[(size_t)bh * D + tid % D] : 0.0f;   // 0 without V smoothing
+  const float dv_ch = DO_V ? b.v_scale[(size_t)bh * D + tid % D] : 0.0f;
+  const float vbar_ch = DO_V ? b.v_mean[(size_t)bh * D + tid % D] : 0.0f;   // 0 without V smoothing
   v4i qraw[DO_Q ? NQP : 1][2];
   if constexpr (DO_Q) {
     const int c0 = 16 * (tid % LPT);
@@ -356,7 +464,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
     const int nval = min(kBQ, io.n - i0);
     constexpr int PPH = NQP / 2;   // Q passes per half (64 tokens)
     static_assert(PPH * TPP == 64, "a half is 64 tokens");
-    float qs = 0.0f;
+    float qs = 0.0f, qss = 0.0f;   // qss: sum of squares (MODE 1)
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       if (h) lds_barrier();   // the first half has been summed
@@ -376,17 +484,26 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 #pragma unroll
             for (int t = 0; t < 16; t++) x[t] = sQ[(t0 + t) * D + tid];
 #pragma unroll
-            for (int t = 0; t < 16; t++) qs = qs + in_to_f32<IN>(x[t]);
+            for (int t = 0; t < 16; t++) {
+              const float xf = in_to_f32<IN>(x[t]);
+              qs = qs + xf;
+              if constexpr (MODE == 1) qss = qss + xf * xf;
+            }
           }
         } else {
-          for (int t = 0; t < nh; t++) qs = qs + in_to_f32<IN>(sQ[t * D + tid]);
+          for (int t = 0; t < nh; t++) {
+            const float xf = in_to_f32<IN>(sQ[t * D + tid]);
+            qs = qs + xf;
+            if constexpr (MODE == 1) qss = qss + xf * xf;
+          }
         }
       }
     }
     if (tid < D) {
       const float m = qs / (float)nval;
       sQM[tid] = m;
-      b.q_mean[((size_t)bh * d.NQB + qb) * D + tid] = m;
+      if constexpr (MODE != 2) b.q_mean[((size_t)bh * d.NQB + qb) * D + tid] = m;
+      if constexpr (MODE == 1) sStat[kBQ + tid] = fmaxf(qss - qs * m, 0.0f);
     }
     lds_barrier();
     float qm[16];
@@ -401,7 +518,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
     // three bf16 pieces of this block's channel means for the compensation
     // kernel: pieces 1 and 2 in k_part, piece 3 in v_part (both are free once
     // the K means and V scales are final)
-    if (tid < LPT) {
+    if (MODE != 2 && tid < LPT) {
       uint16_t* p12 = (uint16_t*)b.k_part + ((size_t)bh * d.NQB + qb) * 2 * D;
       uint16_t* p3s = (uint16_t*)b.v_part + ((size_t)bh * d.NQB + qb) * D;
 #pragma unroll
@@ -428,9 +545,12 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 16; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPT>(amax);
+      if constexpr (MODE == 1) {
+        if (sub == 0) sStat[tid / LPT + TPP * p] = amax * amax;   // 0 past the head's tokens
+      }
       const float dq = amax / kQmax;
       float cq[16];
-      int_codes_f<16, BITS>(g, dq, cq);
+      int_codes_f<16, CB>(g, dq, cq);
       if constexpr (BITS == 4) {
         // FP6 tile layout: this lane's 16 channels are fields 16*(sub&1)..+15
         // of group c0/64 in half (c0/32)&1 of the row's chunk
@@ -463,6 +583,17 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
         *(v4i*)(b.q_codes + (qrowp + i) * D + 16 * sub) = pk;
       }
       if (sub == 0) b.q_scale[qrowp + i] = dq;
+    }
+    if constexpr (MODE == 1) {
+      // the block's statistics: token order, channel order (two waves)
+      lds_barrier();
+      if (tid == 0 || tid == 64) {
+        const float* src = tid == 0 ? sStat : sStat + kBQ;
+        const int cnt = tid == 0 ? kBQ : D;
+        float acc = 0.0f;
+        for (int e = 0; e < cnt; e++) acc = acc + src[e];
+        b.stat_qblk[((size_t)bh * d.NQB + qb) * 2 + (tid == 0 ? 0 : 1)] = acc;
+      }
     }
   }
   // ---- K: a group (T, hh) holds keys 32T + 8u + 4hh + w (u, w in 0..3);
@@ -498,9 +629,12 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 32; e++) amax = fmaxf(amax, fabsf(g[e]));
       amax = group_max<LPG>(amax);
+      if constexpr (MODE == 1) {
+        if (sub == 0) sStat[j - i0] = j < io.n ? amax * amax : 0.0f;   // keys past the head count 0
+      }
       const float dk = amax / kQmax;
       float ck[32];
-      int_codes_f<32, BITS>(g, dk, ck);
+      int_codes_f<32, CB>(g, dk, ck);
       if constexpr (BITS == 4) {
         // FP6 tile layout: this lane's 32 channels are group sub/2 of half sub&1
         uint32_t w[6];
@@ -538,10 +672,18 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       }
       if ((lane % LPG) == 0) b.k_scale[krowp / kKGroup + (i0 / kKGroup) + grp] = dk;
     }
+    if constexpr (MODE == 1) {
+      lds_barrier();
+      if (tid == 0) {
+        float acc = 0.0f;
+        for (int e = 0; e < kBK; e++) acc = acc + sStat[e];
+        b.stat_kblk[(size_t)bh * d.NQBk + qb] = acc;
+      }
+    }
   }
   // ---- V: 16-key chunks of one channel -> 16 FP8 bytes (channel tid mod D,
   //      chunks tid / D + (256 / D) i); the block is in LDS since the K step
-  if constexpr (DO_KV) {
+  if constexpr (DO_V) {
     static_assert(256 % D == 0, "whole channels per pass");
     uint8_t* vout = b.v_codes + ((size_t)bh * d.NQBk + qb) * D * kBK;
     const int ch = tid % D;
@@ -709,7 +851,7 @@ __global__ void fp8_encode_kernel(const float* __restrict__ in, uint8_t* __restr
   }
 }
 
-template <int IN, int D, int BITS>
+template <int IN, int D, int BITS, int MODE = 0>
 void launch_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, const Dims& d, const Bufs& b,
                   hipStream_t s) {
   // Packed sequences quantize a token block of Q, K and V in one workgroup
@@ -717,12 +859,16 @@ void launch_quant(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
   // and the key/value side as two launches: their smaller workgroups (92 and
   // 133 VGPRs against 138 with 50 KB of LDS) keep more bytes in flight (LLM
   // prefill B4 H32 N4096: prepass 234 -> 227 us; the headline unchanged).
-  if (d.self_attention() && d.cu) {
-    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartBoth>), dim3(d.BH(), d.NQB), dim3(256), 0, s, q, k, v, d, b);
-  } else {
-    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartQ>), dim3(d.NQB, d.BH()), dim3(256), 0, s, q, k, v, d, b);
-    hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartKV>), dim3(d.NQBk, d.BHk()), dim3(256), 0, s, q, k, v, d, b);
+  if constexpr (MODE == 0) {
+    if (d.self_attention() && d.cu) {
+      hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartBoth, 0>), dim3(d.BH(), d.NQB), dim3(256), 0, s, q, k, v, d,
+                         b);
+      return;
+    }
   }
+  hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartQ, MODE>), dim3(d.NQB, d.BH()), dim3(256), 0, s, q, k, v, d, b);
+  hipLaunchKernelGGL((quant_kernel<IN, D, BITS, kPartKV, MODE>), dim3(d.NQBk, d.BHk()), dim3(256), 0, s, q, k, v, d,
+                     b);
 }
 
 template <int IN, int D>
@@ -732,11 +878,22 @@ hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims&
   const uint16_t* v16 = (const uint16_t*)v;
   constexpr int CPW = 256 / (D / 2);
   auto nstat = [](long long chunks) { return dim3((unsigned)((chunks + CPW - 1) / CPW)); };
-  hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s, k16, v16,
-                     d, b);
-  hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(D), 0, s, d, b);
-  if (d.QB == 8) launch_quant<IN, D, 8>(q16, k16, v16, d, b, s);
-  else launch_quant<IN, D, 4>(q16, k16, v16, d, b, s);
+  if (d.AD) {
+    // adaptive width: statistics with the INT8 pass, the choice per K/V head,
+    // then the INT4 heads' codes rewritten
+    hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV, true>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s, k16,
+                       v16, d, b);
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3(d.BHk()), dim3(D), 0, s, d, b);
+    launch_quant<IN, D, 8, 1>(q16, k16, v16, d, b, s);
+    hipLaunchKernelGGL(decide_kernel, dim3(d.BHk()), dim3(64), 0, s, d, b);
+    launch_quant<IN, D, 8, 2>(q16, k16, v16, d, b, s);
+  } else {
+    hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV, false>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s,
+                       k16, v16, d, b);
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3(d.BHk()), dim3(D), 0, s, d, b);
+    if (d.QB == 8) launch_quant<IN, D, 8>(q16, k16, v16, d, b, s);
+    else launch_quant<IN, D, 4>(q16, k16, v16, d, b, s);
+  }
   const dim3 ds_grid = d.cu ? dim3(d.BH(), d.NQBk) : dim3(d.NQBk, d.BH());
   hipLaunchKernelGGL((delta_s_kernel<IN, D>), ds_grid, dim3(256), 0, s, k16, d, b);
   return hipGetLastError();
@@ -758,13 +915,13 @@ hipError_t launch_v_stats(const void* v, int in_dtype, const Dims& d, const Bufs
   const int cpw = 256 / (d.D / 2);
   const dim3 grid((unsigned)(((long long)d.BHk() * d.NQBk + cpw - 1) / cpw));
   if (in_dtype == kBF16) {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<1, 64, kPartV, false>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<1, 128, kPartV, false>), grid, dim3(256), 0, s, nullptr, v16, d, b);
   } else {
-    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
-    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartV>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    if (d.D == 64) hipLaunchKernelGGL((stats_kernel<0, 64, kPartV, false>), grid, dim3(256), 0, s, nullptr, v16, d, b);
+    else hipLaunchKernelGGL((stats_kernel<0, 128, kPartV, false>), grid, dim3(256), 0, s, nullptr, v16, d, b);
   }
-  hipLaunchKernelGGL(finalize_kernel, dim3(d.BHk()), dim3(d.D), 0, s, d, b);
+  hipLaunchKernelGGL(finalize_kernel<false>, dim3(d.BHk()), dim3(d.D), 0, s, d, b);
   return hipGetLastError();
 }
 

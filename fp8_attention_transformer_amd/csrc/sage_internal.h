@@ -13,7 +13,7 @@ namespace sage {
 constexpr int kBQ = 128;      // tokens per Q-smoothing block, per mean chunk, per query tile
 constexpr int kBK = 128;      // keys per online-softmax block (also the level-1 P~V block)
 constexpr int kKGroup = 16;   // keys per K scale group (two groups per 32-key tile)
-constexpr int kContractVersion = 1;
+constexpr int kContractVersion = 2;
 
 enum InDtype { kF16 = 0, kBF16 = 1 };
 enum OutDtype { kOutF16 = 0, kOutBF16 = 1, kOutF32 = 2 };
@@ -48,8 +48,13 @@ struct Dims {
   int Hk, Nk;
   int NPk;   // Nk rounded up to a multiple of 128
   int NQBk;  // NPk / 128: key blocks per head
-  int QB;    // bits per Q/K code: 4 (INT4, stored as FP6) or 8 (INT8)
+  int QB;    // bits per Q/K code: 4 (INT4, stored as FP6) or 8 (INT8 layout)
   int SV;    // 1: smooth V (subtract the per-channel V mean before FP8)
+  // 1: adaptive width (QB == 8 layout): the prepass picks INT4 (codes in
+  // [-7, 7], stored as int8) or INT8 per K/V head from its statistics and
+  // the softmax scale sm.
+  int AD;
+  float sm;
   // Packed variable-length batches (self-attention only): when cu is not
   // null, head b*H + h is sequence b, tokens cu[b] .. cu[b+1]-1 of a
   // token-major [T, H, D] tensor, and N is the maximum length (it sets the
@@ -115,6 +120,12 @@ struct Bufs {
   float* v_part;      // [B,Hk,NQBk,2,D] per-chunk V channel max and min; then bf16 q_mean
                       //                 piece 3 as [B,H,NQB,D]
   float* v_mean;      // [B,Hk,D]        V channel means (zeros without V smoothing)
+  // adaptive width only
+  float* m2_part;     // [B,Hk,NQBk,2,D] per-chunk K and V channel sums of squares
+  float* stat_head;   // [B,Hk,8]        A_Q, E_Q, A_K, E_K, EV, V2 of each K/V head (and its query heads)
+  float* stat_qblk;   // [B,H,NQB,2]     per query block: sum of amax^2, sum of centred squares
+  float* stat_kblk;   // [B,Hk,NQBk]     per key block: sum of the keys' group amax^2
+  int32_t* head_bits; // [B,Hk]          chosen width (4 or 8)
 };
 
 // Decoding step (one query token per head): per-range partial outputs.

@@ -26,7 +26,9 @@ EXPORTED = [
     "sage_attn_fwd_cross", "sage_attn_quantized_cross",
     "sage_decode_split_keys", "sage_decode_workspace_bytes", "sage_attn_decode",
     "sage_split_keys", "sage_split_workspace_bytes", "sage_attn_fwd_split", "sage_attn_fwd_static",
+    "sage_quant_smooth_adaptive", "sage_quant_smooth_adaptive_cross",
 ]
+ADAPTIVE = 0   # qk_bits value of the adaptive width (INT4 or INT8 per key/value head)
 STATIC_SCRATCH_BYTES = 128 << 20   # SAGE_STATIC_SCRATCH_BYTES
 
 
@@ -34,7 +36,7 @@ class QuantBufs(ctypes.Structure):
     """Mirror of sage_quant_bufs (device pointers)."""
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "q_codes", "k_codes", "q_scale", "k_scale", "q_mean", "k_mean", "v_codes", "v_scale", "delta_s",
-        "k_part", "v_part", "v_mean")]
+        "k_part", "v_part", "v_mean", "m2_part", "adapt_stat", "head_bits")]
 
 
 class SageError(RuntimeError):
@@ -105,6 +107,11 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd_split.restype = i32
         L.sage_attn_fwd_static.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32, i32, P]
         L.sage_attn_fwd_static.restype = i32
+        L.sage_quant_smooth_adaptive.argtypes = [P, P, P, i32, i32, i32, i32, i32, f32, i32,
+                                                 ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth_adaptive.restype = i32
+        L.sage_quant_smooth_adaptive_cross.argtypes = [P, P, P] + [i32] * 7 + [f32, i32, ctypes.POINTER(QuantBufs), P]
+        L.sage_quant_smooth_adaptive_cross.restype = i32
         _lib = L
     return _lib
 
@@ -137,6 +144,21 @@ def quant_smooth(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, H: i
                  bufs: QuantBufs, stream: int = 0, qk_bits: int = 4, smooth_v: bool = False) -> None:
     _check(lib().sage_quant_smooth(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, qk_bits, int(bool(smooth_v)),
                                    ctypes.byref(bufs), stream), "sage_quant_smooth")
+
+
+def quant_smooth_adaptive(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, H: int, N: int, D: int,
+                          sm_scale: float, bufs: QuantBufs, stream: int = 0, smooth_v: bool = False) -> None:
+    _check(lib().sage_quant_smooth_adaptive(q_ptr, k_ptr, v_ptr, in_dtype, B, H, N, D, float(sm_scale),
+                                            int(bool(smooth_v)), ctypes.byref(bufs), stream),
+           "sage_quant_smooth_adaptive")
+
+
+def quant_smooth_adaptive_cross(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, B: int, Hq: int, Hkv: int,
+                                Nq: int, Nk: int, D: int, sm_scale: float, bufs: QuantBufs, stream: int = 0,
+                                smooth_v: bool = False) -> None:
+    _check(lib().sage_quant_smooth_adaptive_cross(q_ptr, k_ptr, v_ptr, in_dtype, B, Hq, Hkv, Nq, Nk, D,
+                                                  float(sm_scale), int(bool(smooth_v)), ctypes.byref(bufs), stream),
+           "sage_quant_smooth_adaptive_cross")
 
 
 def attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, B: int, H: int, N: int, D: int, causal: bool,
@@ -308,8 +330,10 @@ def attn(q, k, v, causal: bool = False, sm_scale: float | None = None, out_dtype
          out=None, qk_bits: int = 4, smooth_v: bool = False):
     """Drop-in attention: q [B, Hq, Nq, D], k and v [B, Hkv, Nk, D] fp16/bf16
     device tensors (Hq a multiple of Hkv; Hq == Hkv and Nq == Nk for plain
-    self-attention).  qk_bits 4: INT4 Q/K codes, 8: INT8; smooth_v: subtract
-    the V channel means before FP8; a causal mask is aligned at the last key."""
+    self-attention).  qk_bits 4: INT4 Q/K codes, 8: INT8, 0 (ADAPTIVE): INT4 or
+    INT8 per key/value head as the adaptive-width rule picks (the choice is in
+    the workspace, see head_bits); smooth_v: subtract the V channel means
+    before FP8; a causal mask is aligned at the last key."""
     import torch
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("q must be [B, Hq, Nq, D] and k, v one [B, Hkv, Nk, D] shape")
@@ -433,3 +457,24 @@ def attn_split(q, k, v, causal: bool = False, sm_scale: float | None = None, out
                    _torch_dtype_code(q.dtype), _torch_dtype_code(out.dtype), workspace.data_ptr(), workspace.numel(),
                    _stream_handle(q.device), qk_bits, smooth_v, split_keys)
     return out, workspace
+
+
+def head_bits(workspace: Workspace):
+    """The code width chosen for each key/value head by the last adaptive
+    prepass into this workspace: int32 [B, Hkv] on the device (4 or 8)."""
+    import torch
+    qb = workspace.bufs()
+    n = workspace.B * (workspace.Hkv or workspace.H)
+    off = qb.head_bits - workspace.ptr
+    return workspace.tensor[off:off + 4 * n].view(torch.int32).view(workspace.B, workspace.Hkv or workspace.H)
+
+
+def adapt_stats(workspace: Workspace):
+    """The adaptive-width statistics of the last adaptive prepass: fp32
+    [B, Hkv, 6] = A_Q, E_Q, A_K, E_K, EV, V2 per key/value head."""
+    import torch
+    qb = workspace.bufs()
+    hk = workspace.Hkv or workspace.H
+    n = workspace.B * hk * 8
+    off = qb.adapt_stat - workspace.ptr
+    return workspace.tensor[off:off + 4 * n].view(torch.float32).view(workspace.B, hk, 8)[:, :, :6]

@@ -34,8 +34,27 @@
  *    method's default) or 8 (INT8 in [-127, 127], the more accurate choice
  *    the adaptive quantization of SageAttention2 (summary page, Key
  *    Contribution 3) falls back to where INT4 loses accuracy; same
- *    granularity, scale = amax/qmax).  Any other value is SAGE_ERR_INVALID.
- *    Buffers written with one qk_bits must be read with the same value.
+ *    granularity, scale = amax/qmax), or 0 where an entry point says so: the
+ *    adaptive width.  Any other value is SAGE_ERR_INVALID.  Buffers written
+ *    with one qk_bits must be read with the same value (0 and 8 share the
+ *    8-bit layout).
+ *  - Adaptive width (qk_bits 0).  The summary page names an adaptive
+ *    quantization that keeps end-to-end metrics but does not define it.
+ *    Here, per key/value head (with its query heads), the prepass predicts
+ *    the variance INT4 codes add to the softmax logits, modelling a code
+ *    error as uniform over half a step (delta = amax/7):
+ *      sigma^2 = sm_scale^2/12 * (mean amax_q^2/49 * mean |K - kmean|^2
+ *                                 + mean amax_k^2/49 * mean |Q - qmean|^2),
+ *    and weights it by rho = E|V - vmean|^2 / (E|V - vmean|^2 + |vmean|^2)
+ *    (the cosine loss of O is about sigma^2 * rho / 2 when attention falls
+ *    on one key).  The head gets INT4 codes (values in [-7, 7], scale
+ *    amax/7) iff sigma^2 * rho <= 0.02, else INT8; both are stored in the
+ *    8-bit layout and multiplied on the INT8 matrix core, so one launch
+ *    serves heads of both widths.  The statistics are fp32 sums in a fixed
+ *    order (see head_bits / adapt_stat below), the comparison is in fp64;
+ *    the choice is deterministic.  Supported by the dense entry points
+ *    (self-attention, cross-attention, grouped heads, split key ranges), not
+ *    by packed sequences or the decoding step.
  *  - smooth_v (0 or 1): smooth V before its FP8 quantization by subtracting
  *    the per-channel mean over all N tokens, added back to O in the epilogue
  *    (the smoothing of Q and V of the technical-report summary, Key
@@ -100,6 +119,24 @@ typedef enum { SAGE_F16 = 0, SAGE_BF16 = 1, SAGE_F32 = 2 } sage_dtype;
  *                    maxima and minima, later reused for bf16 pieces of q_mean
  *  v_mean            fp32  [B,H,D]       V channel means over all N tokens with
  *                    smooth_v, zeros without; added to O by the fused kernel
+ *  m2_part           fp32  [B,H,NQB,2,D] scratch (adaptive width): per-chunk K
+ *                    and V sums of squares
+ *  adapt_stat        fp32  [B*H*8 + B*H*NQB*2 + B*H*NQB] (adaptive width):
+ *                    first [B,H,8]: per head A_Q, E_Q, A_K, E_K, EV, V2, -, -
+ *                    (A_Q: sum over tokens of amax^2 of the smoothed query,
+ *                    summed per 128-token block in token order, then over
+ *                    blocks in order; E_Q: per block the sum over channels
+ *                    of max(0, SSQ - SQ * qmean) with SQ, SSQ the block's
+ *                    sequential sums of Q and Q^2, over blocks in order; A_K:
+ *                    per 128-key block the sum in key order of the key's
+ *                    group amax^2, over blocks in order; E_K, EV: sums over
+ *                    channels of max(0, SS - S * mean) with S, SS the chunked
+ *                    sums of K, V and K^2, V^2 and mean = S/N; V2: sum over
+ *                    channels of S_V * vmean), then scratch
+ *  head_bits         int32 [B,H]         code width chosen per head (4 or 8),
+ *                    written by the adaptive width
+ * For grouped or cross-attention shapes the key/value-side arrays (k_*,
+ * v_*, m2_part, head_bits, the per-head statistics) use Hkv and Nk.
  */
 typedef struct {
   uint8_t* q_codes;
@@ -114,9 +151,13 @@ typedef struct {
   float* k_part;
   float* v_part;
   float* v_mean;
+  float* m2_part;
+  float* adapt_stat;
+  int32_t* head_bits;
 } sage_quant_bufs;
 
-/* Version of the contract constants above (1 = 128/128/16). */
+/* Version of the contract constants above (2 = 128/128/16 blocks and groups,
+ * the adaptive width rule above, this sage_quant_bufs layout). */
 int sage_contract_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -150,6 +191,16 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
                               hipStream_t stream);
 
 /*
+ * The prepass with the adaptive width (qk_bits 0 above): the per-head
+ * choice needs the softmax scale sm_scale (> 0, finite).  Writes the code
+ * arrays in the 8-bit layout, the scales of each head's width, head_bits and
+ * the statistics of adapt_stat.  Read the buffers with qk_bits 0 (or 8).
+ */
+sage_status sage_quant_smooth_adaptive(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int H,
+                                       int N, int D, float sm_scale, int smooth_v, const sage_quant_bufs* out,
+                                       hipStream_t stream);
+
+/*
  * Attention forward: O = SageAttention2(Q, K, V), i.e. the prepass above
  * followed by the fused kernel (INT4 QK^T on the FP6 matrix core, exact,
  * dequantization with the compensation term, online softmax over 128-key
@@ -159,7 +210,7 @@ sage_status sage_quant_smooth(const void* q, const void* k, const void* v, sage_
  *            must not alias q, k, v or the workspace
  *  causal    nonzero: query i attends to keys j <= i
  *  sm_scale  softmax scale (> 0, finite), usually 1/sqrt(D)
- *  qk_bits   4 (INT4 Q/K codes) or 8 (INT8)
+ *  qk_bits   4 (INT4 Q/K codes), 8 (INT8) or 0 (adaptive width per head)
  *  smooth_v  1: subtract the V channel means before FP8, add them to O
  *  workspace device buffer of at least sage_workspace_bytes(B,H,N,D) bytes;
  *            afterwards it holds the sage_quant_bufs of this call
@@ -217,6 +268,10 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
  * sage_workspace_bytes_cross.  With Hq = Hkv = H and Nq = Nk = N every call
  * below is the self-attention call above (the same layout and results).
  * Limits: B*Hq <= 65535, Nq and Nk rounded up to 128 at most 2^24.
+ * qk_bits 0 (adaptive width) is accepted by sage_attn_fwd_cross,
+ * sage_attn_quantized_cross (the 8-bit layout) and sage_attn_fwd_split;
+ * sage_quant_smooth_cross takes 4 or 8, sage_quant_smooth_adaptive_cross the
+ * adaptive width.
  */
 size_t sage_workspace_bytes_cross(int B, int Hq, int Hkv, int Nq, int Nk, int D);
 
@@ -226,6 +281,12 @@ sage_status sage_quant_bufs_from_workspace_cross(void* ws, size_t bytes, int B, 
 sage_status sage_quant_smooth_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B, int Hq,
                                     int Hkv, int Nq, int Nk, int D, int qk_bits, int smooth_v,
                                     const sage_quant_bufs* out, hipStream_t stream);
+
+/* The adaptive-width prepass of this geometry: one width per K/V head, its
+ * statistics pooling the query heads of its group (head order). */
+sage_status sage_quant_smooth_adaptive_cross(const void* q, const void* k, const void* v, sage_dtype in_dtype, int B,
+                                             int Hq, int Hkv, int Nq, int Nk, int D, float sm_scale, int smooth_v,
+                                             const sage_quant_bufs* out, hipStream_t stream);
 
 sage_status sage_attn_fwd_cross(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Nq,
                                 int Nk, int D, int causal, float sm_scale, int qk_bits, int smooth_v,
@@ -318,6 +379,7 @@ sage_status sage_attn_decode(const void* q, const void* k, const void* v, void* 
  * Each sequence is smoothed, quantized and attended on its own (its own K and
  * V means, 128-token Q blocks from its first token, compensation rows, causal
  * mask), exactly as a dense call with B = 1, N = its length would do.
+ * qk_bits 4 or 8 (the adaptive width is not offered for packed sequences).
  */
 sage_status sage_quant_smooth_varlen(const void* q, const void* k, const void* v, sage_dtype in_dtype,
                                      const int* cu_seqlens, int nseq, int max_seqlen, int total_tokens, int H, int D,

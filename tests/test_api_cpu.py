@@ -14,6 +14,7 @@ from fp8_attention_transformer_amd import sage
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x10000000  # never dereferenced: validation fails first
+NF = len(sage.QuantBufs._fields_)   # arrays of a buffer set
 
 
 def _declared():
@@ -32,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_contract_and_status_strings():
-    assert sage.contract_version() == 1
+    assert sage.contract_version() == 2
     for st in (sage.OK, sage.ERR_INVALID, sage.ERR_UNSUPPORTED, sage.ERR_WORKSPACE, sage.ERR_HIP):
         assert sage.status_string(st).startswith("SAGE_")
 
@@ -48,7 +49,8 @@ def _sizes(B, H, N, D):
     NQB = NP // 128
     BH = B * H
     return [BH * NP * D, BH * NP * D, BH * NP * 4, BH * NP // 16 * 4, BH * NQB * D * 4, BH * D * 4,
-            BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * 2 * D * 4, BH * NQB * 2 * D * 4, BH * D * 4]
+            BH * NP * D, BH * D * 4, BH * NQB * NP * 4, BH * NQB * 2 * D * 4, BH * NQB * 2 * D * 4, BH * D * 4,
+            BH * NQB * 2 * D * 4, (BH * 8 + BH * NQB * 2 + BH * NQB) * 4, BH * 4]
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 256, 64), (4, 32, 4096, 128), (2, 48, 17776, 64), (1, 1, 1, 128)])
@@ -92,7 +94,7 @@ def _attn(**kw):
     (dict(sm_scale=math.inf), sage.ERR_INVALID), (dict(in_dtype=sage.F32), sage.ERR_INVALID),
     (dict(in_dtype=7), sage.ERR_INVALID), (dict(out_dtype=5), sage.ERR_INVALID),
     (dict(ws_bytes=100), sage.ERR_WORKSPACE), (dict(o=FAKE + 64), sage.ERR_INVALID),
-    (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID), (dict(qk_bits=0), sage.ERR_INVALID),
+    (dict(o=FAKE + (4 << 30) + 4096), sage.ERR_INVALID), (dict(qk_bits=-1), sage.ERR_INVALID),
     (dict(qk_bits=2), sage.ERR_INVALID), (dict(qk_bits=6), sage.ERR_INVALID), (dict(qk_bits=16), sage.ERR_INVALID),
     (dict(smooth_v=2), sage.ERR_INVALID), (dict(smooth_v=-1), sage.ERR_INVALID),
     # inputs and workspace start on a 16-byte boundary (read in 16-byte pieces)
@@ -105,13 +107,13 @@ def test_attn_fwd_validation(kw, expect):
 
 def test_quant_smooth_and_debug_validation():
     L = sage.lib()
-    qb = sage.QuantBufs(*([FAKE] * 12))
+    qb = sage.QuantBufs(*([FAKE] * NF))
     assert L.sage_quant_smooth(None, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
     assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.F32, 1, 1, 10, 64, 4, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
-    bad = sage.QuantBufs(*([FAKE] * 11 + [0]))
+    bad = sage.QuantBufs(*([FAKE] * (NF - 1) + [0]))
     assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(bad), None) == sage.ERR_INVALID
-    for i in range(12):   # every array of the buffer set on a 16-byte boundary
-        off = [FAKE] * 12
+    for i in range(NF):   # every array of the buffer set on a 16-byte boundary
+        off = [FAKE] * NF
         off[i] = FAKE + 4
         mis = sage.QuantBufs(*off)
         assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 4, 0, ctypes.byref(mis),
@@ -174,7 +176,7 @@ def test_fp6_tile_layout_helpers():
 
 def test_varlen_validation():
     L = sage.lib()
-    qb = sage.QuantBufs(*([FAKE] * 12))
+    qb = sage.QuantBufs(*([FAKE] * NF))
     qs = L.sage_quant_smooth_varlen
     ok_args = (FAKE, FAKE, FAKE, sage.BF16, FAKE, 3, 256, 500, 2, 64, 4, 0, ctypes.byref(qb), None)
     for i, bad in [(4, None), (5, 0), (6, 0), (7, 0), (9, 96), (10, 5), (11, 2), (3, sage.F32)]:
@@ -199,7 +201,7 @@ def _sizes_cross(B, Hq, Hk, Nq, Nk, D):
     part = BHk * NKB * 2 * D * 4
     return [BHq * NPq * D, BHk * NPk * D, BHq * NPq * 4, BHk * NPk // 16 * 4, BHq * NQB * D * 4, BHk * D * 4,
             BHk * NPk * D, BHk * D * 4, BHq * NQB * NPk * 4, max(part, BHq * NQB * 2 * D * 2),
-            max(part, BHq * NQB * D * 2), BHk * D * 4]
+            max(part, BHq * NQB * D * 2), BHk * D * 4, part, (BHk * 8 + BHq * NQB * 2 + BHk * NKB) * 4, BHk * 4]
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 2, 1, 8192, 128), (16, 32, 8, 1, 4096, 128), (2, 6, 3, 1000, 77, 64),
@@ -233,7 +235,7 @@ def test_cross_validation():
     assert ws(1, 4, 2, 10, 1 << 25, 64) == 0
     assert ws(1, 4, 2, 10, 10, 96) == 0
     assert ws(1, 4, 2, 1, 10, 64) > 0
-    qb = sage.QuantBufs(*([FAKE] * 12))
+    qb = sage.QuantBufs(*([FAKE] * NF))
     qs = L.sage_quant_smooth_cross
     ok = (FAKE, FAKE, FAKE, sage.BF16, 1, 4, 2, 1, 300, 64, 4, 0, ctypes.byref(qb), None)
     for i, bad in [(0, None), (3, sage.F32), (5, 3), (6, 3), (7, 0), (8, 0), (9, 96), (10, 5), (11, 2)]:
@@ -310,3 +312,32 @@ def test_static_entry_rejects_before_any_device_call():
     args = lambda shape: (FAKE, FAKE, FAKE, FAKE + (1 << 30)) + shape + (0, 0.1, 4, 0, sage.BF16, sage.BF16, None)
     assert L.sage_attn_fwd_static(*args(big)) == sage.ERR_WORKSPACE
     assert L.sage_attn_fwd_static(*args((1, 1, 10, 96))) == sage.ERR_INVALID
+
+
+def test_adaptive_width_validation():
+    """qk_bits 0 (adaptive width): the prepass entry points that take 4 or 8
+    reject it, the adaptive prepass needs a positive finite sm_scale, packed
+    sequences reject it; all before any device call."""
+    L = sage.lib()
+    qb = sage.QuantBufs(*([FAKE] * NF))
+    assert L.sage_quant_smooth(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 0, 0, ctypes.byref(qb),
+                               None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth_cross(FAKE, FAKE, FAKE, sage.BF16, 1, 4, 2, 10, 300, 64, 0, 0, ctypes.byref(qb),
+                                     None) == sage.ERR_INVALID
+    qa = L.sage_quant_smooth_adaptive
+    for sm in (0.0, -1.0, math.nan, math.inf):
+        assert qa(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, sm, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert qa(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 96, 0.1, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert qa(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 0.1, 2, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert qa(FAKE, FAKE, FAKE, sage.BF16, 1, 1, 10, 64, 0.1, 0, None, None) == sage.ERR_INVALID
+    qac = L.sage_quant_smooth_adaptive_cross
+    assert qac(FAKE, FAKE, FAKE, sage.BF16, 1, 4, 3, 10, 300, 64, 0.1, 0, ctypes.byref(qb), None) == sage.ERR_INVALID
+    assert L.sage_quant_smooth_varlen(FAKE, FAKE, FAKE, sage.BF16, FAKE, 3, 256, 500, 2, 64, 0, 0, ctypes.byref(qb),
+                                      None) == sage.ERR_INVALID
+    ws_bytes = sage.workspace_bytes(3, 2, 256, 64)
+    assert L.sage_attn_fwd_varlen(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE, 3, 256, 500, 2,
+                                  64, 0, 0.125, 0, 0, sage.BF16, sage.F32, FAKE + (4 << 30), ws_bytes,
+                                  None) == sage.ERR_INVALID
+    # the dense forward accepts 0 as far as argument checks go: a bad sm_scale is still caught first
+    assert _attn(qk_bits=0, sm_scale=0.0) == sage.ERR_INVALID
+    assert _attn(qk_bits=0, ws_bytes=100) == sage.ERR_WORKSPACE
