@@ -39,12 +39,48 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def host_threads() -> int:
+def host_cpus() -> int:
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+# The oracle's threads: every CPU the process may use, at most 16 (a GPU machine
+# gives one GPU's jobs a share of 16 CPUs, whatever more the host shows).
+def host_threads() -> int:
+    return max(1, min(host_cpus(), 16))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_warmup(fn, ms: float) -> int:
+    """Run the step back to back for about ms milliseconds after one call that
+    loads the kernels; returns the number of calls.  From a cold start the
+    GPU runs the headline step slower for its first ~25 calls (measured per
+    call: 1.86 ms on call 2, settling at 1.42-1.43 ms from about call 25, the
+    same with the buffers pre-touched and after 200 ms of unrelated matrix
+    products, since loading the kernels on the first call idles the GPU)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    n = 1
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
 
 
 def measured_traffic(workload: str):
@@ -75,7 +111,8 @@ def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool =
     dt = 0 if w.dtype == wl.F16 else 1
     q, k, v = wl.generate(w, heads=slice(0, 1))
     t0 = time.perf_counter()
-    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth, qk_bits=qk_bits, smooth_v=smooth_v)
+    # the adaptive width of a head depends on that head alone (self-attention)
+    z = oracle.quant_smooth(q, k, v, dt, nthreads=nth, qk_bits=qk_bits, smooth_v=smooth_v, sm_scale=w.scale)
     t_pre = time.perf_counter() - t0
     N, D = w.N, w.D
     rng = np.random.default_rng(0)
@@ -103,6 +140,8 @@ def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool =
         "value": ops / t_total / 1e12,
         "unit": "TOPS",
         "cores": nth,
+        "cpus_visible": host_cpus(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"head 0 of {w.B * w.H}: oracle prepass ({t_pre:.2f}s, counted pro rata) + mirror attention of "
                    f"{rows.size} random query rows ({t_rows:.2f}s); ops = 4*D*keys per row"),
@@ -123,7 +162,12 @@ def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool =
     return base, acc
 
 
-def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4, smooth_v: bool = False):
+def bits_label(qk_bits: int) -> str:
+    return "int4/int8 adaptive+fp8" if qk_bits == 0 else f"int{qk_bits}+fp8"
+
+
+def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4, smooth_v: bool = False,
+        warm_ms: float = 100.0):
     import numpy as np
     import torch
 
@@ -144,7 +188,10 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     # self-attention through the dense entry points, other geometries through
     # the cross-geometry ones (the dense calls are the Hkv = H, Nk = N case)
     def pre():
-        if w.self_attention:
+        if qk_bits == sage.ADAPTIVE:
+            sage.quant_smooth_adaptive_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D,
+                                             w.scale, bufs, sh, smooth_v=smooth_v)
+        elif w.self_attention:
             sage.quant_smooth(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, N, D, bufs, sh,
                               qk_bits=qk_bits, smooth_v=smooth_v)
         else:
@@ -167,6 +214,7 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
             sage.attn_fwd_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Hk, N, Nk, D, w.causal,
                                 w.scale, in_code, in_code, ws.ptr, ws.nbytes, sh, qk_bits=qk_bits, smooth_v=smooth_v)
 
+    warm_calls = device_warmup(full, warm_ms) if warm_ms > 0 else 0
     for _ in range(warmup):
         full()
     torch.cuda.synchronize()
@@ -208,12 +256,17 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"int{qk_bits}+fp8",
+        "dtype": bits_label(qk_bits),
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D, "causal": w.causal,
-                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale, "qk_bits": qk_bits,
-                   "smooth_v": smooth_v},
+                   "in_dtype": w.dtype, "out_dtype": w.dtype, "sm_scale": w.scale,
+                   "qk_bits": "adaptive" if qk_bits == 0 else qk_bits, "smooth_v": smooth_v},
+        "device_warmup": {"ms": warm_ms, "calls": warm_calls},
     }
+    if qk_bits == sage.ADAPTIVE:
+        hb = sage.head_bits(ws).cpu().numpy()
+        rec["config"]["heads_int4"] = int((hb == 4).sum())
+        rec["config"]["heads_int8"] = int((hb == 8).sum())
     if not w.self_attention:
         rec["config"].update({"Hkv": Hk, "Nk": Nk, "ops": "4*B*H*N*Nk*D (causal: minus 2*B*H*N^2*D)"})
     rec.update({
@@ -321,8 +374,12 @@ def run_split(w, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = Fal
                             w.scale, in_code, in_code, ws.data_ptr(), ws.numel(), sh, qk_bits, smooth_v, split)
 
     def pre():
-        sage.quant_smooth_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D, bufs, sh,
-                                qk_bits=qk_bits, smooth_v=smooth_v)
+        if qk_bits == sage.ADAPTIVE:
+            sage.quant_smooth_adaptive_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D,
+                                             w.scale, bufs, sh, smooth_v=smooth_v)
+        else:
+            sage.quant_smooth_cross(q.data_ptr(), k.data_ptr(), v.data_ptr(), in_code, B, H, Hk, N, Nk, D, bufs, sh,
+                                    qk_bits=qk_bits, smooth_v=smooth_v)
 
     def timed(fn):
         for _ in range(warmup):
@@ -344,7 +401,7 @@ def run_split(w, steps: int, warmup: int, qk_bits: int = 4, smooth_v: bool = Fal
     return {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"int{qk_bits}+fp8", "data": "synthetic",
+        "dtype": bits_label(qk_bits), "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hk, "N": N, "Nk": Nk, "D": D, "causal": w.causal,
                    "in_dtype": w.dtype, "out_dtype": w.dtype, "qk_bits": qk_bits, "smooth_v": smooth_v,
                    "split_keys": split, "entry": "sage_attn_fwd_split",
@@ -428,16 +485,17 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # The GPU runs the first ~20-30 full calls of a process up to 20% slower
-    # (clocks and caches settling; per-step HIP events on the headline:
-    # 1.76 ms mean over steps 0-19, 1.455 ms from step 40 on)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--device-warmup-ms", type=float, default=100.0,
+                    help="before the warm-up steps, run the step back to back for this long (the GPU settles over "
+                         "its first ~25 calls of the headline step, ~40 ms); 0 to skip")
     ap.add_argument("--workload", default=None,
                     help="workload name (dense or packed), or 'all' (default: the N=16k D=128 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--qk-bits", type=int, default=4, choices=(4, 8),
-                    help="width of the Q/K codes: 4 (INT4, the method's default) or 8 (INT8)")
+    ap.add_argument("--qk-bits", default="4", choices=("4", "8", "adaptive"),
+                    help="width of the Q/K codes: 4 (INT4, the method's default), 8 (INT8), or adaptive (INT4 or "
+                         "INT8 per key/value head by the predicted accuracy; dense workloads)")
     ap.add_argument("--smooth-v", action="store_true", help="subtract the V channel means before FP8 (added back to O)")
     ap.add_argument("--general-path", action="store_true",
                     help="run decoding and chunked-prefill workloads through the general cross-geometry entry points "
@@ -471,16 +529,20 @@ def main():
         todo = [packed[args.workload]]
     else:
         todo = [wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE]
+    qk_bits = 0 if args.qk_bits == "adaptive" else int(args.qk_bits)
     for w in todo:
         if isinstance(w, wl.PackedWorkload):
-            rec = run_packed(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
+            if qk_bits == 0:
+                print(f"{w.name}: the adaptive width is not offered for packed sequences; skipped", file=sys.stderr)
+                continue
+            rec = run_packed(w, args.steps, args.warmup, qk_bits, args.smooth_v)
         elif w.N == 1 and not w.self_attention and not args.general_path:
             rec = run_decode(w, args.steps, args.warmup, args.smooth_v)
         elif not w.self_attention and not args.general_path:
-            rec = run_split(w, args.steps, args.warmup, args.qk_bits, args.smooth_v)
+            rec = run_split(w, args.steps, args.warmup, qk_bits, args.smooth_v)
         else:
-            rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, args.qk_bits,
-                      args.smooth_v)
+            rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, qk_bits,
+                      args.smooth_v, args.device_warmup_ms)
         print(json.dumps(rec), flush=True)
 
 

@@ -122,6 +122,21 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
   }
 }
 
+// acc + src[0] + src[1] + ... + src[n-1], added in index order by one thread,
+// 16 values loaded per batch (the loads do not wait for the additions).
+__device__ __forceinline__ float lds_ordered_sum(const float* src, int n, float acc = 0.0f) {
+  int i = 0;
+  for (; i + 16 <= n; i += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) x[u] = src[i + u];
+#pragma unroll
+    for (int u = 0; u < 16; u++) acc = acc + x[u];
+  }
+  for (; i < n; i++) acc = acc + src[i];
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // finalize: grid (B*Hk), D threads.  K mean = (sum of chunk sums, in chunk
 // order) / Nk; likewise the V mean when V is smoothed (else 0).  V scale =
@@ -133,8 +148,8 @@ __global__ void __launch_bounds__(256) stats_kernel(const uint16_t* __restrict__
 // without V smoothing), summed over channels in channel order into E_K, EV
 // and V2 of the head.
 template <bool AD>
-__global__ void finalize_kernel(Dims d, Bufs b) {
-  constexpr int U = 32;   // chunks whose partials are loaded together
+__global__ void __launch_bounds__(128) finalize_kernel(Dims d, Bufs b) {
+  constexpr int U = AD ? 16 : 32;   // chunks whose partials are loaded together
   const int bh = blockIdx.x, c = threadIdx.x, D = d.D;
   const size_t base = (size_t)bh * d.NQBk * 2 * D + c;
   float tot = 0.0f, vtot = 0.0f, vx = -__builtin_inff(), vn = __builtin_inff();
@@ -190,44 +205,52 @@ __global__ void finalize_kernel(Dims d, Bufs b) {
     sEV[c] = fmaxf(ssv - vtot * vbs, 0.0f);
     sV2[c] = vtot * vbs;
     __syncthreads();
-    if (c == 0) {
-      float ek = 0.0f, ev = 0.0f, v2 = 0.0f;
-      for (int cc = 0; cc < D; cc++) {
-        ek = ek + sEK[cc];
-        ev = ev + sEV[cc];
-        v2 = v2 + sV2[cc];
-      }
-      b.stat_head[(size_t)bh * 8 + 3] = ek;
-      b.stat_head[(size_t)bh * 8 + 4] = ev;
-      b.stat_head[(size_t)bh * 8 + 5] = v2;
+    if (c < 3) {   // three threads, one sum each, in channel order
+      const float* src = c == 0 ? sEK : (c == 1 ? sEV : sV2);
+      b.stat_head[(size_t)bh * 8 + 3 + c] = lds_ordered_sum(src, D);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// decide (adaptive width): grid (B*Hk), one thread per K/V head sums the block
-// statistics in order (key blocks; the group's query heads in head order,
-// each over its query blocks) and chooses, in fp64: INT4 iff
+// decide (adaptive width): grid (B*Hk), 256 threads.  The block statistics are
+// summed in order (key blocks; the group's query heads in head order, each
+// over its query blocks): the workgroup stages 1024 partials at a time in LDS
+// (every load in flight at once) and thread 0 adds them in order.  Then, in
+// fp64, INT4 iff
 //   sm^2 * (A_Q*E_K + A_K*E_Q) * EV <= 11.76 * (G*Nq) * Nk * (EV + V2),
 // i.e. the predicted INT4 logit variance sigma^2 (uniform rounding,
 // delta = amax/7) times rho = EV / (EV + V2) is at most 0.02.
-__global__ void decide_kernel(Dims d, Bufs b) {
-  if (threadIdx.x != 0) return;
+constexpr int kDecideChunk = 1024;
+
+// Sum of n values src[i*stride] in index order (the result in thread 0).
+__device__ float ordered_sum(const float* __restrict__ src, int stride, int n, float* buf) {
+  float acc = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kDecideChunk) {
+    const int m = min(kDecideChunk, n - c0);
+    for (int i = threadIdx.x; i < m; i += blockDim.x) buf[i] = src[(size_t)(c0 + i) * stride];
+    __syncthreads();
+    if (threadIdx.x == 0) acc = lds_ordered_sum(buf, m, acc);
+    __syncthreads();
+  }
+  return acc;
+}
+
+__global__ void __launch_bounds__(256) decide_kernel(Dims d, Bufs b) {
+  __shared__ float buf[kDecideChunk];
   const int bhk = blockIdx.x, G = d.H / d.Hk;
   const int bb = bhk / d.Hk, hk = bhk % d.Hk;
-  float ak = 0.0f;
-  for (int kb = 0; kb < d.NQBk; kb++) ak = ak + b.stat_kblk[(size_t)bhk * d.NQBk + kb];
+  const float ak = ordered_sum(b.stat_kblk + (size_t)bhk * d.NQBk, 1, d.NQBk, buf);
   float aq = 0.0f, eq = 0.0f;
   for (int g = 0; g < G; g++) {
     const size_t bh = (size_t)bb * d.H + (size_t)hk * G + g;
-    float a = 0.0f, e = 0.0f;
-    for (int qb = 0; qb < d.NQB; qb++) {
-      a = a + b.stat_qblk[(bh * d.NQB + qb) * 2];
-      e = e + b.stat_qblk[(bh * d.NQB + qb) * 2 + 1];
-    }
+    const float* qs = b.stat_qblk + bh * d.NQB * 2;
+    const float a = ordered_sum(qs, 2, d.NQB, buf);
+    const float e = ordered_sum(qs + 1, 2, d.NQB, buf);
     aq = aq + a;
     eq = eq + e;
   }
+  if (threadIdx.x != 0) return;
   float* st = b.stat_head + (size_t)bhk * 8;
   const float ek = st[3], ev = st[4], v2 = st[5];
   const double sm = (double)d.sm;
@@ -588,10 +611,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
       // the block's statistics: token order, channel order (two waves)
       lds_barrier();
       if (tid == 0 || tid == 64) {
-        const float* src = tid == 0 ? sStat : sStat + kBQ;
-        const int cnt = tid == 0 ? kBQ : D;
-        float acc = 0.0f;
-        for (int e = 0; e < cnt; e++) acc = acc + src[e];
+        const float acc = tid == 0 ? lds_ordered_sum(sStat, kBQ) : lds_ordered_sum(sStat + kBQ, D);
         b.stat_qblk[((size_t)bh * d.NQB + qb) * 2 + (tid == 0 ? 0 : 1)] = acc;
       }
     }
@@ -674,11 +694,7 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
     }
     if constexpr (MODE == 1) {
       lds_barrier();
-      if (tid == 0) {
-        float acc = 0.0f;
-        for (int e = 0; e < kBK; e++) acc = acc + sStat[e];
-        b.stat_kblk[(size_t)bh * d.NQBk + qb] = acc;
-      }
+      if (tid == 0) b.stat_kblk[(size_t)bh * d.NQBk + qb] = lds_ordered_sum(sStat, kBK);
     }
   }
   // ---- V: 16-key chunks of one channel -> 16 FP8 bytes (channel tid mod D,
@@ -885,7 +901,7 @@ hipError_t prepass_impl(const void* q, const void* k, const void* v, const Dims&
                        v16, d, b);
     hipLaunchKernelGGL(finalize_kernel<true>, dim3(d.BHk()), dim3(D), 0, s, d, b);
     launch_quant<IN, D, 8, 1>(q16, k16, v16, d, b, s);
-    hipLaunchKernelGGL(decide_kernel, dim3(d.BHk()), dim3(64), 0, s, d, b);
+    hipLaunchKernelGGL(decide_kernel, dim3(d.BHk()), dim3(256), 0, s, d, b);
     launch_quant<IN, D, 8, 2>(q16, k16, v16, d, b, s);
   } else {
     hipLaunchKernelGGL((stats_kernel<IN, D, kPartKV, false>), nstat((long long)d.BHk() * d.NQBk), dim3(256), 0, s,
