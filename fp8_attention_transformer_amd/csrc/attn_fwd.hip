@@ -13,12 +13,13 @@
 // 32 queries).  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
 // core tiles: every lane then holds one query and 16 keys of each 32-key tile,
 // so the dequantization factor is one scalar per lane and tile (per-token Q
-// scale times the scale of the lane's 16-key K group) and row reductions of
-// the online softmax stay inside a lane plus one exchange with the partner
+// scale times the scale of the lane's 16-key K group) and the row maximum of
+// the online softmax stays inside a lane plus one exchange with the partner
 // lane 32 away.  P~ stays in registers: converted to e4m3 it is directly the
 // B operand of the FP8 matrix core (v_mfma_f32_32x32x64_f8f6f4) computing
 // O^T += V^T P~^T, with V stored by the prepass in the matching permuted
-// channel-major layout.
+// channel-major layout, and the row sum l' of the same e4m3 values (an
+// all-ones A operand).
 //
 // INT4 codes on the FP6 matrix core.  gfx950 has no INT4 matrix instruction,
 // but every integer in [-7, 7] is exact in FP6 e2m3, and the f8f6f4
@@ -36,17 +37,14 @@ namespace {
 
 constexpr float kLog2_448 = 8.80735492205760410744f;
 
-// Values of lane l and lane l^32 (the two half-waves hold the same query):
-// v_permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second, so with both operands equal to v the two results
-// hold, in every lane, v of the lane itself and of its partner.
+// The larger of the values of lane l and lane l^32 (the two half-waves hold
+// the same query): v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second, so with both operands equal to v
+// the two results hold, in every lane, v of the lane itself and of its
+// partner.
 __device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Code layout and operand shapes.  BITS 4: FP6 tiles of lane chunks (see
@@ -306,27 +304,33 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
   const float mref = SPLIT ? (mnew == -__builtin_inff() ? 0.0f : mnew) : mnew;
   alpha = __builtin_amdgcn_exp2f(as.m - mref);
   const float mm = mref - kLog2_448;
-  // ---- p' = exp2(s2 - mm) in [0, 448]; row sum; P~ -> e4m3 B operands
-  float part[4][4];   // independent partial row sums (tile, register quad)
+  // ---- p' = exp2(s2 - mm) in [0, 448]; P~ -> e4m3 B operands (the row sum
+  //      of the e4m3 values follows on the matrix core: row_sum)
 #pragma unroll
   for (int T = 0; T < 4; T++) {
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) p[r] = __builtin_amdgcn_exp2f(s2[T][r] - mm);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) part[T][q4] = (p[4 * q4] + p[4 * q4 + 1]) + (p[4 * q4 + 2] + p[4 * q4 + 3]);
-#pragma unroll
     for (int w = 0; w < 4; w++)
       P8[T >> 1][4 * (T & 1) + w] =
           (int)fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3], __float_as_int(s2[T][4 * w]));
     if constexpr (PIPE) pv_quarter<D, CAUSAL>(as, P8p, cVp, n, h, T);
   }
-  float tsum[4];
-#pragma unroll
-  for (int T = 0; T < 4; T++) tsum[T] = (part[T][0] + part[T][1]) + (part[T][2] + part[T][3]);
-  const float rowsum = pair_sum((tsum[0] + tsum[1]) + (tsum[2] + tsum[3]));
-  as.l = alpha * as.l + rowsum;
   as.m = mnew;
+}
+
+// l' = alpha * l' + (the block's row sum of P~): the sum of the e4m3 values
+// that multiply V, on the FP8 matrix core: an all-ones A operand (e4m3 1.0 =
+// 0x38) against P~ gives, in every accumulator row of the lane's query, the
+// sum over the block's 128 keys (FP8 products exact, fp32 accumulation).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void row_sum(AttnState<D, CAUSAL>& as, const v8i* P8, float alpha) {
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  v16f rs = {};
+  rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8[0], rs, 0, 0, 0, 0, 0, 0);
+  rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8[1], rs, 0, 0, 0, 0, 0, 0);
+  as.l = alpha * as.l + rs[0];
 }
 
 // O = alpha * O (the running buffer, once the previous block's products are in it)
@@ -478,6 +482,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
       float alpha;
       softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha,
                                             nullptr, nullptr, n);
+      row_sum<D, CAUSAL>(as, P8, alpha);
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++) {
 #pragma unroll
@@ -518,6 +523,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
       const uint8_t* cVp = bV(t > tb ? slot ^ 1 : 0);
       softmax_part<D, CAUSAL, SPLIT, true>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha_p, P8p,
                                        cVp, n);
+      row_sum<D, CAUSAL>(as, P8, alpha_p);
       P8p[0] = P8[0];
       P8p[1] = P8[1];
       wait_vmcnt<0>();   // K codes of block t+1 and V bytes of block t have landed (this wave's copies)

@@ -160,7 +160,8 @@ __device__ __forceinline__ void decode8(const v4i& raw, float* x) {
 //  E  per (head, block): the running maximum after that block (from the
 //     carried maximum and the block maxima before it, exactly the online
 //     recurrence), alpha, p' = exp2(s - m + log2 448), its FP8 rounding
-//     (decoded in place of the score) and the block's row sum;
+//     (decoded in place of the score) and the block's row sum of those
+//     e4m3 values;
 //  V  FP8 codes of V on the fly, O = alpha*O, then O += P~ V block by block;
 //     one thread per head carries the running maximum and l' = alpha*l' +
 //     rowsum into the next chunk.
@@ -351,9 +352,9 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeArgs a) {
       const float mm = mnew - kLog2_448;
       float* row = &sS[h][i * kBK + 2 * lane];
       const float p0 = __builtin_amdgcn_exp2f(row[0] - mm), p1 = __builtin_amdgcn_exp2f(row[1] - mm);
-      const float rs = wave_sum_dpp(p0 + p1);
       float q0, q1;
       fp8x2_decode<false>(fp8x2(p0, p1), q0, q1);
+      const float rs = wave_sum_dpp(q0 + q1);   // the row sum of the e4m3 values that weight V
       row[0] = q0;
       row[1] = q1;
       if (lane == 0) {

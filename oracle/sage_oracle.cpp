@@ -66,7 +66,10 @@
 //     s2 = fma((float)acc, (dq*dk)*ks, DeltaS*ks).
 //   - Online softmax over BK = 128-key blocks in ascending order.
 //     mm = m_t - log2(448);  p' = exp2(s2 - mm) in [0, 448];  P8 = e4m3(p');
-//     l' = alpha*l' + sum(p')  (p' before FP8 rounding).
+//     l' = alpha*l' + sum(dec(P8)): the row sum of the FP8 P~ that multiplies
+//     V (the pages quantize P~ and say nothing of the normalizer; summing the
+//     values that weight V keeps every output row a convex combination of the
+//     dequantized V rows).  Without P~ quantization the sum is of p' itself.
 //   - Two-level P~V: R_t = sum_j dec(P8_j)*dec(V8_j) in a fresh fp32 buffer per
 //     block; O_t = fma(alpha_t, O_{t-1}, R_t).
 //   - Epilogue: O = (O_T * vscale) / l'_T (+ vmean with V smoothing).
@@ -461,8 +464,9 @@ enum { MIRROR_QUANT_P = 1 };
 // Inputs are the canonical prepass arrays (geometry as for the prepass).
 // Outputs: O[r][c] (fp32) and, per row, slack[r]: an upper bound on how far O
 // may move if any P~ element whose value p' lies within relative distance eps
-// of an FP8 rounding midpoint were rounded the other way (used to tolerate exp2
-// implementation differences).  Optional lse[r] = (final running max m, final
+// of an FP8 rounding midpoint were rounded the other way (a diagnostic of exp2
+// implementation differences): per such element step * (max|v_j| + 448 *
+// max vscale) / l', weighted like the element.  Optional lse[r] = (final running max m, final
 // l') for diagnostics.
 //
 // kv_split (0: none): keys are cut into consecutive ranges of kv_split keys (a
@@ -499,6 +503,8 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
     const uint8_t* vh = v_codes + bhk * (int64_t)Nk * D;
     const float* ds = delta_s + (bhq * NQB + i / BQ_MEAN) * Nk;
     const float* dvec = v_scale + bhk * D;
+    float vbound = 0.0f;   // bound on |O| before V smoothing: every |dec(V8) * vscale| <= 448 * vscale
+    for (int c = 0; c < D; c++) vbound = std::max(vbound, 448.0f * dvec[c]);
     const float dq = q_scale[flat];
     const int64_t jend = causal ? i + 1 + (Nk - Nq) : Nk;  // keys j < jend are allowed
     // per-range states, merged below
@@ -531,7 +537,7 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
         for (int64_t j = t0; j < t1; j++) {
           float pj = (j < jend) ? std::exp2(s2[j - t0] - mm) : 0.0f;
           p[j - t0] = pj;
-          rowsum = rowsum + pj;
+          rowsum = rowsum + ((flags & MIRROR_QUANT_P) ? e4m3_decode(e4m3_encode(pj)) : pj);
         }
         // P~ -> FP8 and the level-1 partial R_t in a fresh fp32 buffer
         std::fill(R.begin(), R.end(), 0.0f);
@@ -546,10 +552,12 @@ int oracle_attn_mirror(const int8_t* q_codes, const float* q_scale, const int8_t
             float lo = pj * (1.0f - eps), hi = pj * (1.0f + eps);
             uint8_t clo = e4m3_encode(lo), chi = e4m3_encode(hi);
             if (clo != chi) {
+              // the flip moves the numerator by step * v_j and l' by step, so
+              // O by step * (v_j - O) / l': bounded with |O| <= 448 * max vscale
               float step = std::fabs(e4m3_decode(chi) - e4m3_decode(clo));
               float vm = 0.0f;
               for (int c = 0; c < D; c++) vm = std::max(vm, std::fabs(e4m3_decode(vh[j * D + c]) * dvec[c]));
-              blk_slack += step * vm;
+              blk_slack += step * (vm + vbound);
             }
           }
         }

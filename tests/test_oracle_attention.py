@@ -277,11 +277,13 @@ def _one_row_quant(oracle_lib, ds_keys, v_rows, v_scale, sm_scale):
         delta_s=np.asarray(ds_keys, np.float32)[None, None, None], v_mean=np.zeros((1, 1, D), np.float32))
 
 
-def test_midpoint_slack_is_the_code_flip_effect(oracle_lib):
+def test_midpoint_slack_bounds_the_code_flip_effect(oracle_lib):
     """The mirror's diagnostic slack: with exactly one P~ element within the
-    window of an e4m3 rounding midpoint, the slack equals the effect on O of
-    rounding that element the other way, max_c |step * v_c * vscale_c| / l';
-    with no element near a midpoint it is zero."""
+    window of an e4m3 rounding midpoint, the slack is step * (max_c |v_c *
+    vscale_c| + 448 * max vscale) / l' and bounds the effect on O of rounding
+    that element the other way (the flip moves the numerator by step * v and
+    the row sum l', a sum of the FP8 P~ values, by step); with no element near
+    a midpoint it is zero."""
     D, scale = 64, 0.5
     ks = np.float32(scale) * np.float32(1.44269504088896340736)
     log2_448 = np.float32(8.80735492205760410744)
@@ -305,14 +307,34 @@ def test_midpoint_slack_is_the_code_flip_effect(oracle_lib):
     # p' = 272 is the midpoint of the e4m3 neighbours 256 and 288
     O, slack, l, p1 = row(272.0)
     assert abs(p1 / 272.0 - 1) < 2.0 ** -16
+    assert l in (448.0 + 256.0, 448.0 + 288.0)          # l' sums the FP8 values of P~
     step = 288.0 - 256.0
-    flip = step * np.abs(vdec[1]).max() / l            # effect of rounding p'_1 the other way
-    assert slack == pytest.approx(flip, rel=1e-5)
-    # the same number from the two outputs: both roundings of P~_1, normalised by l'
-    O_lo = (448.0 * vdec[0] + 256.0 * vdec[1]) / l
-    O_hi = (448.0 * vdec[0] + 288.0 * vdec[1]) / l
-    assert np.abs(O_hi - O_lo).max() == pytest.approx(slack, rel=1e-5)
+    bound = step * (np.abs(vdec[1]).max() + 448.0 * v_scale.max()) / l
+    assert slack == pytest.approx(bound, rel=1e-5)
+    # the two roundings of P~_1, each normalised by its own row sum
+    O_lo = (448.0 * vdec[0] + 256.0 * vdec[1]) / (448.0 + 256.0)
+    O_hi = (448.0 * vdec[0] + 288.0 * vdec[1]) / (448.0 + 288.0)
     assert min(np.abs(O - O_lo).max(), np.abs(O - O_hi).max()) <= 1e-6 * np.abs(O_lo).max()
+    flip = np.abs(O_hi - O_lo).max()
+    assert flip <= slack
     # away from any midpoint (p' = 300, between the midpoints 272 and 304): no slack
     _, slack0, _, _ = row(300.0)
     assert slack0 == 0.0
+
+
+def test_row_sum_is_the_sum_of_fp8_p(oracle_lib):
+    """l' (lse[:, 1]) is the sum of the e4m3 values of P~, and O the
+    corresponding convex combination of the dequantized V rows: three keys at
+    p' = 448, 300 (FP8 288) and 100 (FP8 96)."""
+    D, scale = 64, 0.5
+    ks = np.float32(scale) * np.float32(1.44269504088896340736)
+    rng = np.random.default_rng(4)
+    v_rows = rng.integers(0, 0x7F, (3, D)).astype(np.uint8)
+    v_scale = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    ds = [0.0] + [np.float32(np.float32(np.log2(t / 448.0)) / ks) for t in (300.0, 100.0)]
+    z = _one_row_quant(oracle_lib, ds, v_rows, v_scale, scale)
+    O, _, lse = oracle_lib.attn_mirror(z, False, scale)
+    assert float(lse[0, 1]) == 448.0 + 288.0 + 96.0
+    vdec = oracle_lib.e4m3_decode(v_rows).astype(np.float64) * v_scale
+    ref = (448.0 * vdec[0] + 288.0 * vdec[1] + 96.0 * vdec[2]) / (448.0 + 288.0 + 96.0)
+    assert np.abs(O[0] - ref).max() <= 1e-6 * np.abs(ref).max()
