@@ -333,9 +333,13 @@ __device__ __forceinline__ void row_sum(AttnState<D, CAUSAL>& as, const v8i* P8,
   as.l = alpha * as.l + rs[0];
 }
 
-// O = alpha * O (the running buffer, once the previous block's products are in it)
+// O = alpha * O (the running buffer, once the previous block's products are
+// in it).  Skipped when no running maximum of the wave moved (alpha = 1 in
+// every lane, and O * 1 = O): on long key ranges the maxima settle and most
+// blocks need no rescale.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void rescale(AttnState<D, CAUSAL>& as, float alpha) {
+  if (!__any(alpha != 1.0f)) return;
 #pragma unroll
   for (int dt = 0; dt < D / 32; dt++)
 #pragma unroll
@@ -483,10 +487,9 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
       softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha,
                                             nullptr, nullptr, n);
       row_sum<D, CAUSAL>(as, P8, alpha);
+      rescale<D, CAUSAL>(as, alpha);
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++) {
-#pragma unroll
-        for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
         pv_mfma<D, CAUSAL>(as, P8, bV(slot), n, h, dt, 0);
         pv_mfma<D, CAUSAL>(as, P8, bV(slot), n, h, dt, 1);
       }
