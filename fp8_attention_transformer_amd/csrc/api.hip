@@ -630,4 +630,12 @@ sage_status sage_fp8_encode_debug(const float* in, uint8_t* out, size_t n, hipSt
   return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
 }
 
+sage_status sage_fp8_mfma_debug(const uint8_t* a, const uint8_t* b, const float* c, float* d, hipStream_t stream) {
+  if (!a || !b || !c || !d) return SAGE_ERR_INVALID;
+  const sage_status dc = device_check();
+  if (dc != SAGE_OK) return dc;
+  const hipError_t e = sage::launch_fp8_mfma_debug(a, b, c, d, stream);
+  return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP;
+}
+
 }  // extern "C"

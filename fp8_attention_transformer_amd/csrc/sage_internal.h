@@ -160,5 +160,6 @@ hipError_t launch_attn_split(const Bufs& b, const Dims& d, int causal, float ks,
 hipError_t launch_qk_debug(const Bufs& b, const Dims& d, int bh, int q0, int k0, int nq, int nk,
                            int32_t* out, hipStream_t s);
 hipError_t launch_fp8_encode(const float* in, uint8_t* out, size_t n, hipStream_t s);
+hipError_t launch_fp8_mfma_debug(const uint8_t* a, const uint8_t* b, const float* c, float* d, hipStream_t s);
 
 }  // namespace sage

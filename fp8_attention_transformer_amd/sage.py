@@ -26,7 +26,7 @@ EXPORTED = [
     "sage_attn_fwd_cross", "sage_attn_quantized_cross",
     "sage_decode_split_keys", "sage_decode_workspace_bytes", "sage_attn_decode",
     "sage_split_keys", "sage_split_workspace_bytes", "sage_attn_fwd_split", "sage_attn_fwd_static",
-    "sage_quant_smooth_adaptive", "sage_quant_smooth_adaptive_cross",
+    "sage_quant_smooth_adaptive", "sage_quant_smooth_adaptive_cross", "sage_fp8_mfma_debug",
 ]
 ADAPTIVE = 0   # qk_bits value of the adaptive width (INT4 or INT8 per key/value head)
 STATIC_SCRATCH_BYTES = 128 << 20   # SAGE_STATIC_SCRATCH_BYTES
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.sage_qk_int32_debug.restype = i32
         L.sage_fp8_encode_debug.argtypes = [P, P, sz, P]
         L.sage_fp8_encode_debug.restype = i32
+        L.sage_fp8_mfma_debug.argtypes = [P, P, P, P, P]
+        L.sage_fp8_mfma_debug.restype = i32
         L.sage_quant_smooth_varlen.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, i32, i32,
                                                ctypes.POINTER(QuantBufs), P]
         L.sage_quant_smooth_varlen.restype = i32
@@ -192,6 +194,12 @@ def qk_int32_debug(bufs: QuantBufs, B: int, H: int, N: int, D: int, bh: int, q0:
 
 def fp8_encode_debug(in_ptr: int, out_ptr: int, n: int, stream: int = 0) -> None:
     _check(lib().sage_fp8_encode_debug(in_ptr, out_ptr, n, stream), "sage_fp8_encode_debug")
+
+
+def fp8_mfma_debug(a_ptr: int, b_ptr: int, c_ptr: int, d_ptr: int, stream: int = 0) -> None:
+    """d = a*b + c on the FP8 matrix core: a uint8 [32][64], b uint8 [64][32]
+    (e4m3 codes), c and d fp32 [32][32], device pointers."""
+    _check(lib().sage_fp8_mfma_debug(a_ptr, b_ptr, c_ptr, d_ptr, stream), "sage_fp8_mfma_debug")
 
 
 def quant_smooth_varlen(q_ptr: int, k_ptr: int, v_ptr: int, in_dtype: int, cu_ptr: int, nseq: int, max_seqlen: int,

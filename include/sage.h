@@ -413,6 +413,17 @@ sage_status sage_qk_int32_debug(const sage_quant_bufs* qb, int B, int H, int N, 
  */
 sage_status sage_fp8_encode_debug(const float* in, uint8_t* out, size_t n, hipStream_t stream);
 
+/*
+ * Debug: one FP8 (OCP e4m3fn) 32x32x64 matrix-core product with fp32
+ * accumulator, the instruction of the fused kernel's P~V products and row
+ * sums (the arXiv abstract page's FP8 P~V): d = a * b + c.
+ * a: device uint8 [32][64] (e4m3 codes, row-major), b: device uint8 [64][32],
+ * c, d: device fp32 [32][32] row-major (d may equal c).  Lane l of the wave
+ * feeds row l%32 of a and column l%32 of b with k = 32*(l/32) .. +31 in byte
+ * order.  For tests of how the products are accumulated.
+ */
+sage_status sage_fp8_mfma_debug(const uint8_t* a, const uint8_t* b, const float* c, float* d, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
