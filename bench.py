@@ -166,8 +166,29 @@ def bits_label(qk_bits: int) -> str:
     return "int4/int8 adaptive+fp8" if qk_bits == 0 else f"int{qk_bits}+fp8"
 
 
+def cos_sim_heads(w, out_gpu, heads, nrows: int = 96):
+    """Cosine similarity of the GPU output against unquantized FP32 attention
+    (the oracle's exact mode) on nrows random query rows of each listed head."""
+    import numpy as np
+
+    import oracle
+    from fp8_attention_transformer_amd import workloads as wl
+
+    dt = 0 if w.dtype == wl.F16 else 1
+    rng = np.random.default_rng(1)
+    g, f = [], []
+    for hd in heads:
+        q, k, v = wl.generate(w, heads=slice(hd, hd + 1))
+        rows = np.sort(rng.choice(w.N, min(w.N, nrows), replace=False))
+        O_fp, _ = oracle.attn_exact(q, k, v, dt, w.causal, w.scale, 0, rows=rows, nthreads=host_threads())
+        g.append(out_gpu[hd][rows].astype(np.float64))
+        f.append(O_fp)
+    g, f = np.concatenate(g), np.concatenate(f)
+    return float((g * f).sum() / (np.linalg.norm(g) * np.linalg.norm(f)))
+
+
 def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int = 4, smooth_v: bool = False,
-        warm_ms: float = 100.0):
+        warm_ms: float = 100.0, cos_heads=None):
     import numpy as np
     import torch
 
@@ -288,6 +309,10 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
     if cpu and w.self_attention:
         o_host = out.float().cpu().numpy().reshape(B * H, N, D)[0]
         rec["cpu_baseline"], rec["accuracy"] = cpu_baseline_leg(w, o_host, cpu_seconds, qk_bits, smooth_v)
+    if cos_heads and w.self_attention:
+        o_host = out.float().cpu().numpy().reshape(B * H, N, D)
+        rec["accuracy"] = {"cos_sim_vs_fp32_sampled": cos_sim_heads(w, o_host, cos_heads),
+                           "heads": list(cos_heads), "rows_per_head": min(N, 96)}
     return rec
 
 
@@ -500,6 +525,9 @@ def main():
     ap.add_argument("--general-path", action="store_true",
                     help="run decoding and chunked-prefill workloads through the general cross-geometry entry points "
                          "(no decode kernel, no split key ranges)")
+    ap.add_argument("--no-adaptive-leg", action="store_true",
+                    help="skip the second measurement of the default run with the adaptive width (the mode that "
+                         "keeps cosine similarity against FP32 attention >= 0.99)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -543,6 +571,24 @@ def main():
         else:
             rec = run(w, args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_seconds, qk_bits,
                       args.smooth_v, args.device_warmup_ms)
+            if args.workload is None and qk_bits == 4 and not args.no_adaptive_leg:
+                # The same workload with the adaptive width: INT4 codes reach
+                # cosine similarity 0.89-0.92 against FP32 attention on these
+                # inputs, INT4/INT8 chosen per K/V head keeps it >= 0.99.
+                ad = run(w, args.steps, args.warmup, False, 0.0, 0, args.smooth_v, args.device_warmup_ms,
+                         cos_heads=(0, w.B * w.H // 2, w.B * w.H - 1))
+                rec["adaptive"] = {
+                    "value": ad["value"], "unit": "TOPS", "ms_per_step": ad["ms_per_step"],
+                    "dtype": ad["dtype"], "heads_int4": ad["config"]["heads_int4"],
+                    "heads_int8": ad["config"]["heads_int8"],
+                    "fused_us": ad["roofline"]["kernel_us"], "fused_frac": ad["roofline"]["frac"],
+                    "prepass_us": ad["breakdown"]["prepass_us"],
+                    "cos_sim_vs_fp32_sampled": ad["accuracy"]["cos_sim_vs_fp32_sampled"],
+                    "cos_sim_sample": ad["accuracy"],
+                }
+                if "accuracy" in rec:
+                    rec["accuracy"]["note"] = ("INT4 codes (the method's default); 'adaptive' holds the same "
+                                               "workload with INT4/INT8 chosen per K/V head")
         print(json.dumps(rec), flush=True)
 
 
