@@ -135,6 +135,10 @@ def test_quant_smooth_and_debug_validation():
     assert L.sage_attn_quantized(ctypes.byref(qb), FAKE, 1, 1, 10, 64, 0, 0.0, 8, sage.F32, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(None, FAKE, 10, None) == sage.ERR_INVALID
     assert L.sage_fp8_encode_debug(FAKE, FAKE, 0, None) == sage.ERR_INVALID
+    for i in range(4):   # every pointer of the FP8 product debug call
+        ptrs = [FAKE] * 4
+        ptrs[i] = None
+        assert L.sage_fp8_mfma_debug(*ptrs, None) == sage.ERR_INVALID, i
 
 
 def test_product_package_does_not_import_the_oracle():
