@@ -28,9 +28,13 @@ bool shape_ok(int B, int Hq, int Hkv, int Nq, int Nk, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return false;
   if (Hq % Hkv) return false;
   if (D != 64 && D != 128) return false;
-  // keep every index computed in 32-bit arithmetic inside the kernels in range
+  // keep every index computed in 32-bit arithmetic inside the kernels in range,
+  // and every buffer resource within its 32-bit byte range: the 16-bit K or
+  // V rows of a head (decoding step, 2*D bytes a row) and the DeltaS rows of
+  // a query head (NQB * NPk fp32, written through one resource)
   const long long NPq = ((long long)Nq + 127) / 128 * 128, NPk = ((long long)Nk + 127) / 128 * 128;
-  if (NPq > (1LL << 24) || NPk > (1LL << 24)) return false;
+  if (NPq > (1LL << 23) || NPk > (1LL << 23)) return false;
+  if (NPq / 128 * NPk >= (1LL << 30)) return false;
   if ((long long)B * Hq > 65535) return false;   // grid y dimension of the prepass
   if ((long long)B * Hq * (NPq / 128) > (1LL << 30)) return false;
   if ((long long)B * Hkv * (NPk / 128) > (1LL << 30)) return false;

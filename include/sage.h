@@ -267,7 +267,9 @@ sage_status sage_attn_quantized(const sage_quant_bufs* qb, void* o, int B, int H
  * (NPk = Nk rounded up to 128).  Size the workspace with
  * sage_workspace_bytes_cross.  With Hq = Hkv = H and Nq = Nk = N every call
  * below is the self-attention call above (the same layout and results).
- * Limits: B*Hq <= 65535, Nq and Nk rounded up to 128 at most 2^24.
+ * Limits: B*Hq <= 65535; Nq and Nk rounded up to 128 at most 2^23; and
+ * (Nq rounded up to 128) / 128 * (Nk rounded up to 128) below 2^30 (the
+ * DeltaS rows of one query head: self-attention N up to ~370k tokens).
  * qk_bits 0 (adaptive width) is accepted by sage_attn_fwd_cross,
  * sage_attn_quantized_cross (the 8-bit layout) and sage_attn_fwd_split;
  * sage_quant_smooth_cross takes 4 or 8, sage_quant_smooth_adaptive_cross the

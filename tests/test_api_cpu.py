@@ -39,9 +39,18 @@ def test_contract_and_status_strings():
 
 
 @pytest.mark.parametrize("shape", [(0, 1, 10, 64), (1, 0, 10, 64), (1, 1, 0, 64), (1, 1, 10, 96), (1, 1, 10, 32),
-                                   (1, 1, 1 << 25, 64)])
+                                   (1, 1, 1 << 25, 64), (1, 1, (1 << 23) + 1, 64), (1, 1, 400000, 128)])
 def test_workspace_bytes_invalid(shape):
     assert sage.workspace_bytes(*shape) == 0
+
+
+def test_workspace_bytes_limits():
+    """The largest accepted shapes: DeltaS rows of a head below 2^30 fp32
+    (N = 360000 self-attention), keys up to 2^23 against few queries."""
+    assert sage.workspace_bytes(1, 1, 360000, 128) > 0
+    L = sage.lib()
+    assert L.sage_workspace_bytes_cross(1, 1, 1, 128, 1 << 23, 128) > 0
+    assert L.sage_workspace_bytes_cross(1, 1, 1, 128, (1 << 23) + 1, 128) == 0
 
 
 def _sizes(B, H, N, D):
