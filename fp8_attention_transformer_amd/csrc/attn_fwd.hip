@@ -15,7 +15,9 @@
 // rounding order differs from the separate partial).
 //
 // gfx950 mapping.  A workgroup owns one 128-query block of one head (4 waves x
-// 32 queries).  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
+// 32 queries); on long dense non-causal key ranges, two adjacent blocks (8
+// waves, one workgroup per CU) that share every staged K/V block, staged
+// three blocks deep.  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
 // core tiles: every lane then holds one query and 16 keys of each 32-key tile,
 // so the dequantization factor is one scalar per lane and tile (per-token Q
 // scale times the scale of the lane's 16-key K group) and the row maximum of
@@ -38,6 +40,8 @@
 // core (v_mfma_i32_32x32x32_i8).
 #include "sage_internal.h"
 #include "sage_device.h"
+
+#include <type_traits>
 
 namespace sage {
 namespace {
@@ -202,6 +206,17 @@ __device__ __forceinline__ void stage_v_async(uint8_t* sV, __amdgpu_buffer_rsrc_
   for (int i = 0; i < VCH; i++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(sV + 4096 * i + 1024 * wave), 16, voff, vb + 4096 * i, 0,
                                              0);
+}
+
+// NR copy rounds of 4 KB (256 lanes x 16 bytes) from the global chunks at
+// base + 4096 i + 1024 wave + off to LDS dst + 4096 i + 1024 wave.
+template <int NR>
+__device__ __forceinline__ void stage_rounds(uint8_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t base, int wave,
+                                             uint32_t off) {
+  const uint32_t b = base + 1024u * wave;
+#pragma unroll
+  for (int i = 0; i < NR; i++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + 4096 * i + 1024 * wave), 16, off, b + 4096 * i, 0, 0);
 }
 
 template <int D, bool CAUSAL>
@@ -380,17 +395,31 @@ constexpr int kPipeMaxBlocks = 96;
 // SPLIT: workgroup (head, key range, query block) runs the method over one
 // range of key blocks from an empty state and writes its unnormalised state
 // (O, running max, row sum) for a merge kernel (dense geometry only).
-template <int D, int BITS, bool CAUSAL, bool SPLIT, bool PIPE>
-__global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o, int out_dtype,
-                                                      SplitParts sp) {
+// QPW = 2: 8-wave workgroups over two adjacent query blocks (waves 4-7 the
+// second), each K/V block copied once for both (the first block's waves copy
+// K, the second's V); the two waves of a SIMD then come from one workgroup.
+template <int D, int BITS, bool CAUSAL, bool SPLIT, bool PIPE, int QPW = 1>
+__global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o,
+                                                                int out_dtype, SplitParts sp) {
+  static_assert(QPW == 1 || (!CAUSAL && !SPLIT && !PIPE), "two query blocks per workgroup: dense non-causal");
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int NDT = D / 32;
   // K/V staging: two LDS stages of one 128-key block each (double buffer),
   // as separate arrays so the compiler can tell the block being read from the
   // block being filled by the asynchronous copies.
-  __shared__ __align__(16) uint8_t sK0[kBK * ROWB], sK1[kBK * ROWB];
+  // two query blocks per workgroup: K stages rounded up to whole V copy rounds
+  constexpr int KSLOT = QPW == 2 ? (D * kBK > kBK * ROWB ? D * kBK : kBK * ROWB) : kBK * ROWB;
+  __shared__ __align__(16) uint8_t sK0[KSLOT], sK1[KSLOT];
   __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK];
-  __shared__ float sDS0[kBK], sDS1[kBK];
+  __shared__ float sDS0[QPW * kBK], sDS1[QPW * kBK];
+  // a third stage (two query blocks per workgroup): block t+2 is copied while block t is computed
+  __shared__ __align__(16) uint8_t sK2[QPW == 2 ? KSLOT : 16], sV2[QPW == 2 ? D * kBK : 16];
+  __shared__ float sDS2[QPW == 2 ? QPW * kBK : 4], sKS2[QPW == 2 ? kBK / kKGroup : 4];
+  // raw compensation rows (both query blocks) and K scales (64 lanes, the 8
+  // scales repeated) of each stage, copied straight into LDS
+  __shared__ __align__(16) float sRD0[QPW == 2 ? QPW * kBK : 4], sRD1[QPW == 2 ? QPW * kBK : 4],
+      sRD2[QPW == 2 ? QPW * kBK : 4];
+  __shared__ __align__(16) float sRK0[QPW == 2 ? 64 : 4], sRK1[QPW == 2 ? 64 : 4], sRK2[QPW == 2 ? 64 : 4];
   __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup];
   __shared__ float sVS[D], sVM[D];   // V scales and means of the head, for the epilogue
   auto bK = [&](int i) { return i == 0 ? sK0 : sK1; };
@@ -400,7 +429,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = QPW == 1 ? 0 : wave8 >> 2;   // which query block of the workgroup
+  const int wave = wave8 & 3;                   // wave within its query block
+  const int htid = tid & 255;                   // thread within its query block
   const int n = lane & 31, h = lane >> 5;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -438,13 +470,16 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(kblk, (uint32_t)d.NPk * ROWB);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(vblk, (uint32_t)d.NPk * D);
   auto issue_k = [&](int t, int slot) {   // K codes, compensation row and K scales of block t
-    stage_k_async<D, BITS>(bK(slot), rk, t, wave, koff);
-    ds_reg = dsrow[t * kBK + (tid & (kBK - 1))];
-    ks_reg = kscl[t * (kBK / kKGroup) + (tid & (kBK / kKGroup - 1))];
+    if (QPW == 1 || half == 0) stage_k_async<D, BITS>(bK(slot), rk, t, wave, koff);
+    ds_reg = dsrow[t * kBK + (htid & (kBK - 1))];
+    ks_reg = kscl[t * (kBK / kKGroup) + (htid & (kBK / kKGroup - 1))];
   };
   auto publish = [&](int slot) {   // compensation row and K scales of the block -> LDS
-    if (tid < kBK) bDS(slot)[tid] = ds_reg * ks;
+    if (htid < kBK) bDS(slot)[half * kBK + htid] = ds_reg * ks;
     if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg;
+  };
+  auto issue_v = [&](int t, int slot) {
+    if (QPW == 1 || half == 1) stage_v_async<D>(bV(slot), rv, t, wave, voff);
   };
 
   // The head's V scales and means (read by the epilogue) load first, so the
@@ -455,7 +490,7 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     vm_reg = b.v_mean[(size_t)bhk * D + tid];
   }
   issue_k(tb, 0);
-  stage_v_async<D>(bV(0), rv, tb, wave, voff);
+  issue_v(tb, 0);
 
   QOperand<D, BITS> qop;
   load_q_operand<D, BITS>(b.q_codes + hrowp * ROWB, qrow, h, qop);
@@ -477,7 +512,95 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
   }
   __syncthreads();
 
-  if constexpr (!PIPE) {
+  if constexpr (QPW == 2) {
+    // Three LDS stages: iteration t copies block t+2 (K codes, V bytes, the
+    // raw compensation rows and K scales, all straight into LDS) and computes
+    // block t; its wait at the end covers block t+1 only.  Unrolled by three
+    // so that every stage is a named array in every step: the compiler then
+    // tells the stage being read from the ones being filled and adds no wait
+    // of its own for the copies in flight.
+    constexpr int KCH = kBK * ROWB / 16 / 256, VCH = D * kBK / 16 / 256;   // copies per wave and block
+    static_assert(KCH <= VCH && VCH * 4096 <= KSLOT, "copy rounds of K and V");
+    auto issue_kv = [&](int t, auto slotc) {   // K codes (first block's waves) or V bytes (second's) of block t
+      constexpr int sl = decltype(slotc)::value;
+      if (half == 0) {
+        // VCH rounds of K as well (FP6 codes: the last round reads the start
+        // of the next block, or zeros past the head), so that every wave
+        // issues the same copies per block and its waits count them exactly
+        stage_rounds<VCH>(sl == 0 ? sK0 : (sl == 1 ? sK1 : sK2), rk, (uint32_t)t * (kBK * ROWB), wave, koff);
+      } else {
+        stage_rounds<VCH>(sl == 0 ? sV0 : (sl == 1 ? sV1 : sV2), rv, (uint32_t)t * (D * kBK), wave, voff);
+      }
+    };
+    // raw compensation row of this wave's query block (two dword rounds of 64
+    // lanes: every wave of the block copies the whole row, the same bytes to
+    // the same place) and the K scales (lane l: scale l mod 8)
+    const __amdgpu_buffer_rsrc_t rd = head_rsrc(dsrow, (uint32_t)d.NPk * 4);
+    const __amdgpu_buffer_rsrc_t rks = head_rsrc(kscl, (uint32_t)d.NPk / kKGroup * 4);
+    auto issue_sc = [&](int t, auto slotc) {
+      constexpr int sl = decltype(slotc)::value;
+      float* rdd = (sl == 0 ? sRD0 : (sl == 1 ? sRD1 : sRD2)) + half * kBK;
+      float* rkd = sl == 0 ? sRK0 : (sl == 1 ? sRK1 : sRK2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)rdd, 4, 4u * lane, (uint32_t)t * kBK * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)(rdd + 64), 4, 4u * lane, (uint32_t)t * kBK * 4 + 256, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)rkd, 4, 4u * (lane & 7),
+                                               (uint32_t)t * (kBK / kKGroup) * 4, 0, 0);
+    };
+    auto publish3 = [&](auto slotc) {   // compensation row times the log2-domain scale
+      constexpr int sl = decltype(slotc)::value;
+      float* dsd = sl == 0 ? sDS0 : (sl == 1 ? sDS1 : sDS2);
+      const float* rdd = sl == 0 ? sRD0 : (sl == 1 ? sRD1 : sRD2);
+      if (htid < kBK) dsd[half * kBK + htid] = rdd[half * kBK + htid] * ks;
+    };
+    auto step = [&](int t, auto c, auto n1, auto n2) {
+      constexpr int sc = decltype(c)::value;
+      const uint8_t* cK = sc == 0 ? sK0 : (sc == 1 ? sK1 : sK2);
+      const uint8_t* cV = sc == 0 ? sV0 : (sc == 1 ? sV1 : sV2);
+      const float* cDS = (sc == 0 ? sDS0 : (sc == 1 ? sDS1 : sDS2)) + half * kBK;
+      const float* cKS = sc == 0 ? sRK0 : (sc == 1 ? sRK1 : sRK2);
+      // unconditional: past the range the last block is copied again into a
+      // free stage, so every wave issues the same loads in every step
+      issue_kv(min(t + 2, te - 1), n2);
+      issue_sc(min(t + 2, te - 1), n2);
+      const bool need_mask = ragged && t == nkb - 1;
+      v16f S[4];
+      qk_part<D, BITS>(S, qop, cK, n, h);
+      v8i P8[2];
+      float alpha;
+      softmax_part<D, CAUSAL, SPLIT, false>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha, nullptr,
+                                            nullptr, n);
+      row_sum<D, CAUSAL>(as, P8, alpha);
+      rescale<D, CAUSAL>(as, alpha);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) {
+        pv_mfma<D, CAUSAL>(as, P8, cV, n, h, dt, 0);
+        pv_mfma<D, CAUSAL>(as, P8, cV, n, h, dt, 1);
+      }
+      // block t+1 has landed (this wave's copies and loads; block t+2's
+      // copies, issued last, may still be in flight)
+      wait_vmcnt<VCH + 3>();
+      publish3(n1);
+      lds_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    issue_kv(min(tb + 1, te - 1), I1{});
+    issue_sc(min(tb + 1, te - 1), I1{});
+    // block tb's scales: the common prologue staged them in sKS0; copy them to
+    // the raw stage the key loop reads (lanes 0-7 of each wave, same values)
+    if (lane < kBK / kKGroup) sRK0[lane] = sKS0[lane];
+    lds_barrier();
+    for (int t = tb; t < te; t += 3) {
+      step(t, I0{}, I1{}, I2{});
+      if (t + 1 >= te) break;
+      step(t + 1, I1{}, I2{}, I0{});
+      if (t + 2 >= te) break;
+      step(t + 2, I2{}, I0{}, I1{});
+    }
+    wait_vmcnt<0>();   // no copy into LDS outlives the workgroup
+  } else if constexpr (!PIPE) {
     // Plain key loop: iteration t stages block t+1 (K codes and V bytes) and
     // runs block t's S^T tiles, softmax and P~V in sequence.
     for (int t = tb; t < te; t++) {
@@ -485,15 +608,15 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
       const bool ahead = t + 1 < te;   // block t+1 exists: stage it now
       if (ahead) {
         issue_k(t + 1, slot ^ 1);
-        stage_v_async<D>(bV(slot ^ 1), rv, t + 1, wave, voff);
+        issue_v(t + 1, slot ^ 1);
       }
       const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
       v16f S[4];
       qk_part<D, BITS>(S, qop, bK(slot), n, h);
       v8i P8[2];
       float alpha;
-      softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha,
-                                            nullptr, nullptr, n);
+      softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot) + half * kBK, bKS(slot), dq, ks, t, klim, h, nk, need_mask,
+                                            P8, alpha, nullptr, nullptr, n);
       row_sum<D, CAUSAL>(as, P8, alpha);
       rescale<D, CAUSAL>(as, alpha);
 #pragma unroll
@@ -624,6 +747,10 @@ __global__ void __launch_bounds__(256, 2) attn_kernel(Bufs b, Dims d, float ks, 
     bh = logical / npair;
     qb0 = d.NQB - 1 - p;
     if (p != qb0) qb1 = p;
+  } else if (QPW == 2) {
+    const int np = d.NQB / 2;
+    bh = logical / np;
+    qb0 = 2 * (logical % np) + half;
   } else {
     const int hs = logical / d.NQB;
     bh = d.cu ? logical % d.BH() : (SPLIT ? hs / sp.S : hs);
@@ -742,7 +869,18 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   // bit-identical results.
   const int mean_blocks = SPLIT ? sp.split_blocks : (causal ? (d.NQBk + 1) / 2 : d.NQBk);
   bool launched = false;
+  // Long dense non-causal ranges at D = 128: two query blocks per workgroup
+  // (measured against one, bit-identical: N 16384 INT4 +1.6%, INT8 +4.3%;
+  // N 32768 INT4 +0.4%, INT8 +3.7%).
+  if constexpr (D == 128 && !SPLIT) {
+    if (!causal && !d.cu && d.NQB % 2 == 0 && mean_blocks > kPipeMaxBlocks) {
+      hipLaunchKernelGGL((attn_kernel<D, BITS, false, false, false, 2>), dim3(d.NQB / 2 * d.BH()), dim3(512), 0, s, b,
+                         d, ks, o, out_dtype, sp);
+      launched = true;
+    }
+  }
   if constexpr (D == 128) {
+    if (!launched)
     if (mean_blocks <= kPipeMaxBlocks) {
       if (causal)
         hipLaunchKernelGGL((attn_kernel<D, BITS, true, SPLIT, true>), grid, dim3(256), 0, s, b, d, ks, o, out_dtype, sp);

@@ -27,6 +27,11 @@ CASES = [
     (2, 4, 1, 257, 257, 128, True, 8, True),       # multi-query, square
     (1, 2, 1, 129, 4096, 128, True, 4, False),     # short chunk at the end of a long cache
     (1, 4, 4, 33, 300, 64, False, 8, True),        # plain heads, cross lengths
+    # long non-causal key ranges with an even number of query blocks run two
+    # query blocks per workgroup (three-deep K/V staging); ragged keys, ragged
+    # queries, grouped heads
+    (1, 4, 2, 256, 12900, 128, False, 4, False),
+    (1, 2, 2, 250, 12500, 128, False, 8, True),
 ]
 
 
