@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       // free stage, so every wave issues the same loads in every step
       issue_kv(min(t + 2, te - 1), n2);
       issue_sc(min(t + 2, te - 1), n2);
-      const bool need_mask = ragged && t == nkb - 1;
+      const bool need_mask = ragged && t == nkb - 1;   // (non-causal)
       v16f S[4];
       qk_part<D, BITS>(S, qop, cK, n, h);
       v8i P8[2];
@@ -741,16 +741,16 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
   // D = 64 keeps two call sites: its code is smaller, and the loop would cost
   // it 35 registers and its third wave per SIMD.
   int bh, rng = 0, qb0, qb1 = -1;
-  if (CAUSAL && !SPLIT && !d.cu && (int)gridDim.x != d.NQB * d.BH()) {
+  if (QPW == 2) {
+    const int np = d.NQB / 2;
+    bh = logical / np;
+    qb0 = 2 * (logical % np) + half;
+  } else if (CAUSAL && !SPLIT && !d.cu && (int)gridDim.x != d.NQB * d.BH()) {
     const int npair = (d.NQB + 1) / 2;
     const int p = logical % npair;
     bh = logical / npair;
     qb0 = d.NQB - 1 - p;
     if (p != qb0) qb1 = p;
-  } else if (QPW == 2) {
-    const int np = d.NQB / 2;
-    bh = logical / np;
-    qb0 = 2 * (logical % np) + half;
   } else {
     const int hs = logical / d.NQB;
     bh = d.cu ? logical % d.BH() : (SPLIT ? hs / sp.S : hs);
@@ -869,11 +869,15 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   // bit-identical results.
   const int mean_blocks = SPLIT ? sp.split_blocks : (causal ? (d.NQBk + 1) / 2 : d.NQBk);
   bool launched = false;
-  // Long dense non-causal ranges at D = 128: two query blocks per workgroup
-  // (measured against one, bit-identical: N 16384 INT4 +1.6%, INT8 +4.3%;
-  // N 32768 INT4 +0.4%, INT8 +3.7%).
+  // Dense non-causal D = 128 with an even number of query blocks: two query
+  // blocks per workgroup (measured against one, bit-identical, builds
+  // interleaved: N 16384 INT4 +1.6%, INT8 +4.3%; N 32768 +0.4%, +3.7%;
+  // against the pipelined loop: DiT +0.7-1.8%, +7%; N 8192 +2.7-4.4%, +7-8%).
+  // Causal ranges keep one block per workgroup: a two-block form (the first
+  // block's waves masked through the second's extra key block, pairs
+  // heaviest first) measured 1% slower on N 16384 and 3% on N 32768.
   if constexpr (D == 128 && !SPLIT) {
-    if (!causal && !d.cu && d.NQB % 2 == 0 && mean_blocks > kPipeMaxBlocks) {
+    if (!causal && !d.cu && d.NQB % 2 == 0) {
       hipLaunchKernelGGL((attn_kernel<D, BITS, false, false, false, 2>), dim3(d.NQB / 2 * d.BH()), dim3(512), 0, s, b,
                          d, ks, o, out_dtype, sp);
       launched = true;

@@ -32,6 +32,7 @@ CASES = [
     # queries, grouped heads
     (1, 4, 2, 256, 12900, 128, False, 4, False),
     (1, 2, 2, 250, 12500, 128, False, 8, True),
+    (1, 2, 1, 256, 100, 128, False, 4, False),     # two query blocks, one (ragged) key block
 ]
 
 

@@ -32,6 +32,9 @@ SMALL = [
     wl.custom(1, 1, 640, 128, causal=True, seed=106, t_noise_scale=0.5, k_offset_std=4.0),
     wl.custom(1, 3, 1000, 64, causal=True, seed=107, outlier_channels=8, outlier_scale=15.0, outliers_in_k=True,
               k_offset_std=5.0),
+    # D = 128, non-causal, two query blocks (one 8-wave workgroup per pair): a
+    # two-block key range with ragged queries and keys
+    wl.custom(1, 2, 200, 128, seed=108, k_offset_std=3.0, v_offset_std=1.0),
 ]
 FULL = [wl.LLM, wl.DIT, wl.VIDEO] + wl.LONG
 FULL_CASES = [(w, 4) for w in FULL] + [(w, 8) for w in (wl.LLM, wl.VIDEO, wl.HEADLINE)]
