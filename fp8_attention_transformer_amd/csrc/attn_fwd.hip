@@ -15,9 +15,9 @@
 // rounding order differs from the separate partial).
 //
 // gfx950 mapping.  A workgroup owns one 128-query block of one head (4 waves x
-// 32 queries); on long dense non-causal key ranges, two adjacent blocks (8
-// waves, one workgroup per CU) that share every staged K/V block, staged
-// three blocks deep.  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
+// 32 queries); for dense non-causal calls at D = 128, two adjacent blocks (8
+// waves, one workgroup per CU) that share every staged K/V block, over four
+// LDS stages.  Scores are built transposed, S^T = K * Q^T, on 32x32 matrix-
 // core tiles: every lane then holds one query and 16 keys of each 32-key tile,
 // so the dequantization factor is one scalar per lane and tile (per-token Q
 // scale times the scale of the lane's 16-key K group) and the row maximum of
@@ -398,10 +398,11 @@ constexpr int kPipeMaxBlocks = 96;
 // QPW = 2: 8-wave workgroups over two adjacent query blocks (waves 4-7 the
 // second), each K/V block copied once for both (the first block's waves copy
 // K, the second's V); the two waves of a SIMD then come from one workgroup.
+// Only with the pipelined key loop (four LDS stages).
 template <int D, int BITS, bool CAUSAL, bool SPLIT, bool PIPE, int QPW = 1>
 __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d, float ks, void* __restrict__ o,
                                                                 int out_dtype, SplitParts sp) {
-  static_assert(QPW == 1 || (!CAUSAL && !SPLIT && !PIPE), "two query blocks per workgroup: dense non-causal");
+  static_assert(QPW == 1 || (!CAUSAL && !SPLIT && PIPE), "two query blocks per workgroup: dense non-causal, pipelined");
   constexpr int ROWB = QKCfg<D, BITS>::ROWB;
   constexpr int NDT = D / 32;
   // K/V staging: two LDS stages of one 128-key block each (double buffer),
@@ -412,14 +413,17 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
   __shared__ __align__(16) uint8_t sK0[KSLOT], sK1[KSLOT];
   __shared__ __align__(16) uint8_t sV0[D * kBK], sV1[D * kBK];
   __shared__ float sDS0[QPW * kBK], sDS1[QPW * kBK];
-  // a third stage (two query blocks per workgroup): block t+2 is copied while block t is computed
-  __shared__ __align__(16) uint8_t sK2[QPW == 2 ? KSLOT : 16], sV2[QPW == 2 ? D * kBK : 16];
-  __shared__ float sDS2[QPW == 2 ? QPW * kBK : 4], sKS2[QPW == 2 ? kBK / kKGroup : 4];
-  // raw compensation rows (both query blocks) and K scales (64 lanes, the 8
-  // scales repeated) of each stage, copied straight into LDS
-  __shared__ __align__(16) float sRD0[QPW == 2 ? QPW * kBK : 4], sRD1[QPW == 2 ? QPW * kBK : 4],
-      sRD2[QPW == 2 ? QPW * kBK : 4];
-  __shared__ __align__(16) float sRK0[QPW == 2 ? 64 : 4], sRK1[QPW == 2 ? 64 : 4], sRK2[QPW == 2 ? 64 : 4];
+  // Two query blocks per workgroup: four stages (block t+2 is copied while
+  // block t is computed and block t-1's V is still read); the raw
+  // compensation rows (both query blocks) and K scales (64 lanes, the 8
+  // scales repeated) of each stage are copied straight into LDS.
+  constexpr bool S4 = QPW == 2;
+  __shared__ __align__(16) uint8_t sK2[S4 ? KSLOT : 16], sV2[S4 ? D * kBK : 16];
+  __shared__ __align__(16) uint8_t sK3[S4 ? KSLOT : 16], sV3[S4 ? D * kBK : 16];
+  __shared__ float sDS2[S4 ? QPW * kBK : 4], sDS3[S4 ? QPW * kBK : 4];
+  __shared__ __align__(16) float sRD0[S4 ? QPW * kBK : 4], sRD1[S4 ? QPW * kBK : 4], sRD2[S4 ? QPW * kBK : 4],
+      sRD3[S4 ? QPW * kBK : 4];
+  __shared__ __align__(16) float sRK0[S4 ? 64 : 4], sRK1[S4 ? 64 : 4], sRK2[S4 ? 64 : 4], sRK3[S4 ? 64 : 4];
   __shared__ float sKS0[kBK / kKGroup], sKS1[kBK / kKGroup];
   __shared__ float sVS[D], sVM[D];   // V scales and means of the head, for the epilogue
   auto bK = [&](int i) { return i == 0 ? sK0 : sK1; };
@@ -513,91 +517,98 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
   __syncthreads();
 
   if constexpr (QPW == 2) {
-    // Three LDS stages: iteration t copies block t+2 (K codes, V bytes, the
-    // raw compensation rows and K scales, all straight into LDS) and computes
-    // block t; its wait at the end covers block t+1 only.  Unrolled by three
-    // so that every stage is a named array in every step: the compiler then
-    // tells the stage being read from the ones being filled and adds no wait
-    // of its own for the copies in flight.
-    constexpr int KCH = kBK * ROWB / 16 / 256, VCH = D * kBK / 16 / 256;   // copies per wave and block
-    static_assert(KCH <= VCH && VCH * 4096 <= KSLOT, "copy rounds of K and V");
-    auto issue_kv = [&](int t, auto slotc) {   // K codes (first block's waves) or V bytes (second's) of block t
-      constexpr int sl = decltype(slotc)::value;
-      if (half == 0) {
-        // VCH rounds of K as well (FP6 codes: the last round reads the start
-        // of the next block, or zeros past the head), so that every wave
-        // issues the same copies per block and its waits count them exactly
-        stage_rounds<VCH>(sl == 0 ? sK0 : (sl == 1 ? sK1 : sK2), rk, (uint32_t)t * (kBK * ROWB), wave, koff);
-      } else {
-        stage_rounds<VCH>(sl == 0 ? sV0 : (sl == 1 ? sV1 : sV2), rv, (uint32_t)t * (D * kBK), wave, voff);
-      }
+    // Two query blocks, pipelined over four LDS stages.  Step t copies block
+    // t+2 (K codes by the first block's waves, V bytes by the second's, the
+    // raw compensation rows and K scales by all, straight into LDS), computes
+    // block t's S^T tiles, rescales O by block t-1's alpha and runs block t's
+    // softmax with block t-1's P~V products spread through it (as in the
+    // pipelined loop below); its wait at the end covers block t+1 only.  The
+    // loop is unrolled by four so that every stage is a named array in every
+    // step: the compiler then tells the stages being read from the ones being
+    // filled and adds no wait of its own for the copies in flight (with a
+    // stage chosen at run time it waits for every copy before the first
+    // read).  K is copied in as many 4 KB rounds as V (the 12 KB FP6 block:
+    // the extra round reads the start of the next block, or zeros past the
+    // head), so every wave issues the same copies per step and the waits
+    // count them exactly; nothing is loaded into registers across a step.
+    constexpr int VCH = D * kBK / 16 / 256;   // copy rounds per wave and block
+    static_assert(VCH * 4096 <= KSLOT && kBK * ROWB <= VCH * 4096, "copy rounds of K and V");
+    auto K_ = [&](auto c) -> uint8_t* { constexpr int x = decltype(c)::value; return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sK2 : sK3; };
+    auto V_ = [&](auto c) -> uint8_t* { constexpr int x = decltype(c)::value; return x == 0 ? sV0 : x == 1 ? sV1 : x == 2 ? sV2 : sV3; };
+    auto DS_ = [&](auto c) -> float* { constexpr int x = decltype(c)::value; return x == 0 ? sDS0 : x == 1 ? sDS1 : x == 2 ? sDS2 : sDS3; };
+    auto RD_ = [&](auto c) -> float* { constexpr int x = decltype(c)::value; return x == 0 ? sRD0 : x == 1 ? sRD1 : x == 2 ? sRD2 : sRD3; };
+    auto RK_ = [&](auto c) -> float* { constexpr int x = decltype(c)::value; return x == 0 ? sRK0 : x == 1 ? sRK1 : x == 2 ? sRK2 : sRK3; };
+    auto issue_kv = [&](int t, auto c) {
+      if (half == 0) stage_rounds<VCH>(K_(c), rk, (uint32_t)t * (kBK * ROWB), wave, koff);
+      else stage_rounds<VCH>(V_(c), rv, (uint32_t)t * (D * kBK), wave, voff);
     };
-    // raw compensation row of this wave's query block (two dword rounds of 64
-    // lanes: every wave of the block copies the whole row, the same bytes to
-    // the same place) and the K scales (lane l: scale l mod 8)
     const __amdgpu_buffer_rsrc_t rd = head_rsrc(dsrow, (uint32_t)d.NPk * 4);
     const __amdgpu_buffer_rsrc_t rks = head_rsrc(kscl, (uint32_t)d.NPk / kKGroup * 4);
-    auto issue_sc = [&](int t, auto slotc) {
-      constexpr int sl = decltype(slotc)::value;
-      float* rdd = (sl == 0 ? sRD0 : (sl == 1 ? sRD1 : sRD2)) + half * kBK;
-      float* rkd = sl == 0 ? sRK0 : (sl == 1 ? sRK1 : sRK2);
+    auto issue_sc = [&](int t, auto c) {
+      float* rdd = RD_(c) + half * kBK;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)rdd, 4, 4u * lane, (uint32_t)t * kBK * 4, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr_t)(rdd + 64), 4, 4u * lane, (uint32_t)t * kBK * 4 + 256, 0,
                                                0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)rkd, 4, 4u * (lane & 7),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)RK_(c), 4, 4u * (lane & 7),
                                                (uint32_t)t * (kBK / kKGroup) * 4, 0, 0);
     };
-    auto publish3 = [&](auto slotc) {   // compensation row times the log2-domain scale
-      constexpr int sl = decltype(slotc)::value;
-      float* dsd = sl == 0 ? sDS0 : (sl == 1 ? sDS1 : sDS2);
-      const float* rdd = sl == 0 ? sRD0 : (sl == 1 ? sRD1 : sRD2);
-      if (htid < kBK) dsd[half * kBK + htid] = rdd[half * kBK + htid] * ks;
+    auto publish = [&](auto c) {
+      if (htid < kBK) DS_(c)[half * kBK + htid] = RD_(c)[half * kBK + htid] * ks;
     };
-    auto step = [&](int t, auto c, auto n1, auto n2) {
-      constexpr int sc = decltype(c)::value;
-      const uint8_t* cK = sc == 0 ? sK0 : (sc == 1 ? sK1 : sK2);
-      const uint8_t* cV = sc == 0 ? sV0 : (sc == 1 ? sV1 : sV2);
-      const float* cDS = (sc == 0 ? sDS0 : (sc == 1 ? sDS1 : sDS2)) + half * kBK;
-      const float* cKS = sc == 0 ? sRK0 : (sc == 1 ? sRK1 : sRK2);
-      // unconditional: past the range the last block is copied again into a
-      // free stage, so every wave issues the same loads in every step
+    v8i P8p[2] = {};
+    float alpha_p = 1.0f;
+    auto step = [&](int t, auto c, auto n1, auto n2, auto pv) {
       issue_kv(min(t + 2, te - 1), n2);
       issue_sc(min(t + 2, te - 1), n2);
-      const bool need_mask = ragged && t == nkb - 1;   // (non-causal)
+      const bool need_mask = ragged && t == nkb - 1;
       v16f S[4];
-      qk_part<D, BITS>(S, qop, cK, n, h);
+      qk_part<D, BITS>(S, qop, K_(c), n, h);
+      rescale<D, CAUSAL>(as, alpha_p);
       v8i P8[2];
-      float alpha;
-      softmax_part<D, CAUSAL, SPLIT, false>(as, S, cDS, cKS, dq, ks, t, klim, h, nk, need_mask, P8, alpha, nullptr,
-                                            nullptr, n);
-      row_sum<D, CAUSAL>(as, P8, alpha);
-      rescale<D, CAUSAL>(as, alpha);
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) {
-        pv_mfma<D, CAUSAL>(as, P8, cV, n, h, dt, 0);
-        pv_mfma<D, CAUSAL>(as, P8, cV, n, h, dt, 1);
-      }
-      // block t+1 has landed (this wave's copies and loads; block t+2's
-      // copies, issued last, may still be in flight)
+      // block t-1's V stage (before the first block: stage 3, zeroed, with P8p = 0)
+      const uint8_t* cVp = V_(pv);
+      softmax_part<D, CAUSAL, SPLIT, true>(as, S, DS_(c) + half * kBK, RK_(c), dq, ks, t, klim, h, nk, need_mask, P8,
+                                           alpha_p, P8p, cVp, n);
+      row_sum<D, CAUSAL>(as, P8, alpha_p);
+      P8p[0] = P8[0];
+      P8p[1] = P8[1];
       wait_vmcnt<VCH + 3>();
-      publish3(n1);
+      publish(n1);
       lds_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     issue_kv(min(tb + 1, te - 1), I1{});
     issue_sc(min(tb + 1, te - 1), I1{});
-    // block tb's scales: the common prologue staged them in sKS0; copy them to
-    // the raw stage the key loop reads (lanes 0-7 of each wave, same values)
     if (lane < kBK / kKGroup) sRK0[lane] = sKS0[lane];
+    // the first step's "previous block" products read stage 3 with P8p = 0:
+    // zero bytes there, so that they add exactly zero
+#pragma unroll
+    for (int i = 0; i < D * kBK / 16 / 512; i++) *(v4i*)(sV3 + 16 * (tid + 512 * i)) = v4i{0, 0, 0, 0};
     lds_barrier();
-    for (int t = tb; t < te; t += 3) {
-      step(t, I0{}, I1{}, I2{});
+    int tl = tb;   // the last block
+    for (int t = tb; t < te; t += 4) {
+      tl = t;
+      step(t, I0{}, I1{}, I2{}, I3{});
       if (t + 1 >= te) break;
-      step(t + 1, I1{}, I2{}, I0{});
+      tl = t + 1;
+      step(t + 1, I1{}, I2{}, I3{}, I0{});
       if (t + 2 >= te) break;
-      step(t + 2, I2{}, I0{}, I1{});
+      tl = t + 2;
+      step(t + 2, I2{}, I3{}, I0{}, I1{});
+      if (t + 3 >= te) break;
+      tl = t + 3;
+      step(t + 3, I3{}, I0{}, I1{}, I2{});
+    }
+    // the last block's P~V (its V stage is (tl - tb) mod 4)
+    rescale<D, CAUSAL>(as, alpha_p);
+    {
+      const int sl = (tl - tb) & 3;
+      const uint8_t* cVl = sl == 0 ? sV0 : sl == 1 ? sV1 : sl == 2 ? sV2 : sV3;
+#pragma unroll
+      for (int j = 0; j < 2 * NDT; j++) pv_mfma<D, CAUSAL>(as, P8p, cVl, n, h, j % NDT, j / NDT);
     }
     wait_vmcnt<0>();   // no copy into LDS outlives the workgroup
   } else if constexpr (!PIPE) {
@@ -870,15 +881,18 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   const int mean_blocks = SPLIT ? sp.split_blocks : (causal ? (d.NQBk + 1) / 2 : d.NQBk);
   bool launched = false;
   // Dense non-causal D = 128 with an even number of query blocks: two query
-  // blocks per workgroup (measured against one, bit-identical, builds
-  // interleaved: N 16384 INT4 +1.6%, INT8 +4.3%; N 32768 +0.4%, +3.7%;
-  // against the pipelined loop: DiT +0.7-1.8%, +7%; N 8192 +2.7-4.4%, +7-8%).
+  // blocks per workgroup, pipelined (measured, bit-identical, builds
+  // interleaved; first with three stages and no pipelining against one block
+  // per workgroup: N 16384 INT4 +1.6%, INT8 +4.3%; N 32768 +0.4%, +3.7%;
+  // against the one-block pipelined loop: DiT +0.7-1.8%, +7%; N 8192
+  // +2.7-4.4%, +7-8%; then the four-stage pipelined form against that:
+  // INT4 +1.2-2.4% on all four, INT8 within 0.5%).
   // Causal ranges keep one block per workgroup: a two-block form (the first
   // block's waves masked through the second's extra key block, pairs
   // heaviest first) measured 1% slower on N 16384 and 3% on N 32768.
   if constexpr (D == 128 && !SPLIT) {
     if (!causal && !d.cu && d.NQB % 2 == 0) {
-      hipLaunchKernelGGL((attn_kernel<D, BITS, false, false, false, 2>), dim3(d.NQB / 2 * d.BH()), dim3(512), 0, s, b,
+      hipLaunchKernelGGL((attn_kernel<D, BITS, false, false, true, 2>), dim3(d.NQB / 2 * d.BH()), dim3(512), 0, s, b,
                          d, ks, o, out_dtype, sp);
       launched = true;
     }
