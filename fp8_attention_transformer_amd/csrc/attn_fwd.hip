@@ -887,9 +887,10 @@ hipError_t attn_impl(const Bufs& b, const Dims& d, int causal, float ks, void* o
   // against the one-block pipelined loop: DiT +0.7-1.8%, +7%; N 8192
   // +2.7-4.4%, +7-8%; then the four-stage pipelined form against that:
   // INT4 +1.2-2.4% on all four, INT8 within 0.5%).
-  // Causal ranges keep one block per workgroup: a two-block form (the first
-  // block's waves masked through the second's extra key block, pairs
-  // heaviest first) measured 1% slower on N 16384 and 3% on N 32768.
+  // Causal ranges keep one block per workgroup: the two-block form (the
+  // first block's waves masked through the second's extra key block, pairs
+  // heaviest first) measured 2-3% slower on N 8192-32768 and 16-18% on LLM
+  // prefill (B4 H32 N4096), where it replaces the heavy/light pairing.
   if constexpr (D == 128 && !SPLIT) {
     if (!causal && !d.cu && d.NQB % 2 == 0) {
       hipLaunchKernelGGL((attn_kernel<D, BITS, false, false, true, 2>), dim3(d.NQB / 2 * d.BH()), dim3(512), 0, s, b,
