@@ -277,9 +277,17 @@ __device__ __forceinline__ void pv_quarter(AttnState<D, CAUSAL>& as, const v8i* 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The softmax of block t.  nk: valid keys of the head; klim: the last key
-// this lane's query may see (causal); need_mask: some key of block t is
-// masked for some query of the workgroup (wave-uniform).  PIPE (the
+// Keys past the head's last key are masked by their compensation entry in LDS
+// (-inf, so fma(S, c, -inf) = -inf), with no branch and no per-key test in
+// the loop.  At D = 64 the loop also keeps a branch that masks them (the same
+// -inf): without the branch the scheduler spreads the work and takes the
+// kernel past 168 registers, costing it its third wave per SIMD.
+template <int D>
+constexpr bool kTailBranch = D == 64;
+
+// The softmax of block t.  klim: the last key this lane's query may see
+// (causal); need_mask: some key of block t is masked for some query of the
+// workgroup (wave-uniform): causally, or at D = 64 past the last key.  PIPE (the
 // pipelined key loop): P8p and cVp are the previous block's P~ and V slot:
 // its 2*D/32 P~V products (which accumulate
 // into O, already rescaled by that block's alpha) are spread over this
@@ -301,11 +309,11 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
       const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
       s2[T][r] = __builtin_fmaf(S[T][r], c, cDS[key]);
     }
-    if (need_mask) {
+    if ((CAUSAL || kTailBranch<D>) && need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const int key = t * kBK + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool bad = (key >= nk) || (CAUSAL && key > klim);
+        const bool bad = (kTailBranch<D> && key >= nk) || (CAUSAL && key > klim);
         if (bad) s2[T][r] = -__builtin_inff();
       }
     }
@@ -347,13 +355,23 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
 // 0x38) against P~ gives, in every accumulator row of the lane's query, the
 // sum over the block's 128 keys (each value exact; as in the P~V products,
 // values 2^13 below the largest of their 8-key group drop out of its sum).
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void row_sum(AttnState<D, CAUSAL>& as, const v8i* P8, float alpha) {
+__device__ __forceinline__ v16f row_sum_mfma(const v8i* P8) {
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
   v16f rs = {};
   rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8[0], rs, 0, 0, 0, 0, 0, 0);
   rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, P8[1], rs, 0, 0, 0, 0, 0, 0);
+  return rs;
+}
+
+// The update itself, placed after the code that follows the products (the
+// next block's copies, the compensation row, the barrier): every register of
+// the accumulator stays allocated until then, so no vector instruction in
+// between writes one of them while the matrix core still does (which would
+// cost a wait of the product's full duration).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void row_sum_late(AttnState<D, CAUSAL>& as, const v16f& rs, float alpha) {
   as.l = alpha * as.l + rs[0];
+  asm volatile("" ::"v"(rs));
 }
 
 // O = alpha * O (the running buffer, once the previous block's products are
@@ -478,8 +496,10 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
     ds_reg = dsrow[t * kBK + (htid & (kBK - 1))];
     ks_reg = kscl[t * (kBK / kKGroup) + (htid & (kBK / kKGroup - 1))];
   };
-  auto publish = [&](int slot) {   // compensation row and K scales of the block -> LDS
-    if (htid < kBK) bDS(slot)[half * kBK + htid] = ds_reg * ks;
+  // compensation row (-inf past the head's last key: those keys are masked)
+  // and K scales of block t -> LDS
+  auto publish = [&](int slot, int t) {
+    if (htid < kBK) bDS(slot)[half * kBK + htid] = t * kBK + htid < nk ? ds_reg * ks : -__builtin_inff();
     if (tid < kBK / kKGroup) bKS(slot)[tid] = ks_reg;
   };
   auto issue_v = [&](int t, int slot) {
@@ -509,7 +529,7 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
   as.l = 0.0f;
 
   wait_vmcnt<0>();
-  publish(0);
+  publish(0, tb);
   if (tid < D) {
     sVS[tid] = vs_reg;
     sVM[tid] = vm_reg;
@@ -552,29 +572,30 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (lds_ptr_t)RK_(c), 4, 4u * (lane & 7),
                                                (uint32_t)t * (kBK / kKGroup) * 4, 0, 0);
     };
-    auto publish = [&](auto c) {
-      if (htid < kBK) DS_(c)[half * kBK + htid] = RD_(c)[half * kBK + htid] * ks;
+    auto publish = [&](auto c, int t) {
+      if (htid < kBK)
+        DS_(c)[half * kBK + htid] = t * kBK + htid < nk ? RD_(c)[half * kBK + htid] * ks : -__builtin_inff();
     };
     v8i P8p[2] = {};
     float alpha_p = 1.0f;
     auto step = [&](int t, auto c, auto n1, auto n2, auto pv) {
       issue_kv(min(t + 2, te - 1), n2);
       issue_sc(min(t + 2, te - 1), n2);
-      const bool need_mask = ragged && t == nkb - 1;
       v16f S[4];
       qk_part<D, BITS>(S, qop, K_(c), n, h);
       rescale<D, CAUSAL>(as, alpha_p);
       v8i P8[2];
       // block t-1's V stage (before the first block: stage 3, zeroed, with P8p = 0)
       const uint8_t* cVp = V_(pv);
-      softmax_part<D, CAUSAL, SPLIT, true>(as, S, DS_(c) + half * kBK, RK_(c), dq, ks, t, klim, h, nk, need_mask, P8,
+      softmax_part<D, CAUSAL, SPLIT, true>(as, S, DS_(c) + half * kBK, RK_(c), dq, ks, t, klim, h, nk, false, P8,
                                            alpha_p, P8p, cVp, n);
-      row_sum<D, CAUSAL>(as, P8, alpha_p);
+      const v16f rs = row_sum_mfma(P8);
       P8p[0] = P8[0];
       P8p[1] = P8[1];
       wait_vmcnt<VCH + 3>();
-      publish(n1);
+      publish(n1, min(t + 1, te - 1));
       lds_barrier();
+      row_sum_late<D, CAUSAL>(as, rs, alpha_p);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -621,14 +642,14 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
         issue_k(t + 1, slot ^ 1);
         issue_v(t + 1, slot ^ 1);
       }
-      const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
+      const bool need_mask = (CAUSAL && t >= tmask) || (kTailBranch<D> && ragged && t == nkb - 1);
       v16f S[4];
       qk_part<D, BITS>(S, qop, bK(slot), n, h);
       v8i P8[2];
       float alpha;
       softmax_part<D, CAUSAL, SPLIT, false>(as, S, bDS(slot) + half * kBK, bKS(slot), dq, ks, t, klim, h, nk, need_mask,
                                             P8, alpha, nullptr, nullptr, n);
-      row_sum<D, CAUSAL>(as, P8, alpha);
+      const v16f rs = row_sum_mfma(P8);
       rescale<D, CAUSAL>(as, alpha);
 #pragma unroll
       for (int dt = 0; dt < NDT; dt++) {
@@ -637,8 +658,9 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       }
       if (ahead) {
         wait_vmcnt<0>();   // block t+1 has landed (this wave's copies)
-        publish(slot ^ 1);
+        publish(slot ^ 1, t + 1);
       }
+      row_sum_late<D, CAUSAL>(as, rs, alpha);
       __syncthreads();
     }
   } else {
@@ -661,18 +683,19 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       v16f S[4];
       qk_part<D, BITS>(S, qop, bK(slot), n, h);
       rescale<D, CAUSAL>(as, alpha_p);
-      const bool need_mask = (CAUSAL && t >= tmask) || (ragged && t == nkb - 1);
+      const bool need_mask = (CAUSAL && t >= tmask) || (kTailBranch<D> && ragged && t == nkb - 1);
       v8i P8[2];
       // the previous block's V slot; in the first iteration any valid slot (its
       // products with P8p = 0 add zero)
       const uint8_t* cVp = bV(t > tb ? slot ^ 1 : 0);
       softmax_part<D, CAUSAL, SPLIT, true>(as, S, bDS(slot), bKS(slot), dq, ks, t, klim, h, nk, need_mask, P8, alpha_p, P8p,
                                        cVp, n);
-      row_sum<D, CAUSAL>(as, P8, alpha_p);
+      const v16f rs = row_sum_mfma(P8);
       P8p[0] = P8[0];
       P8p[1] = P8[1];
       wait_vmcnt<0>();   // K codes of block t+1 and V bytes of block t have landed (this wave's copies)
-      if (ahead) publish(slot ^ 1);
+      if (ahead) publish(slot ^ 1, t + 1);
+      row_sum_late<D, CAUSAL>(as, rs, alpha_p);
     }
     // the last block's P~V
     rescale<D, CAUSAL>(as, alpha_p);
