@@ -277,6 +277,19 @@ __device__ __forceinline__ void pv_quarter(AttnState<D, CAUSAL>& as, const v8i* 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// O = alpha * O (the running buffer, once the previous block's products are
+// in it).  Skipped when no running maximum of the wave moved (alpha = 1 in
+// every lane, and O * 1 = O): on long key ranges the maxima settle and most
+// blocks need no rescale.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void rescale(AttnState<D, CAUSAL>& as, float alpha) {
+  if (!__any(alpha != 1.0f)) return;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; dt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
+}
+
 // Keys past the head's last key are masked by their compensation entry in LDS
 // (-inf, so fma(S, c, -inf) = -inf), with no branch and no per-key test in
 // the loop.  At D = 64 the loop also keeps a branch that masks them (the same
@@ -328,6 +341,11 @@ __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16
     tmax[T] = fmaxf(fmaxf(c0, s2[T][7]), fmaxf(c1, s2[T][15]));
   }
   const float bmax = pair_max(fmaxf(fmaxf(fmaxf(tmax[0], tmax[1]), tmax[2]), tmax[3]));
+  // Pipelined: O = alpha(t-1) * O before block t-1's products below.  Here, not
+  // between the S^T products and the dequantization: its wave-uniform branch
+  // would end the basic block there and keep the scheduler from starting the
+  // dequantization and maxima of the first tiles under the later products.
+  if constexpr (PIPE) rescale<D, CAUSAL>(as, alpha);
   const float mnew = fmaxf(as.m, bmax);
   // Split key ranges: a query may see no key of a range yet (its running max
   // stays -inf); referencing 0 then keeps alpha, p' and the state at 0.
@@ -372,19 +390,6 @@ template <int D, bool CAUSAL>
 __device__ __forceinline__ void row_sum_late(AttnState<D, CAUSAL>& as, const v16f& rs, float alpha) {
   as.l = alpha * as.l + rs[0];
   asm volatile("" ::"v"(rs));
-}
-
-// O = alpha * O (the running buffer, once the previous block's products are
-// in it).  Skipped when no running maximum of the wave moved (alpha = 1 in
-// every lane, and O * 1 = O): on long key ranges the maxima settle and most
-// blocks need no rescale.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void rescale(AttnState<D, CAUSAL>& as, float alpha) {
-  if (!__any(alpha != 1.0f)) return;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; dt++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) as.O[dt][r] = as.O[dt][r] * alpha;
 }
 
 // Two outputs as one packed pair of 16-bit values, each rounded to nearest
@@ -583,7 +588,6 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       issue_sc(min(t + 2, te - 1), n2);
       v16f S[4];
       qk_part<D, BITS>(S, qop, K_(c), n, h);
-      rescale<D, CAUSAL>(as, alpha_p);
       v8i P8[2];
       // block t-1's V stage (before the first block: stage 3, zeroed, with P8p = 0)
       const uint8_t* cVp = V_(pv);
@@ -682,7 +686,6 @@ __global__ void __launch_bounds__(256 * QPW, 2 / QPW) attn_kernel(Bufs b, Dims d
       if (t > tb) stage_v_async<D>(bV(slot), rv, t, wave, voff);
       v16f S[4];
       qk_part<D, BITS>(S, qop, bK(slot), n, h);
-      rescale<D, CAUSAL>(as, alpha_p);
       const bool need_mask = (CAUSAL && t >= tmask) || (kTailBranch<D> && ragged && t == nkb - 1);
       v8i P8[2];
       // the previous block's V slot; in the first iteration any valid slot (its
