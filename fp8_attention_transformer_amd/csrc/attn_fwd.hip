@@ -301,12 +301,13 @@ constexpr bool kTailBranch = D == 64;
 // The softmax of block t.  klim: the last key this lane's query may see
 // (causal); need_mask: some key of block t is masked for some query of the
 // workgroup (wave-uniform): causally, or at D = 64 past the last key.  PIPE (the
-// pipelined key loop): P8p and cVp are the previous block's P~ and V slot:
-// its 2*D/32 P~V products (which accumulate
-// into O, already rescaled by that block's alpha) are spread over this
-// block's exponentials, so the matrix core works on them while the vector
-// unit works here.  For the first block of a range P8p is zero (the products
-// add exactly zero).
+// pipelined key loop): P8p and cVp are the previous block's P~ and V slot,
+// and `alpha` holds that block's alpha on entry: O is rescaled by it once
+// this block's maximum is known, then the previous block's 2*D/32 P~V
+// products (accumulated into O) are spread over this block's exponentials,
+// so the matrix core works on them while the vector unit works here; `alpha`
+// leaves with this block's alpha.  For the first block of a range P8p is zero
+// (the products add exactly zero).
 template <int D, bool CAUSAL, bool SPLIT, bool PIPE>
 __device__ __forceinline__ void softmax_part(AttnState<D, CAUSAL>& as, const v16f* S, const float* cDS,
                                              const float* cKS, float dq, float ks, int t, int klim, int h, int nk,
