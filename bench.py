@@ -96,6 +96,20 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+def measured_counters(workload: str):
+    """The fused kernel's hardware-counter readings (L2 hit rate, VALU and
+    matrix-core busy fractions, their overlap, wave waits) from the same
+    committed record, under the same conditions as measured_traffic."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("counters")
+
+
 def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool = False):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the prepass of head 0 and the mirror-mode attention of a set of
@@ -301,6 +315,7 @@ def run(w, steps: int, warmup: int, cpu: bool, cpu_seconds: float, qk_bits: int 
             "kernel": "attn_kernel",
             "kernel_us": round(attn_ms * 1e3, 2),
         },
+        "counters": measured_counters(w.name),
         "breakdown": {"prepass_us": round(pre_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                       "sequential_step_us": round((pre_ms + attn_ms) * 1e3, 2),
                       "e2e_frac_of_peak": round(value / PEAK_TOPS, 4)},

@@ -354,3 +354,24 @@ def test_adaptive_width_validation():
     # the dense forward accepts 0 as far as argument checks go: a bad sm_scale is still caught first
     assert _attn(qk_bits=0, sm_scale=0.0) == sage.ERR_INVALID
     assert _attn(qk_bits=0, ws_bytes=100) == sage.ERR_WORKSPACE
+
+
+def test_bench_counter_record_matches_source():
+    """The committed traffic/counter record of the fused kernel is keyed to the
+    current kernel source (bench.py reports it only then), and its fields are
+    consistent: HBM bytes from the FETCH/WRITE counts and their copy factors,
+    fractions within [0, 1]."""
+    import json
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert t["source_hash"] == bench.kernel_source_hash()
+    cal = t["copy_calibration"]
+    want = int(t["fetch_kib_counted"] * 1024 * cal["fetch_factor"] + t["write_kib_counted"] * 1024 * cal["write_factor"])
+    assert t["bytes_per_launch"] == want
+    assert bench.measured_traffic(t["workload"]) == want
+    c = bench.measured_counters(t["workload"])
+    assert c is not None
+    for k in ("l2_hit_rate", "valu_busy_frac", "mfma_busy_frac", "mfma_overlapped_with_valu_frac", "wave_wait_frac"):
+        assert 0.0 <= c[k] <= 1.0, k
+    assert bench.measured_counters("no_such_workload") is None
