@@ -83,9 +83,9 @@ def device_warmup(fn, ms: float) -> int:
     return n
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter summary, if it was taken on this workload and this kernel source."""
+def counter_record(workload: str):
+    """The committed rocprofv3 record of the fused kernel, if it was taken on
+    this workload and this kernel source (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -93,21 +93,22 @@ def measured_traffic(workload: str):
         return None
     if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel (FETCH_SIZE and WRITE_SIZE
+    scaled by a plain copy's readings), from the committed record."""
+    t = counter_record(workload)
+    return t.get("bytes_per_launch") if t else None
 
 
 def measured_counters(workload: str):
     """The fused kernel's hardware-counter readings (L2 hit rate, VALU and
-    matrix-core busy fractions, their overlap, wave waits) from the same
-    committed record, under the same conditions as measured_traffic."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != kernel_source_hash() or t.get("workload") != workload:
-        return None
-    return t.get("counters")
+    matrix-core busy fractions, their overlap, wave waits), from the same
+    record."""
+    t = counter_record(workload)
+    return t.get("counters") if t else None
 
 
 def cpu_baseline_leg(w, out_gpu, target_s: float, qk_bits: int, smooth_v: bool = False):
