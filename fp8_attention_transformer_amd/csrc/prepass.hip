@@ -731,6 +731,10 @@ __global__ void __launch_bounds__(256) quant_kernel(const uint16_t* __restrict__
 // split into three bf16 pieces (x = x1 + x2 + x3 up to 2^-24 |x|) and the six
 // products x_a*y_b with a + b <= 4 are accumulated in fp32, which reproduces
 // an fp32 dot product to within a few units in the last place.
+// Cache-policy operand of the raw buffer stores: bit 1 marks a store
+// non-temporal (streamed past the caches).
+constexpr int kStoreNT = 2;
+
 template <int IN, int D>
 __global__ void __launch_bounds__(256, 3) delta_s_kernel(const uint16_t* __restrict__ k, Dims d, Bufs b) {
   constexpr int NK = D / 16;   // k-steps of the 32x32x16 bf16 MFMA
@@ -830,11 +834,15 @@ __global__ void __launch_bounds__(256, 3) delta_s_kernel(const uint16_t* __restr
     if (more) {
       // A whole tile: exactly 16 stores, issued after the next tile's copies.
       // The wait below lets those stores stay in flight and holds only for
-      // the copies (the counter retires in issue order).
+      // the copies (the counter retires in issue order).  The compensation
+      // array is written once and read once by the attention kernel: its
+      // stores are non-temporal (cache policy bit 1, "nt"; measured, values
+      // unchanged: headline prepass 145.7 -> 138.1 us, LLM prefill -1.2%,
+      // DiT -1.7%, the attention kernel unchanged).
 #pragma unroll
       for (int r = 0; r < 16; r++) {
         const uint32_t row = (uint32_t)(qt + 8 * (r >> 2) + (r & 3));
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, kStoreNT);
       }
       wait_vmcnt<16>();
       // A bare barrier: the release fence of __syncthreads() would wait for
@@ -849,7 +857,7 @@ __global__ void __launch_bounds__(256, 3) delta_s_kernel(const uint16_t* __restr
         const int q2 = qt + 8 * (r >> 2) + 4 * h + (r & 3);
         if (q2 < nqb) {
           const uint32_t row = (uint32_t)(qt + 8 * (r >> 2) + (r & 3));
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[r]), ro, obase, row * d.NPk * 4, kStoreNT);
         }
       }
     }
